@@ -1,0 +1,84 @@
+/*
+ * oracle.h -- plain, slow, fp64 CPU reference for paged grouped-query attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The HIP library never
+ * links, includes or calls it, and this file shares no code with it.
+ *
+ * All pointers are HOST pointers owned by the caller.  Element data is either
+ * fp32 (dtype ORACLE_F32) or raw bf16 bit patterns (ORACLE_BF16, uint16 per
+ * element); every value is widened exactly to double before any arithmetic.
+ *
+ * Layouts (row-major, innermost last):
+ *   packed K/V        [T, Hkv, d]        T = total tokens, sequences concatenated
+ *   decode Q          [B, Hq, d]         one query token per sequence
+ *   prefill Q         [T, Hq, d]
+ *   KV page pool      [num_blocks, Hkv, block_size, d]   (separate K and V pools)
+ *   block_table       int32 [B, max_blocks_per_seq]      logical page -> physical block
+ *   cu_seqlens        int32 [B+1]                        prefix sums of lengths
+ *
+ * Return value: ORACLE_OK, or ORACLE_EINVAL for a bad argument, or
+ * ORACLE_ERANGE when the data breaks the caller's contract (a block id
+ * outside the pool, a position past the block table, decreasing cu_seqlens).
+ */
+#ifndef PGQA_ORACLE_H
+#define PGQA_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_OK = 0, ORACLE_EINVAL = 1, ORACLE_ERANGE = 2 };
+
+/* Scatter packed K/V of each sequence's new tokens into the page pools.
+ * Token t of sequence b sits at logical position start_pos[b] + (t - cu_seqlens[b]);
+ * position p lives in block block_table[b][p / block_size], slot p % block_size.
+ * Element bytes are copied unchanged. */
+int oracle_paged_kv_write(const void* k, const void* v, const int32_t* cu_seqlens,
+                          const int32_t* start_pos, const int32_t* block_table,
+                          int32_t max_blocks_per_seq, void* k_cache, void* v_cache,
+                          int32_t batch, int32_t num_blocks, int32_t block_size,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t dtype);
+
+/* Inverse of the write: copy positions [0, context_lens[b]) of every sequence
+ * out of the pools into packed [sum(context_lens), Hkv, d] arrays. */
+int oracle_paged_kv_gather(const void* k_cache, const void* v_cache, const int32_t* block_table,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           void* k_out, void* v_out, int32_t batch, int32_t num_blocks,
+                           int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t dtype);
+
+/* Decode: one query token per sequence attends to every cached position
+ * [0, context_lens[b]) of its sequence.  Query head qh reads KV head
+ * qh / (Hq / Hkv).  out is fp64 [B, Hq, d]; a sequence with no context gets 0.
+ * probs (may be NULL) receives the softmax weights, fp64 [B, Hq, probs_stride],
+ * entries past the context left untouched.  num_threads <= 0 uses the default. */
+int oracle_gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, double scale, int32_t dtype, double* out,
+                            double* probs, int32_t probs_stride, int32_t num_threads);
+
+/* Packed variable-length prefill with a block-diagonal (optionally causal) mask.
+ * Row i of sequence s (cu_seqlens[s] <= i < cu_seqlens[s+1]) attends to keys j of
+ * the same sequence with j <= i when causal, else to all of that sequence.
+ * rows (may be NULL) lists the packed row indices to evaluate; NULL means every
+ * row 0..T-1 with num_rows = T.  out is fp64 [num_rows, Hq, d]. */
+int oracle_gqa_varlen_prefill(const void* q, const void* k, const void* v,
+                              const int32_t* cu_seqlens, int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, double scale,
+                              int32_t causal, int32_t dtype, const int32_t* rows,
+                              int32_t num_rows, double* out, int32_t num_threads);
+
+/* Number of OpenMP threads a parallel region would use (for reporting). */
+int oracle_max_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PGQA_ORACLE_H */

@@ -1,0 +1,409 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each ``pin_*`` takes a loaded :class:`oracle.Oracle` and raises (AssertionError or
+the oracle's own error) when the oracle disagrees with what the pages and the
+mathematics fix:
+
+* a library routine: ``torch.nn.functional.scaled_dot_product_attention`` in
+  float64 on dense K/V rebuilt from the packed inputs (never from the pages),
+  with its ``enable_gqa`` head expansion;
+* brute force on tiny inputs: one dense block-diagonal masked softmax over the
+  whole packed batch, in numpy;
+* closed forms: one key -> its value; zero query -> mean of values; constant
+  values; two keys with a hand-derived sigmoid weight; one dominant key;
+* invariants: weights sum to one, GQA equals MHA on repeated KV heads, placement
+  of pages does not change the output, decode equals the last prefill row,
+  batch independence, and the packing example printed on the pages.
+
+The same battery runs against copies of the oracle with a planted mistake
+(see test_oracle_mutants.py); every mistake there must fail at least one pin.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+from pathlib import Path
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import workload as W
+from oracle import ERANGE, EINVAL, OracleError
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+REL = 1e-12   # fp64 agreement between two exact-in-real-arithmetic evaluations
+
+
+def f64(a: np.ndarray) -> np.ndarray:
+    """Exact widening of generator arrays (float32 or bf16 bits) to float64."""
+    if a.dtype == np.uint16:
+        return W.bf16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
+
+
+def close(a, b, rel=REL, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.isfinite(a).all(), f"{what}: non-finite values"
+    scale = max(1.0, float(np.abs(b).max()) if b.size else 1.0)
+    err = float(np.abs(a - b).max()) if a.size else 0.0
+    assert err <= rel * scale, f"{what}: max err {err:.3e} > {rel * scale:.3e}"
+
+
+def fill_pages(orc, case: W.DecodeCase, table=None, num_blocks=None):
+    """Oracle-written page pools for a decode case (NaN sentinel elsewhere)."""
+    table = case.block_table if table is None else table
+    nb = case.num_blocks if num_blocks is None else num_blocks
+    kc = W.nan_pool(nb, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)
+    vc = W.nan_pool(nb, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)
+    orc.paged_kv_write(case.k, case.v, case.cu_ctx, case.start_pos, table, kc, vc)
+    return kc, vc
+
+
+def decode(orc, case: W.DecodeCase, **kw):
+    kc, vc = fill_pages(orc, case)
+    return orc.gqa_paged_decode(case.q, kc, vc, case.block_table, case.context_lens, case.scale, **kw)
+
+
+def sdpa_decode(case: W.DecodeCase) -> np.ndarray:
+    """Library attention of each sequence's single query over its packed K/V."""
+    out = np.zeros((case.batch, case.num_q_heads, case.head_dim))
+    q, k, v = f64(case.q), f64(case.k), f64(case.v)
+    for b in range(case.batch):
+        a, e = int(case.cu_ctx[b]), int(case.cu_ctx[b + 1])
+        if e == a:
+            continue
+        qt = torch.from_numpy(q[b]).unsqueeze(0).unsqueeze(2)             # [1, Hq, 1, d]
+        kt = torch.from_numpy(k[a:e]).permute(1, 0, 2).unsqueeze(0)      # [1, Hkv, n, d]
+        vt = torch.from_numpy(v[a:e]).permute(1, 0, 2).unsqueeze(0)
+        r = F.scaled_dot_product_attention(qt, kt.contiguous(), vt.contiguous(),
+                                           scale=float(case.scale), enable_gqa=True)
+        out[b] = r[0, :, 0].numpy()
+    return out
+
+
+def sdpa_prefill(case: W.PrefillCase, causal: bool) -> np.ndarray:
+    """Library attention run separately on every sequence of a packed batch."""
+    q, k, v = f64(case.q), f64(case.k), f64(case.v)
+    out = np.zeros_like(q)
+    for s in range(case.batch):
+        a, e = int(case.cu_seqlens[s]), int(case.cu_seqlens[s + 1])
+        if e == a:
+            continue
+        qt = torch.from_numpy(q[a:e]).permute(1, 0, 2).unsqueeze(0)
+        kt = torch.from_numpy(k[a:e]).permute(1, 0, 2).unsqueeze(0)
+        vt = torch.from_numpy(v[a:e]).permute(1, 0, 2).unsqueeze(0)
+        r = F.scaled_dot_product_attention(qt.contiguous(), kt.contiguous(), vt.contiguous(),
+                                           is_causal=causal, scale=float(case.scale), enable_gqa=True)
+        out[a:e] = r[0].permute(1, 0, 2).numpy()
+    return out
+
+
+def blockdiag_bruteforce(case: W.PrefillCase, causal: bool) -> np.ndarray:
+    """One dense T x T masked softmax over the whole packed batch (numpy)."""
+    q, k, v = f64(case.q), f64(case.k), f64(case.v)
+    T = case.total_tokens
+    G = case.num_q_heads // case.num_kv_heads
+    seq_of = np.repeat(np.arange(case.batch), case.lengths)
+    allowed = seq_of[:, None] == seq_of[None, :]
+    if causal:
+        allowed &= np.arange(T)[:, None] >= np.arange(T)[None, :]
+    kk = np.repeat(k, G, axis=1)   # [T, Hq, d]: query head qh reads KV head qh // G
+    vv = np.repeat(v, G, axis=1)
+    s = np.einsum("ihd,jhd->hij", q, kk) * float(case.scale)
+    s = np.where(allowed[None], s, -np.inf)
+    s = s - s.max(axis=2, keepdims=True)
+    w = np.exp(s)
+    w = w / w.sum(axis=2, keepdims=True)
+    return np.einsum("hij,jhd->ihd", w, vv)
+
+
+# A small sweep of decode shapes: (lengths, Hq, Hkv, d, bs, dtype, seed)
+DECODE_SWEEP = [
+    ([5, 11], 4, 2, 16, 4, W.F32, 11),
+    ([1, 2, 3, 40], 4, 4, 8, 1, W.F32, 12),
+    ([17, 9], 8, 1, 16, 8, W.BF16, 13),
+    ([6, 33, 12], 6, 3, 8, 2, W.BF16, 14),
+    ([40], 4, 2, 16, 8, W.BF16, 15),
+    ([3, 24, 7, 1], 8, 2, 8, 4, W.F32, 16),
+]
+
+PREFILL_SWEEP = [
+    ([3, 9, 5], 4, 2, 16, W.F32, 21),
+    ([1, 7, 12], 6, 3, 8, W.BF16, 22),
+    ([20], 8, 1, 8, W.BF16, 23),
+    ([4, 4, 10, 2], 4, 4, 16, W.F32, 24),
+]
+
+
+# ---------------------------------------------------------------------------
+# library routine and brute force
+# ---------------------------------------------------------------------------
+
+def pin_decode_matches_library(orc):
+    for lens, hq, hkv, d, bs, dt, seed in DECODE_SWEEP:
+        c = W.make_decode_case(lens, hq, hkv, d, bs, dt, seed)
+        close(decode(orc, c), sdpa_decode(c), what=f"decode {lens} {hq}/{hkv} d{d} bs{bs} {dt}")
+
+
+def pin_prefill_matches_library(orc):
+    for lens, hq, hkv, d, dt, seed in PREFILL_SWEEP:
+        c = W.make_prefill_case(lens, hq, hkv, d, 4, dt, seed)
+        for causal in (True, False):
+            got = orc.gqa_varlen_prefill(c.q, c.k, c.v, c.cu_seqlens, c.scale, causal=causal)
+            close(got, sdpa_prefill(c, causal), what=f"prefill {lens} causal={causal}")
+
+
+def pin_prefill_matches_bruteforce(orc):
+    for lens, hq, hkv, d, dt, seed in PREFILL_SWEEP[:3]:
+        c = W.make_prefill_case(lens, hq, hkv, d, 4, dt, seed)
+        for causal in (True, False):
+            got = orc.gqa_varlen_prefill(c.q, c.k, c.v, c.cu_seqlens, c.scale, causal=causal)
+            close(got, blockdiag_bruteforce(c, causal), what=f"brute force {lens} causal={causal}")
+
+
+def pin_prefill_row_sampling(orc):
+    c = W.make_prefill_case([5, 14, 3], 4, 2, 8, 4, W.BF16, 25)
+    full = orc.gqa_varlen_prefill(c.q, c.k, c.v, c.cu_seqlens, c.scale)
+    rows = np.array([0, 4, 5, 18, 21, 7], dtype=np.int32)
+    part = orc.gqa_varlen_prefill(c.q, c.k, c.v, c.cu_seqlens, c.scale, rows=rows)
+    assert np.array_equal(part, full[rows]), "sampled rows differ from the full evaluation"
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+
+def pin_single_key_returns_its_value(orc):
+    """With one cached token the only weight is 1, so the output is that value exactly."""
+    c = W.make_decode_case([1, 1, 1], 4, 2, 16, 4, W.F32, 31)
+    out = decode(orc, c)
+    G = c.num_q_heads // c.num_kv_heads
+    expect = np.repeat(f64(c.v), G, axis=1)     # [B, Hq, d] since every context is one token
+    assert np.array_equal(out, expect), "one-token context must return the value row exactly"
+
+
+def pin_prefill_first_row_is_value(orc):
+    """Causal row 0 of each sequence sees only its own key, so it equals its value row."""
+    c = W.make_prefill_case([3, 9, 5], 4, 2, 16, 4, W.F32, 32)
+    out = orc.gqa_varlen_prefill(c.q, c.k, c.v, c.cu_seqlens, c.scale, causal=True)
+    G = c.num_q_heads // c.num_kv_heads
+    for a in c.cu_seqlens[:-1]:
+        assert np.array_equal(out[a], np.repeat(f64(c.v[a]), G, axis=0)), f"row {a}"
+
+
+def pin_zero_query_gives_mean(orc):
+    """q = 0 makes every score 0 and every weight 1/n: the output is the mean value."""
+    c = W.make_decode_case([7, 19], 4, 2, 8, 4, W.F32, 33)
+    c.q[...] = 0.0
+    out = decode(orc, c)
+    G = c.num_q_heads // c.num_kv_heads
+    v = f64(c.v)
+    for b in range(c.batch):
+        a, e = c.cu_ctx[b], c.cu_ctx[b + 1]
+        close(out[b], np.repeat(v[a:e].mean(axis=0), G, axis=0), rel=1e-14, what="mean")
+
+
+def pin_constant_values(orc):
+    """If every value row is the same vector, any weighting returns it."""
+    c = W.make_decode_case([9, 4], 8, 2, 8, 4, W.F32, 34)
+    row = np.arange(1, 9, dtype=np.float32) * np.float32(0.5)
+    c.v[...] = row
+    out = decode(orc, c)
+    close(out, np.broadcast_to(row.astype(np.float64), out.shape), rel=1e-14, what="constant")
+
+
+def pin_two_keys_sigmoid(orc):
+    """Two keys: weight of key 0 is 1 / (1 + exp(-(s0 - s1))), worked by hand.
+
+    d = 4, q = (2, 0, 0, 0), k0 = (3, 0, 0, 0), k1 = (0, 1, 0, 0), scale = 1/sqrt(4) = 0.5,
+    so s0 = 0.5 * 6 = 3, s1 = 0, and out = sig(3) v0 + (1 - sig(3)) v1.
+    """
+    c = W.make_decode_case([2], 1, 1, 4, 2, W.F32, 35, scale=0.5)
+    c.q[...] = 0.0
+    c.q[0, 0, 0] = 2.0
+    c.k[...] = 0.0
+    c.k[0, 0, 0] = 3.0
+    c.k[1, 0, 1] = 1.0
+    c.v[0, 0, :] = [1.0, 2.0, 3.0, 4.0]
+    c.v[1, 0, :] = [-1.0, 0.5, 0.0, 8.0]
+    w0 = 1.0 / (1.0 + math.exp(-3.0))
+    expect = w0 * np.array([1.0, 2.0, 3.0, 4.0]) + (1.0 - w0) * np.array([-1.0, 0.5, 0.0, 8.0])
+    out, probs = decode(orc, c, want_probs=True)
+    close(out[0, 0], expect, rel=1e-15, what="two-key output")
+    close(probs[0, 0, :2], [w0, 1.0 - w0], rel=1e-15, what="two-key weights")
+
+
+def pin_dominant_key_large_logits(orc):
+    """One key aligned with a huge query dominates; softmax stays exact for logits ~ 1e3."""
+    c = W.make_decode_case([6], 2, 1, 4, 4, W.F32, 36, scale=0.5)
+    c.q[...] = 0.0
+    c.q[0, :, 0] = 40.0
+    c.k[...] = 0.0
+    c.k[3, 0, 0] = 50.0          # s = 0.5 * 40 * 50 = 1000 for key 3, 0 for the rest
+    out = decode(orc, c)
+    expect = np.repeat(f64(c.v[3]), 2, axis=0)
+    close(out[0], expect, rel=1e-15, what="dominant key")
+
+
+def pin_weights_sum_to_one(orc):
+    for lens, hq, hkv, d, bs, dt, seed in DECODE_SWEEP[:4]:
+        c = W.make_decode_case(lens, hq, hkv, d, bs, dt, seed)
+        _, p = decode(orc, c, want_probs=True)
+        for b, n in enumerate(c.context_lens):
+            s = p[b, :, :n].sum(axis=1)
+            assert np.all(np.abs(s - 1.0) < 1e-12), f"weights sum {s}"
+            assert np.all(p[b, :, :n] >= 0.0)
+
+
+def pin_identical_keys_uniform(orc):
+    """All keys equal -> all scores equal -> uniform weights 1/n."""
+    c = W.make_decode_case([5, 12], 4, 2, 8, 4, W.F32, 37)
+    c.k[...] = c.k[0]
+    _, p = decode(orc, c, want_probs=True)
+    for b, n in enumerate(c.context_lens):
+        close(p[b, :, :n], np.full((4, n), 1.0 / n), rel=1e-14, what="uniform weights")
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+
+def pin_gqa_equals_repeated_mha(orc):
+    """GQA(Hq, Hkv) equals MHA(Hq) when each KV head is repeated for its G query heads."""
+    c = W.make_decode_case([13, 6, 21], 6, 3, 8, 4, W.BF16, 41)
+    G = 2
+    m = W.make_decode_case([13, 6, 21], 6, 6, 8, 4, W.BF16, 41)
+    m.q = c.q
+    m.k = np.repeat(c.k, G, axis=1)
+    m.v = np.repeat(c.v, G, axis=1)
+    m.block_table, m.num_blocks = c.block_table, c.num_blocks
+    assert np.array_equal(decode(orc, c), decode(orc, m)), "GQA differs from repeated-head MHA"
+    p = W.make_prefill_case([5, 8], 6, 3, 8, 4, W.BF16, 42)
+    got = orc.gqa_varlen_prefill(p.q, p.k, p.v, p.cu_seqlens, p.scale)
+    mha = orc.gqa_varlen_prefill(p.q, np.repeat(p.k, G, axis=1), np.repeat(p.v, G, axis=1),
+                                 p.cu_seqlens, p.scale)
+    assert np.array_equal(got, mha), "prefill GQA differs from repeated-head MHA"
+
+
+def pin_placement_invariance(orc):
+    """Another page permutation, a larger pool and extra table columns leave the output bit-identical."""
+    c = W.make_decode_case([9, 30, 4], 4, 2, 8, 4, W.BF16, 43)
+    base = decode(orc, c)
+    rng = np.random.default_rng(99)
+    table, nb = W.place_pages(rng, c.context_lens, c.block_size, pool_factor=3.0, extra_cols=5)
+    kc, vc = fill_pages(orc, c, table=table, num_blocks=nb)
+    moved = orc.gqa_paged_decode(c.q, kc, vc, table, c.context_lens, c.scale)
+    assert np.array_equal(base, moved), "output depends on physical placement"
+
+
+def pin_batch_independence(orc):
+    c = W.make_decode_case([9, 30, 4], 4, 2, 8, 4, W.F32, 44)
+    full = decode(orc, c)
+    for b in range(c.batch):
+        a, e = c.cu_ctx[b], c.cu_ctx[b + 1]
+        one = W.make_decode_case([int(c.context_lens[b])], 4, 2, 8, 4, W.F32, 45)
+        one.q, one.k, one.v = c.q[b:b + 1].copy(), c.k[a:e].copy(), c.v[a:e].copy()
+        assert np.array_equal(decode(orc, one)[0], full[b]), f"sequence {b} depends on its batch"
+
+
+def pin_decode_equals_last_prefill_row(orc):
+    """Decode over pages written from a prefill batch equals each sequence's last causal row."""
+    p = W.make_prefill_case([6, 13, 1], 4, 2, 16, 4, W.BF16, 46)
+    pre = orc.gqa_varlen_prefill(p.q, p.k, p.v, p.cu_seqlens, p.scale, causal=True)
+    kc = W.nan_pool(p.num_blocks, p.num_kv_heads, p.block_size, p.head_dim, p.dtype)
+    vc = W.nan_pool(p.num_blocks, p.num_kv_heads, p.block_size, p.head_dim, p.dtype)
+    orc.paged_kv_write(p.k, p.v, p.cu_seqlens, np.zeros(p.batch, np.int32), p.block_table, kc, vc)
+    last = p.cu_seqlens[1:] - 1
+    dec = orc.gqa_paged_decode(p.q[last], kc, vc, p.block_table, p.lengths, p.scale)
+    close(dec, pre[last], what="decode vs last prefill row")
+
+
+def pin_packing_example(orc):
+    """The pages' packing example: lengths 3, 9, 5 -> 17 packed tokens, no cross-sequence mixing."""
+    g = json.loads((GOLDEN / "packing_3_9_5.json").read_text())
+    p = W.make_prefill_case(g["lengths"], 4, 2, 8, 4, W.F32, 47)
+    assert p.total_tokens == g["total_tokens"]
+    assert p.cu_seqlens.tolist() == g["cu_seqlens"]
+    out = orc.gqa_varlen_prefill(p.q, p.k, p.v, p.cu_seqlens, p.scale, causal=True)
+    assert out.shape[0] == g["total_tokens"]
+    for s in range(p.batch):
+        a, e = g["cu_seqlens"][s], g["cu_seqlens"][s + 1]
+        alone = orc.gqa_varlen_prefill(p.q[a:e], p.k[a:e], p.v[a:e], np.array([0, e - a], np.int32),
+                                       p.scale, causal=True)
+        assert np.array_equal(alone, out[a:e]), f"segment {s} is affected by its neighbours"
+
+
+def pin_noncausal_last_row_equals_causal(orc):
+    """The last row of a sequence sees every key of it under both masks."""
+    p = W.make_prefill_case([4, 11], 4, 2, 8, 4, W.BF16, 48)
+    last = p.cu_seqlens[1:] - 1
+    a = orc.gqa_varlen_prefill(p.q, p.k, p.v, p.cu_seqlens, p.scale, causal=True, rows=last)
+    b = orc.gqa_varlen_prefill(p.q, p.k, p.v, p.cu_seqlens, p.scale, causal=False, rows=last)
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# paged write and gather
+# ---------------------------------------------------------------------------
+
+def pin_write_gather_roundtrip(orc):
+    for lens, hq, hkv, d, bs, dt, seed in DECODE_SWEEP:
+        c = W.make_decode_case(lens, hq, hkv, d, bs, dt, seed)
+        kc, vc = fill_pages(orc, c)
+        k2, v2 = orc.paged_kv_gather(kc, vc, c.block_table, c.context_lens)
+        assert k2.tobytes() == c.k.tobytes() and v2.tobytes() == c.v.tobytes(), "gather(write(K)) != K"
+        # every slot not covered by a valid position keeps the sentinel
+        used = np.zeros((c.num_blocks, c.block_size), dtype=bool)
+        for b, n in enumerate(c.context_lens):
+            for pos in range(int(n)):
+                used[c.block_table[b, pos // bs], pos % bs] = True
+        sentinel = W.nan_pool(1, 1, 1, 1, dt).reshape(-1)[0]
+        kbits = kc.view(np.uint16 if dt == W.BF16 else np.uint32)
+        sbits = np.asarray(sentinel).view(kbits.dtype)
+        assert np.all(kbits.transpose(0, 2, 1, 3)[~used] == sbits), "an unused slot was written"
+        assert not np.any(np.isnan(f64(k2)))
+
+
+def pin_write_chunks_equal_one_write(orc):
+    """Writing tokens in two chunks (second chunk at start_pos = first chunk's length) equals one write."""
+    c = W.make_decode_case([10, 23, 5], 4, 2, 8, 4, W.BF16, 51)
+    kc1, vc1 = fill_pages(orc, c)
+    kc2 = W.nan_pool(c.num_blocks, 2, 4, 8, c.dtype)
+    vc2 = W.nan_pool(c.num_blocks, 2, 4, 8, c.dtype)
+    first = np.array([3, 11, 5], dtype=np.int32)
+    second = c.context_lens - first
+    k1, v1, k2, v2 = [], [], [], []
+    for b in range(c.batch):
+        a = int(c.cu_ctx[b])
+        k1.append(c.k[a:a + first[b]]); v1.append(c.v[a:a + first[b]])
+        k2.append(c.k[a + first[b]:c.cu_ctx[b + 1]]); v2.append(c.v[a + first[b]:c.cu_ctx[b + 1]])
+    orc.paged_kv_write(np.concatenate(k1), np.concatenate(v1), W.cu_from_lengths(first),
+                       np.zeros(3, np.int32), c.block_table, kc2, vc2)
+    orc.paged_kv_write(np.concatenate(k2), np.concatenate(v2), W.cu_from_lengths(second),
+                       first, c.block_table, kc2, vc2)
+    assert kc1.tobytes() == kc2.tobytes() and vc1.tobytes() == vc2.tobytes()
+
+
+def pin_contract_errors(orc):
+    c = W.make_decode_case([5, 11], 4, 2, 16, 4, W.F32, 52)
+    kc, vc = fill_pages(orc, c)
+    bad = c.block_table.copy()
+    bad[1, 2] = c.num_blocks          # outside the pool
+    try:
+        orc.gqa_paged_decode(c.q, kc, vc, bad, c.context_lens, c.scale)
+        raise AssertionError("out-of-pool block id not reported")
+    except OracleError as e:
+        assert str(ERANGE) in str(e)
+    try:
+        orc.gqa_paged_decode(c.q[:, :3], kc, vc, c.block_table, c.context_lens, c.scale)
+        raise AssertionError("Hq % Hkv != 0 not reported")
+    except OracleError as e:
+        assert str(EINVAL) in str(e)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

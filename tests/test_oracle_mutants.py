@@ -1,0 +1,77 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin.
+
+Each mutant is a textual edit of oracle.c compiled into a throw-away library in a
+temporary directory (the committed oracle is never touched).  The edits are the
+plausible slips of this computation: a wrong head mapping, a dropped or doubled
+scale, a dropped normalisation, an off-by-one in the causal range or the context,
+a leak across sequences, a wrong page slot, values swapped for keys, an ignored
+start position, a wrong query row, a float accumulator, a flipped exponent sign,
+a missing max subtraction.  Every edit keeps memory accesses inside the buffers,
+so a mutant can only produce wrong numbers, not crash the test process.
+"""
+
+import shutil
+from pathlib import Path
+
+import pytest
+
+import oracle_pins as P
+from oracle import Oracle
+from oracle.build import build
+
+SRC = Path(__file__).resolve().parent.parent / "oracle"
+
+# (id, text in oracle.c, replacement)
+MUTANTS = [
+    ("interleaved_kv_head", "const int32_t h = qh / group;", "const int32_t h = qh % num_kv_heads;"),
+    ("scale_dropped", "return scale * acc;", "return acc;"),
+    ("scale_squared", "return scale * acc;", "return scale * scale * acc;"),
+    ("no_normalisation", "for (int64_t j = 0; j < n; ++j) p[j] = p[j] / z;", ""),
+    ("no_max_subtraction", "p[j] = exp(s[j] - m);", "p[j] = exp(s[j]);"),
+    ("exp_sign_flipped", "p[j] = exp(s[j] - m);", "p[j] = exp(m - s[j]);"),
+    ("decode_drops_last_token", "const int64_t n = context_lens[b];", "const int64_t n = context_lens[b] - 1;"),
+    ("causal_excludes_diagonal", "const int64_t last = causal ? i :", "const int64_t last = causal ? i - 1 :"),
+    ("cross_sequence_leak", "const int64_t first = cu_seqlens[seq];", "const int64_t first = 0;"),
+    ("decode_slot_shifted", "const int64_t slot = j % block_size;", "const int64_t slot = (j + 1) % block_size;"),
+    ("values_are_keys", "softmax_weighted_sum(s, n, v_cache, voff", "softmax_weighted_sum(s, n, k_cache, voff"),
+    ("write_ignores_start_pos", "const int64_t pos = (int64_t)start_pos[b] + (t - cu_seqlens[b]);",
+     "const int64_t pos = (t - cu_seqlens[b]);"),
+    ("gather_ignores_head", "const int64_t src = page_offset(blk, h, slot,", "const int64_t src = page_offset(blk, 0, slot,"),
+    ("query_of_head_zero", "const int64_t qo = u * head_dim;", "const int64_t qo = (u - qh) * head_dim;"),
+    ("prefill_kv_head_zero", "const int64_t ko = ((first + j) * num_kv_heads + h)",
+     "const int64_t ko = ((first + j) * num_kv_heads + 0)"),
+    ("float_accumulator", "double acc = 0.0;\n    for (int32_t x = 0; x < head_dim; ++x) acc += elem(q,",
+     "float acc = 0.0f;\n    for (int32_t x = 0; x < head_dim; ++x) acc += elem(q,"),
+    ("table_ignored", "int64_t blk = block_table[(int64_t)b * max_blocks_per_seq + page];",
+     "int64_t blk = ((int64_t)b * max_blocks_per_seq + page) % num_blocks;"),
+]
+
+
+def _build_variant(tmp: Path, old: str, new: str) -> Oracle:
+    shutil.copy(SRC / "oracle.h", tmp / "oracle.h")
+    text = (SRC / "oracle.c").read_text()
+    if old is not None:
+        assert old in text, f"mutation target not found: {old!r}"
+        text = text.replace(old, new)
+    (tmp / "oracle.c").write_text(text)
+    return Oracle(build(tmp / "oracle.c", tmp / "liboracle_variant.so", extra_flags=("-w",)))
+
+
+def _failures(orc):
+    failed = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(orc)
+        except Exception as e:  # a pin fails by assertion or by the oracle's own error
+            failed.append((pin.__name__, type(e).__name__))
+    return failed
+
+
+def test_unmutated_copy_passes(tmp_path):
+    assert _failures(_build_variant(tmp_path, None, None)) == []
+
+
+@pytest.mark.parametrize("mid,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, mid, old, new):
+    failed = _failures(_build_variant(tmp_path, old, new))
+    assert failed, f"planted mistake {mid} passed every pin"
