@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged GQA hot path on one MI355X.
+
+Headline: decode KV-read GB/s on the Llama-3-8B-shaped decode workload (B = 64,
+context lengths U[512, 4096], Hq = 32, Hkv = 8, d = 128, block_size 16, bf16).
+One step = the decode step of the hot path on that batch:
+  1. paged_kv_write of each sequence's newest token (position ctx-1) into its page,
+  2. gqa_paged_decode over every cached position (split-KV + merge kernels).
+``value`` = algorithmic K/V bytes read per step / wall time per step.
+
+Inputs stay resident in HBM.  Four copies of the page pools (about 0.77 GB each)
+are used round-robin, so the 256 MB Infinity Cache cannot serve a step from the
+previous one.  Secondary line items: the packed varlen causal prefill workload
+(paged write + MFMA prefill) in TFLOP/s, and the fp64 CPU oracle on the same
+decode batch as a reported baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+COPIES = 4
+
+
+def _args():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill line item")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle timing budget")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_leg(args, torch, pg, W, T):
+    case = W.make_workload("llama3_8b_decode")
+    B, hq, hkv, d, bs = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size
+    kv_bytes = case.kv_bytes()
+    log(f"decode workload: B={B} ctx sum={int(case.context_lens.sum())} KV bytes={kv_bytes}")
+
+    table = T.to_dev(case.block_table)
+    ctx = T.to_dev(case.context_lens)
+    k_all, v_all = T.to_dev(case.k), T.to_dev(case.v)
+    cu_all, sp0 = T.to_dev(case.cu_ctx), T.to_dev(case.start_pos)
+    # newest token of every sequence (its K/V is written by each step)
+    last = case.cu_ctx[1:] - 1
+    k_new, v_new = T.to_dev(np.ascontiguousarray(case.k[last])), T.to_dev(np.ascontiguousarray(case.v[last]))
+    cu_new = T.to_dev(np.arange(B + 1, dtype=np.int32))
+    sp_new = T.to_dev((case.context_lens - 1).astype(np.int32))
+    q = T.to_dev(case.q)
+    pools = []
+    for _ in range(COPIES):
+        kc = T.nan_pool_dev(case.num_blocks, hkv, bs, d, case.dtype)
+        vc = T.nan_pool_dev(case.num_blocks, hkv, bs, d, case.dtype)
+        pg.paged_kv_write(k_all, v_all, cu_all, sp0, table, kc, vc)
+        pools.append((kc, vc))
+    del k_all, v_all
+    out = torch.empty_like(q)
+    ws = pg.decode_workspace(B, hq, hkv, d, 0, q.device)
+    scale = float(case.scale)
+    maxctx = case.max_context_len
+
+    def step(i, ev=None):
+        kc, vc = pools[i % COPIES]
+        pg.paged_kv_write(k_new, v_new, cu_new, sp_new, table, kc, vc)
+        if ev is not None:
+            ev[0].record()
+        pg.gqa_paged_decode(q, kc, vc, table, ctx, maxctx, scale=scale, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_per_step = wall * 1e3 / args.steps
+    return {
+        "case": case, "kv_bytes": kv_bytes, "ms_per_step": ms_per_step,
+        "decode_ms_mean": float(dec_ms.mean()), "decode_ms_median": float(np.median(dec_ms)),
+        "decode_ms_p10": float(np.percentile(dec_ms, 10)), "decode_ms_p90": float(np.percentile(dec_ms, 90)),
+        "out": out, "pools": pools,
+    }
+
+
+def prefill_leg(args, torch, pg, W, T):
+    p = W.make_workload("varlen_prefill")
+    q, k, v = T.to_dev(p.q), T.to_dev(p.k), T.to_dev(p.v)
+    cu = T.to_dev(p.cu_seqlens)
+    sp = T.to_dev(np.zeros(p.batch, np.int32))
+    table = T.to_dev(p.block_table)
+    kc = T.nan_pool_dev(p.num_blocks, p.num_kv_heads, p.block_size, p.head_dim, p.dtype)
+    vc = T.nan_pool_dev(p.num_blocks, p.num_kv_heads, p.block_size, p.head_dim, p.dtype)
+    out = torch.empty_like(q)
+    scale = float(p.scale)
+
+    def step(ev=None):
+        pg.paged_kv_write(k, v, cu, sp, table, kc, vc)
+        if ev is not None:
+            ev[0].record()
+        pg.gqa_varlen_prefill(q, k, v, cu, p.max_seqlen, scale=scale, causal=True, out=out)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(max(3, args.warmup // 4)):
+        step()
+    torch.cuda.synchronize()
+    n = max(10, args.steps // 4)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    t0 = time.perf_counter()
+    for i in range(n):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    flops = p.flops()
+    tf = flops / (pre_ms.mean() * 1e-3) / 1e12
+    return {
+        "workload": "varlen_prefill", "tokens": p.total_tokens, "flops_per_call": flops,
+        "prefill_ms_mean": float(pre_ms.mean()), "ms_per_step": wall * 1e3 / n,
+        "tflops": tf, "tokens_per_s": p.total_tokens / (pre_ms.mean() * 1e-3),
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / BF16_MFMA_PEAK_TFLOPS, "traffic": None},
+    }
+
+
+def cpu_baseline(args, case, W):
+    """The fp64 oracle, as it stands, on the same decode step (write + decode),
+    repeated until at least --cpu-seconds of host time have been spent."""
+    import oracle
+    orc = oracle.default()
+    kc = W.nan_pool(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)
+    vc = W.nan_pool(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)
+    orc.paged_kv_write(case.k, case.v, case.cu_ctx, case.start_pos, case.block_table, kc, vc)
+    last = case.cu_ctx[1:] - 1
+    cu_new = np.arange(case.batch + 1, dtype=np.int32)
+    sp_new = (case.context_lens - 1).astype(np.int32)
+    k_new, v_new = np.ascontiguousarray(case.k[last]), np.ascontiguousarray(case.v[last])
+    reps, t0 = 0, time.perf_counter()
+    ref = None
+    while True:
+        orc.paged_kv_write(k_new, v_new, cu_new, sp_new, case.block_table, kc, vc)
+        ref = orc.gqa_paged_decode(case.q, kc, vc, case.block_table, case.context_lens, case.scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds or reps >= 50:
+            break
+    per_step = el / reps
+    return ref, {"value": case.kv_bytes() / per_step / 1e9, "unit": "GB/s", "cores": orc.max_threads(),
+                 "kind": "oracle", "seconds_per_step": per_step,
+                 "sample": f"the full decode step of the same workload (paged write of the 64 newest tokens + "
+                           f"fp64 decode of all 64 sequences), repeated {reps}x over {el:.1f} s"}
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+    here = os.path.dirname(os.path.abspath(__file__))
+    sys.path.insert(0, here)
+    sys.path.insert(0, os.path.join(here, "tests"))
+    import torch
+    import workload as W
+    import paged_gqa_kv_02_amd as pg
+    import gpu_helpers as T
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    dec = decode_leg(args, torch, pg, W, T)
+    kv = dec["kv_bytes"]
+    value = kv / (dec["ms_per_step"] * 1e-3) / 1e9
+    achieved = kv / (dec["decode_ms_mean"] * 1e-3) / 1e9
+    case = dec["case"]
+    line = {
+        "metric": "decode KV-read GB/s (Llama-3-8B-shaped GQA decode, B=64)",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), bf16-rounded)",
+        "config": {"workload": "llama3_8b_decode", "batch": case.batch, "num_q_heads": case.num_q_heads,
+                   "num_kv_heads": case.num_kv_heads, "head_dim": case.head_dim, "block_size": case.block_size,
+                   "context_lens": "U[512,4096] seed 2", "kv_bytes_per_step": kv,
+                   "tokens_per_step": case.batch},
+        "tokens_per_s": round(case.batch / (dec["ms_per_step"] * 1e-3), 1),
+        "decode_call_us": {"mean": round(dec["decode_ms_mean"] * 1e3, 2),
+                           "median": round(dec["decode_ms_median"] * 1e3, 2),
+                           "p10": round(dec["decode_ms_p10"] * 1e3, 2), "p90": round(dec["decode_ms_p90"] * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gqa_paged_decode (split + merge kernels, one call)"},
+    }
+    if not args.no_prefill:
+        log("prefill leg")
+        line["prefill"] = prefill_leg(args, torch, pg, W, T)
+    if not args.no_cpu_baseline:
+        log("cpu baseline leg (oracle)")
+        ref, cb = cpu_baseline(args, case, W)
+        line["cpu_baseline"] = cb
+        got = T.to_f64(dec["out"])
+        e = T.errors(got, ref)
+        line["parity_vs_oracle"] = {k: float(f"{v:.3e}") for k, v in e.items()}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,185 @@
+/*
+ * paged_gqa.h -- C ABI of libpaged_gqa.so: grouped-query attention read through
+ * a paged KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * Problem statement these calls implement (the pages are cited by title and
+ * section; no call depends on anything beyond them):
+ *   - Attention(Q, K, V) = softmax(Q K^T * scale) V with scale = 1/sqrt(d):
+ *     "Modern LLM Inference -- Workloads, Bottlenecks, and Optimization
+ *     Techniques" (gozhiyuan.github.io, stanford-llm-11), subsection "Why
+ *     Cross-Layer Attention Shares K/V but Not Q", attention equation.
+ *   - Grouped-query attention: Hq query heads share Hkv KV heads, query head
+ *     qh reads KV head qh / (Hq / Hkv), and Hq must be a multiple of Hkv:
+ *     same notes, section 4.1; "The Ultimate Guide to LLM Inference
+ *     Optimization- Part 2" (wpnews.pro), section "Grouped Query Attention";
+ *     itinai.com/?p=48087, second paragraph (5-D grouped query layout).
+ *   - Paged KV cache: each sequence's K/V live in fixed-size blocks anywhere
+ *     in a pool, located through a per-sequence block table: "Advanced
+ *     Optimizations: MQA, GQA, and PagedAttention" (tryclaro.ai), sections
+ *     "PagedAttention: The OS Analogy" and "Optimizing Block Size"; the
+ *     Ultimate Guide, section "Paged Attention"; the lecture notes, section 8.2.
+ *   - Packed variable-length batches with a block-diagonal, optionally causal
+ *     mask built from the true lengths (cu_seqlens): itinai.com/?p=48087, first
+ *     paragraph; the lecture notes, section 8.1 (selective batching).
+ *   - Prefill (whole prompt, compute-bound) and decode (one new token per
+ *     sequence, memory-bound) are separate phases: the lecture notes, section 2;
+ *     the Ultimate Guide, introduction.
+ *
+ * Conventions shared by every call
+ *   - Every array argument is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or keeps device memory, never
+ *     synchronises, and keeps no state between calls (thread-safe).
+ *   - Element arrays hold PGQA_F32 (float) or PGQA_BF16 (bfloat16 bit
+ *     patterns, 2 bytes each); out has the dtype of q.  Index arrays are int32.
+ *   - Element pointers and the workspace must be 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on it and returns.
+ *   - Return value: PGQA_OK, or an error code.  Arguments are checked on the
+ *     host before any HIP call; a failed check returns PGQA_EINVAL,
+ *     PGQA_ENOTSUP or PGQA_ENOSPC and enqueues nothing.  PGQA_EHIP reports a
+ *     failed launch.  No exception or abort crosses this boundary.
+ *   - Device-side contents are the caller's promise and are not checked on
+ *     the host: block ids in [0, num_blocks) for every used page, context
+ *     lengths in [0, max_context_len], cu_seqlens non-decreasing.  Kernels
+ *     clamp every index they read, so a broken promise gives unspecified
+ *     numbers but never an access outside the caller's buffers; the KV write
+ *     skips tokens whose block id is outside the pool.
+ *
+ * Layouts (row-major, innermost last)
+ *   packed K/V            [T, Hkv, d]          T = total tokens of the batch
+ *   decode q / out        [B, Hq, d]           one query token per sequence
+ *   prefill q / out       [T, Hq, d]
+ *   k_cache, v_cache      [num_blocks, Hkv, block_size, d]
+ *   block_table           [B, max_blocks_per_seq]  logical page -> physical block
+ *   cu_seqlens            [B + 1], cu_seqlens[0] = 0, cu_seqlens[B] = T
+ */
+#ifndef PAGED_GQA_H
+#define PAGED_GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PGQA_F32 = 0, PGQA_BF16 = 1 } pgqa_dtype;
+
+enum {
+    PGQA_OK = 0,
+    PGQA_EINVAL = 1,  /* invalid argument: null or misaligned pointer, negative size,
+                         Hq % Hkv != 0, max_context_len beyond the block table, ... */
+    PGQA_ENOTSUP = 2, /* valid but not built: head_dim, block_size, group size or dtype */
+    PGQA_ENOSPC = 3,  /* decode workspace smaller than gqa_paged_decode_workspace_size() */
+    PGQA_EHIP = 4     /* a HIP launch failed */
+};
+
+/* Supported shapes: head_dim in {16, 32, 64, 128}; block_size a power of two in
+ * [1, 256]; Hq / Hkv in {1, 2, 4, 8, 16, 32, 64}. */
+
+/*
+ * paged_kv_write -- scatter packed new K/V rows into the page pools.
+ * Defined by the paging passages above: token t of sequence b (cu_seqlens[b] <= t
+ * < cu_seqlens[b+1]) is logical position pos = start_pos[b] + (t - cu_seqlens[b]);
+ * it goes to block block_table[b][pos / block_size], slot pos % block_size, for
+ * every KV head h:  k_cache[blk][h][slot][:] = k[t][h][:]  (same for v).
+ * Bytes are copied unchanged (bit-exact).  Tokens whose page lies past the
+ * table row or whose block id is outside [0, num_blocks) are skipped.
+ *   k, v         [total_tokens, Hkv, d] packed new rows (read)
+ *   cu_seqlens   [batch + 1] token offsets of each sequence in k / v
+ *   start_pos    [batch] logical position of each sequence's first new token
+ *   block_table  [batch, max_blocks_per_seq]
+ *   k_cache, v_cache [num_blocks, Hkv, block_size, d] (written in place)
+ */
+int paged_kv_write(const void* k, const void* v,
+                   const int32_t* cu_seqlens, const int32_t* start_pos,
+                   const int32_t* block_table, int32_t max_blocks_per_seq,
+                   void* k_cache, void* v_cache,
+                   int32_t batch, int32_t total_tokens, int32_t num_blocks,
+                   int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                   pgqa_dtype dtype, void* stream);
+
+/*
+ * paged_kv_gather -- the exact inverse of paged_kv_write: reads position
+ * start_pos[b] + (t - cu_seqlens[b]) of sequence b out of the pools into packed
+ * row t of k_out / v_out (bit-exact copy).  With start_pos = 0 and cu_seqlens
+ * the prefix sums of the context lengths it unpacks every cached token.  Rows
+ * whose page is past the table row or outside the pool are left untouched.
+ * Exported so that the write can be checked on the device.
+ */
+int paged_kv_gather(const void* k_cache, const void* v_cache,
+                    const int32_t* cu_seqlens, const int32_t* start_pos,
+                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                    void* k_out, void* v_out,
+                    int32_t batch, int32_t total_tokens, int32_t num_blocks,
+                    int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                    pgqa_dtype dtype, void* stream);
+
+/*
+ * Bytes of device workspace gqa_paged_decode needs for these sizes: fp32
+ * split-KV partials (running max, sum and unnormalised output per query
+ * head) for at most (num_splits + batch * Hkv) pieces.  num_splits = 0 sizes
+ * it for the library's own choice.  Returns 0 for invalid sizes.
+ */
+size_t gqa_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t num_splits);
+
+/*
+ * gqa_paged_decode -- one query token per sequence attends to every cached
+ * position [0, context_lens[b]) of its sequence (the decode phase reads the
+ * whole KV cache of earlier tokens: the Ultimate Guide, introduction; the
+ * lecture notes, section 2).  For query head qh, with h = qh / (Hq / Hkv):
+ *   s_j = scale * dot(q[b][qh], K_j),  K_j = k_cache[block_table[b][j / bs]][h][j % bs]
+ *   out[b][qh] = sum_j softmax(s)_j * V_j        (exact softmax; fp32 accumulation)
+ * A sequence with context length 0 gets an all-zero output.
+ * Work is split into num_splits equal shares of all (sequence, KV head) tiles
+ * (0 = library choice, which fills the GPU); a sequence cut across shares is
+ * merged exactly with a log-sum-exp reduction in a second kernel.  The
+ * result is deterministic for a given num_splits.
+ *   q            [batch, Hq, d]
+ *   k_cache, v_cache [num_blocks, Hkv, block_size, d]
+ *   block_table  [batch, max_blocks_per_seq]; entries past ceil(ctx/bs) never read
+ *   context_lens [batch]
+ *   max_context_len  host-side upper bound of context_lens;
+ *                    must be <= max_blocks_per_seq * block_size
+ *   scale        softmax scale, normally 1/sqrt(head_dim)
+ *   out          [batch, Hq, d] (written)
+ *   workspace    >= gqa_paged_decode_workspace_size(batch, Hq, Hkv, d, num_splits) bytes
+ * Errors: PGQA_EINVAL, PGQA_ENOTSUP, PGQA_ENOSPC (workspace too small), PGQA_EHIP.
+ */
+int gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens,
+                     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                     int32_t max_context_len, float scale, pgqa_dtype dtype,
+                     void* out, int32_t num_splits,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gqa_varlen_prefill -- packed variable-length prefill with a block-diagonal
+ * mask (itinai.com/?p=48087, first paragraph; the lecture notes, section 8.1).
+ * Row i of sequence s (cu_seqlens[s] <= i < cu_seqlens[s+1]), query head qh,
+ * KV head h = qh / (Hq / Hkv):
+ *   out[i][qh] = sum_j softmax_j(scale * dot(q[i][qh], k[j][h])) * v[j][h]
+ * over keys j of the same sequence with j <= i (causal != 0) or all of them.
+ * QK^T and PV run on bf16 MFMA with fp32 accumulation; P is rounded to bf16
+ * for the PV product.  bf16 only.
+ *   q [total_tokens, Hq, d], k / v [total_tokens, Hkv, d], out [total_tokens, Hq, d]
+ *   cu_seqlens [batch + 1]; max_seqlen = host-side upper bound of the lengths
+ */
+int gqa_varlen_prefill(const void* q, const void* k, const void* v,
+                       const int32_t* cu_seqlens, int32_t batch, int32_t total_tokens,
+                       int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, float scale, int32_t causal, pgqa_dtype dtype,
+                       void* out, void* stream);
+
+/* Static, human-readable text of a status code. */
+const char* pgqa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_GQA_H */

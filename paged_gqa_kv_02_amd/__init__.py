@@ -1,0 +1,12 @@
+"""Grouped-query attention over a paged KV cache for AMD Instinct MI355X (gfx950).
+
+The product is the C-ABI library libpaged_gqa.so (include/paged_gqa.h) built
+from the HIP sources in csrc/; this package is its thin torch front end.
+"""
+
+from ._lib import PgqaError, LIB_PATH
+from .ops import (decode_workspace, gqa_paged_decode, gqa_paged_decode_workspace_size, gqa_varlen_prefill,
+                  paged_kv_gather, paged_kv_write)
+
+__all__ = ["PgqaError", "LIB_PATH", "paged_kv_write", "paged_kv_gather", "gqa_paged_decode",
+           "gqa_paged_decode_workspace_size", "decode_workspace", "gqa_varlen_prefill"]

@@ -1,0 +1,156 @@
+// api.cpp -- the C ABI of libpaged_gqa.so (declared in include/paged_gqa.h):
+// host-side argument checks, then launches on the caller's stream.  Every check
+// runs before any HIP call, so a rejected call enqueues nothing.
+#include "paged_gqa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "launch.hpp"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool pow2_log2(int32_t x, int32_t* lg) {
+    if (x <= 0 || (x & (x - 1))) return false;
+    int32_t l = 0;
+    while ((1 << l) < x) ++l;
+    *lg = l;
+    return true;
+}
+
+bool head_dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+int elem_bytes(pgqa_dtype dt) { return dt == PGQA_BF16 ? 2 : (dt == PGQA_F32 ? 4 : 0); }
+
+constexpr int32_t kMaxDecodeBatch = 8192;
+
+int check_elem_ptr(const void* p) { return (p && aligned(p, 16)) ? PGQA_OK : PGQA_EINVAL; }
+int check_index_ptr(const void* p) { return (p && aligned(p, 4)) ? PGQA_OK : PGQA_EINVAL; }
+
+int check_copy_args(const void* a, const void* b, const int32_t* cu, const int32_t* sp, const int32_t* bt,
+                    int32_t max_blocks_per_seq, void* c, void* d, int32_t batch, int32_t total_tokens,
+                    int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                    pgqa_dtype dtype, int32_t* bs_log2) {
+    if (batch < 0 || total_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0)
+        return PGQA_EINVAL;
+    if (elem_bytes(dtype) == 0) return PGQA_ENOTSUP;
+    if (!head_dim_ok(head_dim)) return PGQA_ENOTSUP;
+    if (!pow2_log2(block_size, bs_log2) || block_size > 256) return PGQA_ENOTSUP;
+    if ((int64_t)batch * max_blocks_per_seq > INT32_MAX) return PGQA_EINVAL;
+    if (check_elem_ptr(a) || check_elem_ptr(b) || check_elem_ptr(c) || check_elem_ptr(d)) return PGQA_EINVAL;
+    if (check_index_ptr(cu) || check_index_ptr(sp) || check_index_ptr(bt)) return PGQA_EINVAL;
+    return PGQA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PGQA_OK : PGQA_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pgqa_status_string(int status) {
+    switch (status) {
+        case PGQA_OK: return "ok";
+        case PGQA_EINVAL: return "invalid argument";
+        case PGQA_ENOTSUP: return "unsupported shape or dtype";
+        case PGQA_ENOSPC: return "decode workspace too small";
+        case PGQA_EHIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int paged_kv_write(const void* k, const void* v, const int32_t* cu_seqlens, const int32_t* start_pos,
+                   const int32_t* block_table, int32_t max_blocks_per_seq, void* k_cache, void* v_cache,
+                   int32_t batch, int32_t total_tokens, int32_t num_blocks, int32_t block_size,
+                   int32_t num_kv_heads, int32_t head_dim, pgqa_dtype dtype, void* stream) {
+    int32_t lg = 0;
+    const int rc = check_copy_args(k, v, cu_seqlens, start_pos, block_table, max_blocks_per_seq, k_cache, v_cache,
+                                   batch, total_tokens, num_blocks, block_size, num_kv_heads, head_dim, dtype, &lg);
+    if (rc != PGQA_OK) return rc;
+    if (batch == 0 || total_tokens == 0) return PGQA_OK;
+    pgqa::KvCopyLaunch L{k, v, k_cache, v_cache, cu_seqlens, start_pos, block_table, max_blocks_per_seq,
+                         batch, total_tokens, num_blocks, lg, num_kv_heads, head_dim, elem_bytes(dtype)};
+    return hip_status(pgqa::launch_kv_copy(L, true, (hipStream_t)stream));
+}
+
+int paged_kv_gather(const void* k_cache, const void* v_cache, const int32_t* cu_seqlens, const int32_t* start_pos,
+                    const int32_t* block_table, int32_t max_blocks_per_seq, void* k_out, void* v_out,
+                    int32_t batch, int32_t total_tokens, int32_t num_blocks, int32_t block_size,
+                    int32_t num_kv_heads, int32_t head_dim, pgqa_dtype dtype, void* stream) {
+    int32_t lg = 0;
+    const int rc = check_copy_args(k_cache, v_cache, cu_seqlens, start_pos, block_table, max_blocks_per_seq, k_out,
+                                   v_out, batch, total_tokens, num_blocks, block_size, num_kv_heads, head_dim,
+                                   dtype, &lg);
+    if (rc != PGQA_OK) return rc;
+    if (batch == 0 || total_tokens == 0) return PGQA_OK;
+    pgqa::KvCopyLaunch L{k_cache, v_cache, k_out, v_out, cu_seqlens, start_pos, block_table, max_blocks_per_seq,
+                         batch, total_tokens, num_blocks, lg, num_kv_heads, head_dim, elem_bytes(dtype)};
+    return hip_status(pgqa::launch_kv_copy(L, false, (hipStream_t)stream));
+}
+
+size_t gqa_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t num_splits) {
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_splits < 0) return 0;
+    if (num_q_heads % num_kv_heads) return 0;
+    const int64_t splits = num_splits > 0 ? num_splits : pgqa::kDecodeMaxSplits;
+    const int64_t slots = splits + (int64_t)batch * num_kv_heads;
+    const int64_t group = num_q_heads / num_kv_heads;
+    return (size_t)(slots * group * (head_dim + 2) * 4);
+}
+
+int gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                     int32_t max_context_len, float scale, pgqa_dtype dtype, void* out, int32_t num_splits,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
+        max_context_len < 0 || num_splits < 0)
+        return PGQA_EINVAL;
+    if (num_q_heads % num_kv_heads) return PGQA_EINVAL;
+    const int es = elem_bytes(dtype);
+    if (es == 0 || !head_dim_ok(head_dim)) return PGQA_ENOTSUP;
+    int32_t lg = 0;
+    if (!pow2_log2(block_size, &lg) || block_size > 256) return PGQA_ENOTSUP;
+    if (!pgqa::decode_supported(es, head_dim, num_q_heads / num_kv_heads)) return PGQA_ENOTSUP;
+    if (batch > kMaxDecodeBatch) return PGQA_ENOTSUP;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PGQA_EINVAL;
+    if ((int64_t)batch * max_blocks_per_seq > INT32_MAX) return PGQA_EINVAL;
+    if ((int64_t)batch * num_kv_heads * (int64_t)max_context_len > INT32_MAX) return PGQA_EINVAL;
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff()) return PGQA_EINVAL;
+    if (check_elem_ptr(q) || check_elem_ptr(k_cache) || check_elem_ptr(v_cache) || check_elem_ptr(out))
+        return PGQA_EINVAL;
+    if (check_index_ptr(block_table) || check_index_ptr(context_lens)) return PGQA_EINVAL;
+    if (batch == 0) return PGQA_OK;
+    const size_t need = gqa_paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, num_splits);
+    if (!workspace || !aligned(workspace, 16)) return workspace_bytes < need ? PGQA_ENOSPC : PGQA_EINVAL;
+    if (workspace_bytes < need) return PGQA_ENOSPC;
+    pgqa::DecodeLaunch L{q, k_cache, v_cache, block_table, context_lens, out, workspace, max_blocks_per_seq,
+                         batch, num_q_heads, num_kv_heads, head_dim, lg, num_blocks, max_context_len,
+                         num_splits, dtype == PGQA_BF16 ? 1 : 0, scale};
+    return hip_status(pgqa::launch_decode(L, (hipStream_t)stream));
+}
+
+int gqa_varlen_prefill(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t batch,
+                       int32_t total_tokens, int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, float scale, int32_t causal, pgqa_dtype dtype, void* out,
+                       void* stream) {
+    if (batch < 0 || total_tokens < 0 || max_seqlen < 0 || num_q_heads <= 0 || num_kv_heads <= 0)
+        return PGQA_EINVAL;
+    if (num_q_heads % num_kv_heads) return PGQA_EINVAL;
+    if (dtype != PGQA_BF16 && dtype != PGQA_F32) return PGQA_ENOTSUP;
+    if (dtype != PGQA_BF16) return PGQA_ENOTSUP;
+    if (!pgqa::prefill_supported(head_dim, num_q_heads / num_kv_heads)) return PGQA_ENOTSUP;
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff()) return PGQA_EINVAL;
+    if ((int64_t)total_tokens * num_q_heads * head_dim > ((int64_t)1 << 40)) return PGQA_EINVAL;
+    if (check_elem_ptr(q) || check_elem_ptr(k) || check_elem_ptr(v) || check_elem_ptr(out)) return PGQA_EINVAL;
+    if (check_index_ptr(cu_seqlens)) return PGQA_EINVAL;
+    if (batch == 0 || total_tokens == 0 || max_seqlen == 0) return PGQA_OK;
+    pgqa::PrefillLaunch L{q, k, v, cu_seqlens, out, batch, total_tokens, max_seqlen, num_q_heads, num_kv_heads,
+                          head_dim, causal ? 1 : 0, scale};
+    return hip_status(pgqa::launch_prefill(L, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// device_common.hpp -- small gfx950 device helpers shared by the kernels of
+// libpaged_gqa.so: bf16 packing, DPP lane reductions, LDS-DMA loads and
+// explicit wait counters.  Wave64 throughout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pgqa {
+
+#define PGQA_LDS __attribute__((address_space(3)))
+
+typedef uint32_t u32;
+typedef __attribute__((ext_vector_type(4))) u32 u32x4;
+typedef __attribute__((ext_vector_type(2))) u32 u32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+
+constexpr int kWave = 64;
+
+// Finite stand-in for -inf as the initial running max: keeps every exp2 argument
+// finite, so an empty token group yields weight 0 instead of NaN.
+constexpr float kMaxInit = -1.0e30f;
+
+// ---- bf16 <-> fp32 -------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(u32 w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(u32 w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ u32 f32_to_bf16_bits(float f) {
+    u32 u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// bf16 pair dot product accumulated in fp32: acc + a.lo*b.lo + a.hi*b.hi
+__device__ __forceinline__ float dot2_bf16(u32 a, u32 b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                           acc, false);
+}
+
+// ---- cross-lane ---------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of LANES lanes (LANES in {1, 2, 4, 8, 16, 32}); every
+// lane of a group ends with the same bits (each step adds a commutative pair).
+template <int LANES>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(LANES == 1 || LANES == 2 || LANES == 4 || LANES == 8 || LANES == 16 || LANES == 32, "");
+    if constexpr (LANES >= 2) x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (LANES >= 4) x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (LANES >= 8) x += dpp_f32<0x141>(x);  // row_half_mirror: quad 0 <-> quad 1
+    if constexpr (LANES >= 16) x += dpp_f32<0x140>(x); // row_mirror: half-row 0 <-> 1
+    if constexpr (LANES >= 32)                          // ds_swizzle xor 16 within 32 lanes
+        x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+    return x;
+}
+
+__device__ __forceinline__ float shfl_xor_f32(float x, int mask) {
+    const int lane = __lane_id();
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, shfl_xor_f32(x, m));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+    for (int m = 32; m >= 1; m >>= 1) x += shfl_xor_f32(x, m);
+    return x;
+}
+
+// ---- memory ---------------------------------------------------------------
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at
+// lds_row + 16 * l (lds_row must be wave-uniform and 16-byte aligned).
+__device__ __forceinline__ void load_lds_16(const void* gsrc, PGQA_LDS void* lds_row) {
+    __builtin_amdgcn_global_load_lds(gsrc, lds_row, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N), leaving the other counters unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Runtime count in [0, MAXN]: branches to the constant-immediate wait.
+template <int MAXN>
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+    if constexpr (MAXN <= 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (n >= MAXN) wait_vmcnt<MAXN>();
+        else wait_vmcnt_dyn<MAXN - 1>(n);
+    }
+}
+
+__device__ __forceinline__ u32x4 lds_read_16(const PGQA_LDS void* p) {
+    return *(const PGQA_LDS u32x4*)p;
+}
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+}  // namespace pgqa

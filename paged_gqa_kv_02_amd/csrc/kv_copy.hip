@@ -1,0 +1,108 @@
+// kv_copy.hip -- paged K/V write (packed rows -> pages) and its inverse gather.
+//
+// Token t of sequence b is logical position start_pos[b] + (t - cu_seqlens[b]);
+// that position lives in block block_table[b][pos / bs], slot pos % bs (paging
+// through a block table: "Advanced Optimizations: MQA, GQA, and PagedAttention",
+// section "PagedAttention: The OS Analogy"; "The Ultimate Guide to LLM
+// Inference Optimization- Part 2", section "Paged Attention").
+//
+// Pure HBM copy work.  One thread moves one 16-byte chunk of one (token, head)
+// row of K and the same chunk of V; consecutive threads walk a row, so both the
+// packed side and the page side are read and written in whole 256-byte rows
+// (bf16, d = 128).  Element bytes are never interpreted, so the copy is
+// bit-exact for any dtype.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace pgqa {
+
+namespace {
+
+struct CopyArgs {
+    const char* src_k;
+    const char* src_v;
+    char* dst_k;
+    char* dst_v;
+    const int32_t* cu_seqlens;
+    const int32_t* start_pos;
+    const int32_t* block_table;
+    int64_t total_chunks;       // total_tokens * Hkv * chunks_per_row
+    int32_t batch;
+    int32_t total_tokens;
+    int32_t max_blocks_per_seq;
+    int32_t num_blocks;
+    int32_t block_size_log2;
+    int32_t num_kv_heads;
+    int32_t chunks_per_row;     // head_dim * elem_bytes / 16
+};
+
+// Sequence owning packed token t: the last b with cu_seqlens[b] <= t.
+__device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int batch, int t) {
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// TO_PAGES = true: packed -> pages (write); false: pages -> packed (gather).
+template <bool TO_PAGES>
+__global__ __launch_bounds__(256) void kv_copy_kernel(CopyArgs a) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.total_chunks; i += stride) {
+        const int c = (int)(i % a.chunks_per_row);
+        const int64_t row = i / a.chunks_per_row;          // t * Hkv + h
+        const int h = (int)(row % a.num_kv_heads);
+        const int t = (int)(row / a.num_kv_heads);
+        const int b = find_seq(a.cu_seqlens, a.batch, t);
+        const int64_t pos = (int64_t)a.start_pos[b] + (t - a.cu_seqlens[b]);
+        const int64_t page = pos >> a.block_size_log2;
+        if (pos < 0 || page >= a.max_blocks_per_seq) continue;
+        const int blk = a.block_table[(int64_t)b * a.max_blocks_per_seq + page];
+        if (blk < 0 || blk >= a.num_blocks) continue;
+        const int64_t slot = pos & ((1 << a.block_size_log2) - 1);
+        const int64_t page_row = (((int64_t)blk * a.num_kv_heads + h) << a.block_size_log2) + slot;
+        const int64_t packed_off = (row * a.chunks_per_row + c) * 16;
+        const int64_t page_off = (page_row * a.chunks_per_row + c) * 16;
+        const int64_t s_off = TO_PAGES ? packed_off : page_off;
+        const int64_t d_off = TO_PAGES ? page_off : packed_off;
+        const u32x4 kx = *(const u32x4*)(a.src_k + s_off);
+        const u32x4 vx = *(const u32x4*)(a.src_v + s_off);
+        *(u32x4*)(a.dst_k + d_off) = kx;
+        *(u32x4*)(a.dst_v + d_off) = vx;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_kv_copy(const KvCopyLaunch& L, bool to_pages, hipStream_t stream) {
+    CopyArgs a;
+    a.src_k = (const char*)L.src_k;
+    a.src_v = (const char*)L.src_v;
+    a.dst_k = (char*)L.dst_k;
+    a.dst_v = (char*)L.dst_v;
+    a.cu_seqlens = L.cu_seqlens;
+    a.start_pos = L.start_pos;
+    a.block_table = L.block_table;
+    a.batch = L.batch;
+    a.total_tokens = L.total_tokens;
+    a.max_blocks_per_seq = L.max_blocks_per_seq;
+    a.num_blocks = L.num_blocks;
+    a.block_size_log2 = L.block_size_log2;
+    a.num_kv_heads = L.num_kv_heads;
+    a.chunks_per_row = L.head_dim * L.elem_bytes / 16;
+    a.total_chunks = (int64_t)L.total_tokens * L.num_kv_heads * a.chunks_per_row;
+    if (a.total_chunks == 0 || L.batch == 0) return hipSuccess;
+    const int threads = 256;
+    int64_t blocks = (a.total_chunks + threads - 1) / threads;
+    if (blocks > 65536) blocks = 65536;  // grid-stride beyond this
+    if (to_pages)
+        hipLaunchKernelGGL(kv_copy_kernel<true>, dim3((unsigned)blocks), dim3(threads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(kv_copy_kernel<false>, dim3((unsigned)blocks), dim3(threads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace pgqa

@@ -1,0 +1,84 @@
+// launch.hpp -- internal host-side launch descriptors of libpaged_gqa.so.
+// Validation happens in api.cpp; these launchers assume valid arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pgqa {
+
+struct KvCopyLaunch {
+    const void* src_k;
+    const void* src_v;
+    void* dst_k;
+    void* dst_v;
+    const int32_t* cu_seqlens;
+    const int32_t* start_pos;
+    const int32_t* block_table;
+    int32_t max_blocks_per_seq;
+    int32_t batch;
+    int32_t total_tokens;
+    int32_t num_blocks;
+    int32_t block_size_log2;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t elem_bytes;
+};
+
+// to_pages = true: packed -> pages; false: pages -> packed.
+hipError_t launch_kv_copy(const KvCopyLaunch& L, bool to_pages, hipStream_t stream);
+
+struct DecodeLaunch {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_table;
+    const int32_t* context_lens;
+    void* out;
+    void* workspace;
+    int32_t max_blocks_per_seq;
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_size_log2;
+    int32_t num_blocks;
+    int32_t max_context_len;
+    int32_t num_splits;   // 0 = choose
+    int32_t is_bf16;
+    float scale;
+};
+
+// Largest number of splits (workgroups of the split-KV kernel) the library picks itself.
+constexpr int32_t kDecodeMaxSplits = 4096;
+
+// Tokens per tile of the decode kernel for this element size and head_dim.
+int32_t decode_tile_tokens(int32_t elem_bytes, int32_t head_dim);
+
+// Is there a decode kernel for this (dtype, head_dim, group size)?
+bool decode_supported(int32_t elem_bytes, int32_t head_dim, int32_t group);
+
+hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
+
+struct PrefillLaunch {
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* cu_seqlens;
+    void* out;
+    int32_t batch;
+    int32_t total_tokens;
+    int32_t max_seqlen;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t causal;
+    float scale;
+};
+
+bool prefill_supported(int32_t head_dim, int32_t group);
+
+hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream);
+
+}  // namespace pgqa

@@ -1,0 +1,128 @@
+"""Thin torch front end of the C ABI: argument marshalling only.
+
+Every function takes torch tensors on the GPU, checks dtypes / shapes / layout
+enough to build the C call, passes ``data_ptr()``s and the current stream's
+handle, and raises :class:`PgqaError` on a non-OK status.  All computation runs
+in the HIP kernels of libpaged_gqa.so; torch only owns memory and streams.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import PGQA_BF16, PGQA_F32, check, lib
+
+_DT = {torch.bfloat16: PGQA_BF16, torch.float32: PGQA_F32}
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"expected bfloat16 or float32, got {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _dev(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _i32(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if t.dtype != torch.int32:
+            raise TypeError(f"index tensors must be int32, got {t.dtype}")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def paged_kv_write(k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, start_pos: torch.Tensor,
+                   block_table: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Scatter packed k, v [T, Hkv, d] into k_cache, v_cache [num_blocks, Hkv, bs, d] in place."""
+    _dev(k, v, cu_seqlens, start_pos, block_table, k_cache, v_cache)
+    _i32(cu_seqlens, start_pos, block_table)
+    nb, hkv, bs, d = k_cache.shape
+    st = lib().paged_kv_write(k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), start_pos.data_ptr(),
+                              block_table.data_ptr(), block_table.shape[1], k_cache.data_ptr(), v_cache.data_ptr(),
+                              cu_seqlens.numel() - 1, k.shape[0], nb, bs, hkv, d, _dtype(k), _stream())
+    check("paged_kv_write", st)
+
+
+def paged_kv_gather(k_cache: torch.Tensor, v_cache: torch.Tensor, cu_seqlens: torch.Tensor,
+                    start_pos: torch.Tensor, block_table: torch.Tensor, total_tokens: int,
+                    k_out: Optional[torch.Tensor] = None,
+                    v_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Inverse of paged_kv_write: packed [total_tokens, Hkv, d] copies of the cached rows."""
+    nb, hkv, bs, d = k_cache.shape
+    if k_out is None:
+        k_out = torch.empty((total_tokens, hkv, d), dtype=k_cache.dtype, device=k_cache.device)
+    if v_out is None:
+        v_out = torch.empty((total_tokens, hkv, d), dtype=k_cache.dtype, device=k_cache.device)
+    _dev(k_cache, v_cache, cu_seqlens, start_pos, block_table, k_out, v_out)
+    _i32(cu_seqlens, start_pos, block_table)
+    st = lib().paged_kv_gather(k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens.data_ptr(), start_pos.data_ptr(),
+                               block_table.data_ptr(), block_table.shape[1], k_out.data_ptr(), v_out.data_ptr(),
+                               cu_seqlens.numel() - 1, total_tokens, nb, bs, hkv, d, _dtype(k_cache), _stream())
+    check("paged_kv_gather", st)
+    return k_out, v_out
+
+
+def gqa_paged_decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                    num_splits: int = 0) -> int:
+    return int(lib().gqa_paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, num_splits))
+
+
+def decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, num_splits: int = 0,
+                     device=None) -> torch.Tensor:
+    n = gqa_paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, num_splits)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device or "cuda")
+
+
+def gqa_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                     context_lens: torch.Tensor, max_context_len: int, scale: Optional[float] = None,
+                     out: Optional[torch.Tensor] = None, num_splits: int = 0,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention: q [B, Hq, d] over paged K/V -> out [B, Hq, d]."""
+    B, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    if d2 != d:
+        raise ValueError("head_dim mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = decode_workspace(B, hq, hkv, d, num_splits, q.device)
+    _dev(q, k_cache, v_cache, block_table, context_lens, out, workspace)
+    _i32(block_table, context_lens)
+    st = lib().gqa_paged_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+                                block_table.shape[1], context_lens.data_ptr(), B, hq, hkv, d, bs, nb,
+                                int(max_context_len), float(scale), _dtype(q), out.data_ptr(), int(num_splits),
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream())
+    check("gqa_paged_decode", st)
+    return out
+
+
+def gqa_varlen_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                       max_seqlen: int, scale: Optional[float] = None, causal: bool = True,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed varlen prefill: q [T, Hq, d], k / v [T, Hkv, d] -> out [T, Hq, d]."""
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(q, k, v, cu_seqlens, out)
+    _i32(cu_seqlens)
+    st = lib().gqa_varlen_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
+                                  cu_seqlens.numel() - 1, T, int(max_seqlen), hq, hkv, d, float(scale),
+                                  int(bool(causal)), _dtype(q), out.data_ptr(), _stream())
+    check("gqa_varlen_prefill", st)
+    return out

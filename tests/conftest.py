@@ -19,3 +19,12 @@ def pytest_configure(config):
 def orc():
     import oracle
     return oracle.default()
+
+
+@pytest.fixture(scope="session")
+def built_lib():
+    """Path of libpaged_gqa.so, building it first if this tree has none yet."""
+    from paged_gqa_kv_02_amd import build as B
+    if not B.LIB.exists():
+        B.build()
+    return B.LIB

@@ -1,0 +1,121 @@
+"""The C ABI on the CPU: the library loads, exports what the header declares, and
+rejects bad arguments on the host before any HIP call (no GPU needed)."""
+
+import ctypes as C
+import subprocess
+
+import pytest
+
+from paged_gqa_kv_02_amd import _lib as L
+
+EINVAL, ENOTSUP, ENOSPC = 1, 2, 3
+F32, BF16 = 0, 1
+
+# Fake, 16-byte-aligned, non-null "device pointers": validation never dereferences them.
+P = [0x10000 * (i + 1) for i in range(12)]
+
+
+@pytest.fixture(scope="module")
+def lib(built_lib):
+    return L.load(built_lib)
+
+
+def test_header_declares_the_calls():
+    names = L.header_functions()
+    for n in ("paged_kv_write", "paged_kv_gather", "gqa_paged_decode", "gqa_paged_decode_workspace_size",
+              "gqa_varlen_prefill", "pgqa_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(built_lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", str(built_lib)], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in L.header_functions():
+        assert n in exported, f"{n} declared in paged_gqa.h but not exported"
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.pgqa_status_string(s)
+    assert b"unknown" in lib.pgqa_status_string(99)
+
+
+def _write(lib, **kw):
+    a = dict(k=P[0], v=P[1], cu=P[2], sp=P[3], bt=P[4], maxb=4, kc=P[5], vc=P[6], batch=2, T=10, nb=8, bs=16,
+             hkv=2, d=128, dt=BF16)
+    a.update(kw)
+    return lib.paged_kv_write(a["k"], a["v"], a["cu"], a["sp"], a["bt"], a["maxb"], a["kc"], a["vc"], a["batch"],
+                              a["T"], a["nb"], a["bs"], a["hkv"], a["d"], a["dt"], None)
+
+
+def test_write_validation(lib):
+    assert _write(lib, k=None) == EINVAL
+    assert _write(lib, k=P[0] + 4) == EINVAL          # misaligned element pointer
+    assert _write(lib, cu=P[2] + 2) == EINVAL         # misaligned index pointer
+    assert _write(lib, batch=-1) == EINVAL
+    assert _write(lib, nb=0) == EINVAL
+    assert _write(lib, d=96) == ENOTSUP
+    assert _write(lib, bs=24) == ENOTSUP
+    assert _write(lib, bs=512) == ENOTSUP
+    assert _write(lib, dt=7) == ENOTSUP
+    assert _write(lib, batch=0) == 0                  # nothing to do: OK without touching HIP
+    assert _write(lib, T=0) == 0
+
+
+def _decode(lib, **kw):
+    a = dict(q=P[0], kc=P[1], vc=P[2], bt=P[3], maxb=4, cl=P[4], batch=2, hq=8, hkv=2, d=128, bs=16, nb=8,
+             maxctx=64, scale=0.125, dt=BF16, out=P[5], splits=0, ws=P[6], wsb=1 << 30)
+    a.update(kw)
+    return lib.gqa_paged_decode(a["q"], a["kc"], a["vc"], a["bt"], a["maxb"], a["cl"], a["batch"], a["hq"],
+                                a["hkv"], a["d"], a["bs"], a["nb"], a["maxctx"], a["scale"], a["dt"], a["out"],
+                                a["splits"], a["ws"], a["wsb"], None)
+
+
+def test_decode_validation(lib):
+    assert _decode(lib, hq=6, hkv=4) == EINVAL         # Hq % Hkv != 0
+    assert _decode(lib, maxctx=65) == EINVAL           # beyond max_blocks_per_seq * block_size
+    assert _decode(lib, maxctx=-1) == EINVAL
+    assert _decode(lib, out=None) == EINVAL
+    assert _decode(lib, q=P[0] + 8) == EINVAL
+    assert _decode(lib, splits=-1) == EINVAL
+    assert _decode(lib, scale=float("nan")) == EINVAL
+    assert _decode(lib, d=80) == ENOTSUP
+    assert _decode(lib, hq=24, hkv=2) == ENOTSUP       # group 12 not built
+    assert _decode(lib, hq=256, hkv=2) == ENOTSUP      # group 128 not built
+    assert _decode(lib, bs=3) == ENOTSUP
+    assert _decode(lib, dt=5) == ENOTSUP
+    assert _decode(lib, batch=9000) == ENOTSUP
+    need = lib.gqa_paged_decode_workspace_size(2, 8, 2, 128, 0)
+    assert need > 0
+    assert _decode(lib, wsb=need - 1) == ENOSPC
+    assert _decode(lib, ws=None, wsb=0) == ENOSPC
+    assert _decode(lib, batch=0) == 0
+
+
+def test_workspace_size_formula(lib):
+    # (splits + B * Hkv) pieces x G heads x (d + 2) floats
+    assert lib.gqa_paged_decode_workspace_size(64, 32, 8, 128, 100) == (100 + 512) * 4 * 130 * 4
+    assert lib.gqa_paged_decode_workspace_size(8, 64, 8, 128, 0) == (4096 + 64) * 8 * 130 * 4
+    assert lib.gqa_paged_decode_workspace_size(2, 6, 4, 128, 0) == 0
+    assert lib.gqa_paged_decode_workspace_size(-1, 8, 2, 128, 0) == 0
+
+
+def _prefill(lib, **kw):
+    a = dict(q=P[0], k=P[1], v=P[2], cu=P[3], batch=3, T=17, maxs=9, hq=32, hkv=8, d=128, scale=0.088,
+             causal=1, dt=BF16, out=P[4])
+    a.update(kw)
+    return lib.gqa_varlen_prefill(a["q"], a["k"], a["v"], a["cu"], a["batch"], a["T"], a["maxs"], a["hq"],
+                                  a["hkv"], a["d"], a["scale"], a["causal"], a["dt"], a["out"], None)
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib, hq=30) == EINVAL
+    assert _prefill(lib, T=-1) == EINVAL
+    assert _prefill(lib, cu=None) == EINVAL
+    assert _prefill(lib, out=P[4] + 2) == EINVAL
+    assert _prefill(lib, dt=F32) == ENOTSUP             # bf16 MFMA path only
+    assert _prefill(lib, d=32) == ENOTSUP
+    assert _prefill(lib, hq=24, hkv=8) == ENOTSUP       # group 3
+    assert _prefill(lib, batch=0) == 0
+    assert _prefill(lib, T=0) == 0

@@ -1,0 +1,120 @@
+"""Paged GQA decode on the GPU against the fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import workload as W
+from gpu_helpers import DevDecode, assert_close, oracle_decode, say, to_bits, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+DECODE_WORKLOADS = ["tiny_f32", "llama3_8b_decode", "long_ctx_decode", "mqa_decode"]
+
+
+@pytest.mark.parametrize("key", DECODE_WORKLOADS)
+def test_workload_matches_oracle(orc, key):
+    """Full-size workloads, in the launch configuration the benchmark times (library split choice)."""
+    case = W.make_workload(key)
+    say(f"decode {key} B={case.batch} Hq={case.num_q_heads} Hkv={case.num_kv_heads}")
+    dev = DevDecode(case)
+    out = to_f64(dev.decode())
+    torch.cuda.synchronize()
+    ref = oracle_decode(orc, case)
+    e = assert_close(out, ref, case.dtype, key)
+    say(f"decode {key}: {e}")
+
+
+@pytest.mark.parametrize("key", ["llama3_8b_decode", "mqa_decode"])
+def test_sharpened_queries(orc, key):
+    """q scaled by 4 (exact in bf16) makes the softmax peaked and the outputs O(1)."""
+    case = W.make_workload(key)
+    q4 = W.f32_to_bf16_bits(W.bf16_bits_to_f32(case.q) * np.float32(4.0))
+    case.q = q4
+    say(f"decode sharpened {key}")
+    out = to_f64(DevDecode(case).decode())
+    ref = oracle_decode(orc, case)
+    assert np.abs(ref).max() > 0.5
+    assert_close(out, ref, case.dtype, f"sharpened {key}")
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (8, 2), (16, 2), (8, 1), (16, 1), (32, 1), (64, 1)])
+def test_shapes(orc, dtype, d, hq, hkv):
+    lens = [1, 17, 96, 203, 3]
+    case = W.make_decode_case(lens, hq, hkv, d, 16, dtype, seed=hq * 100 + hkv * 10 + d)
+    say(f"decode shape {dtype} d{d} {hq}/{hkv}")
+    out = to_f64(DevDecode(case).decode())
+    assert_close(out, oracle_decode(orc, case), dtype, f"{dtype} d{d} {hq}/{hkv}")
+
+
+@pytest.mark.parametrize("bs", [1, 2, 4, 8, 16, 32, 64, 256])
+def test_block_sizes(orc, bs):
+    case = W.make_decode_case([1, bs, bs + 1, 3 * bs - 1, 150], 8, 2, 128, bs, W.BF16, seed=300 + bs)
+    say(f"decode bs{bs}")
+    out = to_f64(DevDecode(case).decode())
+    assert_close(out, oracle_decode(orc, case), W.BF16, f"bs{bs}")
+
+
+def test_edge_contexts(orc):
+    """Empty, single-token, page- and tile-aligned and ragged contexts in one batch."""
+    lens = [0, 1, 15, 16, 17, 31, 32, 33, 64, 65, 0, 1000]
+    case = W.make_decode_case(lens, 32, 8, 128, 16, W.BF16, seed=41)
+    say("decode edge contexts")
+    out = to_f64(DevDecode(case).decode())
+    ref = oracle_decode(orc, case)
+    assert np.all(out[0] == 0) and np.all(out[10] == 0), "empty context must give zeros"
+    assert_close(out, ref, W.BF16, "edge contexts")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 64, 997, 4096])
+def test_split_counts(orc, splits):
+    """Any split of the work gives the oracle's answer and is deterministic run to run."""
+    case = W.make_decode_case([700, 33, 2100, 1, 0, 4096, 515], 32, 8, 128, 16, W.BF16, seed=51)
+    say(f"decode splits={splits}")
+    dev = DevDecode(case)
+    a = dev.decode(num_splits=splits)
+    b = dev.decode(num_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "not deterministic"
+    assert_close(to_f64(a), oracle_decode(orc, case), W.BF16, f"splits={splits}")
+
+
+def test_placement_invariance():
+    """Another page permutation, a bigger pool and extra table columns: bit-identical output."""
+    case = W.make_decode_case([300, 45, 1024, 7], 32, 8, 128, 16, W.BF16, seed=61)
+    say("decode placement invariance")
+    base = DevDecode(case).decode(num_splits=5)
+    table, nb = W.place_pages(np.random.default_rng(5), case.context_lens, 16, pool_factor=3.0, extra_cols=9)
+    moved = DevDecode(case, table=table, num_blocks=nb).decode(num_splits=5)
+    torch.cuda.synchronize()
+    assert torch.equal(base.view(torch.int16), moved.view(torch.int16))
+
+
+def test_batch_independence():
+    """A sequence's output does not depend on the rest of its batch (single share each)."""
+    case = W.make_decode_case([300, 45, 1024, 7], 8, 2, 128, 16, W.BF16, seed=62)
+    say("decode batch independence")
+    full = DevDecode(case).decode(num_splits=1)
+    for b in range(case.batch):
+        a, e = int(case.cu_ctx[b]), int(case.cu_ctx[b + 1])
+        one = W.make_decode_case([int(case.context_lens[b])], 8, 2, 128, 16, W.BF16, seed=63)
+        one.q, one.k, one.v = case.q[b:b + 1].copy(), case.k[a:e].copy(), case.v[a:e].copy()
+        alone = DevDecode(one).decode(num_splits=1)
+        torch.cuda.synchronize()
+        assert torch.equal(alone[0].view(torch.int16), full[b].view(torch.int16)), f"sequence {b}"
+
+
+def test_gqa_equals_repeated_mha():
+    """GQA(32, 8) on the GPU equals MHA(32) with each KV head repeated 4 times (same splits)."""
+    case = W.make_decode_case([130, 77], 32, 8, 128, 16, W.BF16, seed=64)
+    mha = W.make_decode_case([130, 77], 32, 32, 128, 16, W.BF16, seed=64)
+    mha.q = case.q
+    mha.k = np.repeat(case.k, 4, axis=1)
+    mha.v = np.repeat(case.v, 4, axis=1)
+    say("decode GQA vs repeated MHA")
+    g = DevDecode(case).decode(num_splits=1)
+    m = DevDecode(mha).decode(num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.allclose(g.float(), m.float(), atol=1e-2, rtol=0)
