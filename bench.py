@@ -38,6 +38,8 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill line item")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle timing budget")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (scale for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -162,7 +164,7 @@ def cpu_baseline(args, case, W):
         ref = orc.gqa_paged_decode(case.q, kc, vc, case.block_table, case.context_lens, case.scale)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= args.cpu_seconds or reps >= 50:
+        if el >= args.cpu_seconds or reps >= 1000:
             break
     per_step = el / reps
     return ref, {"value": case.kv_bytes() / per_step / 1e9, "unit": "GB/s", "cores": orc.max_threads(),
@@ -187,6 +189,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.calibrate_copy:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch give
+        # the counter-to-bytes scale used for the decode kernel's HBM traffic.
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "dispatches": 5}), flush=True)
+        return 0
 
     dec = decode_leg(args, torch, pg, W, T)
     kv = dec["kv_bytes"]
