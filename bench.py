@@ -38,6 +38,11 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill line item")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle timing budget")
+    ap.add_argument("--decode-workload", default="llama3_8b_decode",
+                    choices=["llama3_8b_decode", "long_ctx_decode", "mqa_decode", "tiny_f32"],
+                    help="decode workload to time (the headline is llama3_8b_decode)")
+    ap.add_argument("--num-splits", type=int, default=0,
+                    help="decode work shares (0 = the library's choice)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (scale for HBM byte counters)")
     return ap.parse_args()
@@ -48,7 +53,7 @@ def log(msg):
 
 
 def decode_leg(args, torch, pg, W, T):
-    case = W.make_workload("llama3_8b_decode")
+    case = W.make_workload(args.decode_workload)
     B, hq, hkv, d, bs = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size
     kv_bytes = case.kv_bytes()
     log(f"decode workload: B={B} ctx sum={int(case.context_lens.sum())} KV bytes={kv_bytes}")
@@ -71,7 +76,7 @@ def decode_leg(args, torch, pg, W, T):
         pools.append((kc, vc))
     del k_all, v_all
     out = torch.empty_like(q)
-    ws = pg.decode_workspace(B, hq, hkv, d, 0, q.device)
+    ws = pg.decode_workspace(B, hq, hkv, d, args.num_splits, q.device)
     scale = float(case.scale)
     maxctx = case.max_context_len
 
@@ -80,7 +85,8 @@ def decode_leg(args, torch, pg, W, T):
         pg.paged_kv_write(k_new, v_new, cu_new, sp_new, table, kc, vc)
         if ev is not None:
             ev[0].record()
-        pg.gqa_paged_decode(q, kc, vc, table, ctx, maxctx, scale=scale, out=out, workspace=ws)
+        pg.gqa_paged_decode(q, kc, vc, table, ctx, maxctx, scale=scale, out=out, num_splits=args.num_splits,
+                            workspace=ws)
         if ev is not None:
             ev[1].record()
 
@@ -207,13 +213,14 @@ def main():
     achieved = kv / (dec["decode_ms_mean"] * 1e-3) / 1e9
     case = dec["case"]
     line = {
-        "metric": "decode KV-read GB/s (Llama-3-8B-shaped GQA decode, B=64)",
+        "metric": ("decode KV-read GB/s (Llama-3-8B-shaped GQA decode, B=64)" if args.decode_workload == "llama3_8b_decode"
+                   else f"decode KV-read GB/s ({args.decode_workload})"),
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(dec["ms_per_step"], 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), bf16-rounded)",
-        "config": {"workload": "llama3_8b_decode", "batch": case.batch, "num_q_heads": case.num_q_heads,
+        "config": {"workload": args.decode_workload, "batch": case.batch, "num_q_heads": case.num_q_heads,
                    "num_kv_heads": case.num_kv_heads, "head_dim": case.head_dim, "block_size": case.block_size,
-                   "context_lens": "U[512,4096] seed 2", "kv_bytes_per_step": kv,
+                   "context_lens": W.WORKLOADS[args.decode_workload].description, "kv_bytes_per_step": kv,
                    "tokens_per_step": case.batch},
         "tokens_per_s": round(case.batch / (dec["ms_per_step"] * 1e-3), 1),
         "decode_call_us": {"mean": round(dec["decode_ms_mean"] * 1e3, 2),

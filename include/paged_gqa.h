@@ -117,9 +117,10 @@ int paged_kv_gather(const void* k_cache, const void* v_cache,
 
 /*
  * Bytes of device workspace gqa_paged_decode needs for these sizes: fp32
- * split-KV partials (running max, sum and unnormalised output per query
- * head) for at most (num_splits + batch * Hkv) pieces.  num_splits = 0 sizes
- * it for the library's own choice.  Returns 0 for invalid sizes.
+ * split-KV partials (running max, sum and unnormalised output per query head)
+ * for at most (num_splits + batch * Hkv) pieces.  num_splits = 0 sizes it for
+ * the library's own choice.  Returns 0 for invalid sizes.  Its contents need no
+ * initialisation; two calls that may run at the same time must not share it.
  */
 size_t gqa_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads,
                                        int32_t num_kv_heads, int32_t head_dim,
@@ -134,9 +135,9 @@ size_t gqa_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads,
  *   out[b][qh] = sum_j softmax(s)_j * V_j        (exact softmax; fp32 accumulation)
  * A sequence with context length 0 gets an all-zero output.
  * Work is split into num_splits equal shares of all (sequence, KV head) tiles
- * (0 = library choice, which fills the GPU); a sequence cut across shares is
- * merged exactly with a log-sum-exp reduction in a second kernel.  The
- * result is deterministic for a given num_splits.
+ * (0 = library choice, which fills the GPU); the partials of a sequence cut
+ * across shares are merged exactly (log-sum-exp, in share order) by a second
+ * kernel.  The result is deterministic for a given num_splits.
  *   q            [batch, Hq, d]
  *   k_cache, v_cache [num_blocks, Hkv, block_size, d]
  *   block_table  [batch, max_blocks_per_seq]; entries past ceil(ctx/bs) never read

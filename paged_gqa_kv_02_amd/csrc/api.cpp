@@ -95,10 +95,7 @@ size_t gqa_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32
                                        int32_t head_dim, int32_t num_splits) {
     if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_splits < 0) return 0;
     if (num_q_heads % num_kv_heads) return 0;
-    const int64_t splits = num_splits > 0 ? num_splits : pgqa::kDecodeMaxSplits;
-    const int64_t slots = splits + (int64_t)batch * num_kv_heads;
-    const int64_t group = num_q_heads / num_kv_heads;
-    return (size_t)(slots * group * (head_dim + 2) * 4);
+    return pgqa::decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, num_splits);
 }
 
 int gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,

@@ -19,22 +19,30 @@
 //    therefore balance across the 256 CUs.  A share that covers a whole
 //    segment writes the output; a segment cut across shares writes fp32
 //    partials (running max m, sum l, unnormalised o) merged by decode_merge.
-//  * Streaming: each tile is 4 KB of K plus 4 KB of V (bf16, d = 128), moved
-//    with 16-byte-per-lane global->LDS DMA (global_load_lds_dwordx4) into a
-//    ring of NSTAGE tiles, so loads for later tiles are in flight while the
-//    current one is computed and no VGPRs are tied up by the prefetch.
+//    (Merging inside the split kernel by the last-arriving share needs
+//    device-scope release fences, which write back every XCD's L2 and cost far
+//    more than the second launch.)
+//  * Streaming: a tile is RPT 1 KB rows of K plus RPT rows of V, moved with
+//    16-byte-per-lane global->LDS DMA (global_load_lds_dwordx4) into a ring of
+//    kStages tiles, so loads for later tiles are in flight while the current
+//    one is computed and no VGPRs are tied up by the prefetch.
 //  * Lane mapping: LPT = d*elem/16 lanes cover one token row (16 lanes for
 //    bf16 d = 128), so one wave row holds TPR = 64/LPT tokens.  Each lane keeps
 //    its 16-byte slice of the G query rows in registers; every K row is read
 //    once from LDS and used for all G query heads of the group.
-//  * Dot products: v_dot2_f32_bf16 (fp32 accumulate) then a DPP butterfly over
-//    the LPT lanes of the row.  Softmax state (m, l, o) is kept per lane and
-//    merged across the TPR token groups with shuffles once per share.
-//  * Online softmax with a lazy rescale: o and l are rescaled only when the
-//    running max grows by more than 8 (log2 units), which keeps every weight
+//  * Scores: v_dot2_f32_bf16 partial dot products, then a reduce-scatter
+//    butterfly of DPP exchanges over the LPT lanes of the row: each exchange
+//    both adds and halves the heads a lane keeps, so a lane ends with the full
+//    score of one head (11 DPP steps instead of 16 for 4 heads, and one exp per
+//    lane instead of 4).  The weights are then broadcast back across the row
+//    (DPP row_newbcast) for the P.V accumulation in fp32.
+//  * Online softmax in log2 units with the scale folded into the exponent,
+//    p = exp2(s * scale*log2e - m), and a lazy rescale: o and l are rescaled
+//    only when a running max grows by more than 8, which keeps every weight
 //    <= 256 and is exact because the final o / l uses the same reference max.
-//  * Masking selects (never multiplies): scores past the context become -inf
-//    and V rows past the context are zeroed, so NaN in unused slots cannot leak.
+//  * Masking selects (never multiplies) and only on the ragged last tile of a
+//    sequence: scores past the context become -inf and V rows past the context
+//    are zeroed, so NaN in unused slots cannot leak.
 //  * Large groups (G >= 16) use G/8 waves per workgroup sharing one ring; each
 //    wave owns 8 query heads.
 #include "device_common.hpp"
@@ -42,6 +50,13 @@
 
 #include <math.h>
 #include <mutex>
+
+#ifndef PGQA_DECODE_STAGES
+#define PGQA_DECODE_STAGES 2
+#endif
+#ifndef PGQA_DECODE_RPT
+#define PGQA_DECODE_RPT 8
+#endif
 
 namespace pgqa {
 
@@ -63,23 +78,115 @@ struct DecodeArgs {
     int32_t num_blocks;
     int32_t bs_log2;
     int32_t ctx_cap;     // max_context_len: device context lengths are clamped to it
-    int32_t num_splits;  // number of shares == gridDim.x of the split kernel
+    int32_t num_splits;  // requested shares == gridDim.x of the split kernel
     float scale_log2;    // scale * log2(e): scores live in log2 units, weights use exp2
 };
+
+constexpr int kStages = PGQA_DECODE_STAGES;   // ring depth (tiles) of the split kernel
+constexpr int kRows = PGQA_DECODE_RPT;        // 1 KB wave rows per tile, for K and for V
+static_assert(kStages >= 2 && kStages <= 6, "ring depth");
+static_assert(kRows == 1 || kRows == 2 || kRows == 4 || kRows == 8 || kRows == 16, "rows per tile");
 
 template <int ES, int D>
 struct Geo {
     static constexpr int EPL = 16 / ES;          // elements per lane per 16-byte load
     static constexpr int LPT = D / EPL;          // lanes per token row
     static constexpr int TPR = kWave / LPT;      // tokens per 1 KB wave row
-    static constexpr int RPT = 4;                // wave rows per tile, for K and for V
+    static constexpr int RPT = kRows;            // wave rows per tile
     static constexpr int TT = RPT * TPR;         // tokens per tile
     static constexpr int ROWB = 1024;
     static constexpr int TILEB = 2 * RPT * ROWB; // bytes of K + V per tile
-    static_assert(LPT >= 1 && LPT <= 32 && TPR * LPT == kWave, "unsupported head_dim / dtype");
+    static_assert(LPT >= 2 && LPT <= 32 && TPR * LPT == kWave, "unsupported head_dim / dtype");
 };
 
-constexpr int kStages = 3;   // ring depth (tiles) of the split kernel
+constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
+
+// Reduce-scatter of GW per-lane partial dot products over the LPT lanes of a
+// token row.  Split step s (partner distance LPT >> (s+1)) halves the values a
+// lane keeps: the lane with that distance bit set keeps the upper half of its
+// heads.  After NSPLIT steps each lane holds VPL full sums, for heads
+// head_off(lane) .. +VPL; the remaining steps only add.
+template <int LPT, int GW>
+struct Scatter {
+    static constexpr int NSPLIT = ilog2c(GW) < ilog2c(LPT) ? ilog2c(GW) : ilog2c(LPT);
+    static constexpr int VPL = GW >> NSPLIT;
+
+    __device__ static int head_off(int lane) {
+        int off = 0;
+#pragma unroll
+        for (int s = 0; s < NSPLIT; ++s)
+            if (lane & (LPT >> (s + 1))) off += GW >> (s + 1);
+        return off;
+    }
+    // Lane (within the token group) that holds head g, and which of its values.
+    static constexpr int owner(int g) {
+        int lane = 0, rem = g;
+        for (int s = 0; s < NSPLIT; ++s) {
+            const int half = GW >> (s + 1);
+            if (rem >= half) {
+                lane |= LPT >> (s + 1);
+                rem -= half;
+            }
+        }
+        return lane;
+    }
+    static constexpr int slot(int g) {
+        int rem = g;
+        for (int s = 0; s < NSPLIT; ++s) {
+            const int half = GW >> (s + 1);
+            if (rem >= half) rem -= half;
+        }
+        return rem;
+    }
+};
+
+// Exchange with a partner at distance DLT inside an aligned group of 2*DLT lanes
+// (the partner has bit DLT flipped; row_half_mirror also flips the bits below,
+// which the later steps sum over).
+template <int DLT>
+__device__ __forceinline__ float xchg(float x) {
+    if constexpr (DLT == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+    else if constexpr (DLT == 8) return dpp_f32<0x128>(x);   // row_ror:8 == lane ^ 8 within 16
+    else if constexpr (DLT == 4) return dpp_f32<0x141>(x);   // row_half_mirror
+    else if constexpr (DLT == 2) return dpp_f32<0x4E>(x);    // quad_perm [2,3,0,1]
+    else return dpp_f32<0xB1>(x);                              // quad_perm [1,0,3,2]
+}
+
+template <int DLT, int N>
+__device__ __forceinline__ void scatter_steps(float* v, int lane) {
+    if constexpr (DLT >= 1) {
+        if constexpr (N > 1) {
+            const bool hi = (lane & DLT) != 0;
+#pragma unroll
+            for (int k = 0; k < N / 2; ++k) {
+                const float keep = hi ? v[N / 2 + k] : v[k];
+                const float send = hi ? v[k] : v[N / 2 + k];
+                v[k] = keep + xchg<DLT>(send);
+            }
+            scatter_steps<DLT / 2, N / 2>(v, lane);
+        } else {
+            v[0] += xchg<DLT>(v[0]);
+            scatter_steps<DLT / 2, 1>(v, lane);
+        }
+    }
+}
+
+// Value of lane OWNER of this lane's token group, broadcast to the whole group.
+template <int LPT, int OWNER>
+__device__ __forceinline__ float group_bcast(float x, int lane) {
+    if constexpr (LPT == 16) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + OWNER, 0xF, 0xF, false));
+    } else if constexpr (LPT == 4) {
+        constexpr int ctrl = OWNER | (OWNER << 2) | (OWNER << 4) | (OWNER << 6);
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, false));
+    } else if constexpr (LPT == 2) {
+        constexpr int ctrl = OWNER | (OWNER << 2) | ((2 + OWNER) << 4) | ((2 + OWNER) << 6);
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, false));
+    } else {
+        const int src = (lane & ~(LPT - 1)) | OWNER;
+        return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+    }
+}
 
 __device__ __forceinline__ int tiles_of(int ctx, int cap, int tt) {
     ctx = clampi(ctx, 0, cap);
@@ -130,36 +237,69 @@ __device__ __forceinline__ void store_out16(char* dst, const float* f, float inv
     }
 }
 
+// The block-table entries of the pages a piece streams, one per lane: lane k
+// holds the block of page base + k.  A tile's block ids are then read with
+// v_readlane (no memory access on the issue path); the window moves forward
+// (one vector load) when a page is 64 or more past its base.  Entries are
+// clamped to the sequence's last page and to the pool, so every read is in range.
+struct PageWin {
+    const int32_t* bt_row;
+    int last_page;
+    int num_blocks;
+    int base;
+    int reg;
+
+    __device__ __forceinline__ void load(int first, int lane) {
+        base = first;
+        reg = clampi(bt_row[min(first + lane, last_page)], 0, num_blocks - 1);
+    }
+    __device__ __forceinline__ int get(int page, int lane) {
+        if (page - base >= kWave) load(page, lane);
+        return __builtin_amdgcn_readlane(reg, page - base);
+    }
+};
+
 // Issue the global->LDS loads of one tile (token rows of K, then of V) into
-// ring slot `slot`.  Wave `wave` issues the loads li with li % W == wave, so each
-// wave issues exactly 2*RPT/W loads per tile (the wait counts rely on it).
+// ring slot `slot`.  Wave `wave` issues the loads li with li % W == wave (the
+// wait counts rely on the per-wave count being fixed).
 template <int ES, int D, int W>
 __device__ __forceinline__ void issue_tile(const DecodeArgs& a, PGQA_LDS char* ring, int slot, int tile,
-                                           int h, int ctx, const int32_t* __restrict__ bt_row,
-                                           int wave, int lane) {
+                                           int h, int ctx, PageWin& win, int wave, int lane) {
     using Gm = Geo<ES, D>;
     const int tg = lane / Gm::LPT;
     const int bs_mask = (1 << a.bs_log2) - 1;
     const int tile_tok = tile * Gm::TT;
     PGQA_LDS char* dst = ring + slot * Gm::TILEB;
-    if (Gm::TT <= (1 << a.bs_log2)) {
-        // The tile lies inside one page (the page is allocated because the tile
-        // starts before the context end), and its K rows are one contiguous
-        // 4 KB run of that page: row r of the tile is bytes [1024 r, 1024 r + 1024).
-        // Slots past the context are read (in bounds) and masked in compute.
-        const int bid = clampi(bt_row[tile_tok >> a.bs_log2], 0, a.num_blocks - 1);
-        const int64_t run = ((((int64_t)bid * a.num_kv_heads + h) << a.bs_log2) + (tile_tok & bs_mask)) * (D * ES);
-        const char* kp = a.k_cache + run + lane * 16;
-        const char* vp = a.v_cache + run + lane * 16;
+    if (Gm::TPR <= (1 << a.bs_log2)) {
+        // Every 1 KB row (TPR tokens) lies in one page, so row r is one
+        // contiguous run of that page.  Row starts are clamped to the last row
+        // holding a context token (TPR-aligned): rows past the context re-read
+        // that row (in bounds) and are masked in compute.
+        const int last_row_tok = (ctx - 1) & ~(Gm::TPR - 1);
+        int64_t run[Gm::RPT];
+        if (Gm::TT <= (1 << a.bs_log2)) {
+            // The whole tile is in one page (it starts before the context end).
+            const int bid = win.get(tile_tok >> a.bs_log2, lane);
+            const int64_t base = ((((int64_t)bid * a.num_kv_heads + h) << a.bs_log2) + (tile_tok & bs_mask)) * (D * ES);
+#pragma unroll
+            for (int r = 0; r < Gm::RPT; ++r) run[r] = base + r * Gm::ROWB + lane * 16;
+        } else {
+#pragma unroll
+            for (int r = 0; r < Gm::RPT; ++r) {
+                const int tok = min(tile_tok + r * Gm::TPR, last_row_tok);
+                const int bid = win.get(tok >> a.bs_log2, lane);
+                run[r] = ((((int64_t)bid * a.num_kv_heads + h) << a.bs_log2) + (tok & bs_mask)) * (D * ES) + lane * 16;
+            }
+        }
 #pragma unroll
         for (int li = 0; li < 2 * Gm::RPT; ++li) {
             if (li % W != wave) continue;
             const int r = li % Gm::RPT;
             const bool isv = li >= Gm::RPT;
-            load_lds_16((isv ? vp : kp) + r * Gm::ROWB, dst + li * Gm::ROWB);
+            load_lds_16((isv ? a.v_cache : a.k_cache) + run[r], dst + li * Gm::ROWB);
         }
     } else {
-        // Pages smaller than a tile: each lane looks up its own token's page
+        // Pages smaller than a row: each lane looks up its own token's page
         // (positions clamped to the context so every table read is in range).
         const int c = lane % Gm::LPT;
         int blk[Gm::RPT];
@@ -167,7 +307,7 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, PGQA_LDS char* r
 #pragma unroll
         for (int r = 0; r < Gm::RPT; ++r) {
             tok[r] = min(tile_tok + r * Gm::TPR + tg, ctx - 1);
-            blk[r] = clampi(bt_row[tok[r] >> a.bs_log2], 0, a.num_blocks - 1);
+            blk[r] = clampi(win.bt_row[tok[r] >> a.bs_log2], 0, a.num_blocks - 1);
         }
 #pragma unroll
         for (int li = 0; li < 2 * Gm::RPT; ++li) {
@@ -181,13 +321,158 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, PGQA_LDS char* r
     }
 }
 
+template <int LPT, int OWNER>
+__device__ __forceinline__ u32 group_bcast_u32(u32 x, int lane) {
+    return __float_as_uint(group_bcast<LPT, OWNER>(__uint_as_float(x), lane));
+}
+
+template <int LPT, int GW, int G0 = 0>
+__device__ __forceinline__ void bcast_heads_u32(const u32* vals, u32* out, int lane) {
+    if constexpr (G0 < GW) {
+        using S = Scatter<LPT, GW>;
+        out[G0] = group_bcast_u32<LPT, S::owner(G0)>(vals[S::slot(G0)], lane);
+        bcast_heads_u32<LPT, GW, G0 + 1>(vals, out, lane);
+    }
+}
+
+// Broadcast each head's owned value (vals[slot(g)] at lane owner(g)) to every
+// lane of the token group: out[g] for g < GW.
+template <int LPT, int GW, int G0 = 0>
+__device__ __forceinline__ void bcast_heads(const float* vals, float* out, int lane) {
+    if constexpr (G0 < GW) {
+        using S = Scatter<LPT, GW>;
+        out[G0] = group_bcast<LPT, S::owner(G0)>(vals[S::slot(G0)], lane);
+        bcast_heads<LPT, GW, G0 + 1>(vals, out, lane);
+    }
+}
+
+// One tile: scores, online-softmax update and P.V for this wave's GW heads.
+// FULL: every token of the tile is inside the context (no masking needed).
+template <bool FULL, int ES, int D, int GW>
+__device__ __forceinline__ void tile_compute(const PGQA_LDS char* kb, const PGQA_LDS char* vb, const u32x4* qv,
+                                             float* m, float* l, float (*o)[16 / ES], int tok0, int ctx, float c,
+                                             int lane) {
+    using Gm = Geo<ES, D>;
+    using S = Scatter<Gm::LPT, GW>;
+    constexpr int EPL = Gm::EPL, RPT = Gm::RPT, TPR = Gm::TPR, VPL = S::VPL;
+
+    float s[RPT][VPL];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const u32x4 kx = lds_read_16(kb + r * Gm::ROWB);
+        float v[GW];
+#pragma unroll
+        for (int g = 0; g < GW; ++g) v[g] = slice_dot<ES>(qv[g], kx);
+        scatter_steps<Gm::LPT / 2, GW>(v, lane);
+        const bool valid = FULL || (tok0 + r * TPR < ctx);
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) s[r][k] = valid ? v[k] : -INFINITY;
+    }
+    bool need = false;
+    float mt[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        float x = s[0][k];
+#pragma unroll
+        for (int r = 1; r < RPT; ++r) x = fmaxf(x, s[r][k]);
+        mt[k] = x * c;
+        need |= mt[k] > m[k] + 8.0f;
+    }
+    if (__builtin_expect(__any(need), 0)) {
+        float alpha[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            alpha[k] = 1.0f;
+            if (mt[k] > m[k] + 8.0f) {
+                alpha[k] = __builtin_amdgcn_exp2f(m[k] - mt[k]);
+                m[k] = mt[k];
+                l[k] *= alpha[k];
+            }
+        }
+        float ag[GW];
+        bcast_heads<Gm::LPT, GW>(alpha, ag, lane);
+#pragma unroll
+        for (int g = 0; g < GW; ++g)
+#pragma unroll
+            for (int x = 0; x < EPL; ++x) o[g][x] *= ag[g];
+    }
+    if constexpr (ES == 2) {
+        // P.V on v_dot2_f32_bf16 over pairs of token rows (r, r+1): the two rows'
+        // values of one dim are packed into one register (v_perm_b32), each
+        // owned weight pair is rounded to bf16 once (v_cvt_pk_bf16_f32) and
+        // broadcast as one packed word per head; accumulation stays in fp32.
+        static_assert(RPT % 2 == 0, "bf16 P.V pairs token rows");
+#pragma unroll
+        for (int r = 0; r < RPT; r += 2) {
+            u32 pk[VPL];
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r][k], c, -m[k]));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1][k], c, -m[k]));
+                l[k] += p0 + p1;
+                pk[k] = pack_bf16x2_rne_hw(p0, p1);
+            }
+            u32 pg[GW];
+            bcast_heads_u32<Gm::LPT, GW>(pk, pg, lane);
+            u32x4 v0 = lds_read_16(vb + r * Gm::ROWB);
+            u32x4 v1 = lds_read_16(vb + (r + 1) * Gm::ROWB);
+            if (!FULL) {
+                if (tok0 + r * TPR >= ctx) v0 = u32x4{0, 0, 0, 0};
+                if (tok0 + (r + 1) * TPR >= ctx) v1 = u32x4{0, 0, 0, 0};
+            }
+            const u32 w0[4] = {v0.x, v0.y, v0.z, v0.w};
+            const u32 w1[4] = {v1.x, v1.y, v1.z, v1.w};
+            u32 vp[EPL];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                vp[2 * i] = __builtin_amdgcn_perm(w1[i], w0[i], 0x05040100u);      // (row r, row r+1) of dim 2i
+                vp[2 * i + 1] = __builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u);  // ... of dim 2i+1
+            }
+#pragma unroll
+            for (int g = 0; g < GW; ++g)
+#pragma unroll
+                for (int x = 0; x < EPL; ++x) o[g][x] = dot2_bf16(pg[g], vp[x], o[g][x]);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            float p[VPL];
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                p[k] = __builtin_amdgcn_exp2f(fmaf(s[r][k], c, -m[k]));
+                l[k] += p[k];
+            }
+            float pg[GW];
+            bcast_heads<Gm::LPT, GW>(p, pg, lane);
+            const u32x4 vx = lds_read_16(vb + r * Gm::ROWB);
+            float vf[EPL];
+            unpack16<ES>(vx, vf);
+            if (!FULL && tok0 + r * TPR >= ctx) {
+#pragma unroll
+                for (int x = 0; x < EPL; ++x) vf[x] = 0.0f;
+            }
+#pragma unroll
+            for (int g = 0; g < GW; ++g)
+#pragma unroll
+                for (int x = 0; x < EPL; ++x) o[g][x] = fmaf(pg[g], vf[x], o[g][x]);
+        }
+    }
+}
+
+// Share (workgroup) of the split kernel that holds global tile X, with
+// share w covering tiles [w*total/nw, (w+1)*total/nw).
+__device__ __forceinline__ int64_t share_of(int64_t X, int64_t total, int64_t nw) {
+    return ((X + 1) * nw - 1) / total;
+}
+
 template <int ES, int D, int GW, int W>
 __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     using Gm = Geo<ES, D>;
-    constexpr int EPL = Gm::EPL, LPT = Gm::LPT, TPR = Gm::TPR, RPT = Gm::RPT, TT = Gm::TT;
+    using S = Scatter<Gm::LPT, GW>;
+    constexpr int EPL = Gm::EPL, LPT = Gm::LPT, RPT = Gm::RPT, TT = Gm::TT, VPL = S::VPL;
     constexpr int G = GW * W;
-    constexpr int LPW = 2 * RPT / W;   // loads per wave per tile
-    static_assert((2 * RPT) % W == 0, "loads must split evenly across waves");
+    // Loads per tile: 2*RPT rows, wave w issues rows li with li % W == w.
+    constexpr int LPW_MAX = (2 * RPT + W - 1) / W;
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
     PGQA_LDS char* ring = (PGQA_LDS char*)smem;
@@ -221,6 +506,15 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     const int64_t total = (int64_t)Hkv * pref[B];
     const int64_t NW = min((int64_t)a.num_splits, total);
     const int64_t w = blockIdx.x;
+    // Sequences with no context get zeros (no share visits them).
+    for (int bb = blockIdx.x; bb < B; bb += gridDim.x) {
+        if (pref[bb + 1] != pref[bb]) continue;
+        for (int e = threadIdx.x; e < a.num_q_heads * D; e += 64 * W) {
+            char* dst = a.out + ((int64_t)bb * a.num_q_heads * D + e) * ES;
+            if constexpr (ES == 2) *(uint16_t*)dst = 0;
+            else *(float*)dst = 0.0f;
+        }
+    }
     if (w >= NW) return;
     int64_t X = w * total / NW;
     const int64_t X1 = (w + 1) * total / NW;
@@ -243,13 +537,19 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
 
     const int c = lane % LPT;
     const int tg = lane / LPT;
+    const float cs = a.scale_log2;
+    const int lpw = wave < 2 * RPT ? (2 * RPT - wave + W - 1) / W : 0;   // this wave's loads per tile
 
     while (X < X1) {
         const int n = (int)min((int64_t)(tiles_b - t0), X1 - X);   // tiles in this piece
         const bool whole = (t0 == 0) && (n == tiles_b);
         const int ctx = clampi(a.context_lens[b], 0, a.ctx_cap);
-        const int32_t* bt_row = a.block_table + (int64_t)b * a.max_blocks_per_seq;
         const int qh0 = h * G + wave * GW;
+        PageWin win;
+        win.bt_row = a.block_table + (int64_t)b * a.max_blocks_per_seq;
+        win.last_page = (ctx - 1) >> a.bs_log2;
+        win.num_blocks = a.num_blocks;
+        if (Gm::TPR <= (1 << a.bs_log2)) win.load((t0 * TT) >> a.bs_log2, lane);
 
         // This wave's query slices: GW heads x 16 bytes.
         u32x4 qv[GW];
@@ -257,123 +557,87 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         for (int g = 0; g < GW; ++g)
             qv[g] = *(const u32x4*)(a.q + ((int64_t)(b * a.num_q_heads + qh0 + g) * D + c * EPL) * ES);
 
-        float m[GW], l[GW], o[GW][EPL];
+        // Running max / sum of the heads this lane owns; o for all GW heads.
+        float m[VPL], l[VPL], o[GW][EPL];
 #pragma unroll
-        for (int g = 0; g < GW; ++g) {
-            m[g] = kMaxInit;
-            l[g] = 0.0f;
+        for (int k = 0; k < VPL; ++k) {
+            m[k] = kMaxInit;
+            l[k] = 0.0f;
+        }
+#pragma unroll
+        for (int g = 0; g < GW; ++g)
 #pragma unroll
             for (int x = 0; x < EPL; ++x) o[g][x] = 0.0f;
-        }
 
         // Prologue: fill the first kStages-1 ring slots.
 #pragma unroll
         for (int i = 0; i < kStages - 1; ++i)
-            if (i < n) issue_tile<ES, D, W>(a, ring, i, t0 + i, h, ctx, bt_row, wave, lane);
+            if (i < n) issue_tile<ES, D, W>(a, ring, i, t0 + i, h, ctx, win, wave, lane);
 
-        for (int it = 0; it < n; ++it) {
-            const int tile = t0 + it;
+        // Tiles of the piece: every tile but the piece's last is full (only a
+        // sequence's last tile can be ragged), so the loop body is one path
+        // and the last tile is peeled off with the masked path if it needs it.
+        auto step = [&](int it) {
             const int slot = it % kStages;
-            // Loads issued after this tile's: at most kStages-2 tiles of LPW loads each.
-            wait_vmcnt_dyn<(kStages - 2) * LPW>(LPW * min(kStages - 2, n - 1 - it));
+            // This wave's loads issued after this tile's: at most kStages-2 tiles of lpw each.
+            wait_vmcnt_dyn<(kStages - 2) * LPW_MAX>(lpw * min(kStages - 2, n - 1 - it));
             if constexpr (W > 1) __syncthreads();
             if (it + kStages - 1 < n)
-                issue_tile<ES, D, W>(a, ring, (it + kStages - 1) % kStages, tile + kStages - 1, h, ctx,
-                                     bt_row, wave, lane);
-
-            // ---- compute tile ------------------------------------------------
-            const PGQA_LDS char* kb = ring + (slot * 2) * RPT * Gm::ROWB + lane * 16;
-            const PGQA_LDS char* vb = kb + RPT * Gm::ROWB;
-            const int tok0 = tile * TT + tg;
-            const bool full = (tile + 1) * TT <= ctx;
-
-            float s[RPT][GW];
-#pragma unroll
-            for (int r = 0; r < RPT; ++r) {
-                const u32x4 kx = lds_read_16(kb + r * Gm::ROWB);
-                const bool valid = tok0 + r * TPR < ctx;
-#pragma unroll
-                for (int g = 0; g < GW; ++g) {
-                    const float sc = group_sum<LPT>(slice_dot<ES>(qv[g], kx));
-                    s[r][g] = valid ? sc * a.scale_log2 : -INFINITY;
-                }
-            }
-            bool need = false;
-            float mt[GW];
-#pragma unroll
-            for (int g = 0; g < GW; ++g) {
-                mt[g] = s[0][g];
-#pragma unroll
-                for (int r = 1; r < RPT; ++r) mt[g] = fmaxf(mt[g], s[r][g]);
-                need |= mt[g] > m[g] + 8.0f;
-            }
-            if (__any(need)) {
-#pragma unroll
-                for (int g = 0; g < GW; ++g) {
-                    if (mt[g] > m[g] + 8.0f) {
-                        const float alpha = __builtin_amdgcn_exp2f(m[g] - mt[g]);
-                        m[g] = mt[g];
-                        l[g] *= alpha;
-#pragma unroll
-                        for (int x = 0; x < EPL; ++x) o[g][x] *= alpha;
-                    }
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < RPT; ++r)
-#pragma unroll
-                for (int g = 0; g < GW; ++g) {
-                    s[r][g] = __builtin_amdgcn_exp2f(s[r][g] - m[g]);
-                    l[g] += s[r][g];
-                }
-#pragma unroll
-            for (int r = 0; r < RPT; ++r) {
-                const u32x4 vx = lds_read_16(vb + r * Gm::ROWB);
-                float vf[EPL];
-                unpack16<ES>(vx, vf);
-                if (!full && tok0 + r * TPR >= ctx) {
-#pragma unroll
-                    for (int x = 0; x < EPL; ++x) vf[x] = 0.0f;
-                }
-#pragma unroll
-                for (int g = 0; g < GW; ++g)
-#pragma unroll
-                    for (int x = 0; x < EPL; ++x) o[g][x] = fmaf(s[r][g], vf[x], o[g][x]);
-            }
+                issue_tile<ES, D, W>(a, ring, (it + kStages - 1) % kStages, t0 + it + kStages - 1, h, ctx,
+                                     win, wave, lane);
+            return ring + slot * Gm::TILEB + lane * 16;
+        };
+        for (int it = 0; it < n - 1; ++it) {
+            const PGQA_LDS char* kb = step(it);
+            tile_compute<true, ES, D, GW>(kb, kb + RPT * Gm::ROWB, qv, m, l, o, (t0 + it) * TT + tg, ctx, cs, lane);
+        }
+        {
+            const int it = n - 1;
+            const PGQA_LDS char* kb = step(it);
+            const int tile = t0 + it;
+            if ((tile + 1) * TT <= ctx)
+                tile_compute<true, ES, D, GW>(kb, kb + RPT * Gm::ROWB, qv, m, l, o, tile * TT + tg, ctx, cs, lane);
+            else
+                tile_compute<false, ES, D, GW>(kb, kb + RPT * Gm::ROWB, qv, m, l, o, tile * TT + tg, ctx, cs, lane);
         }
 
-        // ---- merge the TPR token groups of the wave ----------------------------
+        // ---- per-head (m, l) to every lane, then merge the TPR token groups ----
+        float mh[GW], lh[GW];
+        bcast_heads<LPT, GW>(m, mh, lane);
+        bcast_heads<LPT, GW>(l, lh, lane);
 #pragma unroll
         for (int mask = LPT; mask < kWave; mask <<= 1) {
 #pragma unroll
             for (int g = 0; g < GW; ++g) {
-                const float mo = shfl_xor_f32(m[g], mask);
-                const float lo = shfl_xor_f32(l[g], mask);
-                const float mx = fmaxf(m[g], mo);
-                const float a0 = __builtin_amdgcn_exp2f(m[g] - mx);
+                const float mo = shfl_xor_f32(mh[g], mask);
+                const float lo = shfl_xor_f32(lh[g], mask);
+                const float mx = fmaxf(mh[g], mo);
+                const float a0 = __builtin_amdgcn_exp2f(mh[g] - mx);
                 const float a1 = __builtin_amdgcn_exp2f(mo - mx);
-                l[g] = l[g] * a0 + lo * a1;
+                lh[g] = lh[g] * a0 + lo * a1;
 #pragma unroll
                 for (int x = 0; x < EPL; ++x) {
                     const float oo = shfl_xor_f32(o[g][x], mask);
                     o[g][x] = o[g][x] * a0 + oo * a1;
                 }
-                m[g] = mx;
+                mh[g] = mx;
             }
         }
 
-        if (tg == 0) {
-            if (whole) {
+        if (whole) {
+            if (tg == 0) {
 #pragma unroll
                 for (int g = 0; g < GW; ++g) {
-                    const float inv = l[g] > 0.0f ? 1.0f / l[g] : 0.0f;
+                    const float inv = lh[g] > 0.0f ? 1.0f / lh[g] : 0.0f;
                     store_out16<ES>(a.out + ((int64_t)(b * a.num_q_heads + qh0 + g) * D + c * EPL) * ES, o[g], inv);
                 }
-            } else {
-                const int64_t slot_id = w + (int64_t)b * Hkv + h;
+            }
+        } else {
+            const int64_t seg = (int64_t)b * Hkv + h;
+            if (tg == 0) {
 #pragma unroll
                 for (int g = 0; g < GW; ++g) {
-                    const int64_t row = slot_id * G + wave * GW + g;
+                    const int64_t row = (w + seg) * G + wave * GW + g;
                     float* po = a.part_o + row * D + c * EPL;
 #pragma unroll
                     for (int x = 0; x < EPL; x += 4) {
@@ -381,8 +645,8 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
                         *(f32x4*)(po + x) = v4;
                     }
                     if (c == 0) {
-                        a.part_ml[row * 2 + 0] = m[g];
-                        a.part_ml[row * 2 + 1] = l[g];
+                        a.part_ml[row * 2 + 0] = mh[g];
+                        a.part_ml[row * 2 + 1] = lh[g];
                     }
                 }
             }
@@ -405,24 +669,21 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     }
 }
 
-// Share (workgroup) of the split kernel that holds global tile X.
-__device__ __forceinline__ int64_t share_of(int64_t X, int64_t total, int64_t nw) {
-    return ((X + 1) * nw - 1) / total;
-}
-
-// One wave per (sequence, KV head) segment: writes zeros for an empty context,
-// nothing when one share covered the whole segment, else the log-sum-exp merge
-// of the segment's partials in share order (deterministic).
+// One 256-thread workgroup per (sequence, KV head) segment: nothing when one
+// share covered the whole segment (or it is empty), else the log-sum-exp merge
+// of the segment's partials in share order (deterministic).  Every thread owns
+// (head, dim) outputs; the loads of successive shares are independent.
 template <int ES, int D, int G>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int tt) {
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tt) {
+    __shared__ int red[2][4];
+    const int tid = threadIdx.x;
     const int Hkv = a.num_kv_heads;
     const int seg = blockIdx.x;
     const int b = seg / Hkv;
     const int h = seg % Hkv;
 
     int before = 0, all = 0;
-    for (int i = lane; i < a.batch; i += 64) {
+    for (int i = tid; i < a.batch; i += 256) {
         const int t = tiles_of(a.context_lens[i], a.ctx_cap, tt);
         all += t;
         if (i < b) before += t;
@@ -431,44 +692,44 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int tt) 
         before += __shfl_xor(before, mk);
         all += __shfl_xor(all, mk);
     }
-    const int tiles_b = tiles_of(a.context_lens[b], a.ctx_cap, tt);
-    if (tiles_b == 0) {
-        for (int g = 0; g < G; ++g)
-            for (int x = lane; x < D; x += 64) {
-                char* dst = a.out + ((int64_t)(b * a.num_q_heads + h * G + g) * D + x) * ES;
-                if constexpr (ES == 2) *(uint16_t*)dst = 0;
-                else *(float*)dst = 0.0f;
-            }
-        return;
+    if ((tid & 63) == 0) {
+        red[0][tid >> 6] = before;
+        red[1][tid >> 6] = all;
     }
+    __syncthreads();
+    before = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    all = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+
+    const int tiles_b = tiles_of(a.context_lens[b], a.ctx_cap, tt);
+    if (tiles_b == 0) return;   // zero-filled by the split kernel
     const int64_t total = (int64_t)Hkv * all;
     const int64_t nw = min((int64_t)a.num_splits, total);
     const int64_t xs = (int64_t)Hkv * before + (int64_t)h * tiles_b;
-    const int64_t xe = xs + tiles_b - 1;
     const int64_t w0 = share_of(xs, total, nw);
-    const int64_t w1 = share_of(xe, total, nw);
+    const int64_t w1 = share_of(xs + tiles_b - 1, total, nw);
     if (w0 == w1) return;
 
-    for (int g = 0; g < G; ++g) {
-        float mx = -INFINITY;
-        for (int64_t w = w0; w <= w1; ++w) mx = fmaxf(mx, a.part_ml[((w + seg) * G + g) * 2]);
-        float L = 0.0f;
+    for (int e = tid; e < G * D; e += 256) {
+        const int g = e / D;
+        const int x = e % D;
+        float M = -INFINITY, L = 0.0f, acc = 0.0f;
+#pragma unroll 4
         for (int64_t w = w0; w <= w1; ++w) {
-            const float* ml = a.part_ml + ((w + seg) * G + g) * 2;
-            L += __builtin_amdgcn_exp2f(ml[0] - mx) * ml[1];
+            const int64_t row = (w + seg) * G + g;
+            const float mw = a.part_ml[row * 2];
+            const float lw = a.part_ml[row * 2 + 1];
+            const float ow = a.part_o[row * D + x];
+            const float mn = fmaxf(M, mw);
+            const float sa = __builtin_amdgcn_exp2f(M - mn);
+            const float sb = __builtin_amdgcn_exp2f(mw - mn);
+            acc = acc * sa + ow * sb;
+            L = L * sa + lw * sb;
+            M = mn;
         }
-        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-        for (int x = lane; x < D; x += 64) {
-            float acc = 0.0f;
-            for (int64_t w = w0; w <= w1; ++w) {
-                const int64_t row = (w + seg) * G + g;
-                acc += __builtin_amdgcn_exp2f(a.part_ml[row * 2] - mx) * a.part_o[row * D + x];
-            }
-            const float r = acc * inv;
-            char* dst = a.out + ((int64_t)(b * a.num_q_heads + h * G + g) * D + x) * ES;
-            if constexpr (ES == 2) *(uint16_t*)dst = (uint16_t)f32_to_bf16_bits(r);
-            else *(float*)dst = r;
-        }
+        const float r = L > 0.0f ? acc / L : 0.0f;
+        char* dst = a.out + ((int64_t)(b * a.num_q_heads + h * G) * D + e) * ES;
+        if constexpr (ES == 2) *(uint16_t*)dst = (uint16_t)f32_to_bf16_bits(r);
+        else *(float*)dst = r;
     }
 }
 
@@ -558,7 +819,7 @@ int32_t decode_tile_tokens(int32_t elem_bytes, int32_t head_dim) {
     const int epl = 16 / elem_bytes;
     const int lpt = head_dim / epl;
     if (lpt <= 0 || 64 % lpt) return 0;
-    return 4 * (64 / lpt);
+    return kRows * (64 / lpt);
 }
 
 bool decode_supported(int32_t elem_bytes, int32_t head_dim, int32_t group) {
@@ -590,6 +851,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     a.scale_log2 = (float)((double)L.scale * 1.4426950408889634);
 
     const int threads = 64 * e.waves;
+    // ring + tile prefix sums [batch + 1]
     const size_t lds = (size_t)kStages * e.tile_bytes + (((size_t)L.batch + 1) * 4 + 15) / 16 * 16;
     int nw = L.num_splits;
     if (nw <= 0) {
@@ -599,13 +861,21 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     a.num_splits = nw;
     const int64_t slots = (int64_t)nw + (int64_t)L.batch * L.num_kv_heads;
     a.part_o = (float*)L.workspace;
-    a.part_ml = a.part_o + slots * L.num_q_heads / L.num_kv_heads * L.head_dim;
+    a.part_ml = a.part_o + slots * (L.num_q_heads / L.num_kv_heads) * L.head_dim;
 
     hipLaunchKernelGGL(e.split, dim3(nw), dim3(threads), lds, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(e.merge, dim3(L.batch * L.num_kv_heads), dim3(64), 0, stream, a, e.tt);
+    hipLaunchKernelGGL(e.merge, dim3(L.batch * L.num_kv_heads), dim3(256), 0, stream, a, e.tt);
     return hipGetLastError();
+}
+
+size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t num_splits) {
+    const int64_t splits = num_splits > 0 ? num_splits : kDecodeMaxSplits;
+    const int64_t slots = splits + (int64_t)batch * num_kv_heads;
+    const int64_t group = num_q_heads / num_kv_heads;
+    return (size_t)(slots * group * (head_dim + 2) * 4);
 }
 
 }  // namespace pgqa

@@ -41,6 +41,13 @@ __device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// Two fp32 -> packed bf16 pair (lo, hi) with the hardware's round-to-nearest-even.
+__device__ __forceinline__ u32 pack_bf16x2_rne_hw(float lo, float hi) {
+    typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(u32, __builtin_convertvector(v, bf16x2));
+}
+
 // bf16 pair dot product accumulated in fp32: acc + a.lo*b.lo + a.hi*b.hi
 __device__ __forceinline__ float dot2_bf16(u32 a, u32 b, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),

@@ -61,6 +61,10 @@ bool decode_supported(int32_t elem_bytes, int32_t head_dim, int32_t group);
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
 
+// Decode workspace: fp32 partials for (splits + batch * Hkv) pieces x G heads x (head_dim + 2).
+size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t num_splits);
+
 struct PrefillLaunch {
     const void* q;
     const void* k;

@@ -80,6 +80,7 @@ def gqa_paged_decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: 
 
 def decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, num_splits: int = 0,
                      device=None) -> torch.Tensor:
+    """Device workspace for gqa_paged_decode (contents need no initialisation)."""
     n = gqa_paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, num_splits)
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device or "cuda")
 

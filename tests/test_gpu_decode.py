@@ -118,3 +118,24 @@ def test_gqa_equals_repeated_mha():
     m = DevDecode(mha).decode(num_splits=1)
     torch.cuda.synchronize()
     assert torch.allclose(g.float(), m.float(), atol=1e-2, rtol=0)
+
+
+def test_workspace_reuse(orc):
+    """One workspace reused across calls (different split counts and batches,
+    stale partials from the previous call left in it): outputs stay correct."""
+    import paged_gqa_kv_02_amd as pg
+    case = W.make_decode_case([700, 33, 2100, 1, 0, 4096, 515], 32, 8, 128, 16, W.BF16, seed=71)
+    small = W.make_decode_case([300, 45], 32, 8, 128, 16, W.BF16, seed=72)
+    dev, dev_s = DevDecode(case), DevDecode(small)
+    ws = pg.decode_workspace(case.batch, 32, 8, 128, 0)
+    ref = oracle_decode(orc, case)
+    ref_s = oracle_decode(orc, small)
+    for splits in (0, 3, 97, 0):
+        say(f"decode workspace reuse splits={splits}")
+        out = pg.gqa_paged_decode(dev.q, dev.kc, dev.vc, dev.table, dev.ctx, case.max_context_len,
+                                  scale=float(case.scale), num_splits=splits, workspace=ws)
+        out_s = pg.gqa_paged_decode(dev_s.q, dev_s.kc, dev_s.vc, dev_s.table, dev_s.ctx, small.max_context_len,
+                                    scale=float(small.scale), num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(to_f64(out), ref, W.BF16, f"reuse splits={splits}")
+        assert_close(to_f64(out_s), ref_s, W.BF16, f"reuse small splits={splits}")
