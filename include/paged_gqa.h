@@ -169,6 +169,10 @@ int gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
  * for the PV product.  bf16 only.
  *   q [total_tokens, Hq, d], k / v [total_tokens, Hkv, d], out [total_tokens, Hq, d]
  *   cu_seqlens [batch + 1]; max_seqlen = host-side upper bound of the lengths
+ * Errors: PGQA_EINVAL (bad sizes or pointers, or a problem whose workgroup
+ * count would pass 2^31: about (max_seqlen/32) * batch * Hq), PGQA_ENOTSUP
+ * (fp32, head_dim other than 64 / 128, group size not 1, 2 or a multiple of 4
+ * up to 64), PGQA_EHIP.
  */
 int gqa_varlen_prefill(const void* q, const void* k, const void* v,
                        const int32_t* cu_seqlens, int32_t batch, int32_t total_tokens,

@@ -142,6 +142,12 @@ int gqa_varlen_prefill(const void* q, const void* k, const void* v, const int32_
     if (!pgqa::prefill_supported(head_dim, num_q_heads / num_kv_heads)) return PGQA_ENOTSUP;
     if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff()) return PGQA_EINVAL;
     if ((int64_t)total_tokens * num_q_heads * head_dim > ((int64_t)1 << 40)) return PGQA_EINVAL;
+    // Grid size (one workgroup per 32-row query tile, head group and sequence)
+    // and 32-bit K/V offsets inside a 64-key block.
+    if ((int64_t)(max_seqlen / 32 + 1) * ((int64_t)batch * num_kv_heads + 7) * (num_q_heads / num_kv_heads) >
+        INT32_MAX)
+        return PGQA_EINVAL;
+    if ((int64_t)num_kv_heads * head_dim * 2 * 64 > INT32_MAX) return PGQA_EINVAL;
     if (check_elem_ptr(q) || check_elem_ptr(k) || check_elem_ptr(v) || check_elem_ptr(out)) return PGQA_EINVAL;
     if (check_index_ptr(cu_seqlens)) return PGQA_EINVAL;
     if (batch == 0 || total_tokens == 0 || max_seqlen == 0) return PGQA_OK;

@@ -14,17 +14,28 @@
 //    waves are 4 query heads of the KV head's group (or, for G < 4, G heads x
 //    4/G consecutive 32-token blocks), so every K/V tile staged in LDS serves
 //    128 query rows: GQA reuse of K/V across the group.
-//  * Each wave computes S^T = K Q^T for 32 keys x its 32 query rows.  In the
-//    32x32 accumulator layout a lane then holds 16 keys of ONE query row, so the
+//  * K and V tiles of 64 keys stream through a 2-stage LDS ring with
+//    global->LDS DMA (global_load_lds_dwordx4, 16 B per lane, 1 KB per
+//    instruction).  Rows are XOR-swizzled by 16-byte chunk (chunk c of key row r
+//    lands in chunk c ^ f(r), f a per-row bijection); the swizzle is chosen
+//    through each lane's source address, so the global reads stay whole rows,
+//    and makes both LDS read patterns below bank-conflict-free.
+//  * Each wave computes S^T = K Q^T for 64 keys x its 32 query rows.  In the
+//    32x32 accumulator layout a lane then holds 32 keys of ONE query row, so the
 //    row max / sum need a single cross-lane step (lane ^ 32).
-//  * O^T += V^T P^T: the B operand (P^T) is exactly the lane's own S^T values
-//    rounded to bf16, taken in the key order the accumulator layout gives; the
-//    A operand is V^T read from LDS, where V is stored transposed while staged.
-//  * Online softmax in log2 units with a lazy rescale (only when a row max grows
-//    by more than 8), exact because the final O / l uses the same reference.
-//  * Masks select -inf (never multiply); keys past the sequence are staged as
-//    zeros.  Only the diagonal block (causal) and the ragged last block mask.
-//  * Query tiles are launched heaviest-first (reverse order) to shorten the tail.
+//  * O^T += V^T P^T: the B operand (P^T) is the lane's own S^T values rounded to
+//    bf16, taken in the key order the accumulator layout gives; the A operand
+//    (V^T) comes straight from the row-major V tile with ds_read_b64_tr_b16,
+//    the transposing LDS read (two reads give the 8 keys of one dim per lane,
+//    in exactly the B operand's key order).
+//  * Online softmax in log2 units with the scale folded into the exponent and a
+//    lazy rescale (only when a row max grows by more than 8), exact because the
+//    final O / l uses the same reference.
+//  * Masks select -inf (never multiply) and only on the diagonal block (causal)
+//    and the ragged last block; key rows past the sequence are clamped to its
+//    last row (in bounds, masked).
+//  * Tiles of one (sequence, KV head) pair share an XCD (and its L2); each XCD
+//    runs its tiles heaviest-first (reverse query-tile order) to shorten the tail.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -43,51 +54,160 @@ struct PrefillArgs {
     int32_t num_kv_heads;
     int32_t causal;
     float scale_log2;
+    int32_t batch;
+    int32_t nqt;             // query-tile levels (tiles of the longest sequence)
+    int32_t pairs_per_xcd;   // ceil(batch * num_kv_heads / 8)
 };
 
+typedef short __attribute__((ext_vector_type(4))) i16x4;
+
 constexpr int BQ = 32;   // query rows per wave
-constexpr int BN = 32;   // keys per block
+constexpr int BN = 64;   // keys per block
+
+template <int D>
+struct PGeo {
+    static constexpr int ROWB = D * 2;            // bytes per K/V row
+    static constexpr int CPR = D / 8;             // 16-byte chunks per row
+    static constexpr int RPL = 64 / CPR;          // rows per 1 KB wave-load
+    static constexpr int TILEB = BN * ROWB;       // K (or V) tile bytes
+    static constexpr int LOADS = TILEB / 1024;    // wave-loads per K (or V) tile
+    static constexpr int STAGEB = 2 * TILEB;      // K + V tile
+    static constexpr int KSTEPS = D / 16;         // k-steps of S^T over head_dim
+    static constexpr int DBLK = D / 32;           // 32-row blocks of O^T over head_dim
+    static_assert((2 * LOADS) % 4 == 0, "loads split over 4 waves");
+};
+
+// Row r's swizzle key.  LDS has 64 banks of 4 bytes; a 16-byte-per-lane read
+// is served 16 lanes at a time and an 8-byte transposed read 32 lanes at a
+// time, so a read is conflict-free when every lane of a phase hits its own
+// 16-byte bank group.  The K operand read (one chunk from each of 16
+// consecutive rows) needs the key to be a permutation on every aligned run of
+// 16 rows; the transposed V read (chunks 4b .. 4b+3 of 4 consecutive rows)
+// needs the keys of an aligned run of 4 rows to differ in bits 2..3.  For 64-dim
+// rows (two rows per 256-byte bank line) the same holds per row parity.
+template <int D>
+__device__ __forceinline__ int swz_key(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Byte offset of 16-byte chunk c of key row r inside a swizzled tile.
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+    using P = PGeo<D>;
+    return r * P::ROWB + ((c ^ swz_key<D>(r)) << 4);
+}
+
+// DMA of key block kb into ring slot `slot`.  Waves 0 and 1 fetch the K tile,
+// waves 2 and 3 the V tile, NPW 1 KB wave-loads each.  `soff` holds the lane's
+// source offsets relative to the block's first key row (row * row stride +
+// swizzled chunk); a block that runs past the sequence end clamps its rows to
+// the last key instead (those keys are masked out of the scores).
+template <int D>
+struct DmaLane {
+    static constexpr int NPW = 2 * PGeo<D>::LOADS / 4;
+    uint32_t soff[NPW];
+};
+
+template <int D>
+__device__ __forceinline__ void dma_lane_init(DmaLane<D>& dl, int wave, int lane, int64_t kvstride) {
+    using P = PGeo<D>;
+#pragma unroll
+    for (int j = 0; j < DmaLane<D>::NPW; ++j) {
+        const int r = ((wave & 1) * DmaLane<D>::NPW + j) * P::RPL + lane / P::CPR;
+        const int c = (lane % P::CPR) ^ swz_key<D>(r);
+        dl.soff[j] = (uint32_t)(r * kvstride + c * 16);
+    }
+}
+
+// One 16-byte-per-lane LDS DMA: lane l copies 16 bytes from sbase + voff into
+// LDS at lds + 16*l (M0 holds the wave's LDS base).  Written as inline
+// assembly so that the compiler does not track it: its own tracking would make
+// every later LDS read wait for the DMA of the next block as well.  The kernel
+// waits for the DMA explicitly (vmcnt at the top of each block).  M0 is used
+// for nothing else in this file's kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int D>
+__device__ __forceinline__ void issue_block(const PrefillArgs& a, const DmaLane<D>& dl, uint32_t ring, int slot,
+                                            int kb, int seq0, int L, int kvh, int wave, int lane,
+                                            int64_t kvstride) {
+    using P = PGeo<D>;
+    constexpr int NPW = DmaLane<D>::NPW;
+    const bool isv = wave >= 2;
+    const char* base = (isv ? a.v : a.k) + (int64_t)(seq0 + kb * BN) * kvstride + (int64_t)kvh * P::ROWB;
+    const uint32_t dst = ring + slot * P::STAGEB + (isv ? P::TILEB : 0) + (wave & 1) * NPW * 1024;
+    if (kb * BN + BN <= L) {
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) dma16(base, dl.soff[j], dst + j * 1024);
+    } else {
+        const int last = L - 1 - kb * BN;
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) {
+            const int r = ((wave & 1) * NPW + j) * P::RPL + lane / P::CPR;
+            const int c = (lane % P::CPR) ^ swz_key<D>(r);
+            dma16(base, (uint32_t)(min(r, last) * kvstride + c * 16), dst + j * 1024);
+        }
+    }
+}
 
 template <int D, int HG>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+    using P = PGeo<D>;
     constexpr int TB = 4 / HG;               // 32-row token blocks per workgroup
-    constexpr int KSTEPS = D / 16;           // k-steps of S^T over head_dim
-    constexpr int DBLK = D / 32;             // 32-row blocks of O^T over head_dim
-    constexpr int KROW = D * 2 + 16;         // padded K row in LDS (bytes)
-    constexpr int VROW = BN * 2 + 8;         // padded V^T row in LDS (bytes)
-    constexpr int CPR = D / 8;               // 16-byte chunks per K/V row
-    constexpr int CHUNKS = BN * CPR;         // chunks per K (or V) block
-    constexpr int PER_T = (CHUNKS + 255) / 256;
-    static_assert(CHUNKS % 256 == 0, "K/V block must split evenly over 256 threads");
+    constexpr int KSTEPS = P::KSTEPS, DBLK = P::DBLK;
 
-    __shared__ __attribute__((aligned(16))) char k_lds[BN * KROW];
-    __shared__ __attribute__((aligned(16))) char vt_lds[D * VROW];
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    PGQA_LDS char* ring = (PGQA_LDS char*)smem;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5;
     const int l32 = lane & 31;
     const int G = a.num_q_heads / a.num_kv_heads;
     const int groups = G / HG;
 
-    const int s = blockIdx.z;
+    // Work mapping.  Workgroups are dealt to the 8 XCDs round-robin by linear
+    // id and every XCD has its own L2, so all tiles of one (sequence, KV head)
+    // pair stay on one XCD: pair p = seq * Hkv + kvh lives on XCD p % 8.  On
+    // each XCD the tiles run heaviest-first: query-tile level from the top, then
+    // the XCD's pairs, then the head groups sharing the pair's K/V.
+    const int id = blockIdx.x;
+    const int per_level = a.pairs_per_xcd * groups;
+    const int level = (id >> 3) / per_level;
+    const int rem = (id >> 3) - level * per_level;
+    const int pair = (id & 7) + 8 * (rem / groups);
+    if (pair >= a.batch * a.num_kv_heads) return;
+    const int s = pair / a.num_kv_heads;
+    const int kvh = pair - s * a.num_kv_heads;
     const int seq0 = clampi(a.cu_seqlens[s], 0, a.total_tokens);
     const int L = clampi(a.cu_seqlens[s + 1], seq0, a.total_tokens) - seq0;
-    const int qtile = gridDim.x - 1 - blockIdx.x;
+    const int qtile = a.nqt - 1 - level;
     const int tok0 = qtile * TB * BQ;
     if (tok0 >= L) return;
-    const int kvh = blockIdx.y / groups;
-    const int head = kvh * G + (blockIdx.y % groups) * HG + (wave % HG);
+    const int head = kvh * G + (rem % groups) * HG + (wave % HG);
     const int i0 = tok0 + (wave / HG) * BQ;          // this wave's first query row (sequence-local)
 
     const int wg_rows_end = min(L, tok0 + TB * BQ);
     const int nkb = a.causal ? (wg_rows_end + BN - 1) / BN : (L + BN - 1) / BN;
     const bool active = i0 < L;
     const int last_kb = a.causal ? min(nkb - 1, (i0 + BQ - 1) / BN) : nkb - 1;
+    const float cs = a.scale_log2;
 
-    const int64_t qstride = (int64_t)a.num_q_heads * D * 2;    // bytes per packed Q row
-    const int64_t kvstride = (int64_t)a.num_kv_heads * D * 2;  // bytes per packed K/V row
+    const int64_t qstride = (int64_t)a.num_q_heads * D * 2;   // bytes per packed Q row
+    const int64_t kvstride = (int64_t)a.num_kv_heads * P::ROWB;
+
+    // Prologue: first key block in flight while Q is read.
+    DmaLane<D> dl;
+    dma_lane_init<D>(dl, wave, lane, kvstride);
+    const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+    issue_block<D>(a, dl, ring_addr, 0, 0, seq0, L, kvh, wave, lane, kvstride);
 
     // Q^T operand: lane holds row (i0 + l32), d = 16*kk + 8*half .. +8.
     u32x4 qreg[KSTEPS];
@@ -105,70 +225,76 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
 
-    // Register prefetch of one K/V block: thread chunk c -> key c / CPR, 16-byte column c % CPR.
-    u32x4 kpre[PER_T], vpre[PER_T];
-    auto fetch = [&](int kb) {
+    // V^T operand addressing (ds_read_b64_tr_b16): in each 16-lane group, lane j
+    // supplies row (key0 + j/4), dims d0 + 4*(j%4) .. +3 of the V tile; lane i
+    // of the group then receives dims d0 + i of keys key0 .. key0+3.
+    const int gl = lane & 15;
+    const int vrow = gl >> 2;                          // + key0
+    const int vdim = 16 * ((lane >> 4) & 1) + 4 * (gl & 3);   // + 32*db
+    // Per-lane LDS offsets, fixed for the whole key loop.  K: row 32*kb2 + l32
+    // (kb2 adds 32 rows, which keeps the swizzle key), chunk 2*kk + half.
+    // V: rows 16*kk + 4*half + vrow (+8), dims 32*db + vdim; 16*kk rows keep the
+    // swizzle key, so the offsets depend only on (db, lo/hi).
+    int koff[KSTEPS];
 #pragma unroll
-        for (int e = 0; e < PER_T; ++e) {
-            const int ch = tid + e * 256;
-            const int key = kb * BN + ch / CPR;
-            const int col = ch % CPR;
-            if (key < L) {
-                const int64_t off = (int64_t)(seq0 + key) * kvstride + (int64_t)kvh * D * 2 + col * 16;
-                kpre[e] = *(const u32x4*)(a.k + off);
-                vpre[e] = *(const u32x4*)(a.v + off);
-            } else {
-                kpre[e] = u32x4{0, 0, 0, 0};
-                vpre[e] = u32x4{0, 0, 0, 0};
-            }
-        }
-    };
+    for (int kk = 0; kk < KSTEPS; ++kk) koff[kk] = swz<D>(l32, 2 * kk + half);
+    int voff[DBLK][2];
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+        const int dd = 32 * db + vdim;
+        voff[db][0] = swz<D>(4 * half + vrow, dd >> 3) + ((dd & 7) << 1);
+        voff[db][1] = swz<D>(8 + 4 * half + vrow, dd >> 3) + ((dd & 7) << 1);
+    }
 
-    fetch(0);
     for (int kb = 0; kb < nkb; ++kb) {
-        __syncthreads();   // every wave is done reading the previous block
-#pragma unroll
-        for (int e = 0; e < PER_T; ++e) {
-            const int ch = tid + e * 256;
-            const int key = ch / CPR;
-            const int col = ch % CPR;
-            *(u32x4*)(k_lds + key * KROW + col * 16) = kpre[e];
-            const u32 w[4] = {vpre[e].x, vpre[e].y, vpre[e].z, vpre[e].w};
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                *(uint16_t*)(vt_lds + (col * 8 + 2 * x) * VROW + key * 2) = (uint16_t)(w[x] & 0xffffu);
-                *(uint16_t*)(vt_lds + (col * 8 + 2 * x + 1) * VROW + key * 2) = (uint16_t)(w[x] >> 16);
-            }
-        }
-        __syncthreads();
-        if (kb + 1 < nkb) fetch(kb + 1);
+        const int slot = kb & 1;
+        wait_vmcnt<0>();
+        __syncthreads();   // this block's tiles are in LDS; every wave is done with the other slot
+        if (kb + 1 < nkb) issue_block<D>(a, dl, ring_addr, slot ^ 1, kb + 1, seq0, L, kvh, wave, lane, kvstride);
 
         if (active && kb <= last_kb) {
+            const PGQA_LDS char* kt = ring + slot * P::STAGEB;
+            const PGQA_LDS char* vt = kt + P::TILEB;
             const int j0 = kb * BN;
-            // S^T = K Q^T: lane (l32, half) gets rows l32, keys 8*(i/4) + 4*half + i%4.
-            f32x16 st;
+            // S^T = K Q^T: per 32-key half kb2, lane (l32, half) gets row l32,
+            // keys 32*kb2 + 8*(i/4) + 4*half + i%4.
+            f32x16 st[2];
+            u32x4 ka[KSTEPS];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) st[i] = 0.0f;
+            for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = lds_read_16(kt + koff[kk]);
 #pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk) {
-                const u32x4 ka = *(const u32x4*)(k_lds + l32 * KROW + kk * 32 + half * 16);
-                st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka),
-                                                             __builtin_bit_cast(bf16x8, qreg[kk]), st, 0, 0, 0);
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) st[kb2][i] = 0.0f;
+#pragma unroll
+                for (int kk = 0; kk < KSTEPS; ++kk) {
+                    st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[kk]),
+                                                                      __builtin_bit_cast(bf16x8, qreg[kk]), st[kb2],
+                                                                      0, 0, 0);
+                    if (kb2 == 0) ka[kk] = lds_read_16(kt + 32 * P::ROWB + koff[kk]);
+                }
             }
-            const int row = i0 + l32;
-            const bool edge = (j0 + BN > L) || (a.causal && j0 + BN - 1 > i0);
+            // Masking (last block of the sequence, or blocks crossing the
+            // diagonal): key j0 + off is kept iff off <= lim, with
+            // off = 32*kb2 + 8*(i/4) + i%4 and the lane's 4*half folded into lim.
+            if ((j0 + BN > L) || (a.causal && j0 + BN - 1 > i0)) {
+                const int lim = (a.causal ? min(i0 + l32, L - 1) : L - 1) - j0 - 4 * half;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = j0 + 8 * (i >> 2) + 4 * half + (i & 3);
-                const bool ok = !edge || (key < L && (!a.causal || key <= row));
-                st[i] = ok ? st[i] * a.scale_log2 : -INFINITY;
+                for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int off = 32 * kb2 + 8 * (i >> 2) + (i & 3);
+                        st[kb2][i] = off <= lim ? st[kb2][i] : -INFINITY;
+                    }
             }
-            float mt = st[0];
+            float mt = st[0][0];
 #pragma unroll
-            for (int i = 1; i < 16; ++i) mt = fmaxf(mt, st[i]);
-            mt = fmaxf(mt, shfl_xor_f32(mt, 32));
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mt = fmaxf(mt, st[kb2][i]);
+            mt = fmaxf(mt, shfl_xor_f32(mt, 32)) * cs;
             const bool need = mt > m + 8.0f;
-            if (__any(need)) {
+            if (__builtin_expect(__any(need), 0)) {
                 if (need) {
                     const float alpha = __builtin_amdgcn_exp2f(m - mt);
                     m = mt;
@@ -179,31 +305,37 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
                 }
             }
-            u32x4 pb[2];
+            // P^T operand for 16-key step kk: keys 16kk + 8*(jj/4) + 4*half + jj%4,
+            // i.e. accumulator entries 8*(kk%2) .. +7 of half kk/2.
+            u32x4 pb[4];
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
+            for (int kk = 0; kk < 4; ++kk) {
                 float p[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    p[j] = __builtin_amdgcn_exp2f(st[8 * k2 + j] - m);
+                    p[j] = __builtin_amdgcn_exp2f(fmaf(st[kk >> 1][8 * (kk & 1) + j], cs, -m));
                     lsum += p[j];
                 }
-                pb[k2] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                               pack_bf16x2(p[6], p[7])};
+                pb[kk] = u32x4{pack_bf16x2_rne_hw(p[0], p[1]), pack_bf16x2_rne_hw(p[2], p[3]),
+                               pack_bf16x2_rne_hw(p[4], p[5]), pack_bf16x2_rne_hw(p[6], p[7])};
             }
-            // O^T += V^T P^T: A = V^T rows d, keys {16*k2 + 4*half + 0..3, 16*k2 + 8 + 4*half + 0..3}.
+            // O^T += V^T P^T: A = V^T for dims 32*db + l32, keys {16kk + 4*half + 0..3, +8 ..}.
 #pragma unroll
             for (int db = 0; db < DBLK; ++db) {
-                const char* vrow = vt_lds + (db * 32 + l32) * VROW + half * 8;
+                u32x4 va[4];
 #pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) {
-                    const u32x2 lo = *(const u32x2*)(vrow + k2 * 32);
-                    const u32x2 hi = *(const u32x2*)(vrow + k2 * 32 + 16);
-                    const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va),
-                                                                    __builtin_bit_cast(bf16x8, pb[k2]), o[db], 0, 0,
-                                                                    0);
+                for (int kk = 0; kk < 4; ++kk) {
+                    const PGQA_LDS char* vk = vt + 16 * kk * P::ROWB;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PGQA_LDS i16x4*)(vk + voff[db][0]));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PGQA_LDS i16x4*)(vk + voff[db][1]));
+                    va[kk] = u32x4{__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
+                                   __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y};
                 }
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[kk]),
+                                                                    __builtin_bit_cast(bf16x8, pb[kk]), o[db], 0, 0,
+                                                                    0);
             }
         }
     }
@@ -220,8 +352,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         for (int qd = 0; qd < 4; ++qd) {
             const int d = db * 32 + 8 * qd + 4 * half;
             u32x2 w;
-            w.x = pack_bf16x2(o[db][4 * qd + 0] * inv, o[db][4 * qd + 1] * inv);
-            w.y = pack_bf16x2(o[db][4 * qd + 2] * inv, o[db][4 * qd + 3] * inv);
+            w.x = pack_bf16x2_rne_hw(o[db][4 * qd + 0] * inv, o[db][4 * qd + 1] * inv);
+            w.y = pack_bf16x2_rne_hw(o[db][4 * qd + 2] * inv, o[db][4 * qd + 3] * inv);
             *(u32x2*)(op + d * 2) = w;
         }
 }
@@ -243,6 +375,8 @@ bool pick(int head_dim, int group, PrefillFn* fn, int* hg) {
     }
     return false;
 }
+
+size_t lds_bytes(int head_dim) { return head_dim == 128 ? 2 * PGeo<128>::STAGEB : 2 * PGeo<64>::STAGEB; }
 
 }  // namespace
 
@@ -268,10 +402,13 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
     a.num_kv_heads = L.num_kv_heads;
     a.causal = L.causal;
     a.scale_log2 = (float)((double)L.scale * 1.4426950408889634);
+    a.batch = L.batch;
     const int rows_per_wg = (4 / hg) * BQ;
-    const int nqt = (L.max_seqlen + rows_per_wg - 1) / rows_per_wg;
-    dim3 grid(nqt, L.num_kv_heads * (group / hg), L.batch);
-    hipLaunchKernelGGL(fn, grid, dim3(256), 0, stream, a);
+    a.nqt = (L.max_seqlen + rows_per_wg - 1) / rows_per_wg;
+    a.pairs_per_xcd = (int)(((int64_t)L.batch * L.num_kv_heads + 7) / 8);
+    const int64_t wgs = 8 * (int64_t)a.nqt * a.pairs_per_xcd * (group / hg);
+    if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(256), lds_bytes(L.head_dim), stream, a);
     return hipGetLastError();
 }
 
