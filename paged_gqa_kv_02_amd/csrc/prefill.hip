@@ -14,7 +14,7 @@
 //    waves are 4 query heads of the KV head's group (or, for G < 4, G heads x
 //    4/G consecutive 32-token blocks), so every K/V tile staged in LDS serves
 //    128 query rows: GQA reuse of K/V across the group.
-//  * K and V tiles of 64 keys stream through a 2-stage LDS ring with
+//  * K and V tiles of 64 keys stream through two 2-slot LDS rings (K, V) with
 //    global->LDS DMA (global_load_lds_dwordx4, 16 B per lane, 1 KB per
 //    instruction).  Rows are XOR-swizzled by 16-byte chunk (chunk c of key row r
 //    lands in chunk c ^ f(r), f a per-row bijection); the swizzle is chosen
@@ -30,12 +30,20 @@
 //    in exactly the B operand's key order).
 //  * Online softmax in log2 units with the scale folded into the exponent and a
 //    lazy rescale (only when a row max grows by more than 8), exact because the
-//    final O / l uses the same reference.
+//    final O / l uses the same reference.  The row sum l adds the bf16-rounded
+//    weights (v_dot2 with (1, 1)), i.e. exactly the weights the PV product used.
 //  * Masks select -inf (never multiply) and only on the diagonal block (causal)
 //    and the ragged last block; key rows past the sequence are clamped to its
 //    last row (in bounds, masked).
 //  * Tiles of one (sequence, KV head) pair share an XCD (and its L2); each XCD
-//    runs its tiles heaviest-first (reverse query-tile order) to shorten the tail.
+//    works through its pairs one at a time, a pair's tiles heaviest-first, so
+//    K/V is fetched from HBM about once.
+//  * The softmax of key block k overlaps the MFMAs of block k+1's scores
+//    (software pipeline within the wave: two score buffers, separate K and V
+//    rings so K(k+1) and V(k) are resident together).
+//  * The output tile is staged through LDS and written as whole rows.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -106,14 +114,17 @@ __device__ __forceinline__ int swz(int r, int c) {
 template <int D>
 struct DmaLane {
     static constexpr int NPW = 2 * PGeo<D>::LOADS / 4;
-    uint32_t soff[NPW];
+    // Loads j and j + JP are 16 rows apart, which keeps the swizzle key, so
+    // they differ by 16 rows of source only (added to the uniform base).
+    static constexpr int JP = 16 / PGeo<D>::RPL;
+    uint32_t soff[JP];
 };
 
 template <int D>
 __device__ __forceinline__ void dma_lane_init(DmaLane<D>& dl, int wave, int lane, int64_t kvstride) {
     using P = PGeo<D>;
 #pragma unroll
-    for (int j = 0; j < DmaLane<D>::NPW; ++j) {
+    for (int j = 0; j < DmaLane<D>::JP; ++j) {
         const int r = ((wave & 1) * DmaLane<D>::NPW + j) * P::RPL + lane / P::CPR;
         const int c = (lane % P::CPR) ^ swz_key<D>(r);
         dl.soff[j] = (uint32_t)(r * kvstride + c * 16);
@@ -134,18 +145,21 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t
 }
 #pragma clang diagnostic pop
 
+// DMA of one tile of key block kb: waves 0 and 1 fetch K(kb) into K slot
+// kb % 2, waves 2 and 3 fetch V(kb) into V slot kb % 2 (LDS: K slots, then V
+// slots).
 template <int D>
-__device__ __forceinline__ void issue_block(const PrefillArgs& a, const DmaLane<D>& dl, uint32_t ring, int slot,
-                                            int kb, int seq0, int L, int kvh, int wave, int lane,
-                                            int64_t kvstride) {
+__device__ __forceinline__ void issue_tile(const PrefillArgs& a, const DmaLane<D>& dl, uint32_t ring, int kb,
+                                           int seq0, int L, int kvh, int wave, int lane, int64_t kvstride) {
     using P = PGeo<D>;
     constexpr int NPW = DmaLane<D>::NPW;
     const bool isv = wave >= 2;
     const char* base = (isv ? a.v : a.k) + (int64_t)(seq0 + kb * BN) * kvstride + (int64_t)kvh * P::ROWB;
-    const uint32_t dst = ring + slot * P::STAGEB + (isv ? P::TILEB : 0) + (wave & 1) * NPW * 1024;
+    const uint32_t dst = ring + (isv ? 2 * P::TILEB : 0) + (kb & 1) * P::TILEB + (wave & 1) * NPW * 1024;
     if (kb * BN + BN <= L) {
+        constexpr int JP = DmaLane<D>::JP;
 #pragma unroll
-        for (int j = 0; j < NPW; ++j) dma16(base, dl.soff[j], dst + j * 1024);
+        for (int j = 0; j < NPW; ++j) dma16(base + (j / JP) * 16 * kvstride, dl.soff[j % JP], dst + j * 1024);
     } else {
         const int last = L - 1 - kb * BN;
 #pragma unroll
@@ -175,14 +189,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
     // Work mapping.  Workgroups are dealt to the 8 XCDs round-robin by linear
     // id and every XCD has its own L2, so all tiles of one (sequence, KV head)
-    // pair stay on one XCD: pair p = seq * Hkv + kvh lives on XCD p % 8.  On
-    // each XCD the tiles run heaviest-first: query-tile level from the top, then
-    // the XCD's pairs, then the head groups sharing the pair's K/V.
+    // pair stay on one XCD: pair p = seq * Hkv + kvh lives on XCD p % 8.  Each
+    // XCD runs its pairs one after another (so the K/V being read at any time
+    // is that of one or two pairs, which its L2 holds), and a pair's tiles
+    // heaviest-first (query tiles from the last), the head groups sharing the
+    // pair's K/V side by side.
     const int id = blockIdx.x;
-    const int per_level = a.pairs_per_xcd * groups;
-    const int level = (id >> 3) / per_level;
-    const int rem = (id >> 3) - level * per_level;
-    const int pair = (id & 7) + 8 * (rem / groups);
+    const int per_pair = a.nqt * groups;
+    const int kq = (id >> 3) / per_pair;                 // the XCD's kq-th pair
+    const int r2 = (id >> 3) - kq * per_pair;
+    const int level = r2 / groups;
+    const int grp = r2 - level * groups;
+    const int pair = (id & 7) + 8 * kq;
     if (pair >= a.batch * a.num_kv_heads) return;
     const int s = pair / a.num_kv_heads;
     const int kvh = pair - s * a.num_kv_heads;
@@ -191,7 +209,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int qtile = a.nqt - 1 - level;
     const int tok0 = qtile * TB * BQ;
     if (tok0 >= L) return;
-    const int head = kvh * G + (rem % groups) * HG + (wave % HG);
+    const int head = kvh * G + grp * HG + (wave % HG);
     const int i0 = tok0 + (wave / HG) * BQ;          // this wave's first query row (sequence-local)
 
     const int wg_rows_end = min(L, tok0 + TB * BQ);
@@ -203,11 +221,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int64_t qstride = (int64_t)a.num_q_heads * D * 2;   // bytes per packed Q row
     const int64_t kvstride = (int64_t)a.num_kv_heads * P::ROWB;
 
-    // Prologue: first key block in flight while Q is read.
+    // Prologue: K(0), V(0) and K(1) in flight while Q is read.
     DmaLane<D> dl;
     dma_lane_init<D>(dl, wave, lane, kvstride);
     const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
-    issue_block<D>(a, dl, ring_addr, 0, 0, seq0, L, kvh, wave, lane, kvstride);
+    issue_tile<D>(a, dl, ring_addr, 0, seq0, L, kvh, wave, lane, kvstride);
+    if (wave < 2 && nkb > 1) issue_tile<D>(a, dl, ring_addr, 1, seq0, L, kvh, wave, lane, kvstride);
 
     // Q^T operand: lane holds row (i0 + l32), d = 16*kk + 8*half .. +8.
     u32x4 qreg[KSTEPS];
@@ -231,131 +250,186 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int gl = lane & 15;
     const int vrow = gl >> 2;                          // + key0
     const int vdim = 16 * ((lane >> 4) & 1) + 4 * (gl & 3);   // + 32*db
-    // Per-lane LDS offsets, fixed for the whole key loop.  K: row 32*kb2 + l32
-    // (kb2 adds 32 rows, which keeps the swizzle key), chunk 2*kk + half.
-    // V: rows 16*kk + 4*half + vrow (+8), dims 32*db + vdim; 16*kk rows keep the
-    // swizzle key, so the offsets depend only on (db, lo/hi).
-    int koff[KSTEPS];
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) koff[kk] = swz<D>(l32, 2 * kk + half);
-    int voff[DBLK][2];
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-        const int dd = 32 * db + vdim;
-        voff[db][0] = swz<D>(4 * half + vrow, dd >> 3) + ((dd & 7) << 1);
-        voff[db][1] = swz<D>(8 + 4 * half + vrow, dd >> 3) + ((dd & 7) << 1);
-    }
+    // Per-lane LDS offsets, fixed for the whole key loop.  K operand, step kk:
+    // row l32 (+32 per key half, which keeps the swizzle key), chunk 2*kk + half,
+    // i.e. kx ^ (kk << 5).  V operand, dim block db, keys +8h: rows
+    // 4*half + vrow + 8h (+16 per key step, same key), chunk 4*db + vdim/8; the
+    // key of row r + 8 is key(r) ^ 2, so this is (vx ^ (db << 6) ^ (h << 5)) +
+    // 8h rows.  The XORs only touch the chunk field of the offset.
+    const int kx = swz<D>(l32, half);
+    const int vx = swz<D>(4 * half + vrow, vdim >> 3) + ((vdim & 7) << 1);
+    const u32 ones_bf16x2 = 0x3F803F80u;   // (1.0, 1.0) in bf16
 
-    for (int kb = 0; kb < nkb; ++kb) {
-        const int slot = kb & 1;
-        wait_vmcnt<0>();
-        __syncthreads();   // this block's tiles are in LDS; every wave is done with the other slot
-        if (kb + 1 < nkb) issue_block<D>(a, dl, ring_addr, slot ^ 1, kb + 1, seq0, L, kvh, wave, lane, kvstride);
+    // S^T = K Q^T for key block kb (K slot kb % 2): per 32-key half kb2, lane
+    // (l32, half) gets row l32, keys 32*kb2 + 8*(i/4) + 4*half + i%4.
+    auto scores = [&](f32x16 (&st)[2], auto slot) {
+        const PGQA_LDS char* kt = ring + decltype(slot)::value * P::TILEB;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) st[kb2][i] = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk)
+                st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, lds_read_16(kt + 32 * kb2 * P::ROWB + (kx ^ (kk << 5)))),
+                    __builtin_bit_cast(bf16x8, qreg[kk]), st[kb2], 0, 0, 0);
+        }
+    };
 
-        if (active && kb <= last_kb) {
-            const PGQA_LDS char* kt = ring + slot * P::STAGEB;
-            const PGQA_LDS char* vt = kt + P::TILEB;
-            const int j0 = kb * BN;
-            // S^T = K Q^T: per 32-key half kb2, lane (l32, half) gets row l32,
-            // keys 32*kb2 + 8*(i/4) + 4*half + i%4.
-            f32x16 st[2];
-            u32x4 ka[KSTEPS];
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk) ka[kk] = lds_read_16(kt + koff[kk]);
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) st[kb2][i] = 0.0f;
-#pragma unroll
-                for (int kk = 0; kk < KSTEPS; ++kk) {
-                    st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[kk]),
-                                                                      __builtin_bit_cast(bf16x8, qreg[kk]), st[kb2],
-                                                                      0, 0, 0);
-                    if (kb2 == 0) ka[kk] = lds_read_16(kt + 32 * P::ROWB + koff[kk]);
-                }
-            }
-            // Masking (last block of the sequence, or blocks crossing the
-            // diagonal): key j0 + off is kept iff off <= lim, with
-            // off = 32*kb2 + 8*(i/4) + i%4 and the lane's 4*half folded into lim.
-            if ((j0 + BN > L) || (a.causal && j0 + BN - 1 > i0)) {
-                const int lim = (a.causal ? min(i0 + l32, L - 1) : L - 1) - j0 - 4 * half;
-#pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int off = 32 * kb2 + 8 * (i >> 2) + (i & 3);
-                        st[kb2][i] = off <= lim ? st[kb2][i] : -INFINITY;
-                    }
-            }
-            float mt = st[0][0];
+    // One key block: softmax of the block's scores `cur`, overlapped with the
+    // next block's scores into `nxt` (when HAS_NEXT), then O^T += V^T P^T.
+    auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], int kb, auto par, auto has_next) {
+        constexpr int PAR = decltype(par)::value;   // kb % 2
+        const int j0 = kb * BN;
+        // Masking (last block of the sequence, or a block crossing the
+        // diagonal): key j0 + off is kept iff off <= lim, with
+        // off = 32*kb2 + 8*(i/4) + i%4 and the lane's 4*half folded into lim.
+        if ((j0 + BN > L) || (a.causal && j0 + BN - 1 > i0)) {
+            const int lim = (a.causal ? min(i0 + l32, L - 1) : L - 1) - j0 - 4 * half;
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mt = fmaxf(mt, st[kb2][i]);
-            mt = fmaxf(mt, shfl_xor_f32(mt, 32)) * cs;
-            const bool need = mt > m + 8.0f;
-            if (__builtin_expect(__any(need), 0)) {
-                if (need) {
-                    const float alpha = __builtin_amdgcn_exp2f(m - mt);
-                    m = mt;
-                    lsum *= alpha;
-#pragma unroll
-                    for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+                for (int i = 0; i < 16; ++i) {
+                    const int off = 32 * kb2 + 8 * (i >> 2) + (i & 3);
+                    cur[kb2][i] = off <= lim ? cur[kb2][i] : -INFINITY;
                 }
-            }
-            // P^T operand for 16-key step kk: keys 16kk + 8*(jj/4) + 4*half + jj%4,
-            // i.e. accumulator entries 8*(kk%2) .. +7 of half kk/2.
-            u32x4 pb[4];
+        }
+        float mt = cur[0][0];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                float p[8];
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    p[j] = __builtin_amdgcn_exp2f(fmaf(st[kk >> 1][8 * (kk & 1) + j], cs, -m));
-                    lsum += p[j];
-                }
-                pb[kk] = u32x4{pack_bf16x2_rne_hw(p[0], p[1]), pack_bf16x2_rne_hw(p[2], p[3]),
-                               pack_bf16x2_rne_hw(p[4], p[5]), pack_bf16x2_rne_hw(p[6], p[7])};
-            }
-            // O^T += V^T P^T: A = V^T for dims 32*db + l32, keys {16kk + 4*half + 0..3, +8 ..}.
+            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, cur[kb2][i]);
+        mt = fmaxf(mt, shfl_xor_f32(mt, 32)) * cs;
+        const bool need = mt > m + 8.0f;
+        if (__builtin_expect(__any(need), 0)) {
+            if (need) {
+                const float alpha = __builtin_amdgcn_exp2f(m - mt);
+                m = mt;
+                lsum *= alpha;
 #pragma unroll
-            for (int db = 0; db < DBLK; ++db) {
-                u32x4 va[4];
+                for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const PGQA_LDS char* vk = vt + 16 * kk * P::ROWB;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PGQA_LDS i16x4*)(vk + voff[db][0]));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PGQA_LDS i16x4*)(vk + voff[db][1]));
-                    va[kk] = u32x4{__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
-                                   __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y};
-                }
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[kk]),
-                                                                    __builtin_bit_cast(bf16x8, pb[kk]), o[db], 0, 0,
-                                                                    0);
+                    for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
             }
         }
-    }
+        if constexpr (decltype(has_next)::value) scores(nxt, std::integral_constant<int, 1 - PAR>{});
+        // P^T operand for 16-key step kk: keys 16kk + 8*(jj/4) + 4*half + jj%4,
+        // i.e. accumulator entries 8*(kk%2) .. +7 of half kk/2.  The row sum
+        // adds the bf16-rounded weights, the same ones the PV product uses.
+        u32x4 pb[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            float p[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(cur[kk >> 1][8 * (kk & 1) + j], cs, -m));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pb[kk][j] = pack_bf16x2_rne_hw(p[2 * j], p[2 * j + 1]);
+                lsum = dot2_bf16(pb[kk][j], ones_bf16x2, lsum);
+            }
+        }
+        if constexpr (decltype(has_next)::value) {
+            // Interleave: per next-block MFMA one K read and a slice of the
+            // softmax arithmetic, so the VALU work hides under the matrix pipe
+            // and only a few K fragments are live at a time.
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // two K reads ahead
+#pragma unroll
+            for (int i = 0; i < 2 * KSTEPS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                if (i + 2 < 2 * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // K read
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // O^T += V^T P^T: A = V^T for dims 32*db + l32, keys {16kk + 4*half + 0..3, +8 ..}.
+        const PGQA_LDS char* vt = ring + (2 + PAR) * P::TILEB;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+            u32x4 va[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const PGQA_LDS char* vk = vt + 16 * kk * P::ROWB;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PGQA_LDS i16x4*)(vk + (vx ^ (db << 6))));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PGQA_LDS i16x4*)(vk + 8 * P::ROWB + (vx ^ (db << 6) ^ 32)));
+                va[kk] = u32x4{__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
+                               __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y};
+            }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[kk]),
+                                                                __builtin_bit_cast(bf16x8, pb[kk]), o[db], 0, 0, 0);
+        }
+    };
 
+    // Top of block kb: every wave's DMA has landed (K(kb+1), V(kb)) and every
+    // wave is done with K(kb) and V(kb-1), so their slots are refilled with
+    // K(kb+2) and V(kb+1).
+    auto top = [&](int kb) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        const int tb = wave < 2 ? kb + 2 : kb + 1;
+        if (tb < nkb) issue_tile<D>(a, dl, ring_addr, tb, seq0, L, kvh, wave, lane, kvstride);
+    };
+    // Blocks 0 .. kend are computed (kend = last_kb, or -1 for a wave with no
+    // rows); each but the last overlaps the next block's scores.  The two score
+    // buffers alternate, so the loop runs two blocks per trip and every block
+    // fully rewrites the buffer it fills; the ring parity is a compile-time
+    // constant in each copy.  Waves past their last block keep the workgroup's
+    // barriers and DMA going to the end.
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    f32x16 sa[2], sb[2];
+    wait_vmcnt<0>();
+    __syncthreads();
+    const int kend = active ? last_kb : -1;
+    if (kend >= 0) scores(sa, I0{});
+    int kb = 0;
+    for (; kb + 2 <= kend; kb += 2) {
+        top(kb);
+        step(sa, sb, kb, I0{}, std::true_type{});
+        top(kb + 1);
+        step(sb, sa, kb + 1, I1{}, std::true_type{});
+    }
+    if (kb + 1 == kend) {
+        top(kb);
+        step(sa, sb, kb, I0{}, std::true_type{});
+        top(kb + 1);
+        step(sb, sa, kb + 1, I1{}, std::false_type{});
+        kb += 2;
+    } else if (kb == kend) {
+        top(kb);
+        step(sa, sb, kb, I0{}, std::false_type{});
+        kb += 1;
+    }
+    for (; kb < nkb; ++kb) top(kb);
+
+    // Epilogue: O / l rounded to bf16, staged through the idle ring so that
+    // each output row is written whole.  The wave's 32 x D tile goes to LDS
+    // (swizzled like the K/V tiles), then each lane writes one 16-byte chunk of
+    // one row, CPR consecutive lanes per row.
+    __syncthreads();   // every wave is done with the ring
     if (!active) return;
     lsum += shfl_xor_f32(lsum, 32);
-    const int row = i0 + l32;
-    if (row >= L) return;
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-    char* op = a.out + (int64_t)(seq0 + row) * qstride + (int64_t)head * D * 2;
+    PGQA_LDS char* ot = ring + wave * (BQ * P::ROWB);
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
-            const int d = db * 32 + 8 * qd + 4 * half;
+            // dims 32*db + 8*qd + 4*half .. +3 of row l32: chunk 4*db + qd, byte 8*half
             u32x2 w;
             w.x = pack_bf16x2_rne_hw(o[db][4 * qd + 0] * inv, o[db][4 * qd + 1] * inv);
             w.y = pack_bf16x2_rne_hw(o[db][4 * qd + 2] * inv, o[db][4 * qd + 3] * inv);
-            *(u32x2*)(op + d * 2) = w;
+            *(PGQA_LDS u32x2*)(ot + swz<D>(l32, 4 * db + qd) + 8 * half) = w;
         }
+    const int c = lane % P::CPR;
+#pragma unroll
+    for (int t = 0; t < BQ / P::RPL; ++t) {
+        const int r = t * P::RPL + lane / P::CPR;
+        const u32x4 val = lds_read_16(ot + swz<D>(r, c));
+        if (i0 + r < L)
+            *(u32x4*)(a.out + (int64_t)(seq0 + i0 + r) * qstride + (int64_t)head * D * 2 + c * 16) = val;
+    }
 }
 
 typedef void (*PrefillFn)(PrefillArgs);
@@ -376,7 +450,7 @@ bool pick(int head_dim, int group, PrefillFn* fn, int* hg) {
     return false;
 }
 
-size_t lds_bytes(int head_dim) { return head_dim == 128 ? 2 * PGeo<128>::STAGEB : 2 * PGeo<64>::STAGEB; }
+size_t lds_bytes(int head_dim) { return head_dim == 128 ? 4 * PGeo<128>::TILEB : 4 * PGeo<64>::TILEB; }
 
 }  // namespace
 
