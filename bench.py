@@ -48,6 +48,37 @@ def _args():
     return ap.parse_args()
 
 
+def recorded_traffic(path: str):
+    """HBM bytes per call of the decode call and of the prefill kernel, from the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE record (profiles/), each counter
+    scaled by what it reads for a plain copy of known size.  None for a path whose
+    sources have changed since the counters were taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return {"decode": None, "prefill": None}
+    cal = rec["copy_calibration"]
+    out = {}
+    for part in ("decode", "prefill"):
+        r = rec.get(part)
+        if r is None:
+            out[part] = None
+            continue
+        h = hashlib.sha256()
+        for f in r["sources"]:
+            with open(os.path.join(here, f), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest()[:16] != r["sha256_16"]:
+            out[part] = None
+            continue
+        out[part] = int(sum(k["fetch_kib"] * 1024 * cal["fetch_factor"] + k["write_kib"] * 1024 * cal["write_factor"]
+                            for k in r["kernels"].values()))
+    return out
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -207,6 +238,7 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "dispatches": 5}), flush=True)
         return 0
 
+    traffic = recorded_traffic(os.path.join(here, "profiles", "traffic_counters.json"))
     dec = decode_leg(args, torch, pg, W, T)
     kv = dec["kv_bytes"]
     value = kv / (dec["ms_per_step"] * 1e-3) / 1e9
@@ -227,12 +259,13 @@ def main():
                            "median": round(dec["decode_ms_median"] * 1e3, 2),
                            "p10": round(dec["decode_ms_p10"] * 1e3, 2), "p90": round(dec["decode_ms_p90"] * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic["decode"],
                      "kernel": "gqa_paged_decode (split + merge kernels, one call)"},
     }
     if not args.no_prefill:
         log("prefill leg")
         line["prefill"] = prefill_leg(args, torch, pg, W, T)
+        line["prefill"]["roofline"]["traffic"] = traffic["prefill"]
     if not args.no_cpu_baseline:
         log("cpu baseline leg (oracle)")
         ref, cb = cpu_baseline(args, case, W)
