@@ -6,7 +6,10 @@ context lengths U[512, 4096], Hq = 32, Hkv = 8, d = 128, block_size 16, bf16).
 One step = the decode step of the hot path on that batch:
   1. paged_kv_write of each sequence's newest token (position ctx-1) into its page,
   2. gqa_paged_decode over every cached position (split-KV + merge kernels).
-``value`` = algorithmic K/V bytes read per step / wall time per step.
+``value`` = algorithmic K/V bytes read per step / wall time per step, the three
+kernels launched one by one (``--graph`` replays each step as a captured HIP
+graph instead; on this stack that is ~3 % slower).  ``roofline`` times the decode
+call alone (split + merge) with HIP events on its stream, in a second pass.
 
 Inputs stay resident in HBM.  Four copies of the page pools (about 0.77 GB each)
 are used round-robin, so the 256 MB Infinity Cache cannot serve a step from the
@@ -43,6 +46,8 @@ def _args():
                     help="decode workload to time (the headline is llama3_8b_decode)")
     ap.add_argument("--num-splits", type=int, default=0,
                     help="decode work shares (0 = the library's choice)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step as a captured HIP graph instead of launching its kernels one by one")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (scale for HBM byte counters)")
     return ap.parse_args()
@@ -124,15 +129,39 @@ def decode_leg(args, torch, pg, W, T):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    # One HIP graph per pool copy: paged write + split + merge, replayed as one launch.
+    graphs = None
+    if args.graph:
+        graphs = []
+        for i in range(COPIES):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % COPIES].replay()
+        torch.cuda.synchronize()
+
+    # Timed region: exactly --steps steps between two synchronisations.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    if graphs is not None:
+        for i in range(args.steps):
+            graphs[i % COPIES].replay()
+    else:
+        for i in range(args.steps):
+            step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # The decode call alone (split + merge), HIP events on the stream it runs on.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    ms_per_step = wall * 1e3 / args.steps
     return {
         "case": case, "kv_bytes": kv_bytes, "ms_per_step": ms_per_step,
         "decode_ms_mean": float(dec_ms.mean()), "decode_ms_median": float(np.median(dec_ms)),
@@ -253,7 +282,7 @@ def main():
         "config": {"workload": args.decode_workload, "batch": case.batch, "num_q_heads": case.num_q_heads,
                    "num_kv_heads": case.num_kv_heads, "head_dim": case.head_dim, "block_size": case.block_size,
                    "context_lens": W.WORKLOADS[args.decode_workload].description, "kv_bytes_per_step": kv,
-                   "tokens_per_step": case.batch},
+                   "tokens_per_step": case.batch, "launch": "hip_graph" if args.graph else "eager"},
         "tokens_per_s": round(case.batch / (dec["ms_per_step"] * 1e-3), 1),
         "decode_call_us": {"mean": round(dec["decode_ms_mean"] * 1e3, 2),
                            "median": round(dec["decode_ms_median"] * 1e3, 2),
