@@ -96,6 +96,30 @@ __device__ __forceinline__ void load_lds_16(const void* gsrc, PGQA_LDS void* lds
     __builtin_amdgcn_global_load_lds(gsrc, lds_row, 16, 0, 0);
 }
 
+// Global->LDS DMA of 16 bytes per lane (global_load_lds_dwordx4): lane l
+// copies 16 bytes from sbase + voff into LDS at lds + 16*l (M0 holds the
+// wave's LDS base).  Written as inline assembly so that the compiler does not
+// track the load: its own tracking makes later LDS reads wait for every DMA in
+// flight, including the next tile's.  Callers wait for the DMA explicitly
+// (s_waitcnt vmcnt); M0 is used for nothing else in the kernels that call it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// Source sbase + voff (wave-uniform 64-bit base, 32-bit per-lane offset).  The
+// base and LDS address are read from the first lane, which makes them scalar
+// operands even where the compiler cannot prove them uniform.
+__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds) {
+    // readfirstlane returns a signed int: widen each half through uint32_t so
+    // the low half is not sign-extended into the high one.
+    const uint64_t p = (uint64_t)(uintptr_t)sbase;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint64_t s = ((uint64_t)hi << 32) | (uint64_t)lo;
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"((const char*)s),
+                 "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // s_waitcnt vmcnt(N), leaving the other counters unconstrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -131,19 +131,6 @@ __device__ __forceinline__ void dma_lane_init(DmaLane<D>& dl, int wave, int lane
     }
 }
 
-// One 16-byte-per-lane LDS DMA: lane l copies 16 bytes from sbase + voff into
-// LDS at lds + 16*l (M0 holds the wave's LDS base).  Written as inline
-// assembly so that the compiler does not track it: its own tracking would make
-// every later LDS read wait for the DMA of the next block as well.  The kernel
-// waits for the DMA explicitly (vmcnt at the top of each block).  M0 is used
-// for nothing else in this file's kernels.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // DMA of one tile of key block kb: waves 0 and 1 fetch K(kb) into K slot
 // kb % 2, waves 2 and 3 fetch V(kb) into V slot kb % 2 (LDS: K slots, then V
