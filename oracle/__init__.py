@@ -33,8 +33,9 @@ def _bind(lib: C.CDLL) -> C.CDLL:
     lib.oracle_gqa_paged_decode.argtypes = [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _D, _I,
                                             _P, _P, _I, _I]
     lib.oracle_gqa_varlen_prefill.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _D, _I, _I, _P, _I, _P, _I]
+    lib.oracle_gqa_paged_extend.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _D, _I, _P, _I]
     for f in ("oracle_paged_kv_write", "oracle_paged_kv_gather", "oracle_gqa_paged_decode",
-              "oracle_gqa_varlen_prefill", "oracle_max_threads"):
+              "oracle_gqa_varlen_prefill", "oracle_gqa_paged_extend", "oracle_max_threads"):
         getattr(lib, f).restype = C.c_int
     return lib
 
@@ -138,6 +139,25 @@ class Oracle:
                                                 len(cu) - 1, hq, hkv, d, float(scale), int(bool(causal)),
                                                 dt, self._ptr(r), n, self._ptr(out), int(num_threads))
         self._check(rc, "oracle_gqa_varlen_prefill")
+        return out
+
+
+    def gqa_paged_extend(self, q, cu_q, k_cache, v_cache, block_table, context_lens, scale, num_threads: int = 0):
+        """fp64 output [total_q, Hq, d]: every query row over its sequence's cached keys up to its position."""
+        q = self._c(q)
+        dt = self._dtype(q)
+        Tq, hq, d = q.shape
+        nb, hkv, bs, d2 = k_cache.shape
+        assert d2 == d
+        cq = self._c(cu_q, np.int32)
+        bt = self._c(block_table, np.int32)
+        cl = self._c(context_lens, np.int32)
+        out = np.empty((Tq, hq, d), dtype=np.float64)
+        rc = self.lib.oracle_gqa_paged_extend(self._ptr(q), self._ptr(cq), self._ptr(self._c(k_cache)),
+                                              self._ptr(self._c(v_cache)), self._ptr(bt), bt.shape[1],
+                                              self._ptr(cl), len(cl), hq, hkv, d, bs, nb, float(scale), dt,
+                                              self._ptr(out), int(num_threads))
+        self._check(rc, "oracle_gqa_paged_extend")
         return out
 
 

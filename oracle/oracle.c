@@ -307,3 +307,71 @@ int oracle_gqa_varlen_prefill(const void* q, const void* k, const void* v,
     }
     return failed ? ORACLE_EINVAL : ORACLE_OK;
 }
+
+int oracle_gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            double scale, int32_t dtype, double* out, int32_t num_threads) {
+    if (!q || !cu_q || !k_cache || !v_cache || !block_table || !context_lens || !out) return ORACLE_EINVAL;
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+        return ORACLE_EINVAL;
+    if (num_q_heads % num_kv_heads != 0 || !dtype_ok(dtype)) return ORACLE_EINVAL;
+    const int32_t group = num_q_heads / num_kv_heads;
+
+    /* Contract check first (serial), so the parallel part cannot fail. */
+    if (cu_q[0] != 0) return ORACLE_ERANGE;
+    int64_t max_ctx = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        if (cu_q[b + 1] < cu_q[b] || context_lens[b] < 0) return ORACLE_ERANGE;
+        for (int64_t j = 0; j < context_lens[b]; ++j)
+            if (block_of(block_table, max_blocks_per_seq, num_blocks, b, j, block_size) < 0) return ORACLE_ERANGE;
+        if (context_lens[b] > max_ctx) max_ctx = context_lens[b];
+    }
+
+    const int64_t units = (int64_t)cu_q[batch] * num_q_heads;
+    int failed = 0;
+#pragma omp parallel num_threads(pick_threads(num_threads))
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(max_ctx > 0 ? max_ctx : 1));
+        double* p = (double*)malloc(sizeof(double) * (size_t)(max_ctx > 0 ? max_ctx : 1));
+        int64_t* voff = (int64_t*)malloc(sizeof(int64_t) * (size_t)(max_ctx > 0 ? max_ctx : 1));
+        if (!s || !p || !voff) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t u = 0; u < units; ++u) {
+            if (!s || !p || !voff) continue;
+            const int64_t r = u / num_q_heads;
+            const int32_t qh = (int32_t)(u % num_q_heads);
+            const int32_t h = qh / group;
+            int32_t b = 0;
+            while (cu_q[b + 1] <= r) ++b;
+            const int64_t q_len = (int64_t)cu_q[b + 1] - cu_q[b];
+            const int64_t i = r - cu_q[b];
+            /* The query's own position: its sequence's q_len tokens are the last
+             * positions of the context. */
+            const int64_t pos = (int64_t)context_lens[b] - q_len + i;
+            const int64_t n = pos + 1;   /* keys 0 .. pos */
+            double* o = out + u * head_dim;
+            if (n <= 0) {
+                for (int32_t x = 0; x < head_dim; ++x) o[x] = 0.0;
+                continue;
+            }
+            const int64_t qo = u * head_dim;
+            for (int64_t j = 0; j < n; ++j) {
+                const int64_t blk = block_of(block_table, max_blocks_per_seq, num_blocks, b, j, block_size);
+                const int64_t ko = page_offset(blk, h, j % block_size, num_kv_heads, block_size, head_dim);
+                s[j] = scaled_dot(q, qo, k_cache, ko, head_dim, scale, dtype);
+                voff[j] = ko;
+            }
+            softmax_weighted_sum(s, n, v_cache, voff, head_dim, dtype, p, o);
+        }
+        free(s);
+        free(p);
+        free(voff);
+    }
+    return failed ? ORACLE_EINVAL : ORACLE_OK;
+}

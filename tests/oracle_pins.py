@@ -389,6 +389,82 @@ def pin_write_chunks_equal_one_write(orc):
     assert kc1.tobytes() == kc2.tobytes() and vc1.tobytes() == vc2.tobytes()
 
 
+def extend_pages(orc, case: W.ExtendCase):
+    kc = W.nan_pool(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)
+    vc = W.nan_pool(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)
+    orc.paged_kv_write(case.k, case.v, case.cu_ctx, case.start_pos, case.block_table, kc, vc)
+    return kc, vc
+
+
+def extend(orc, case: W.ExtendCase):
+    kc, vc = extend_pages(orc, case)
+    return orc.gqa_paged_extend(case.q, case.cu_q, kc, vc, case.block_table, case.context_lens, case.scale)
+
+
+def sdpa_extend(case: W.ExtendCase) -> np.ndarray:
+    """Library attention per sequence: its query rows against its packed K/V with
+    an explicit boolean mask keeping key j for row i iff j <= ctx - q_len + i."""
+    q, k, v = f64(case.q), f64(case.k), f64(case.v)
+    out = np.zeros_like(q)
+    for b in range(case.batch):
+        qa, qe = int(case.cu_q[b]), int(case.cu_q[b + 1])
+        ka, ke = int(case.cu_ctx[b]), int(case.cu_ctx[b + 1])
+        if qe == qa:
+            continue
+        n, ctx = qe - qa, ke - ka
+        mask = np.arange(ctx)[None, :] <= (ctx - n + np.arange(n))[:, None]
+        qt = torch.from_numpy(q[qa:qe]).permute(1, 0, 2).unsqueeze(0).contiguous()
+        kt = torch.from_numpy(k[ka:ke]).permute(1, 0, 2).unsqueeze(0).contiguous()
+        vt = torch.from_numpy(v[ka:ke]).permute(1, 0, 2).unsqueeze(0).contiguous()
+        r = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(mask), scale=float(case.scale),
+                                           enable_gqa=True)
+        out[qa:qe] = r[0].permute(1, 0, 2).numpy()
+    return out
+
+
+def pin_extend_matches_library(orc):
+    for dt, seed in ((W.F32, 81), (W.BF16, 82)):
+        c = W.make_extend_case([0, 7, 40, 3, 100], [5, 1, 9, 16, 2], 8, 2, 16, 4, dt, seed)
+        close(extend(orc, c), sdpa_extend(c), what=f"extend vs SDPA {dt}")
+
+
+def pin_extend_single_token_is_decode(orc):
+    """One query token per sequence is a decode step (same keys, same order)."""
+    c = W.make_extend_case([4, 0, 37, 12], [1, 1, 1, 1], 8, 4, 16, 4, W.F32, 83)
+    d = W.make_decode_case(c.context_lens, 8, 4, 16, 4, W.F32, 84)
+    d.q, d.k, d.v, d.block_table, d.num_blocks = c.q, c.k, c.v, c.block_table, c.num_blocks
+    close(extend(orc, c), decode(orc, d), rel=0.0, what="extend q_len=1 vs decode")
+
+
+def pin_extend_without_prefix_is_causal_prefill(orc):
+    """No cached prefix: the rows are exactly a causal varlen prefill of the new tokens."""
+    c = W.make_extend_case([0, 0, 0], [6, 1, 13], 8, 2, 16, 4, W.F32, 85)
+    p = W.make_prefill_case(c.q_lens, 8, 2, 16, 4, W.F32, 86)
+    p.q, p.k, p.v = c.q, c.k, c.v
+    close(extend(orc, c), orc.gqa_varlen_prefill(p.q, p.k, p.v, p.cu_seqlens, c.scale, causal=True),
+          what="extend without prefix vs causal prefill")
+
+
+def pin_extend_rows_shift_with_prefix(orc):
+    """Bottom-right alignment: the last row of every sequence sees its whole
+    context, and the first row sees exactly the prefix plus itself (brute force)."""
+    c = W.make_extend_case([9, 2, 30], [4, 7, 3], 4, 2, 16, 4, W.F32, 87)
+    got = extend(orc, c)
+    q, k, v = f64(c.q), f64(c.k), f64(c.v)
+    G = c.num_q_heads // c.num_kv_heads
+    for b in range(c.batch):
+        ka = int(c.cu_ctx[b])
+        ctx, n = int(c.context_lens[b]), int(c.q_lens[b])
+        for i in (0, n - 1):
+            r = int(c.cu_q[b]) + i
+            keys = ctx - n + i + 1
+            for qh in range(c.num_q_heads):
+                h = qh // G
+                s = (k[ka:ka + keys, h] @ q[r, qh]) * float(c.scale)
+                w = np.exp(s - s.max())
+                close(got[r, qh], (w / w.sum()) @ v[ka:ka + keys, h], rel=1e-12, what=f"extend b{b} row{i}")
+
+
 def pin_contract_errors(orc):
     c = W.make_decode_case([5, 11], 4, 2, 16, 4, W.F32, 52)
     kc, vc = fill_pages(orc, c)

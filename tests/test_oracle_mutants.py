@@ -44,6 +44,9 @@ MUTANTS = [
      "float acc = 0.0f;\n    for (int32_t x = 0; x < head_dim; ++x) acc += elem(q,"),
     ("table_ignored", "int64_t blk = block_table[(int64_t)b * max_blocks_per_seq + page];",
      "int64_t blk = ((int64_t)b * max_blocks_per_seq + page) % num_blocks;"),
+    ("extend_top_left_alignment", "const int64_t pos = (int64_t)context_lens[b] - q_len + i;",
+     "const int64_t pos = i;"),
+    ("extend_drops_own_key", "const int64_t n = pos + 1;   /* keys 0 .. pos */", "const int64_t n = pos;"),
 ]
 
 

@@ -243,8 +243,91 @@ def make_prefill_case(lengths: Sequence[int], num_q_heads: int, num_kv_heads: in
                        num_blocks=nblk, scale=np.float32(scale), causal=causal, seed=seed)
 
 
+@dataclass
+class ExtendCase:
+    """Several query tokens per sequence over its paged cache (chunked prefill on
+    a cached prefix, or draft-token verification): sequence b's q_lens[b] query
+    tokens are the last positions of its context_lens[b] cached tokens."""
+    name: str
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    context_lens: np.ndarray      # int32 [B] (prefix + new tokens)
+    q_lens: np.ndarray            # int32 [B]
+    cu_ctx: np.ndarray            # int32 [B+1]
+    cu_q: np.ndarray              # int32 [B+1]
+    q: np.ndarray                 # [sum q_lens, Hq, d]
+    k: np.ndarray                 # [sum ctx, Hkv, d] packed
+    v: np.ndarray                 # [sum ctx, Hkv, d] packed
+    block_table: np.ndarray       # int32 [B, max_blocks_per_seq]
+    num_blocks: int
+    scale: np.float32
+    seed: int = 0
+
+    @property
+    def batch(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def total_q(self) -> int:
+        return int(self.cu_q[-1])
+
+    @property
+    def max_q_len(self) -> int:
+        return int(self.q_lens.max()) if self.batch else 0
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.batch else 0
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def start_pos(self) -> np.ndarray:
+        return np.zeros(self.batch, dtype=np.int32)
+
+    def kv_bytes(self) -> int:
+        """Bytes of K and V that must be read (every cached token once)."""
+        return int(self.context_lens.astype(np.int64).sum()) * self.num_kv_heads * self.head_dim * 2 * elem_bytes(self.dtype)
+
+    def flops(self) -> int:
+        """Algorithmic FLOPs: query i of a sequence attends to prefix + i + 1 keys."""
+        n = self.q_lens.astype(np.int64)
+        pre = self.context_lens.astype(np.int64) - n
+        pairs = (n * pre + n * (n + 1) // 2).sum()
+        return int(pairs) * self.num_q_heads * 4 * self.head_dim
+
+
+def make_extend_case(prefix_lens: Sequence[int], q_lens: Sequence[int], num_q_heads: int, num_kv_heads: int,
+                     head_dim: int, block_size: int = 16, dtype: str = BF16, seed: int = 0, *,
+                     name: str = "custom", rng: Optional[np.random.Generator] = None,
+                     pool_factor: float = 1.25, scale: Optional[float] = None) -> ExtendCase:
+    """Multi-token-query inputs; draws Q, K, V, then the placement (like decode)."""
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    prefix = np.asarray(prefix_lens, dtype=np.int32)
+    qn = np.asarray(q_lens, dtype=np.int32)
+    ctx = (prefix + qn).astype(np.int32)
+    T = int(ctx.astype(np.int64).sum())
+    Tq = int(qn.astype(np.int64).sum())
+    q = _values(rng, (Tq, num_q_heads, head_dim), dtype)
+    k = _values(rng, (T, num_kv_heads, head_dim), dtype)
+    v = _values(rng, (T, num_kv_heads, head_dim), dtype)
+    table, nblk = place_pages(rng, ctx, block_size, pool_factor=pool_factor)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return ExtendCase(name=name, dtype=dtype, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                      head_dim=head_dim, block_size=block_size, context_lens=ctx, q_lens=qn,
+                      cu_ctx=cu_from_lengths(ctx), cu_q=cu_from_lengths(qn), q=q, k=k, v=v,
+                      block_table=table, num_blocks=nblk, scale=np.float32(scale), seed=seed)
+
+
 # ---------------------------------------------------------------------------
-# The five named workloads.
+# The named workloads.
 # ---------------------------------------------------------------------------
 
 @dataclass(frozen=True)
@@ -272,9 +355,20 @@ WORKLOADS = {
     "varlen_prefill": Workload("varlen_prefill", "prefill", 5,
                                "packed varlen causal prefill: 32 seqs, L~U[64,1024], Hq=32, Hkv=8, d=128, bf16, paged copy bs=16",
                                {"batch": 32, "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128, "block_size": 16, "dtype": BF16}),
+    "chunked_prefill": Workload("chunked_prefill", "extend", 6,
+                                "chunked prefill over a paged prefix: 16 seqs, cached prefix~U[0,3072], 512 new tokens each, "
+                                "Hq=32, Hkv=8, d=128, bs=16, bf16",
+                                {"batch": 16, "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
+                                 "dtype": BF16, "q_len": 512}),
+    "spec_verify": Workload("spec_verify", "extend", 7,
+                            "draft-token verification: B=64, ctx~U[512,4096] incl. 4 draft tokens each, "
+                            "Hq=32, Hkv=8, d=128, bs=16, bf16",
+                            {"batch": 64, "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
+                             "dtype": BF16, "q_len": 4}),
 }
 
-WORKLOAD_ORDER: List[str] = ["tiny_f32", "llama3_8b_decode", "long_ctx_decode", "mqa_decode", "varlen_prefill"]
+WORKLOAD_ORDER: List[str] = ["tiny_f32", "llama3_8b_decode", "long_ctx_decode", "mqa_decode", "varlen_prefill",
+                             "chunked_prefill", "spec_verify"]
 
 
 def workload_lengths(key: str, rng: np.random.Generator) -> np.ndarray:
@@ -291,11 +385,15 @@ def workload_lengths(key: str, rng: np.random.Generator) -> np.ndarray:
         return np.clip(n, 16, 8192).astype(np.int32)
     if key == "varlen_prefill":
         return rng.integers(64, 1024, size=32, endpoint=True).astype(np.int32)
+    if key == "chunked_prefill":   # cached prefix lengths
+        return rng.integers(0, 3072, size=16, endpoint=True).astype(np.int32)
+    if key == "spec_verify":       # cached prefix lengths (the context less the 4 draft tokens)
+        return (rng.integers(512, 4096, size=64, endpoint=True) - 4).astype(np.int32)
     raise KeyError(key)
 
 
 def make_workload(key: str):
-    """Build the named workload's inputs (a DecodeCase or a PrefillCase)."""
+    """Build the named workload's inputs (a DecodeCase, PrefillCase or ExtendCase)."""
     w = WORKLOADS[key]
     s = w.summary
     rng = np.random.default_rng(w.seed)
@@ -305,5 +403,9 @@ def make_workload(key: str):
         return make_decode_case(lengths, s["num_q_heads"], s["num_kv_heads"], s["head_dim"],
                                 s["block_size"], s["dtype"], w.seed, name=key, rng=rng,
                                 pool_blocks=pool)
+    if w.kind == "extend":
+        q_lens = np.full(len(lengths), s["q_len"], dtype=np.int32)
+        return make_extend_case(lengths, q_lens, s["num_q_heads"], s["num_kv_heads"], s["head_dim"],
+                                s["block_size"], s["dtype"], w.seed, name=key, rng=rng)
     return make_prefill_case(lengths, s["num_q_heads"], s["num_kv_heads"], s["head_dim"],
                              s["block_size"], s["dtype"], w.seed, name=key, rng=rng)
