@@ -52,6 +52,7 @@
  *   k_cache, v_cache      [num_blocks, Hkv, block_size, d]
  *   block_table           [B, max_blocks_per_seq]  logical page -> physical block
  *   cu_seqlens            [B + 1], cu_seqlens[0] = 0, cu_seqlens[B] = T
+ *   extend q / out        [total_q, Hq, d], rows of sequence b at cu_q[b] ..
  */
 #ifndef PAGED_GQA_H
 #define PAGED_GQA_H
@@ -179,6 +180,46 @@ int gqa_varlen_prefill(const void* q, const void* k, const void* v,
                        int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t head_dim, float scale, int32_t causal, pgqa_dtype dtype,
                        void* out, void* stream);
+
+/*
+ * gqa_paged_extend -- q_len >= 1 new query tokens per sequence attend to the
+ * sequence's paged cache: a chunk of a prompt prefilled on top of an already
+ * cached (possibly shared) prefix (the lecture notes, section 8.2, "Prefix
+ * Sharing"; the Ultimate Guide, section "Paged Attention"), or k draft tokens
+ * that the target model checks in one parallel pass (the lecture notes,
+ * section 7.1, speculative decoding).  The new
+ * tokens' own K/V must already be in the pages (paged_kv_write), so the cache
+ * holds ctx = context_lens[b] positions of which the last q_len are the new
+ * ones.  Query row i of sequence b (0 <= i < q_len = cu_q[b+1] - cu_q[b]) sits
+ * at position p = ctx - q_len + i and, like any causal row (the lecture notes,
+ * section 2: a token depends on the tokens before it), sees
+ * keys 0 .. p of the sequence (bottom-right aligned causal mask); with
+ * q_len = 1 this is gqa_paged_decode, with ctx = q_len it is a causal prefill.
+ * For query head qh, h = qh / (Hq / Hkv), K_j read through the block table as
+ * in gqa_paged_decode:
+ *   out[cu_q[b] + i][qh] = sum_{j <= p} softmax_j(scale * dot(q[cu_q[b] + i][qh], K_j)) V_j
+ * A row with p < 0 (ctx < q_len, a broken promise) gets an all-zero output.
+ * QK^T and PV run on bf16 MFMA with fp32 accumulation; P is rounded to bf16
+ * for the PV product.  bf16 only.
+ *   q, out       [total_q, Hq, d] packed new tokens
+ *   cu_q         [batch + 1] query-row offsets, cu_q[0] = 0, cu_q[batch] = total_q
+ *   k_cache, v_cache [num_blocks, Hkv, block_size, d]
+ *   block_table  [batch, max_blocks_per_seq]
+ *   context_lens [batch] cached positions per sequence, new tokens included
+ *   max_q_len    host-side upper bound of the q_len of every sequence
+ *   max_context_len  host-side upper bound of context_lens;
+ *                    must be <= max_blocks_per_seq * block_size
+ * Errors: PGQA_EINVAL (bad sizes or pointers, or a grid past 2^31 workgroups),
+ * PGQA_ENOTSUP (fp32; head_dim other than 64 / 128; group size not 1, 2 or a
+ * multiple of 4 up to 64; block_size below 4 for head_dim 128 or below 8 for
+ * head_dim 64, the rows one 1 KB load of the kernel covers), PGQA_EHIP.
+ */
+int gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                     int32_t batch, int32_t total_q, int32_t max_q_len,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+                     float scale, pgqa_dtype dtype, void* out, void* stream);
 
 /* Static, human-readable text of a status code. */
 const char* pgqa_status_string(int status);

@@ -33,7 +33,8 @@ def _bind(lib: C.CDLL) -> C.CDLL:
     lib.oracle_gqa_paged_decode.argtypes = [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _D, _I,
                                             _P, _P, _I, _I]
     lib.oracle_gqa_varlen_prefill.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _D, _I, _I, _P, _I, _P, _I]
-    lib.oracle_gqa_paged_extend.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _D, _I, _P, _I]
+    lib.oracle_gqa_paged_extend.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _D, _I, _P, _I,
+                                            _P, _I]
     for f in ("oracle_paged_kv_write", "oracle_paged_kv_gather", "oracle_gqa_paged_decode",
               "oracle_gqa_varlen_prefill", "oracle_gqa_paged_extend", "oracle_max_threads"):
         getattr(lib, f).restype = C.c_int
@@ -142,8 +143,10 @@ class Oracle:
         return out
 
 
-    def gqa_paged_extend(self, q, cu_q, k_cache, v_cache, block_table, context_lens, scale, num_threads: int = 0):
-        """fp64 output [total_q, Hq, d]: every query row over its sequence's cached keys up to its position."""
+    def gqa_paged_extend(self, q, cu_q, k_cache, v_cache, block_table, context_lens, scale, rows=None,
+                         num_threads: int = 0):
+        """fp64 output [total_q or len(rows), Hq, d]: each query row over its sequence's cached keys up to
+        its position."""
         q = self._c(q)
         dt = self._dtype(q)
         Tq, hq, d = q.shape
@@ -152,11 +155,13 @@ class Oracle:
         cq = self._c(cu_q, np.int32)
         bt = self._c(block_table, np.int32)
         cl = self._c(context_lens, np.int32)
-        out = np.empty((Tq, hq, d), dtype=np.float64)
+        r = None if rows is None else self._c(rows, np.int32)
+        n = Tq if r is None else len(r)
+        out = np.empty((n, hq, d), dtype=np.float64)
         rc = self.lib.oracle_gqa_paged_extend(self._ptr(q), self._ptr(cq), self._ptr(self._c(k_cache)),
                                               self._ptr(self._c(v_cache)), self._ptr(bt), bt.shape[1],
                                               self._ptr(cl), len(cl), hq, hkv, d, bs, nb, float(scale), dt,
-                                              self._ptr(out), int(num_threads))
+                                              self._ptr(r), n, self._ptr(out), int(num_threads))
         self._check(rc, "oracle_gqa_paged_extend")
         return out
 

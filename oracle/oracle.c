@@ -313,7 +313,8 @@ int oracle_gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_ca
                             int32_t max_blocks_per_seq, const int32_t* context_lens,
                             int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                            double scale, int32_t dtype, double* out, int32_t num_threads) {
+                            double scale, int32_t dtype, const int32_t* rows,
+                            int32_t num_rows, double* out, int32_t num_threads) {
     if (!q || !cu_q || !k_cache || !v_cache || !block_table || !context_lens || !out) return ORACLE_EINVAL;
     if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
         return ORACLE_EINVAL;
@@ -330,7 +331,13 @@ int oracle_gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_ca
         if (context_lens[b] > max_ctx) max_ctx = context_lens[b];
     }
 
-    const int64_t units = (int64_t)cu_q[batch] * num_q_heads;
+    const int64_t total = cu_q[batch];
+    if (!rows) num_rows = (int32_t)total;
+    if (num_rows < 0) return ORACLE_EINVAL;
+    for (int32_t x = 0; rows && x < num_rows; ++x)
+        if (rows[x] < 0 || rows[x] >= total) return ORACLE_ERANGE;
+
+    const int64_t units = (int64_t)num_rows * num_q_heads;
     int failed = 0;
 #pragma omp parallel num_threads(pick_threads(num_threads))
     {
@@ -344,7 +351,7 @@ int oracle_gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_ca
 #pragma omp for schedule(dynamic, 4)
         for (int64_t u = 0; u < units; ++u) {
             if (!s || !p || !voff) continue;
-            const int64_t r = u / num_q_heads;
+            const int64_t r = rows ? rows[u / num_q_heads] : u / num_q_heads;
             const int32_t qh = (int32_t)(u % num_q_heads);
             const int32_t h = qh / group;
             int32_t b = 0;
@@ -360,7 +367,7 @@ int oracle_gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_ca
                 for (int32_t x = 0; x < head_dim; ++x) o[x] = 0.0;
                 continue;
             }
-            const int64_t qo = u * head_dim;
+            const int64_t qo = (r * num_q_heads + qh) * head_dim;
             for (int64_t j = 0; j < n; ++j) {
                 const int64_t blk = block_of(block_table, max_blocks_per_seq, num_blocks, b, j, block_size);
                 const int64_t ko = page_offset(blk, h, j % block_size, num_kv_heads, block_size, head_dim);

@@ -81,14 +81,17 @@ int oracle_gqa_varlen_prefill(const void* q, const void* k, const void* v,
  * Query row r = cu_q[b] + i sits at position p = context_lens[b] - q_len_b + i
  * and attends to the cached keys j <= p (causal mask aligned to the end of the
  * context).  Query head qh reads KV head qh / (Hq / Hkv).  q is
- * [cu_q[batch], Hq, d]; out is fp64 [cu_q[batch], Hq, d].  A row with no key
- * (p < 0, i.e. q_len_b > context_lens[b]) gets 0. */
+ * [cu_q[batch], Hq, d].  A row with no key (p < 0, i.e. q_len_b >
+ * context_lens[b]) gets 0.  rows (may be NULL) lists the query rows to
+ * evaluate; NULL means every row 0..cu_q[batch]-1 with num_rows = cu_q[batch].
+ * out is fp64 [num_rows, Hq, d]. */
 int oracle_gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_cache,
                             const void* v_cache, const int32_t* block_table,
                             int32_t max_blocks_per_seq, const int32_t* context_lens,
                             int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                            double scale, int32_t dtype, double* out, int32_t num_threads);
+                            double scale, int32_t dtype, const int32_t* rows,
+                            int32_t num_rows, double* out, int32_t num_threads);
 
 /* Number of OpenMP threads a parallel region would use (for reporting). */
 int oracle_max_threads(void);

@@ -156,4 +156,35 @@ int gqa_varlen_prefill(const void* q, const void* k, const void* v, const int32_
     return hip_status(pgqa::launch_prefill(L, (hipStream_t)stream));
 }
 
+int gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                     int32_t batch, int32_t total_q, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_context_len, float scale,
+                     pgqa_dtype dtype, void* out, void* stream) {
+    if (batch < 0 || total_q < 0 || max_q_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+        max_blocks_per_seq <= 0 || max_context_len < 0)
+        return PGQA_EINVAL;
+    if (num_q_heads % num_kv_heads) return PGQA_EINVAL;
+    if (dtype != PGQA_BF16) return PGQA_ENOTSUP;
+    int32_t lg = 0;
+    if (!pow2_log2(block_size, &lg) || block_size > 256) return PGQA_ENOTSUP;
+    if (!pgqa::extend_supported(head_dim, num_q_heads / num_kv_heads, block_size)) return PGQA_ENOTSUP;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PGQA_EINVAL;
+    if ((int64_t)batch * max_blocks_per_seq > INT32_MAX) return PGQA_EINVAL;
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff()) return PGQA_EINVAL;
+    if ((int64_t)total_q * num_q_heads * head_dim > ((int64_t)1 << 40)) return PGQA_EINVAL;
+    // Grid size: one workgroup per 32-row query tile, head group and sequence.
+    if ((int64_t)(max_q_len / 32 + 1) * ((int64_t)batch * num_kv_heads + 7) * (num_q_heads / num_kv_heads) >
+        INT32_MAX)
+        return PGQA_EINVAL;
+    if (check_elem_ptr(q) || check_elem_ptr(k_cache) || check_elem_ptr(v_cache) || check_elem_ptr(out))
+        return PGQA_EINVAL;
+    if (check_index_ptr(cu_q) || check_index_ptr(block_table) || check_index_ptr(context_lens)) return PGQA_EINVAL;
+    if (batch == 0 || total_q == 0 || max_q_len == 0) return PGQA_OK;
+    pgqa::ExtendLaunch L{q, k_cache, v_cache, cu_q, block_table, context_lens, out, batch, total_q, max_q_len,
+                         max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, lg, num_blocks,
+                         max_context_len, scale};
+    return hip_status(pgqa::launch_extend(L, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -85,4 +85,30 @@ bool prefill_supported(int32_t head_dim, int32_t group);
 
 hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream);
 
+struct ExtendLaunch {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* cu_q;
+    const int32_t* block_table;
+    const int32_t* context_lens;
+    void* out;
+    int32_t batch;
+    int32_t total_q;
+    int32_t max_q_len;
+    int32_t max_blocks_per_seq;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_size_log2;
+    int32_t num_blocks;
+    int32_t max_context_len;
+    float scale;
+};
+
+// Is there a paged multi-token kernel for this (head_dim, group size, block size)?
+bool extend_supported(int32_t head_dim, int32_t group, int32_t block_size);
+
+hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream);
+
 }  // namespace pgqa

@@ -42,6 +42,18 @@
 //    (software pipeline within the wave: two score buffers, separate K and V
 //    rings so K(k+1) and V(k) are resident together).
 //  * The output tile is staged through LDS and written as whole rows.
+//
+// The same kernel, instantiated with PAGED = true, serves queries that extend
+// a cached sequence (chunked prefill on top of a cached prefix, or checking k
+// draft tokens): K/V come from the page pools through the block table
+// ("PagedAttention: The OS Analogy", tryclaro.ai; the Ultimate Guide, section
+// "Paged Attention"), and the q_len new rows of a sequence with ctx cached
+// positions (the new ones included) sit at positions ctx - q_len .. ctx - 1, so
+// the causal diagonal is shifted by ctx - q_len (bottom-right alignment).  Each
+// 1 KB wave-load covers 4 (d = 128) or 8 (d = 64) consecutive rows of one
+// page, so its source is one scalar base (block id from a scalar load of the
+// block-table row, fetched one tile ahead) plus the lane's offset, exactly as
+// for packed K/V.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -65,7 +77,19 @@ struct PrefillArgs {
     int32_t batch;
     int32_t nqt;             // query-tile levels (tiles of the longest sequence)
     int32_t pairs_per_xcd;   // ceil(batch * num_kv_heads / 8)
+    // Paged K/V only (k, v are then the pools [num_blocks, Hkv, block_size, d]).
+    const int32_t* block_table;
+    const int32_t* context_lens;
+    int32_t max_blocks_per_seq;
+    int32_t num_blocks;
+    int32_t bs_log2;
+    int32_t ctx_cap;         // host-side bound of context_lens
 };
+
+// Block-table rows are read through the constant address space, which makes
+// the compiler fetch a uniform entry with a scalar load (the table is never
+// written while a kernel runs).
+typedef const __attribute__((address_space(4))) int32_t* ConstI32Ptr;
 
 typedef short __attribute__((ext_vector_type(4))) i16x4;
 
@@ -158,7 +182,86 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const DmaLane<D
     }
 }
 
-template <int D, int HG>
+// Paged K/V: the lane's offset inside wave-load j, relative to that load's
+// first row (the swizzle key only depends on the row modulo 16, and loads j and
+// j + JP are 16 rows apart).
+template <int D>
+__device__ __forceinline__ void dma_lane_init_paged(DmaLane<D>& dl, int lane) {
+    using P = PGeo<D>;
+#pragma unroll
+    for (int j = 0; j < DmaLane<D>::JP; ++j) {
+        const int r = lane / P::CPR;
+        const int c = (lane % P::CPR) ^ swz_key<D>(j * P::RPL + r);
+        dl.soff[j] = (uint32_t)(r * P::ROWB + c * 16);
+    }
+}
+
+// Paged source of one wave: its pool (K for waves 0-1, V for waves 2-3), the
+// sequence's block-table row and the block ids of the next tile it will fetch
+// (one per wave-load, loaded a tile ahead so the scalar loads are off the
+// critical path).
+template <int D>
+struct PagedSrc {
+    static constexpr int NPW = DmaLane<D>::NPW;
+    ConstI32Ptr bt;
+    const char* pool;
+    int64_t head_off;    // kvh * block_size * row bytes
+    int64_t blk_bytes;   // Hkv * block_size * row bytes
+    int lbs;
+    int last;            // last key row of the sequence (ctx - 1)
+    int nb;
+    int id[NPW];
+};
+
+// First key row (relative to the sequence) of wave-load j of tile kb.
+template <int D>
+__device__ __forceinline__ int paged_row0(int kb, int wave, int j) {
+    return kb * BN + ((wave & 1) * DmaLane<D>::NPW + j) * PGeo<D>::RPL;
+}
+
+template <int D>
+__device__ __forceinline__ void paged_load_ids(PagedSrc<D>& ps, int kb, int wave) {
+#pragma unroll
+    for (int j = 0; j < PagedSrc<D>::NPW; ++j)
+        ps.id[j] = clampi(ps.bt[min(paged_row0<D>(kb, wave, j), ps.last) >> ps.lbs], 0, ps.nb - 1);
+}
+
+// DMA of tile kb from the pages (same LDS placement as issue_tile).  A load's
+// rows lie in one page (block_size >= rows per load), so its source is a
+// uniform base plus the lane offset; rows past the sequence end re-read its
+// last row (in bounds; those keys are masked).
+template <int D>
+__device__ __forceinline__ void issue_tile_paged(const PagedSrc<D>& ps, const DmaLane<D>& dl, uint32_t ring,
+                                                 int kb, int wave, int lane) {
+    using P = PGeo<D>;
+    constexpr int NPW = DmaLane<D>::NPW;
+    constexpr int JP = DmaLane<D>::JP;
+    const bool isv = wave >= 2;
+    const uint32_t dst = ring + (isv ? 2 * P::TILEB : 0) + (kb & 1) * P::TILEB + (wave & 1) * NPW * 1024;
+    const int bs_mask = (1 << ps.lbs) - 1;
+    auto base_of = [&](int j, int rb) {
+        return ps.pool + (int64_t)ps.id[j] * ps.blk_bytes + ps.head_off + (int64_t)(rb & bs_mask) * P::ROWB;
+    };
+    if (kb * BN + BN <= ps.last + 1) {
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) {
+            const int row0 = paged_row0<D>(kb, wave, j);
+            dma16(base_of(j, row0), dl.soff[j % JP], dst + j * 1024);
+        }
+    } else {
+        const int r = lane / P::CPR;
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) {
+            const int row0 = paged_row0<D>(kb, wave, j);
+            const int rb = min(row0, ps.last);
+            const int rc = min(row0 + r, ps.last);
+            const int c = (lane % P::CPR) ^ swz_key<D>((j % JP) * P::RPL + r);
+            dma16(base_of(j, rb), (uint32_t)((rc - rb) * P::ROWB + c * 16), dst + j * 1024);
+        }
+    }
+}
+
+template <int D, int HG, bool PAGED>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     using P = PGeo<D>;
     constexpr int TB = 4 / HG;               // 32-row token blocks per workgroup
@@ -191,18 +294,28 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     if (pair >= a.batch * a.num_kv_heads) return;
     const int s = pair / a.num_kv_heads;
     const int kvh = pair - s * a.num_kv_heads;
-    const int seq0 = clampi(a.cu_seqlens[s], 0, a.total_tokens);
-    const int L = clampi(a.cu_seqlens[s + 1], seq0, a.total_tokens) - seq0;
+    // Query rows seq0 .. seq0 + Lq - 1 of the packed q / out.  Keys: Lk rows;
+    // query row i sits at key position koff + i (packed prefill: the sequence's
+    // own rows, koff = 0; paged: the cached context, koff = ctx - q_len) and,
+    // when causal, sees keys 0 .. koff + i.
+    // (Loaded values count as divergent for the compiler: readfirstlane keeps
+    // the sizes, and every branch on them, scalar.)
+    const int seq0 = __builtin_amdgcn_readfirstlane(clampi(a.cu_seqlens[s], 0, a.total_tokens));
+    const int Lq = __builtin_amdgcn_readfirstlane(clampi(a.cu_seqlens[s + 1], seq0, a.total_tokens)) - seq0;
+    const int Lk = PAGED ? __builtin_amdgcn_readfirstlane(clampi(a.context_lens[s], 0, a.ctx_cap)) : Lq;
+    const int koff = PAGED ? Lk - Lq : 0;
     const int qtile = a.nqt - 1 - level;
     const int tok0 = qtile * TB * BQ;
-    if (tok0 >= L) return;
+    if (tok0 >= Lq) return;
     const int head = kvh * G + grp * HG + (wave % HG);
     const int i0 = tok0 + (wave / HG) * BQ;          // this wave's first query row (sequence-local)
 
-    const int wg_rows_end = min(L, tok0 + TB * BQ);
-    const int nkb = a.causal ? (wg_rows_end + BN - 1) / BN : (L + BN - 1) / BN;
-    const bool active = i0 < L;
-    const int last_kb = a.causal ? min(nkb - 1, (i0 + BQ - 1) / BN) : nkb - 1;
+    const int wg_rows_end = min(Lq, tok0 + TB * BQ);
+    const int keys = a.causal ? min(Lk, koff + wg_rows_end) : Lk;   // keys the workgroup reads
+    const int nkb = keys > 0 ? (keys + BN - 1) / BN : 0;
+    const bool active = i0 < Lq;
+    const int last_key = a.causal ? min(Lk, koff + min(i0 + BQ, Lq)) - 1 : Lk - 1;
+    const int last_kb = last_key >= 0 ? last_key / BN : -1;
     const float cs = a.scale_log2;
 
     const int64_t qstride = (int64_t)a.num_q_heads * D * 2;   // bytes per packed Q row
@@ -210,15 +323,37 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
     // Prologue: K(0), V(0) and K(1) in flight while Q is read.
     DmaLane<D> dl;
-    dma_lane_init<D>(dl, wave, lane, kvstride);
+    PagedSrc<D> ps;
     const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
-    issue_tile<D>(a, dl, ring_addr, 0, seq0, L, kvh, wave, lane, kvstride);
-    if (wave < 2 && nkb > 1) issue_tile<D>(a, dl, ring_addr, 1, seq0, L, kvh, wave, lane, kvstride);
+    if constexpr (PAGED) {
+        dma_lane_init_paged<D>(dl, lane);
+        ps.bt = (ConstI32Ptr)(a.block_table + (int64_t)s * a.max_blocks_per_seq);
+        ps.pool = wave >= 2 ? a.v : a.k;
+        ps.lbs = a.bs_log2;
+        ps.head_off = ((int64_t)kvh << a.bs_log2) * P::ROWB;
+        ps.blk_bytes = ((int64_t)a.num_kv_heads << a.bs_log2) * P::ROWB;
+        ps.last = Lk - 1;
+        ps.nb = a.num_blocks;
+        if (nkb > 0) {
+            paged_load_ids<D>(ps, 0, wave);
+            issue_tile_paged<D>(ps, dl, ring_addr, 0, wave, lane);
+            if (wave < 2 && nkb > 1) {
+                paged_load_ids<D>(ps, 1, wave);
+                issue_tile_paged<D>(ps, dl, ring_addr, 1, wave, lane);
+            }
+            const int nt = wave < 2 ? 2 : 1;
+            if (nt < nkb) paged_load_ids<D>(ps, nt, wave);
+        }
+    } else {
+        dma_lane_init<D>(dl, wave, lane, kvstride);
+        issue_tile<D>(a, dl, ring_addr, 0, seq0, Lk, kvh, wave, lane, kvstride);
+        if (wave < 2 && nkb > 1) issue_tile<D>(a, dl, ring_addr, 1, seq0, Lk, kvh, wave, lane, kvstride);
+    }
 
     // Q^T operand: lane holds row (i0 + l32), d = 16*kk + 8*half .. +8.
     u32x4 qreg[KSTEPS];
     {
-        const int row = min(i0 + l32, L - 1);
+        const int row = min(i0 + l32, Lq - 1);
         const char* qp = a.q + (int64_t)(seq0 + row) * qstride + (int64_t)head * D * 2 + half * 16;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) qreg[kk] = *(const u32x4*)(qp + kk * 32);
@@ -271,8 +406,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         // Masking (last block of the sequence, or a block crossing the
         // diagonal): key j0 + off is kept iff off <= lim, with
         // off = 32*kb2 + 8*(i/4) + i%4 and the lane's 4*half folded into lim.
-        if ((j0 + BN > L) || (a.causal && j0 + BN - 1 > i0)) {
-            const int lim = (a.causal ? min(i0 + l32, L - 1) : L - 1) - j0 - 4 * half;
+        if ((j0 + BN > Lk) || (a.causal && j0 + BN - 1 > koff + i0)) {
+            const int lim = (a.causal ? min(koff + i0 + l32, Lk - 1) : Lk - 1) - j0 - 4 * half;
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -355,7 +490,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         wait_vmcnt<0>();
         __syncthreads();
         const int tb = wave < 2 ? kb + 2 : kb + 1;
-        if (tb < nkb) issue_tile<D>(a, dl, ring_addr, tb, seq0, L, kvh, wave, lane, kvstride);
+        if (tb < nkb) {
+            if constexpr (PAGED) {
+                issue_tile_paged<D>(ps, dl, ring_addr, tb, wave, lane);
+                if (tb + 1 < nkb) paged_load_ids<D>(ps, tb + 1, wave);
+            } else {
+                issue_tile<D>(a, dl, ring_addr, tb, seq0, Lk, kvh, wave, lane, kvstride);
+            }
+        }
     };
     // Blocks 0 .. kend are computed (kend = last_kb, or -1 for a wave with no
     // rows); each but the last overlaps the next block's scores.  The two score
@@ -414,24 +556,27 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     for (int t = 0; t < BQ / P::RPL; ++t) {
         const int r = t * P::RPL + lane / P::CPR;
         const u32x4 val = lds_read_16(ot + swz<D>(r, c));
-        if (i0 + r < L)
+        if (i0 + r < Lq)
             *(u32x4*)(a.out + (int64_t)(seq0 + i0 + r) * qstride + (int64_t)head * D * 2 + c * 16) = val;
     }
 }
 
 typedef void (*PrefillFn)(PrefillArgs);
 
+template <bool PAGED>
 bool pick(int head_dim, int group, PrefillFn* fn, int* hg) {
     const int h = group >= 4 ? 4 : group;
     if (group != 1 && group != 2 && group % 4 != 0) return false;
     if (group > 64) return false;
     *hg = h;
     if (head_dim == 128) {
-        *fn = h == 4 ? prefill_kernel<128, 4> : (h == 2 ? prefill_kernel<128, 2> : prefill_kernel<128, 1>);
+        *fn = h == 4 ? prefill_kernel<128, 4, PAGED>
+                     : (h == 2 ? prefill_kernel<128, 2, PAGED> : prefill_kernel<128, 1, PAGED>);
         return true;
     }
     if (head_dim == 64) {
-        *fn = h == 4 ? prefill_kernel<64, 4> : (h == 2 ? prefill_kernel<64, 2> : prefill_kernel<64, 1>);
+        *fn = h == 4 ? prefill_kernel<64, 4, PAGED>
+                     : (h == 2 ? prefill_kernel<64, 2, PAGED> : prefill_kernel<64, 1, PAGED>);
         return true;
     }
     return false;
@@ -439,20 +584,40 @@ bool pick(int head_dim, int group, PrefillFn* fn, int* hg) {
 
 size_t lds_bytes(int head_dim) { return head_dim == 128 ? 4 * PGeo<128>::TILEB : 4 * PGeo<64>::TILEB; }
 
+int rows_per_load(int head_dim) { return head_dim == 128 ? PGeo<128>::RPL : PGeo<64>::RPL; }
+
+// Tile levels, XCD packing and grid size shared by both entry points.
+hipError_t launch(PrefillFn fn, PrefillArgs& a, int hg, int group, int max_q_rows, int head_dim,
+                  hipStream_t stream) {
+    const int rows_per_wg = (4 / hg) * BQ;
+    a.nqt = (max_q_rows + rows_per_wg - 1) / rows_per_wg;
+    a.pairs_per_xcd = (int)(((int64_t)a.batch * a.num_kv_heads + 7) / 8);
+    const int64_t wgs = 8 * (int64_t)a.nqt * a.pairs_per_xcd * (group / hg);
+    if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(256), lds_bytes(head_dim), stream, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool prefill_supported(int32_t head_dim, int32_t group) {
     PrefillFn fn;
     int hg;
-    return pick(head_dim, group, &fn, &hg);
+    return pick<false>(head_dim, group, &fn, &hg);
+}
+
+bool extend_supported(int32_t head_dim, int32_t group, int32_t block_size) {
+    PrefillFn fn;
+    int hg;
+    return pick<true>(head_dim, group, &fn, &hg) && block_size >= rows_per_load(head_dim) && block_size <= 256;
 }
 
 hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
     const int group = L.num_q_heads / L.num_kv_heads;
     PrefillFn fn;
     int hg;
-    if (!pick(L.head_dim, group, &fn, &hg)) return hipErrorInvalidValue;
-    PrefillArgs a;
+    if (!pick<false>(L.head_dim, group, &fn, &hg)) return hipErrorInvalidValue;
+    PrefillArgs a = {};
     a.q = (const char*)L.q;
     a.k = (const char*)L.k;
     a.v = (const char*)L.v;
@@ -464,13 +629,34 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
     a.causal = L.causal;
     a.scale_log2 = (float)((double)L.scale * 1.4426950408889634);
     a.batch = L.batch;
-    const int rows_per_wg = (4 / hg) * BQ;
-    a.nqt = (L.max_seqlen + rows_per_wg - 1) / rows_per_wg;
-    a.pairs_per_xcd = (int)(((int64_t)L.batch * L.num_kv_heads + 7) / 8);
-    const int64_t wgs = 8 * (int64_t)a.nqt * a.pairs_per_xcd * (group / hg);
-    if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(256), lds_bytes(L.head_dim), stream, a);
-    return hipGetLastError();
+    return launch(fn, a, hg, group, L.max_seqlen, L.head_dim, stream);
+}
+
+hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream) {
+    const int group = L.num_q_heads / L.num_kv_heads;
+    PrefillFn fn;
+    int hg;
+    if (!extend_supported(L.head_dim, group, 1 << L.block_size_log2)) return hipErrorInvalidValue;
+    pick<true>(L.head_dim, group, &fn, &hg);
+    PrefillArgs a = {};
+    a.q = (const char*)L.q;
+    a.k = (const char*)L.k_cache;
+    a.v = (const char*)L.v_cache;
+    a.cu_seqlens = L.cu_q;
+    a.out = (char*)L.out;
+    a.total_tokens = L.total_q;
+    a.num_q_heads = L.num_q_heads;
+    a.num_kv_heads = L.num_kv_heads;
+    a.causal = 1;
+    a.scale_log2 = (float)((double)L.scale * 1.4426950408889634);
+    a.batch = L.batch;
+    a.block_table = L.block_table;
+    a.context_lens = L.context_lens;
+    a.max_blocks_per_seq = L.max_blocks_per_seq;
+    a.num_blocks = L.num_blocks;
+    a.bs_log2 = L.block_size_log2;
+    a.ctx_cap = L.max_context_len;
+    return launch(fn, a, hg, group, L.max_q_len, L.head_dim, stream);
 }
 
 }  // namespace pgqa

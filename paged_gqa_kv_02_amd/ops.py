@@ -127,3 +127,27 @@ def gqa_varlen_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seq
                                   int(bool(causal)), _dtype(q), out.data_ptr(), _stream())
     check("gqa_varlen_prefill", st)
     return out
+
+
+def gqa_paged_extend(q: torch.Tensor, cu_q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     block_table: torch.Tensor, context_lens: torch.Tensor, max_q_len: int, max_context_len: int,
+                     scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Several new tokens per sequence over its paged cache (chunked prefill on a cached
+    prefix, draft verification): q [total_q, Hq, d] -> out [total_q, Hq, d].  The new
+    tokens' K/V must already be in the pages; context_lens counts them."""
+    T, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    if d2 != d:
+        raise ValueError("head_dim mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(q, cu_q, k_cache, v_cache, block_table, context_lens, out)
+    _i32(cu_q, block_table, context_lens)
+    st = lib().gqa_paged_extend(q.data_ptr(), cu_q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                block_table.data_ptr(), block_table.shape[1], context_lens.data_ptr(),
+                                cu_q.numel() - 1, T, int(max_q_len), hq, hkv, d, bs, nb, int(max_context_len),
+                                float(scale), _dtype(q), out.data_ptr(), _stream())
+    check("gqa_paged_extend", st)
+    return out

@@ -108,3 +108,33 @@ def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -
         ok = e["max_abs"] <= F32_MAX_ABS
     assert ok, f"{what}: {e}"
     return e
+
+
+class DevExtend:
+    """A multi-token-query case resident on the GPU, its pools written by the HIP kernel."""
+
+    def __init__(self, case: W.ExtendCase, context_lens=None):
+        self.case = case
+        self.q = to_dev(case.q)
+        self.cu_q = to_dev(case.cu_q)
+        self.table = to_dev(case.block_table)
+        self.ctx_np = case.context_lens if context_lens is None else np.asarray(context_lens, np.int32)
+        self.ctx = to_dev(self.ctx_np)
+        self.kc = nan_pool_dev(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)
+        self.vc = nan_pool_dev(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)
+        k, v = to_dev(case.k), to_dev(case.v)
+        pg.paged_kv_write(k, v, to_dev(case.cu_ctx), to_dev(case.start_pos), self.table, self.kc, self.vc)
+        del k, v
+
+    def extend(self) -> torch.Tensor:
+        c = self.case
+        return pg.gqa_paged_extend(self.q, self.cu_q, self.kc, self.vc, self.table, self.ctx, c.max_q_len,
+                                   int(self.ctx_np.max()) if c.batch else 0, scale=float(c.scale))
+
+
+def oracle_extend(orc, case: W.ExtendCase, rows=None, context_lens=None) -> np.ndarray:
+    kc = W.nan_pool(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)
+    vc = W.nan_pool(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)
+    orc.paged_kv_write(case.k, case.v, case.cu_ctx, case.start_pos, case.block_table, kc, vc)
+    ctx = case.context_lens if context_lens is None else np.asarray(context_lens, np.int32)
+    return orc.gqa_paged_extend(case.q, case.cu_q, kc, vc, case.block_table, ctx, case.scale, rows=rows)

@@ -465,6 +465,18 @@ def pin_extend_rows_shift_with_prefix(orc):
                 close(got[r, qh], (w / w.sum()) @ v[ka:ka + keys, h], rel=1e-12, what=f"extend b{b} row{i}")
 
 
+def pin_extend_row_sampling(orc):
+    """Sampled rows (any order, repeats) equal the same rows of the full evaluation,
+    and each equals the library attention of its sequence."""
+    c = W.make_extend_case([11, 0, 6], [5, 3, 9], 4, 2, 16, 4, W.BF16, 88)
+    kc, vc = extend_pages(orc, c)
+    full = orc.gqa_paged_extend(c.q, c.cu_q, kc, vc, c.block_table, c.context_lens, c.scale)
+    rows = np.array([16, 0, 4, 5, 8, 7, 0], dtype=np.int32)
+    part = orc.gqa_paged_extend(c.q, c.cu_q, kc, vc, c.block_table, c.context_lens, c.scale, rows=rows)
+    assert np.array_equal(part, full[rows]), "sampled rows differ from the full evaluation"
+    close(part, sdpa_extend(c)[rows], rel=1e-12, what="sampled extend rows vs library")
+
+
 def pin_contract_errors(orc):
     c = W.make_decode_case([5, 11], 4, 2, 16, 4, W.F32, 52)
     kc, vc = fill_pages(orc, c)

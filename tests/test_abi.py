@@ -23,7 +23,7 @@ def lib(built_lib):
 def test_header_declares_the_calls():
     names = L.header_functions()
     for n in ("paged_kv_write", "paged_kv_gather", "gqa_paged_decode", "gqa_paged_decode_workspace_size",
-              "gqa_varlen_prefill", "pgqa_status_string"):
+              "gqa_varlen_prefill", "gqa_paged_extend", "pgqa_status_string"):
         assert n in names
 
 
@@ -119,3 +119,33 @@ def test_prefill_validation(lib):
     assert _prefill(lib, hq=24, hkv=8) == ENOTSUP       # group 3
     assert _prefill(lib, batch=0) == 0
     assert _prefill(lib, T=0) == 0
+
+
+def _extend(lib, **kw):
+    a = dict(q=P[0], cu=P[1], kc=P[2], vc=P[3], bt=P[4], maxb=4, cl=P[5], batch=2, T=12, maxq=9, hq=32, hkv=8,
+             d=128, bs=16, nb=8, maxctx=64, scale=0.088, dt=BF16, out=P[6])
+    a.update(kw)
+    return lib.gqa_paged_extend(a["q"], a["cu"], a["kc"], a["vc"], a["bt"], a["maxb"], a["cl"], a["batch"],
+                                a["T"], a["maxq"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["maxctx"],
+                                a["scale"], a["dt"], a["out"], None)
+
+
+def test_extend_validation(lib):
+    assert _extend(lib, hq=30) == EINVAL                # Hq % Hkv != 0
+    assert _extend(lib, T=-1) == EINVAL
+    assert _extend(lib, maxq=-1) == EINVAL
+    assert _extend(lib, maxctx=65) == EINVAL            # beyond max_blocks_per_seq * block_size
+    assert _extend(lib, nb=0) == EINVAL
+    assert _extend(lib, cu=None) == EINVAL
+    assert _extend(lib, cl=P[5] + 2) == EINVAL
+    assert _extend(lib, out=P[6] + 2) == EINVAL
+    assert _extend(lib, scale=float("inf")) == EINVAL
+    assert _extend(lib, dt=F32) == ENOTSUP              # bf16 MFMA path only
+    assert _extend(lib, d=32) == ENOTSUP
+    assert _extend(lib, hq=24, hkv=8) == ENOTSUP        # group 3
+    assert _extend(lib, bs=2, maxctx=8) == ENOTSUP      # a 4-row load would cross pages
+    assert _extend(lib, d=64, bs=4, maxctx=16) == ENOTSUP
+    assert _extend(lib, bs=12) == ENOTSUP
+    assert _extend(lib, batch=0) == 0
+    assert _extend(lib, T=0) == 0
+    assert _extend(lib, maxq=0) == 0
