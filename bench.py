@@ -14,8 +14,11 @@ call alone (split + merge) with HIP events on its stream, in a second pass.
 Inputs stay resident in HBM.  Four copies of the page pools (about 0.77 GB each)
 are used round-robin, so the 256 MB Infinity Cache cannot serve a step from the
 previous one.  Secondary line items: the packed varlen causal prefill workload
-(paged write + MFMA prefill) in TFLOP/s, and the fp64 CPU oracle on the same
-decode batch as a reported baseline.
+(paged write + MFMA prefill) in TFLOP/s; multi-token queries over the paged
+cache (chunked prefill of 512-token chunks on cached prefixes, and checking 4
+draft tokens per sequence), each with the roofline its arithmetic intensity
+puts it under; and the fp64 CPU oracle on the same decode batch as a reported
+baseline.
 """
 
 from __future__ import annotations
@@ -40,6 +43,7 @@ def _args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill line item")
+    ap.add_argument("--no-extend", action="store_true", help="skip the multi-token (extend) line items")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle timing budget")
     ap.add_argument("--decode-workload", default="llama3_8b_decode",
                     choices=["llama3_8b_decode", "long_ctx_decode", "mqa_decode", "tiny_f32"],
@@ -211,6 +215,63 @@ def prefill_leg(args, torch, pg, W, T):
     }
 
 
+def extend_leg(key, args, torch, pg, W, T):
+    """One multi-token step on a named workload: write the new tokens' K/V into
+    their pages, then gqa_paged_extend over prefix + new tokens.  HIP events
+    bracket the extend call; two pool copies alternate between steps."""
+    c = W.make_workload(key)
+    q, cu_q = T.to_dev(c.q), T.to_dev(c.cu_q)
+    table, ctx = T.to_dev(c.block_table), T.to_dev(c.context_lens)
+    pools = []
+    for _ in range(2):
+        kc = T.nan_pool_dev(c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim, c.dtype)
+        vc = T.nan_pool_dev(c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim, c.dtype)
+        pg.paged_kv_write(T.to_dev(c.k), T.to_dev(c.v), T.to_dev(c.cu_ctx), T.to_dev(c.start_pos), table, kc, vc)
+        pools.append((kc, vc))
+    new_rows = np.concatenate([np.arange(c.cu_ctx[b + 1] - c.q_lens[b], c.cu_ctx[b + 1])
+                               for b in range(c.batch)]).astype(np.int64)
+    k_new, v_new = T.to_dev(np.ascontiguousarray(c.k[new_rows])), T.to_dev(np.ascontiguousarray(c.v[new_rows]))
+    sp_new = T.to_dev((c.context_lens - c.q_lens).astype(np.int32))
+    out = torch.empty_like(q)
+    scale = float(c.scale)
+
+    def step(i, ev=None):
+        kc, vc = pools[i % 2]
+        pg.paged_kv_write(k_new, v_new, cu_q, sp_new, table, kc, vc)
+        if ev is not None:
+            ev[0].record()
+        pg.gqa_paged_extend(q, cu_q, kc, vc, table, ctx, c.max_q_len, c.max_context_len, scale=scale, out=out)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(max(4, args.warmup // 4)):
+        step(i)
+    torch.cuda.synchronize()
+    n = max(10, args.steps // 4)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    t0 = time.perf_counter()
+    for i in range(n):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    flops, kv = c.flops(), c.kv_bytes()
+    tf = flops / (ms.mean() * 1e-3) / 1e12
+    gbs = kv / (ms.mean() * 1e-3) / 1e9
+    # Bound by arithmetic intensity against the ridge point (peak FLOP/s / peak B/s).
+    mfma = flops / kv > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    roof = ({"bound": "mfma", "achieved": tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": tf / BF16_MFMA_PEAK_TFLOPS, "traffic": None} if mfma else
+            {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+             "traffic": None})
+    return {
+        "workload": key, "batch": c.batch, "query_tokens": c.total_q, "flops_per_call": flops,
+        "kv_bytes_per_call": kv, "extend_us_mean": float(ms.mean() * 1e3), "extend_us_median": float(np.median(ms) * 1e3),
+        "ms_per_step": wall * 1e3 / n, "tflops": tf, "kv_gbs": gbs,
+        "query_tokens_per_s": c.total_q / (ms.mean() * 1e-3), "roofline": roof,
+    }
+
+
 def cpu_baseline(args, case, W):
     """The fp64 oracle, as it stands, on the same decode step (write + decode),
     repeated until at least --cpu-seconds of host time have been spent."""
@@ -295,6 +356,11 @@ def main():
         log("prefill leg")
         line["prefill"] = prefill_leg(args, torch, pg, W, T)
         line["prefill"]["roofline"]["traffic"] = traffic["prefill"]
+    if not args.no_extend:
+        line["extend"] = {}
+        for key in ("chunked_prefill", "spec_verify"):
+            log(f"extend leg {key}")
+            line["extend"][key] = extend_leg(key, args, torch, pg, W, T)
     if not args.no_cpu_baseline:
         log("cpu baseline leg (oracle)")
         ref, cb = cpu_baseline(args, case, W)
