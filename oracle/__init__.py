@@ -35,7 +35,8 @@ def _bind(lib: C.CDLL) -> C.CDLL:
     lib.oracle_gqa_varlen_prefill.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _D, _I, _I, _P, _I, _P, _I]
     lib.oracle_gqa_paged_extend.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _D, _I, _P, _I,
                                             _P, _I]
-    for f in ("oracle_paged_kv_write", "oracle_paged_kv_gather", "oracle_gqa_paged_decode",
+    lib.oracle_paged_kv_copy_blocks.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I]
+    for f in ("oracle_paged_kv_write", "oracle_paged_kv_gather", "oracle_paged_kv_copy_blocks", "oracle_gqa_paged_decode",
               "oracle_gqa_varlen_prefill", "oracle_gqa_paged_extend", "oracle_max_threads"):
         getattr(lib, f).restype = C.c_int
     return lib
@@ -90,6 +91,17 @@ class Oracle:
                                             self._ptr(bt), bt.shape[1], self._ptr(k_cache),
                                             self._ptr(v_cache), len(cu) - 1, nb, bs, hkv, d, dt)
         self._check(rc, "oracle_paged_kv_write")
+
+    def paged_kv_copy_blocks(self, k_cache, v_cache, src, dst):
+        """Copy blocks src[i] -> dst[i] (all KV heads, K and V) in place, in order."""
+        assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous and k_cache.dtype == v_cache.dtype
+        dt = self._dtype(k_cache)
+        s, d_ = self._c(src, np.int32), self._c(dst, np.int32)
+        assert s.shape == d_.shape
+        nb, hkv, bs, d = k_cache.shape
+        rc = self.lib.oracle_paged_kv_copy_blocks(self._ptr(k_cache), self._ptr(v_cache), self._ptr(s),
+                                                  self._ptr(d_), len(s), nb, bs, hkv, d, dt)
+        self._check(rc, "oracle_paged_kv_copy_blocks")
 
     def paged_kv_gather(self, k_cache, v_cache, block_table, context_lens):
         nb, hkv, bs, d = k_cache.shape

@@ -149,6 +149,28 @@ int oracle_paged_kv_gather(const void* k_cache, const void* v_cache, const int32
     return ORACLE_OK;
 }
 
+int oracle_paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
+                                int32_t num_pairs, int32_t num_blocks, int32_t block_size,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t dtype) {
+    if (!k_cache || !v_cache || (num_pairs > 0 && (!src || !dst))) return ORACLE_EINVAL;
+    if (num_pairs < 0 || num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+        return ORACLE_EINVAL;
+    if (!dtype_ok(dtype)) return ORACLE_EINVAL;
+    for (int32_t i = 0; i < num_pairs; ++i)
+        if (src[i] < 0 || src[i] >= num_blocks || dst[i] < 0 || dst[i] >= num_blocks) return ORACLE_ERANGE;
+    const int es = elem_size(dtype);
+    const size_t row_bytes = (size_t)head_dim * es;
+    for (int32_t i = 0; i < num_pairs; ++i)
+        for (int32_t h = 0; h < num_kv_heads; ++h)
+            for (int32_t slot = 0; slot < block_size; ++slot) {
+                const int64_t from = page_offset(src[i], h, slot, num_kv_heads, block_size, head_dim);
+                const int64_t to = page_offset(dst[i], h, slot, num_kv_heads, block_size, head_dim);
+                memmove((char*)k_cache + to * es, (const char*)k_cache + from * es, row_bytes);
+                memmove((char*)v_cache + to * es, (const char*)v_cache + from * es, row_bytes);
+            }
+    return ORACLE_OK;
+}
+
 /*
  * softmax(scores) . values for one query row, in fp64, two passes:
  *   m = max_j s_j;  w_j = exp(s_j - m);  Z = sum_j w_j;  p_j = w_j / Z;

@@ -51,6 +51,14 @@ int oracle_paged_kv_gather(const void* k_cache, const void* v_cache, const int32
                            int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
                            int32_t dtype);
 
+/* Copy-on-write block copy (the lecture notes, section 8.2 "Prefix Sharing": when
+ * sequences diverge only the modified block is copied).  For i = 0 .. num_pairs-1
+ * in order, every KV head's block_size slots of block src[i] are copied, bytes
+ * unchanged, onto block dst[i], in the K pool and in the V pool. */
+int oracle_paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
+                                int32_t num_pairs, int32_t num_blocks, int32_t block_size,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t dtype);
+
 /* Decode: one query token per sequence attends to every cached position
  * [0, context_lens[b]) of its sequence.  Query head qh reads KV head
  * qh / (Hq / Hkv).  out is fp64 [B, Hq, d]; a sequence with no context gets 0.

@@ -389,6 +389,123 @@ def pin_write_chunks_equal_one_write(orc):
     assert kc1.tobytes() == kc2.tobytes() and vc1.tobytes() == vc2.tobytes()
 
 
+def pin_copy_blocks_moves_pages(orc):
+    """A block copy makes the destination pages read back (by the independent
+    gather) exactly as the source pages did, and leaves every other block alone."""
+    c = W.make_decode_case([13, 9, 20], 4, 2, 8, 4, W.BF16, 61)
+    kc, vc = fill_pages(orc, c)
+    used = set(int(x) for x in c.block_table.reshape(-1) if x >= 0)
+    spare = [b for b in range(c.num_blocks) if b not in used]
+    src = np.array([c.block_table[0, 1], c.block_table[2, 4]], dtype=np.int32)   # a full page and a partial one
+    dst = np.array(spare[:2], dtype=np.int32)
+    k0, v0 = kc.copy(), vc.copy()
+    orc.paged_kv_copy_blocks(kc, vc, src, dst)
+    moved = c.block_table.copy()
+    moved[0, 1], moved[2, 4] = dst
+    ka, va = orc.paged_kv_gather(k0, v0, c.block_table, c.context_lens)
+    kb, vb = orc.paged_kv_gather(kc, vc, moved, c.context_lens)
+    assert ka.tobytes() == kb.tobytes() and va.tobytes() == vb.tobytes(), "copied pages read back differently"
+    other = np.ones(c.num_blocks, dtype=bool)
+    other[dst] = False
+    assert kc[other].tobytes() == k0[other].tobytes() and vc[other].tobytes() == v0[other].tobytes()
+    # whole blocks move, tail slots (past the context) included
+    assert kc[dst].tobytes() == k0[src].tobytes() and vc[dst].tobytes() == v0[src].tobytes()
+
+
+def pin_copy_blocks_in_order(orc):
+    """Pairs apply in order: a -> b then b -> c leaves a's contents in c."""
+    kc = W.f32_to_bf16_bits(np.random.default_rng(62).standard_normal((5, 2, 4, 8)).astype(np.float32))
+    vc = W.f32_to_bf16_bits(np.random.default_rng(63).standard_normal((5, 2, 4, 8)).astype(np.float32))
+    k0, v0 = kc.copy(), vc.copy()
+    orc.paged_kv_copy_blocks(kc, vc, np.array([0, 1], np.int32), np.array([1, 2], np.int32))
+    assert kc[2].tobytes() == k0[0].tobytes() and kc[1].tobytes() == k0[0].tobytes()
+    assert vc[2].tobytes() == v0[0].tobytes() and kc[3:].tobytes() == k0[3:].tobytes()
+
+
+def _model_check(m, content, expect):
+    """Invariants of refcounted paging after any operation, against a token-level
+    simulation of the pool: counters equal references, free blocks are unreferenced,
+    no table holds a block twice, and every sequence reads back its own tokens."""
+    refs = np.zeros(m.num_blocks, dtype=np.int64)
+    for sid, table in m.tables.items():
+        assert len(set(table)) == len(table), "a table holds a block twice"
+        assert len(table) == -(-m.lengths[sid] // m.block_size), "table length != pages of the sequence"
+        for b in table:
+            refs[b] += 1
+        got = [content[table[p // m.block_size]][p % m.block_size] for p in range(m.lengths[sid])]
+        assert got == expect[sid], f"sequence {sid} reads back other tokens"
+    assert list(refs) == list(m.ref), "reference counters != references"
+
+
+def pin_block_model_invariants(orc):
+    """Random fork / append / free sequences against a token-level simulation in
+    which the reported copies and every written slot are applied to a pool of labels."""
+    import random
+    from oracle.block_model import BlockModel, OutOfBlocks
+    for trial in range(40):
+        rnd = random.Random(trial)
+        bs = rnd.choice([1, 2, 4, 16])
+        m = BlockModel(rnd.randint(8, 40), bs)
+        content = [[None] * bs for _ in range(m.num_blocks)]
+        expect = {}
+        label = 0
+        for _ in range(120):
+            op = rnd.random()
+            live = sorted(m.tables)
+            if op < 0.15 or not live:
+                sid = m.new_sequence()
+                expect[sid] = []
+            elif op < 0.35:
+                parent = rnd.choice(live)
+                sid = m.fork(parent)
+                expect[sid] = list(expect[parent])
+            elif op < 0.85:
+                sid = rnd.choice(live)
+                n = rnd.randint(0, 2 * bs + 1)
+                try:
+                    cp = m.append(sid, n)
+                except OutOfBlocks:
+                    _model_check(m, content, expect)
+                    continue
+                if cp is not None:
+                    content[cp[1]] = list(content[cp[0]])
+                start = m.lengths[sid] - n
+                for pos in range(start, start + n):
+                    content[m.tables[sid][pos // bs]][pos % bs] = label
+                    expect[sid].append(label)
+                    label += 1
+            else:
+                sid = rnd.choice(live)
+                m.free(sid)
+                del expect[sid]
+            _model_check(m, content, expect)
+
+
+def pin_block_model_shared_prompt(orc):
+    """The pages' scenario: a system prompt shared by 50 requests is stored once; each
+    request that diverges copies only the block it modifies (the prompt's partly
+    filled last block), and the full prompt blocks stay shared by all."""
+    from oracle.block_model import BlockModel
+    bs, prompt = 16, 100                  # 6 full blocks + 4 tokens in a 7th
+    m = BlockModel(200, bs)
+    root = m.new_sequence()
+    assert m.append(root, prompt) is None
+    kids = [m.fork(root) for _ in range(50)]
+    assert len(m.free_blocks()) == 200 - 7, "the prompt is stored once"
+    assert all(m.ref[b] == 51 for b in m.tables[root])
+    copies = [m.append(k, 3) for k in kids]            # 3 new tokens each, inside the 7th block
+    assert all(cp is not None and cp[0] == m.tables[root][6] for cp in copies)
+    assert len({cp[1] for cp in copies}) == 50
+    assert all(m.ref[b] == 51 for b in m.tables[root][:6]), "full prompt blocks stay shared"
+    assert m.ref[m.tables[root][6]] == 1
+    assert m.append(root, 1) is None, "the last holder writes in place"
+    assert len(m.free_blocks()) == 200 - 7 - 50
+    for k in kids:
+        m.free(k)
+    m.free(root)
+    assert len(m.free_blocks()) == 200 and all(r == 0 for r in m.ref)
+
+
 def extend_pages(orc, case: W.ExtendCase):
     kc = W.nan_pool(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)
     vc = W.nan_pool(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)

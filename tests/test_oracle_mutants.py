@@ -47,6 +47,8 @@ MUTANTS = [
     ("extend_top_left_alignment", "const int64_t pos = (int64_t)context_lens[b] - q_len + i;",
      "const int64_t pos = i;"),
     ("extend_drops_own_key", "const int64_t n = pos + 1;   /* keys 0 .. pos */", "const int64_t n = pos;"),
+    ("copy_skips_v", "memmove((char*)v_cache + to * es, (const char*)v_cache + from * es, row_bytes);", ""),
+    ("copy_head_zero", "const int64_t from = page_offset(src[i], h, slot,", "const int64_t from = page_offset(src[i], 0, slot,"),
 ]
 
 
@@ -78,3 +80,45 @@ def test_unmutated_copy_passes(tmp_path):
 def test_mutant_is_caught(tmp_path, mid, old, new):
     failed = _failures(_build_variant(tmp_path, old, new))
     assert failed, f"planted mistake {mid} passed every pin"
+
+
+# Planted mistakes in the block-refcount model (oracle/block_model.py), applied by
+# patching one method of the class for the duration of the test.
+def _append_without_copy(self, seq, n):
+    table, length = self.tables[seq], self.lengths[seq]
+    for _ in range(self._pages(length + n) - len(table)):
+        b = self.free_blocks()[0]
+        self.ref[b] = 1
+        table.append(b)
+    self.lengths[seq] = length + n
+    return None
+
+
+def _free_without_release(self, seq):
+    self.tables.pop(seq)
+    del self.lengths[seq]
+
+
+def _fork_without_reference(self, parent):
+    child = self.new_sequence()
+    self.tables[child] = list(self.tables[parent])
+    self.lengths[child] = self.lengths[parent]
+    return child
+
+
+MODEL_MUTANTS = [("append_without_copy", "append", _append_without_copy),
+                 ("free_without_release", "free", _free_without_release),
+                 ("fork_without_reference", "fork", _fork_without_reference)]
+
+
+@pytest.mark.parametrize("mid,name,fn", MODEL_MUTANTS, ids=[m[0] for m in MODEL_MUTANTS])
+def test_model_mutant_is_caught(monkeypatch, mid, name, fn):
+    from oracle.block_model import BlockModel
+    monkeypatch.setattr(BlockModel, name, fn)
+    failed = []
+    for pin in (P.pin_block_model_invariants, P.pin_block_model_shared_prompt):
+        try:
+            pin(None)
+        except Exception as e:
+            failed.append((pin.__name__, type(e).__name__))
+    assert failed, f"planted mistake {mid} passed every model pin"
