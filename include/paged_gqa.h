@@ -25,7 +25,8 @@
  *     sequence, memory-bound) are separate phases: the lecture notes, section 2;
  *     the Ultimate Guide, introduction.
  *
- * Conventions shared by every call
+ * Conventions shared by every call (the pgqa_bm_* block manager below is
+ * host-only and documented on its own)
  *   - Every array argument is a DEVICE pointer owned by the caller; the
  *     library never allocates, frees or keeps device memory, never
  *     synchronises, and keeps no state between calls (thread-safe).
@@ -220,6 +221,70 @@ int gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_cache, co
                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                      int32_t block_size, int32_t num_blocks, int32_t max_context_len,
                      float scale, pgqa_dtype dtype, void* out, void* stream);
+
+/*
+ * paged_kv_copy_blocks -- the device half of copy-on-write (the lecture notes,
+ * section 8.2, "Prefix Sharing (Copy-on-Write)": when sequences sharing prefix
+ * blocks diverge, only the block being modified is copied).  For every pair p,
+ * the whole of block src_blocks[p] (all KV heads, all block_size slots) is
+ * copied bit for bit onto block dst_blocks[p], in the K pool and in the V pool.
+ * Pairs run concurrently: no dst may equal another pair's src or dst (the
+ * caller's promise; pgqa_bm_append never produces such pairs within one step).
+ * Pairs with an id outside [0, num_blocks) are skipped.
+ *   k_cache, v_cache  [num_blocks, Hkv, block_size, d] (modified in place)
+ *   src_blocks, dst_blocks  [num_pairs] device int32 arrays
+ * Errors: PGQA_EINVAL, PGQA_ENOTSUP (head_dim, block_size or dtype), PGQA_EHIP.
+ */
+int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks, const int32_t* dst_blocks,
+                         int32_t num_pairs, int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_dim, pgqa_dtype dtype, void* stream);
+
+/*
+ * Block manager -- host-side bookkeeping of refcounted KV blocks with
+ * copy-on-write, the block tables the calls above read.  Pages: a sequence's
+ * cache is a list of fixed-size blocks taken from the pool only when a token
+ * needs one and given back when the request ends (the Ultimate Guide, section
+ * "Paged Attention"); blocks carry a reference counter, several sequences may
+ * point at the same prefix blocks, and when they diverge only the modified
+ * block is copied (the lecture notes, section 8.2, "Prefix Sharing").
+ *
+ * Unlike every call above, these are HOST-only calls on a host object: pointer
+ * arguments are host memory, nothing touches the GPU, and a manager must not be
+ * used by two threads at once.  Policy: new blocks are the lowest-numbered free
+ * ones; new sequences get the lowest unused id (>= 0).
+ *
+ *   pgqa_bm_create(num_blocks, block_size)  NULL for sizes <= 0 or no memory.
+ *   pgqa_bm_new_sequence(bm, &seq)          an empty sequence.
+ *   pgqa_bm_fork(bm, parent, &child)        child shares all of parent's blocks
+ *                                           (one more reference each) and its length.
+ *   pgqa_bm_append(bm, seq, n, &src, &dst)  room for n more tokens (positions
+ *       len .. len+n-1).  If the last block is partly filled and shared, it is
+ *       replaced by a fresh block and (src, dst) = (old, new) is returned: copy
+ *       that block on the device (paged_kv_copy_blocks) before writing the new
+ *       tokens; otherwise src = dst = -1.  Pages past the old end get fresh
+ *       blocks.  PGQA_ENOSPC when the pool lacks free blocks (nothing changes);
+ *       PGQA_EINVAL for an unknown sequence or n < 0.
+ *   pgqa_bm_free_sequence(bm, seq)          drops one reference to each of its
+ *                                           blocks; blocks at zero become free.
+ *   pgqa_bm_sequence_length / pgqa_bm_refcount / pgqa_bm_num_free_blocks
+ *                                           -1 for an unknown sequence / block.
+ *   pgqa_bm_block_table(bm, seq, pages, capacity)  writes up to capacity block
+ *       ids of the sequence's pages (logical order) to host memory; returns its
+ *       page count (-1 for an unknown sequence).
+ */
+typedef struct pgqa_block_manager pgqa_block_manager;
+
+pgqa_block_manager* pgqa_bm_create(int32_t num_blocks, int32_t block_size);
+void pgqa_bm_destroy(pgqa_block_manager* bm);
+int pgqa_bm_new_sequence(pgqa_block_manager* bm, int32_t* seq);
+int pgqa_bm_fork(pgqa_block_manager* bm, int32_t parent, int32_t* child);
+int pgqa_bm_append(pgqa_block_manager* bm, int32_t seq, int32_t num_tokens, int32_t* copy_src,
+                   int32_t* copy_dst);
+int pgqa_bm_free_sequence(pgqa_block_manager* bm, int32_t seq);
+int32_t pgqa_bm_sequence_length(const pgqa_block_manager* bm, int32_t seq);
+int32_t pgqa_bm_block_table(const pgqa_block_manager* bm, int32_t seq, int32_t* pages, int32_t capacity);
+int32_t pgqa_bm_refcount(const pgqa_block_manager* bm, int32_t block);
+int32_t pgqa_bm_num_free_blocks(const pgqa_block_manager* bm);
 
 /* Static, human-readable text of a status code. */
 const char* pgqa_status_string(int status);

@@ -28,6 +28,17 @@ _SIGNATURES = {
     "gqa_varlen_prefill": (C.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P]),
     "gqa_paged_extend": (C.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                                    _P, _P]),
+    "paged_kv_copy_blocks": (C.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "pgqa_bm_create": (_P, [_I, _I]),
+    "pgqa_bm_destroy": (None, [_P]),
+    "pgqa_bm_new_sequence": (C.c_int, [_P, C.POINTER(_I)]),
+    "pgqa_bm_fork": (C.c_int, [_P, _I, C.POINTER(_I)]),
+    "pgqa_bm_append": (C.c_int, [_P, _I, _I, C.POINTER(_I), C.POINTER(_I)]),
+    "pgqa_bm_free_sequence": (C.c_int, [_P, _I]),
+    "pgqa_bm_sequence_length": (_I, [_P, _I]),
+    "pgqa_bm_block_table": (_I, [_P, _I, _P, _I]),
+    "pgqa_bm_refcount": (_I, [_P, _I]),
+    "pgqa_bm_num_free_blocks": (_I, [_P]),
     "pgqa_status_string": (C.c_char_p, [C.c_int]),
 }
 
@@ -42,7 +53,8 @@ def header_functions() -> list:
     """Names of the functions include/paged_gqa.h declares."""
     text = HEADER.read_text()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(?:int|size_t|const char\*)\s+(\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(?:int|int32_t|void|size_t|const char\*|pgqa_block_manager\*)\s+(\w+)\s*\(",
+                                 text)))
 
 
 def load(path: Path = LIB_PATH) -> C.CDLL:

@@ -91,6 +91,21 @@ int paged_kv_gather(const void* k_cache, const void* v_cache, const int32_t* cu_
     return hip_status(pgqa::launch_kv_copy(L, false, (hipStream_t)stream));
 }
 
+int paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks, const int32_t* dst_blocks,
+                         int32_t num_pairs, int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_dim, pgqa_dtype dtype, void* stream) {
+    if (num_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PGQA_EINVAL;
+    if (elem_bytes(dtype) == 0 || !head_dim_ok(head_dim)) return PGQA_ENOTSUP;
+    int32_t lg = 0;
+    if (!pow2_log2(block_size, &lg) || block_size > 256) return PGQA_ENOTSUP;
+    if (check_elem_ptr(k_cache) || check_elem_ptr(v_cache)) return PGQA_EINVAL;
+    if (check_index_ptr(src_blocks) || check_index_ptr(dst_blocks)) return PGQA_EINVAL;
+    if (num_pairs == 0) return PGQA_OK;
+    pgqa::BlockCopyLaunch L{k_cache, v_cache, src_blocks, dst_blocks, num_pairs, num_blocks, block_size,
+                            num_kv_heads, head_dim, elem_bytes(dtype)};
+    return hip_status(pgqa::launch_block_copy(L, (hipStream_t)stream));
+}
+
 size_t gqa_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t num_splits) {
     if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_splits < 0) return 0;

@@ -75,7 +75,53 @@ __global__ __launch_bounds__(256) void kv_copy_kernel(CopyArgs a) {
     }
 }
 
+// Copy-on-write block copy.  A block is one contiguous run of Hkv * bs * d
+// elements in each pool, so pair p copies that run of K and of V from block
+// src[p] onto block dst[p]; thread i moves 16-byte chunk i of the flattened
+// (pair, pool, chunk) space.  Pairs whose ids fall outside the pool are skipped.
+struct BlockCopyArgs {
+    char* k;
+    char* v;
+    const int32_t* src;
+    const int32_t* dst;
+    int64_t total_chunks;       // num_pairs * 2 * chunks_per_block
+    int64_t chunks_per_block;   // Hkv * bs * d * elem_bytes / 16
+    int32_t num_blocks;
+};
+
+__global__ __launch_bounds__(256) void kv_block_copy_kernel(BlockCopyArgs a) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.total_chunks; i += stride) {
+        const int64_t c = i % a.chunks_per_block;
+        const int64_t pp = i / a.chunks_per_block;      // 2 * pair + pool
+        const int64_t pair = pp >> 1;
+        char* pool = (pp & 1) ? a.v : a.k;
+        const int s = a.src[pair];
+        const int d = a.dst[pair];
+        if (s < 0 || s >= a.num_blocks || d < 0 || d >= a.num_blocks) continue;
+        const u32x4 x = *(const u32x4*)(pool + ((int64_t)s * a.chunks_per_block + c) * 16);
+        *(u32x4*)(pool + ((int64_t)d * a.chunks_per_block + c) * 16) = x;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_block_copy(const BlockCopyLaunch& L, hipStream_t stream) {
+    BlockCopyArgs a;
+    a.k = (char*)L.k_cache;
+    a.v = (char*)L.v_cache;
+    a.src = L.src;
+    a.dst = L.dst;
+    a.num_blocks = L.num_blocks;
+    a.chunks_per_block = (int64_t)L.num_kv_heads * L.block_size * L.head_dim * L.elem_bytes / 16;
+    a.total_chunks = (int64_t)L.num_pairs * 2 * a.chunks_per_block;
+    if (a.total_chunks == 0) return hipSuccess;
+    const int threads = 256;
+    int64_t blocks = (a.total_chunks + threads - 1) / threads;
+    if (blocks > 65536) blocks = 65536;  // grid-stride beyond this
+    hipLaunchKernelGGL(kv_block_copy_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_kv_copy(const KvCopyLaunch& L, bool to_pages, hipStream_t stream) {
     CopyArgs a;

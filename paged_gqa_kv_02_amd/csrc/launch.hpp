@@ -29,6 +29,21 @@ struct KvCopyLaunch {
 // to_pages = true: packed -> pages; false: pages -> packed.
 hipError_t launch_kv_copy(const KvCopyLaunch& L, bool to_pages, hipStream_t stream);
 
+struct BlockCopyLaunch {
+    void* k_cache;
+    void* v_cache;
+    const int32_t* src;
+    const int32_t* dst;
+    int32_t num_pairs;
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t elem_bytes;
+};
+
+hipError_t launch_block_copy(const BlockCopyLaunch& L, hipStream_t stream);
+
 struct DecodeLaunch {
     const void* q;
     const void* k_cache;

@@ -151,3 +151,17 @@ def gqa_paged_extend(q: torch.Tensor, cu_q: torch.Tensor, k_cache: torch.Tensor,
                                 float(scale), _dtype(q), out.data_ptr(), _stream())
     check("gqa_paged_extend", st)
     return out
+
+
+def paged_kv_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src_blocks: torch.Tensor,
+                         dst_blocks: torch.Tensor) -> None:
+    """Copy whole blocks src_blocks[p] -> dst_blocks[p] (all heads, K and V) in place."""
+    _dev(k_cache, v_cache, src_blocks, dst_blocks)
+    _i32(src_blocks, dst_blocks)
+    if src_blocks.numel() != dst_blocks.numel():
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    nb, hkv, bs, d = k_cache.shape
+    st = lib().paged_kv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), src_blocks.data_ptr(),
+                                    dst_blocks.data_ptr(), src_blocks.numel(), nb, bs, hkv, d, _dtype(k_cache),
+                                    _stream())
+    check("paged_kv_copy_blocks", st)

@@ -23,7 +23,8 @@ def lib(built_lib):
 def test_header_declares_the_calls():
     names = L.header_functions()
     for n in ("paged_kv_write", "paged_kv_gather", "gqa_paged_decode", "gqa_paged_decode_workspace_size",
-              "gqa_varlen_prefill", "gqa_paged_extend", "pgqa_status_string"):
+              "gqa_varlen_prefill", "gqa_paged_extend", "paged_kv_copy_blocks", "pgqa_bm_create", "pgqa_bm_append",
+              "pgqa_bm_fork", "pgqa_bm_free_sequence", "pgqa_status_string"):
         assert n in names
 
 
@@ -149,3 +150,23 @@ def test_extend_validation(lib):
     assert _extend(lib, batch=0) == 0
     assert _extend(lib, T=0) == 0
     assert _extend(lib, maxq=0) == 0
+
+
+def _copy(lib, **kw):
+    a = dict(kc=P[0], vc=P[1], src=P[2], dst=P[3], n=3, nb=8, bs=16, hkv=2, d=128, dt=BF16)
+    a.update(kw)
+    return lib.paged_kv_copy_blocks(a["kc"], a["vc"], a["src"], a["dst"], a["n"], a["nb"], a["bs"], a["hkv"],
+                                    a["d"], a["dt"], None)
+
+
+def test_copy_blocks_validation(lib):
+    assert _copy(lib, n=-1) == EINVAL
+    assert _copy(lib, nb=0) == EINVAL
+    assert _copy(lib, kc=None) == EINVAL
+    assert _copy(lib, vc=P[1] + 8) == EINVAL
+    assert _copy(lib, src=None) == EINVAL
+    assert _copy(lib, dst=P[3] + 1) == EINVAL
+    assert _copy(lib, d=48) == ENOTSUP
+    assert _copy(lib, bs=24) == ENOTSUP
+    assert _copy(lib, dt=9) == ENOTSUP
+    assert _copy(lib, n=0) == 0
