@@ -17,8 +17,9 @@ previous one.  Secondary line items: the packed varlen causal prefill workload
 (paged write + MFMA prefill) in TFLOP/s; multi-token queries over the paged
 cache (chunked prefill of 512-token chunks on cached prefixes, and checking 4
 draft tokens per sequence), each with the roofline its arithmetic intensity
-puts it under; and the fp64 CPU oracle on the same decode batch as a reported
-baseline.
+puts it under; decode of 64 samples over the pages of one shared prompt
+(prefix sharing with copy-on-write), against the same samples unshared; and
+the fp64 CPU oracle on the same decode batch as a reported baseline.
 """
 
 from __future__ import annotations
@@ -44,6 +45,7 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill line item")
     ap.add_argument("--no-extend", action="store_true", help="skip the multi-token (extend) line items")
+    ap.add_argument("--no-shared", action="store_true", help="skip the shared-prefix decode line item")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle timing budget")
     ap.add_argument("--decode-workload", default="llama3_8b_decode",
                     choices=["llama3_8b_decode", "long_ctx_decode", "mqa_decode", "tiny_f32"],
@@ -272,6 +274,88 @@ def extend_leg(key, args, torch, pg, W, T):
     }
 
 
+def shared_prefix_leg(args, torch, pg, W, T):
+    """Decode over pages shared by samples of one prompt.  The library's block
+    manager builds the tables (prompt stored once, its partly filled last block
+    copied on write by each sample), then each step rewrites every sample's newest
+    token and decodes, as in the headline step.  The same samples laid out with no
+    sharing are decoded too, for the comparison and a bitwise check."""
+    c = W.make_workload("shared_prefix_decode")
+    B, hq, hkv, d, bs, P = c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size, c.prompt_len
+    pool = -(-P // bs) + int(sum(-(-int(n) // bs) + 1 for n in c.cont_lens)) + 8
+    bm = pg.BlockManager(pool, bs)
+    kc = T.nan_pool_dev(pool, hkv, bs, d, c.dtype)
+    vc = T.nan_pool_dev(pool, hkv, bs, d, c.dtype)
+    root = bm.new_sequence()
+    bm.append(root, P)
+    pg.paged_kv_write(T.to_dev(c.k_prompt), T.to_dev(c.v_prompt), T.to_dev(np.array([0, P], np.int32)),
+                      T.to_dev(np.zeros(1, np.int32)), T.to_dev(bm.block_tables([root])), kc, vc)
+    kids = [bm.fork(root) for _ in range(B)]
+    cps = [cp for cp in (bm.append(s, int(n)) for s, n in zip(kids, c.cont_lens)) if cp is not None]
+    if cps:
+        pg.paged_kv_copy_blocks(kc, vc, T.to_dev(np.array([a for a, _ in cps], np.int32)),
+                                T.to_dev(np.array([b for _, b in cps], np.int32)))
+    table = T.to_dev(bm.block_tables(kids))
+    cu_cont = c.cu_cont
+    pg.paged_kv_write(T.to_dev(c.k_cont), T.to_dev(c.v_cont), T.to_dev(cu_cont), T.to_dev(np.full(B, P, np.int32)),
+                      table, kc, vc)
+    bm.free(root)
+    blocks_used = pool - bm.num_free_blocks()
+    ctx_np = c.context_lens
+    ctx = T.to_dev(ctx_np)
+    last = cu_cont[1:] - 1
+    k_new, v_new = T.to_dev(np.ascontiguousarray(c.k_cont[last])), T.to_dev(np.ascontiguousarray(c.v_cont[last]))
+    cu_new = T.to_dev(np.arange(B + 1, dtype=np.int32))
+    sp_new = T.to_dev((ctx_np - 1).astype(np.int32))
+    q = T.to_dev(c.q)
+    scale, maxctx = float(c.scale), int(ctx_np.max())
+    ws = pg.decode_workspace(B, hq, hkv, d, 0, q.device)
+
+    def timed(kc_, vc_, table_, out):
+        def step(ev=None):
+            pg.paged_kv_write(k_new, v_new, cu_new, sp_new, table_, kc_, vc_)
+            if ev is not None:
+                ev[0].record()
+            pg.gqa_paged_decode(q, kc_, vc_, table_, ctx, maxctx, scale=scale, out=out, workspace=ws)
+            if ev is not None:
+                ev[1].record()
+        for _ in range(max(5, args.warmup // 2)):
+            step()
+        torch.cuda.synchronize()
+        n = max(20, args.steps // 2)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        t0 = time.perf_counter()
+        for i in range(n):
+            step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return np.array([a.elapsed_time(b) for a, b in evs]), wall * 1e3 / n
+
+    out_sh = torch.empty_like(q)
+    ms_sh, step_sh = timed(kc, vc, table, out_sh)
+    u = c.logical(np.random.default_rng(c.seed))
+    ukc = T.nan_pool_dev(u.num_blocks, hkv, bs, d, c.dtype)
+    uvc = T.nan_pool_dev(u.num_blocks, hkv, bs, d, c.dtype)
+    utable = T.to_dev(u.block_table)
+    pg.paged_kv_write(T.to_dev(u.k), T.to_dev(u.v), T.to_dev(u.cu_ctx), T.to_dev(u.start_pos), utable, ukc, uvc)
+    out_un = torch.empty_like(q)
+    ms_un, _ = timed(ukc, uvc, utable, out_un)
+    same = bool(torch.equal(out_sh.view(torch.int16), out_un.view(torch.int16)))
+    logical, unique = c.logical_kv_bytes(), c.unique_kv_bytes()
+    us = float(ms_sh.mean() * 1e3)
+    hbm = unique / (us * 1e-6) / 1e9
+    return {
+        "workload": "shared_prefix_decode", "batch": B, "prompt_len": P, "logical_kv_bytes": logical,
+        "unique_kv_bytes": unique, "blocks_used": blocks_used, "blocks_unshared": int((u.block_table >= 0).sum()), "cow_copies": len(cps),
+        "decode_us_mean": us, "unshared_decode_us_mean": float(ms_un.mean() * 1e3), "ms_per_step": step_sh,
+        "logical_kv_gbs": logical / (us * 1e-6) / 1e9, "speedup_vs_unshared": float(ms_un.mean() / ms_sh.mean()),
+        "bit_identical_to_unshared": same,
+        "roofline": {"bound": "hbm", "achieved": hbm, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": hbm / HBM_PEAK_GBS, "traffic": None,
+                     "bytes": "unique K/V bytes (prompt once + continuations), the HBM floor"},
+    }
+
+
 def cpu_baseline(args, case, W):
     """The fp64 oracle, as it stands, on the same decode step (write + decode),
     repeated until at least --cpu-seconds of host time have been spent."""
@@ -361,6 +445,9 @@ def main():
         for key in ("chunked_prefill", "spec_verify"):
             log(f"extend leg {key}")
             line["extend"][key] = extend_leg(key, args, torch, pg, W, T)
+    if not args.no_shared:
+        log("shared prefix leg")
+        line["shared_prefix"] = shared_prefix_leg(args, torch, pg, W, T)
     if not args.no_cpu_baseline:
         log("cpu baseline leg (oracle)")
         ref, cb = cpu_baseline(args, case, W)

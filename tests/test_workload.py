@@ -52,7 +52,10 @@ def test_tiny_workload_recipe():
 
 @pytest.mark.parametrize("key,lo,hi,n", [("llama3_8b_decode", 512, 4096, 64),
                                          ("mqa_decode", 16, 8192, 256),
-                                         ("varlen_prefill", 64, 1024, 32)])
+                                         ("varlen_prefill", 64, 1024, 32),
+                                         ("chunked_prefill", 0, 3072, 16),
+                                         ("spec_verify", 508, 4092, 64),
+                                         ("shared_prefix_decode", 64, 2048, 64)])
 def test_length_recipes(key, lo, hi, n):
     lens = W.workload_lengths(key, np.random.default_rng(W.WORKLOADS[key].seed))
     assert lens.shape == (n,) and lens.min() >= lo and lens.max() <= hi
@@ -102,3 +105,13 @@ def test_kv_bytes_and_flops_accounting():
     assert c.flops() == 30 * 8 * 4 * 16
     p = W.make_prefill_case([3, 4], 4, 2, 8, 4, W.BF16, 3)
     assert p.flops() == (6 + 10) * 4 * 4 * 8
+
+
+def test_shared_prefix_case_accounting():
+    c = W.make_shared_prefix_case(20, [3, 5], 4, 2, 8, 4, W.BF16, 9)
+    row = 2 * 8 * 2 * 2
+    assert c.logical_kv_bytes() == (23 + 25) * row and c.unique_kv_bytes() == (20 + 8) * row
+    u = c.logical(np.random.default_rng(0))
+    assert u.context_lens.tolist() == [23, 25]
+    # sample 1 reads the prompt, then its own continuation rows
+    assert np.array_equal(u.k[23:43], c.k_prompt) and np.array_equal(u.k[43:48], c.k_cont[3:8])

@@ -326,6 +326,87 @@ def make_extend_case(prefix_lens: Sequence[int], q_lens: Sequence[int], num_q_he
                       block_table=table, num_blocks=nblk, scale=np.float32(scale), seed=seed)
 
 
+@dataclass
+class SharedPrefixCase:
+    """Several samples decoding from one prompt (prefix sharing): every sample's
+    context is the prompt followed by its own continuation.  Values only; how the
+    pages are shared is decided by the code under test."""
+    name: str
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    prompt_len: int
+    cont_lens: np.ndarray         # int32 [B] tokens each sample added after the fork (>= 1)
+    q: np.ndarray                 # [B, Hq, d] one decode query per sample
+    k_prompt: np.ndarray          # [prompt_len, Hkv, d]
+    v_prompt: np.ndarray
+    k_cont: np.ndarray            # [sum cont_lens, Hkv, d], samples concatenated
+    v_cont: np.ndarray
+    scale: np.float32
+    seed: int = 0
+
+    @property
+    def batch(self) -> int:
+        return int(self.cont_lens.shape[0])
+
+    @property
+    def context_lens(self) -> np.ndarray:
+        return (self.prompt_len + self.cont_lens).astype(np.int32)
+
+    @property
+    def cu_cont(self) -> np.ndarray:
+        return cu_from_lengths(self.cont_lens)
+
+    def _row_bytes(self) -> int:
+        return self.num_kv_heads * self.head_dim * 2 * elem_bytes(self.dtype)
+
+    def logical_kv_bytes(self) -> int:
+        """K/V bytes the samples attend over, each sample's copy of the prompt counted."""
+        return int(self.context_lens.astype(np.int64).sum()) * self._row_bytes()
+
+    def unique_kv_bytes(self) -> int:
+        """K/V bytes of distinct positions: the prompt once plus every continuation."""
+        return (self.prompt_len + int(self.cont_lens.astype(np.int64).sum())) * self._row_bytes()
+
+    def logical(self, rng: np.random.Generator) -> DecodeCase:
+        """The same samples as unshared sequences (packed K/V, a placement of their own)."""
+        parts_k, parts_v = [], []
+        cu = self.cu_cont
+        for b in range(self.batch):
+            parts_k += [self.k_prompt, self.k_cont[cu[b]:cu[b + 1]]]
+            parts_v += [self.v_prompt, self.v_cont[cu[b]:cu[b + 1]]]
+        ctx = self.context_lens
+        table, nb = place_pages(rng, ctx, self.block_size)
+        return DecodeCase(name=self.name + "_unshared", dtype=self.dtype, num_q_heads=self.num_q_heads,
+                          num_kv_heads=self.num_kv_heads, head_dim=self.head_dim, block_size=self.block_size,
+                          context_lens=ctx, cu_ctx=cu_from_lengths(ctx), q=self.q, k=np.concatenate(parts_k),
+                          v=np.concatenate(parts_v), block_table=table, num_blocks=nb, scale=self.scale,
+                          seed=self.seed)
+
+
+def make_shared_prefix_case(prompt_len: int, cont_lens: Sequence[int], num_q_heads: int, num_kv_heads: int,
+                            head_dim: int, block_size: int = 16, dtype: str = BF16, seed: int = 0, *,
+                            name: str = "custom", rng: Optional[np.random.Generator] = None,
+                            scale: Optional[float] = None) -> SharedPrefixCase:
+    """Draw order after the lengths: Q, prompt K, prompt V, continuation K, continuation V."""
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    cont = np.asarray(cont_lens, dtype=np.int32)
+    B, Tc = int(cont.shape[0]), int(cont.astype(np.int64).sum())
+    q = _values(rng, (B, num_q_heads, head_dim), dtype)
+    kp = _values(rng, (prompt_len, num_kv_heads, head_dim), dtype)
+    vp = _values(rng, (prompt_len, num_kv_heads, head_dim), dtype)
+    kc = _values(rng, (Tc, num_kv_heads, head_dim), dtype)
+    vc = _values(rng, (Tc, num_kv_heads, head_dim), dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return SharedPrefixCase(name=name, dtype=dtype, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                            head_dim=head_dim, block_size=block_size, prompt_len=int(prompt_len), cont_lens=cont,
+                            q=q, k_prompt=kp, v_prompt=vp, k_cont=kc, v_cont=vc, scale=np.float32(scale), seed=seed)
+
+
 # ---------------------------------------------------------------------------
 # The named workloads.
 # ---------------------------------------------------------------------------
@@ -360,6 +441,11 @@ WORKLOADS = {
                                 "Hq=32, Hkv=8, d=128, bs=16, bf16",
                                 {"batch": 16, "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
                                  "dtype": BF16, "q_len": 512}),
+    "shared_prefix_decode": Workload("shared_prefix_decode", "shared", 8,
+                                     "64 samples decoding from one 8003-token prompt (shared pages), each with its "
+                                     "own continuation ~U[64,2048]; Hq=32, Hkv=8, d=128, bs=16, bf16",
+                                     {"batch": 64, "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128,
+                                      "block_size": 16, "dtype": BF16, "prompt_len": 8003}),
     "spec_verify": Workload("spec_verify", "extend", 7,
                             "draft-token verification: B=64, ctx~U[512,4096] incl. 4 draft tokens each, "
                             "Hq=32, Hkv=8, d=128, bs=16, bf16",
@@ -368,7 +454,7 @@ WORKLOADS = {
 }
 
 WORKLOAD_ORDER: List[str] = ["tiny_f32", "llama3_8b_decode", "long_ctx_decode", "mqa_decode", "varlen_prefill",
-                             "chunked_prefill", "spec_verify"]
+                             "chunked_prefill", "spec_verify", "shared_prefix_decode"]
 
 
 def workload_lengths(key: str, rng: np.random.Generator) -> np.ndarray:
@@ -389,11 +475,13 @@ def workload_lengths(key: str, rng: np.random.Generator) -> np.ndarray:
         return rng.integers(0, 3072, size=16, endpoint=True).astype(np.int32)
     if key == "spec_verify":       # cached prefix lengths (the context less the 4 draft tokens)
         return (rng.integers(512, 4096, size=64, endpoint=True) - 4).astype(np.int32)
+    if key == "shared_prefix_decode":   # continuation lengths after the shared prompt
+        return rng.integers(64, 2048, size=64, endpoint=True).astype(np.int32)
     raise KeyError(key)
 
 
 def make_workload(key: str):
-    """Build the named workload's inputs (a DecodeCase, PrefillCase or ExtendCase)."""
+    """Build the named workload's inputs (a DecodeCase, PrefillCase, ExtendCase or SharedPrefixCase)."""
     w = WORKLOADS[key]
     s = w.summary
     rng = np.random.default_rng(w.seed)
@@ -403,6 +491,9 @@ def make_workload(key: str):
         return make_decode_case(lengths, s["num_q_heads"], s["num_kv_heads"], s["head_dim"],
                                 s["block_size"], s["dtype"], w.seed, name=key, rng=rng,
                                 pool_blocks=pool)
+    if w.kind == "shared":
+        return make_shared_prefix_case(s["prompt_len"], lengths, s["num_q_heads"], s["num_kv_heads"],
+                                       s["head_dim"], s["block_size"], s["dtype"], w.seed, name=key, rng=rng)
     if w.kind == "extend":
         q_lens = np.full(len(lengths), s["q_len"], dtype=np.int32)
         return make_extend_case(lengths, q_lens, s["num_q_heads"], s["num_kv_heads"], s["head_dim"],
