@@ -30,11 +30,11 @@ class OracleError(RuntimeError):
 def _bind(lib: C.CDLL) -> C.CDLL:
     lib.oracle_paged_kv_write.argtypes = [_P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I]
     lib.oracle_paged_kv_gather.argtypes = [_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I]
-    lib.oracle_gqa_paged_decode.argtypes = [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _D, _I,
+    lib.oracle_gqa_paged_decode.argtypes = [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _D, _I, _I,
                                             _P, _P, _I, _I]
-    lib.oracle_gqa_varlen_prefill.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _D, _I, _I, _P, _I, _P, _I]
-    lib.oracle_gqa_paged_extend.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _D, _I, _P, _I,
-                                            _P, _I]
+    lib.oracle_gqa_varlen_prefill.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _D, _I, _I, _I, _P, _I, _P, _I]
+    lib.oracle_gqa_paged_extend.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _D, _I, _I,
+                                            _P, _I, _P, _I]
     lib.oracle_paged_kv_copy_blocks.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I]
     for f in ("oracle_paged_kv_write", "oracle_paged_kv_gather", "oracle_paged_kv_copy_blocks", "oracle_gqa_paged_decode",
               "oracle_gqa_varlen_prefill", "oracle_gqa_paged_extend", "oracle_max_threads"):
@@ -118,8 +118,9 @@ class Oracle:
         return k_out, v_out
 
     def gqa_paged_decode(self, q, k_cache, v_cache, block_table, context_lens, scale,
-                         want_probs: bool = False, num_threads: int = 0):
-        """fp64 output [B, Hq, d] (and, if asked, probs [B, Hq, max_ctx])."""
+                         want_probs: bool = False, num_threads: int = 0, window: int = 0):
+        """fp64 output [B, Hq, d] (and, if asked, probs [B, Hq, max_ctx]); window > 0 keeps the
+        newest `window` positions only."""
         q = self._c(q)
         dt = self._dtype(q)
         B, hq, d = q.shape
@@ -132,13 +133,14 @@ class Oracle:
         probs = np.zeros((B, hq, max(stride, 1)), dtype=np.float64) if want_probs else None
         rc = self.lib.oracle_gqa_paged_decode(self._ptr(q), self._ptr(self._c(k_cache)),
                                               self._ptr(self._c(v_cache)), self._ptr(bt), bt.shape[1],
-                                              self._ptr(cl), B, hq, hkv, d, bs, nb, float(scale), dt,
-                                              self._ptr(out), self._ptr(probs), max(stride, 1),
+                                              self._ptr(cl), B, hq, hkv, d, bs, nb, float(scale), int(window),
+                                              dt, self._ptr(out), self._ptr(probs), max(stride, 1),
                                               int(num_threads))
         self._check(rc, "oracle_gqa_paged_decode")
         return (out, probs) if want_probs else out
 
-    def gqa_varlen_prefill(self, q, k, v, cu_seqlens, scale, causal=True, rows=None, num_threads: int = 0):
+    def gqa_varlen_prefill(self, q, k, v, cu_seqlens, scale, causal=True, rows=None, num_threads: int = 0,
+                           window: int = 0):
         """fp64 output [T or len(rows), Hq, d]."""
         q, k, v = self._c(q), self._c(k), self._c(v)
         dt = self._dtype(q)
@@ -150,13 +152,13 @@ class Oracle:
         out = np.empty((n, hq, d), dtype=np.float64)
         rc = self.lib.oracle_gqa_varlen_prefill(self._ptr(q), self._ptr(k), self._ptr(v), self._ptr(cu),
                                                 len(cu) - 1, hq, hkv, d, float(scale), int(bool(causal)),
-                                                dt, self._ptr(r), n, self._ptr(out), int(num_threads))
+                                                int(window), dt, self._ptr(r), n, self._ptr(out), int(num_threads))
         self._check(rc, "oracle_gqa_varlen_prefill")
         return out
 
 
     def gqa_paged_extend(self, q, cu_q, k_cache, v_cache, block_table, context_lens, scale, rows=None,
-                         num_threads: int = 0):
+                         num_threads: int = 0, window: int = 0):
         """fp64 output [total_q or len(rows), Hq, d]: each query row over its sequence's cached keys up to
         its position."""
         q = self._c(q)
@@ -172,8 +174,8 @@ class Oracle:
         out = np.empty((n, hq, d), dtype=np.float64)
         rc = self.lib.oracle_gqa_paged_extend(self._ptr(q), self._ptr(cq), self._ptr(self._c(k_cache)),
                                               self._ptr(self._c(v_cache)), self._ptr(bt), bt.shape[1],
-                                              self._ptr(cl), len(cl), hq, hkv, d, bs, nb, float(scale), dt,
-                                              self._ptr(r), n, self._ptr(out), int(num_threads))
+                                              self._ptr(cl), len(cl), hq, hkv, d, bs, nb, float(scale),
+                                              int(window), dt, self._ptr(r), n, self._ptr(out), int(num_threads))
         self._check(rc, "oracle_gqa_paged_extend")
         return out
 

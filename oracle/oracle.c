@@ -209,7 +209,7 @@ int oracle_gqa_paged_decode(const void* q, const void* k_cache, const void* v_ca
                             const int32_t* block_table, int32_t max_blocks_per_seq,
                             const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                            int32_t num_blocks, double scale, int32_t dtype, double* out,
+                            int32_t num_blocks, double scale, int32_t window, int32_t dtype, double* out,
                             double* probs, int32_t probs_stride, int32_t num_threads) {
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out) return ORACLE_EINVAL;
     if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
@@ -250,17 +250,20 @@ int oracle_gqa_paged_decode(const void* q, const void* k_cache, const void* v_ca
                 for (int32_t x = 0; x < head_dim; ++x) o[x] = 0.0;
                 continue;
             }
+            /* Local attention: only the newest `window` positions (the query's
+             * own included) are attended to. */
+            const int64_t lo = (window > 0 && n > window) ? n - window : 0;
             const int64_t qo = u * head_dim;
-            for (int64_t j = 0; j < n; ++j) {
+            for (int64_t j = lo; j < n; ++j) {
                 const int64_t blk = block_of(block_table, max_blocks_per_seq, num_blocks, b, j, block_size);
                 const int64_t slot = j % block_size;
                 const int64_t ko = page_offset(blk, h, slot, num_kv_heads, block_size, head_dim);
-                s[j] = scaled_dot(q, qo, k_cache, ko, head_dim, scale, dtype);
-                voff[j] = ko;
+                s[j - lo] = scaled_dot(q, qo, k_cache, ko, head_dim, scale, dtype);
+                voff[j - lo] = ko;
             }
-            softmax_weighted_sum(s, n, v_cache, voff, head_dim, dtype, p, o);
+            softmax_weighted_sum(s, n - lo, v_cache, voff, head_dim, dtype, p, o);
             if (probs)
-                for (int64_t j = 0; j < n; ++j) probs[u * probs_stride + j] = p[j];
+                for (int64_t j = 0; j < n; ++j) probs[u * probs_stride + j] = j < lo ? 0.0 : p[j - lo];
         }
         free(s);
         free(p);
@@ -272,9 +275,10 @@ int oracle_gqa_paged_decode(const void* q, const void* k_cache, const void* v_ca
 int oracle_gqa_varlen_prefill(const void* q, const void* k, const void* v,
                               const int32_t* cu_seqlens, int32_t batch, int32_t num_q_heads,
                               int32_t num_kv_heads, int32_t head_dim, double scale,
-                              int32_t causal, int32_t dtype, const int32_t* rows,
+                              int32_t causal, int32_t window, int32_t dtype, const int32_t* rows,
                               int32_t num_rows, double* out, int32_t num_threads) {
     if (!q || !k || !v || !cu_seqlens || !out) return ORACLE_EINVAL;
+    if (window > 0 && !causal) return ORACLE_EINVAL;
     if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return ORACLE_EINVAL;
     if (num_q_heads % num_kv_heads != 0 || !dtype_ok(dtype)) return ORACLE_EINVAL;
     const int32_t group = num_q_heads / num_kv_heads;
@@ -312,8 +316,9 @@ int oracle_gqa_varlen_prefill(const void* q, const void* k, const void* v,
              * row inside its own sequence. */
             int32_t seq = 0;
             while (cu_seqlens[seq + 1] <= i) ++seq;
-            const int64_t first = cu_seqlens[seq];
+            int64_t first = cu_seqlens[seq];
             const int64_t last = causal ? i : (int64_t)cu_seqlens[seq + 1] - 1;
+            if (window > 0 && i - window + 1 > first) first = i - window + 1;   /* newest `window` keys */
             const int64_t n = last - first + 1;
             const int64_t qo = (i * num_q_heads + qh) * (int64_t)head_dim;
             for (int64_t j = 0; j < n; ++j) {
@@ -335,7 +340,7 @@ int oracle_gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_ca
                             int32_t max_blocks_per_seq, const int32_t* context_lens,
                             int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                            double scale, int32_t dtype, const int32_t* rows,
+                            double scale, int32_t window, int32_t dtype, const int32_t* rows,
                             int32_t num_rows, double* out, int32_t num_threads) {
     if (!q || !cu_q || !k_cache || !v_cache || !block_table || !context_lens || !out) return ORACLE_EINVAL;
     if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
@@ -389,14 +394,15 @@ int oracle_gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_ca
                 for (int32_t x = 0; x < head_dim; ++x) o[x] = 0.0;
                 continue;
             }
+            const int64_t lo = (window > 0 && n > window) ? n - window : 0;   /* newest `window` keys */
             const int64_t qo = (r * num_q_heads + qh) * head_dim;
-            for (int64_t j = 0; j < n; ++j) {
+            for (int64_t j = lo; j < n; ++j) {
                 const int64_t blk = block_of(block_table, max_blocks_per_seq, num_blocks, b, j, block_size);
                 const int64_t ko = page_offset(blk, h, j % block_size, num_kv_heads, block_size, head_dim);
-                s[j] = scaled_dot(q, qo, k_cache, ko, head_dim, scale, dtype);
-                voff[j] = ko;
+                s[j - lo] = scaled_dot(q, qo, k_cache, ko, head_dim, scale, dtype);
+                voff[j - lo] = ko;
             }
-            softmax_weighted_sum(s, n, v_cache, voff, head_dim, dtype, p, o);
+            softmax_weighted_sum(s, n - lo, v_cache, voff, head_dim, dtype, p, o);
         }
         free(s);
         free(p);

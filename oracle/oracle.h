@@ -59,27 +59,33 @@ int oracle_paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src
                                 int32_t num_pairs, int32_t num_blocks, int32_t block_size,
                                 int32_t num_kv_heads, int32_t head_dim, int32_t dtype);
 
-/* Decode: one query token per sequence attends to every cached position
- * [0, context_lens[b]) of its sequence.  Query head qh reads KV head
- * qh / (Hq / Hkv).  out is fp64 [B, Hq, d]; a sequence with no context gets 0.
- * probs (may be NULL) receives the softmax weights, fp64 [B, Hq, probs_stride],
+/* Local attention (the lecture notes, section 4.4): with window > 0 every
+ * query attends only to the newest `window` positions up to its own (its own
+ * included), i.e. keys p - window + 1 .. p for a query at position p; window
+ * <= 0 means no window.  The three attention calls below take it.
+ *
+ * Decode: one query token per sequence attends to every cached position
+ * [0, context_lens[b]) of its sequence (the query sits at context_lens[b] - 1).
+ * Query head qh reads KV head qh / (Hq / Hkv).  out is fp64 [B, Hq, d]; a
+ * sequence with no context gets 0.  probs (may be NULL) receives the softmax
+ * weights, fp64 [B, Hq, probs_stride] (0 for positions outside the window),
  * entries past the context left untouched.  num_threads <= 0 uses the default. */
 int oracle_gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* block_table, int32_t max_blocks_per_seq,
                             const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                            int32_t num_blocks, double scale, int32_t dtype, double* out,
+                            int32_t num_blocks, double scale, int32_t window, int32_t dtype, double* out,
                             double* probs, int32_t probs_stride, int32_t num_threads);
 
 /* Packed variable-length prefill with a block-diagonal (optionally causal) mask.
  * Row i of sequence s (cu_seqlens[s] <= i < cu_seqlens[s+1]) attends to keys j of
- * the same sequence with j <= i when causal, else to all of that sequence.
- * rows (may be NULL) lists the packed row indices to evaluate; NULL means every
+ * the same sequence with j <= i when causal, else to all of that sequence
+ * (a window needs causal).  rows (may be NULL) lists the packed row indices to evaluate; NULL means every
  * row 0..T-1 with num_rows = T.  out is fp64 [num_rows, Hq, d]. */
 int oracle_gqa_varlen_prefill(const void* q, const void* k, const void* v,
                               const int32_t* cu_seqlens, int32_t batch, int32_t num_q_heads,
                               int32_t num_kv_heads, int32_t head_dim, double scale,
-                              int32_t causal, int32_t dtype, const int32_t* rows,
+                              int32_t causal, int32_t window, int32_t dtype, const int32_t* rows,
                               int32_t num_rows, double* out, int32_t num_threads);
 
 /* Several query tokens per sequence over its paged cache: chunked prefill on
@@ -98,7 +104,7 @@ int oracle_gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_ca
                             int32_t max_blocks_per_seq, const int32_t* context_lens,
                             int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                            double scale, int32_t dtype, const int32_t* rows,
+                            double scale, int32_t window, int32_t dtype, const int32_t* rows,
                             int32_t num_rows, double* out, int32_t num_threads);
 
 /* Number of OpenMP threads a parallel region would use (for reporting). */

@@ -506,6 +506,84 @@ def pin_block_model_shared_prompt(orc):
     assert len(m.free_blocks()) == 200 and all(r == 0 for r in m.ref)
 
 
+def pin_window_decode_is_truncated_context(orc):
+    """Local attention in decode equals plain decode over a context that holds only
+    the newest `window` tokens (rebuilt from the packed rows, fresh placement)."""
+    c = W.make_decode_case([9, 1, 30, 17], 4, 2, 16, 4, W.F32, 71)
+    kc, vc = fill_pages(orc, c)
+    for win in (1, 3, 8, 17, 40):
+        got = orc.gqa_paged_decode(c.q, kc, vc, c.block_table, c.context_lens, c.scale, window=win)
+        keep = np.minimum(c.context_lens, win).astype(np.int32)
+        rows = np.concatenate([np.arange(c.cu_ctx[b + 1] - keep[b], c.cu_ctx[b + 1]) for b in range(c.batch)])
+        t = W.DecodeCase(name="t", dtype=c.dtype, num_q_heads=4, num_kv_heads=2, head_dim=16, block_size=4,
+                         context_lens=keep, cu_ctx=W.cu_from_lengths(keep), q=c.q, k=c.k[rows], v=c.v[rows],
+                         block_table=W.place_pages(np.random.default_rng(win), keep, 4)[0],
+                         num_blocks=W.place_pages(np.random.default_rng(win), keep, 4)[1], scale=c.scale)
+        close(got, decode(orc, t), rel=1e-12, what=f"window {win}")
+
+
+def pin_window_one_returns_own_value(orc):
+    """window = 1: every query sees only its own position, so the output is that value row."""
+    c = W.make_decode_case([5, 12], 4, 2, 16, 4, W.BF16, 72)
+    kc, vc = fill_pages(orc, c)
+    got = orc.gqa_paged_decode(c.q, kc, vc, c.block_table, c.context_lens, c.scale, window=1)
+    v = f64(c.v)
+    for b in range(c.batch):
+        last = int(c.cu_ctx[b + 1]) - 1
+        for qh in range(4):
+            assert np.array_equal(got[b, qh], v[last, qh // 2])
+    p = W.make_prefill_case([6, 3], 4, 2, 8, 4, W.BF16, 73)
+    out = orc.gqa_varlen_prefill(p.q, p.k, p.v, p.cu_seqlens, p.scale, window=1)
+    pv = f64(p.v)
+    for i in range(p.total_tokens):
+        for qh in range(4):
+            assert np.array_equal(out[i, qh], pv[i, qh // 2])
+
+
+def _band_sdpa(q, k, v, scale, rows_pos, nkeys, win):
+    """Library attention of query rows at positions rows_pos over keys 0..nkeys-1 with
+    an explicit mask keeping key j iff pos - win < j <= pos."""
+    mask = (np.arange(nkeys)[None, :] <= rows_pos[:, None]) & (np.arange(nkeys)[None, :] > rows_pos[:, None] - win)
+    qt = torch.from_numpy(q).permute(1, 0, 2).unsqueeze(0).contiguous()
+    kt = torch.from_numpy(k).permute(1, 0, 2).unsqueeze(0).contiguous()
+    vt = torch.from_numpy(v).permute(1, 0, 2).unsqueeze(0).contiguous()
+    r = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(mask), scale=float(scale),
+                                       enable_gqa=True)
+    return r[0].permute(1, 0, 2).numpy()
+
+
+def pin_window_matches_library(orc):
+    """Prefill and multi-token queries with a window against torch SDPA with an explicit band mask."""
+    p = W.make_prefill_case([20, 7, 33], 8, 2, 16, 4, W.F32, 74)
+    for win in (1, 5, 16, 100):
+        got = orc.gqa_varlen_prefill(p.q, p.k, p.v, p.cu_seqlens, p.scale, window=win)
+        want = np.zeros_like(got)
+        for b in range(p.batch):
+            a, e = int(p.cu_seqlens[b]), int(p.cu_seqlens[b + 1])
+            want[a:e] = _band_sdpa(f64(p.q[a:e]), f64(p.k[a:e]), f64(p.v[a:e]), p.scale, np.arange(e - a), e - a, win)
+        close(got, want, rel=1e-12, what=f"prefill window {win}")
+    c = W.make_extend_case([9, 0, 25], [4, 6, 11], 8, 2, 16, 4, W.BF16, 75)
+    kc, vc = extend_pages(orc, c)
+    for win in (1, 4, 13, 64):
+        got = orc.gqa_paged_extend(c.q, c.cu_q, kc, vc, c.block_table, c.context_lens, c.scale, window=win)
+        want = np.zeros_like(got)
+        for b in range(c.batch):
+            qa, qe = int(c.cu_q[b]), int(c.cu_q[b + 1])
+            ka, ke = int(c.cu_ctx[b]), int(c.cu_ctx[b + 1])
+            pos = (ke - ka) - (qe - qa) + np.arange(qe - qa)
+            want[qa:qe] = _band_sdpa(f64(c.q[qa:qe]), f64(c.k[ka:ke]), f64(c.v[ka:ke]), c.scale, pos, ke - ka, win)
+        close(got, want, rel=1e-12, what=f"extend window {win}")
+
+
+def pin_window_weights_outside_are_zero(orc):
+    c = W.make_decode_case([30, 4], 4, 2, 16, 4, W.BF16, 76)
+    kc, vc = fill_pages(orc, c)
+    _, probs = orc.gqa_paged_decode(c.q, kc, vc, c.block_table, c.context_lens, c.scale, want_probs=True,
+                                    window=10)
+    assert np.all(probs[0, :, :20] == 0) and np.all(probs[0, :, 20:30] > 0)
+    assert np.allclose(probs[0].sum(-1), 1.0, rtol=1e-12) and np.allclose(probs[1, :, :4].sum(-1), 1.0, rtol=1e-12)
+
+
 def extend_pages(orc, case: W.ExtendCase):
     kc = W.nan_pool(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)
     vc = W.nan_pool(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)
@@ -607,6 +685,12 @@ def pin_contract_errors(orc):
     try:
         orc.gqa_paged_decode(c.q[:, :3], kc, vc, c.block_table, c.context_lens, c.scale)
         raise AssertionError("Hq % Hkv != 0 not reported")
+    except OracleError as e:
+        assert str(EINVAL) in str(e)
+    p = W.make_prefill_case([4], 4, 2, 8, 4, W.F32, 53)
+    try:
+        orc.gqa_varlen_prefill(p.q, p.k, p.v, p.cu_seqlens, p.scale, causal=False, window=2)
+        raise AssertionError("a window without the causal mask not reported")
     except OracleError as e:
         assert str(EINVAL) in str(e)
 

@@ -31,9 +31,9 @@ MUTANTS = [
     ("exp_sign_flipped", "p[j] = exp(s[j] - m);", "p[j] = exp(m - s[j]);"),
     ("decode_drops_last_token", "const int64_t n = context_lens[b];", "const int64_t n = context_lens[b] - 1;"),
     ("causal_excludes_diagonal", "const int64_t last = causal ? i :", "const int64_t last = causal ? i - 1 :"),
-    ("cross_sequence_leak", "const int64_t first = cu_seqlens[seq];", "const int64_t first = 0;"),
+    ("cross_sequence_leak", "int64_t first = cu_seqlens[seq];", "int64_t first = 0;"),
     ("decode_slot_shifted", "const int64_t slot = j % block_size;", "const int64_t slot = (j + 1) % block_size;"),
-    ("values_are_keys", "softmax_weighted_sum(s, n, v_cache, voff", "softmax_weighted_sum(s, n, k_cache, voff"),
+    ("values_are_keys", "softmax_weighted_sum(s, n - lo, v_cache, voff, head_dim, dtype, p, o);\n            if (probs)", "softmax_weighted_sum(s, n - lo, k_cache, voff, head_dim, dtype, p, o);\n            if (probs)"),
     ("write_ignores_start_pos", "const int64_t pos = (int64_t)start_pos[b] + (t - cu_seqlens[b]);",
      "const int64_t pos = (t - cu_seqlens[b]);"),
     ("gather_ignores_head", "const int64_t src = page_offset(blk, h, slot,", "const int64_t src = page_offset(blk, 0, slot,"),
@@ -47,6 +47,12 @@ MUTANTS = [
     ("extend_top_left_alignment", "const int64_t pos = (int64_t)context_lens[b] - q_len + i;",
      "const int64_t pos = i;"),
     ("extend_drops_own_key", "const int64_t n = pos + 1;   /* keys 0 .. pos */", "const int64_t n = pos;"),
+    ("decode_window_one_extra_key", "const int64_t lo = (window > 0 && n > window) ? n - window : 0;\n            const int64_t qo = u * head_dim;",
+     "const int64_t lo = (window > 0 && n > window) ? n - window - 1 : 0;\n            const int64_t qo = u * head_dim;"),
+    ("prefill_window_one_extra_key", "if (window > 0 && i - window + 1 > first) first = i - window + 1;",
+     "if (window > 0 && i - window > first) first = i - window;"),
+    ("extend_window_ignored", "const int64_t lo = (window > 0 && n > window) ? n - window : 0;   /* newest",
+     "const int64_t lo = 0;   /* newest"),
     ("copy_skips_v", "memmove((char*)v_cache + to * es, (const char*)v_cache + from * es, row_bytes);", ""),
     ("copy_head_zero", "const int64_t from = page_offset(src[i], h, slot,", "const int64_t from = page_offset(src[i], 0, slot,"),
 ]
