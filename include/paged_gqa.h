@@ -25,6 +25,14 @@
  *     sequence, memory-bound) are separate phases: the lecture notes, section 2;
  *     the Ultimate Guide, introduction.
  *
+ * Local attention (the lecture notes, section 4.4): a token may attend only to
+ * the most recent positions.  The attention calls take `window`: 0 means full
+ * (causal) attention; window > 0 keeps, for a query at position p, the keys
+ * p - window + 1 .. p (the newest `window` positions, its own included).
+ * Negative windows are PGQA_EINVAL.  Pages wholly before every query's window
+ * are never read, so a caller may release them (their table entries may then
+ * hold any value).
+ *
  * Conventions shared by every call (the pgqa_bm_* block manager below is
  * host-only and documented on its own)
  *   - Every array argument is a DEVICE pointer owned by the caller; the
@@ -147,6 +155,9 @@ size_t gqa_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads,
  *   max_context_len  host-side upper bound of context_lens;
  *                    must be <= max_blocks_per_seq * block_size
  *   scale        softmax scale, normally 1/sqrt(head_dim)
+ *   window       0, or > 0 for local attention: only positions
+ *                [ctx - window, ctx) are attended to (see "Local attention" above);
+ *                tiles wholly before the window are not read
  *   out          [batch, Hq, d] (written)
  *   workspace    >= gqa_paged_decode_workspace_size(batch, Hq, Hkv, d, num_splits) bytes
  * Errors: PGQA_EINVAL, PGQA_ENOTSUP, PGQA_ENOSPC (workspace too small), PGQA_EHIP.
@@ -156,7 +167,7 @@ int gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* context_lens,
                      int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                     int32_t max_context_len, float scale, pgqa_dtype dtype,
+                     int32_t max_context_len, float scale, int32_t window, pgqa_dtype dtype,
                      void* out, int32_t num_splits,
                      void* workspace, size_t workspace_bytes, void* stream);
 
@@ -166,7 +177,8 @@ int gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
  * Row i of sequence s (cu_seqlens[s] <= i < cu_seqlens[s+1]), query head qh,
  * KV head h = qh / (Hq / Hkv):
  *   out[i][qh] = sum_j softmax_j(scale * dot(q[i][qh], k[j][h])) * v[j][h]
- * over keys j of the same sequence with j <= i (causal != 0) or all of them.
+ * over keys j of the same sequence with j <= i (causal != 0) or all of them;
+ * with window > 0 (causal only, else PGQA_EINVAL) also j > i - window.
  * QK^T and PV run on bf16 MFMA with fp32 accumulation; P is rounded to bf16
  * for the PV product.  bf16 only.
  *   q [total_tokens, Hq, d], k / v [total_tokens, Hkv, d], out [total_tokens, Hq, d]
@@ -179,8 +191,8 @@ int gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
 int gqa_varlen_prefill(const void* q, const void* k, const void* v,
                        const int32_t* cu_seqlens, int32_t batch, int32_t total_tokens,
                        int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
-                       int32_t head_dim, float scale, int32_t causal, pgqa_dtype dtype,
-                       void* out, void* stream);
+                       int32_t head_dim, float scale, int32_t causal, int32_t window,
+                       pgqa_dtype dtype, void* out, void* stream);
 
 /*
  * gqa_paged_extend -- q_len >= 1 new query tokens per sequence attend to the
@@ -194,7 +206,8 @@ int gqa_varlen_prefill(const void* q, const void* k, const void* v,
  * ones.  Query row i of sequence b (0 <= i < q_len = cu_q[b+1] - cu_q[b]) sits
  * at position p = ctx - q_len + i and, like any causal row (the lecture notes,
  * section 2: a token depends on the tokens before it), sees
- * keys 0 .. p of the sequence (bottom-right aligned causal mask); with
+ * keys 0 .. p of the sequence (bottom-right aligned causal mask; with
+ * window > 0 only keys p - window + 1 .. p, blocks before them are not read); with
  * q_len = 1 this is gqa_paged_decode, with ctx = q_len it is a causal prefill.
  * For query head qh, h = qh / (Hq / Hkv), K_j read through the block table as
  * in gqa_paged_decode:
@@ -220,7 +233,7 @@ int gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_cache, co
                      int32_t batch, int32_t total_q, int32_t max_q_len,
                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                      int32_t block_size, int32_t num_blocks, int32_t max_context_len,
-                     float scale, pgqa_dtype dtype, void* out, void* stream);
+                     float scale, int32_t window, pgqa_dtype dtype, void* out, void* stream);
 
 /*
  * paged_kv_copy_blocks -- the device half of copy-on-write (the lecture notes,

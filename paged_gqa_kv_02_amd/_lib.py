@@ -23,11 +23,11 @@ _SIGNATURES = {
     "paged_kv_write": (C.c_int, [_P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "paged_kv_gather": (C.c_int, [_P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "gqa_paged_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
-    "gqa_paged_decode": (C.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _I,
+    "gqa_paged_decode": (C.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _I,
                                    _P, _Z, _P]),
-    "gqa_varlen_prefill": (C.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _P]),
+    "gqa_varlen_prefill": (C.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P]),
     "gqa_paged_extend": (C.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
-                                   _P, _P]),
+                                   _I, _P, _P]),
     "paged_kv_copy_blocks": (C.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "pgqa_bm_create": (_P, [_I, _I]),
     "pgqa_bm_destroy": (None, [_P]),

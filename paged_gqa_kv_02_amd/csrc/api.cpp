@@ -116,10 +116,10 @@ size_t gqa_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32
 int gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
                      int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                     int32_t max_context_len, float scale, pgqa_dtype dtype, void* out, int32_t num_splits,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     int32_t max_context_len, float scale, int32_t window, pgqa_dtype dtype, void* out,
+                     int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
     if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
-        max_context_len < 0 || num_splits < 0)
+        max_context_len < 0 || num_splits < 0 || window < 0)
         return PGQA_EINVAL;
     if (num_q_heads % num_kv_heads) return PGQA_EINVAL;
     const int es = elem_bytes(dtype);
@@ -141,16 +141,17 @@ int gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache, co
     if (workspace_bytes < need) return PGQA_ENOSPC;
     pgqa::DecodeLaunch L{q, k_cache, v_cache, block_table, context_lens, out, workspace, max_blocks_per_seq,
                          batch, num_q_heads, num_kv_heads, head_dim, lg, num_blocks, max_context_len,
-                         num_splits, dtype == PGQA_BF16 ? 1 : 0, scale};
+                         num_splits, dtype == PGQA_BF16 ? 1 : 0, scale, window};
     return hip_status(pgqa::launch_decode(L, (hipStream_t)stream));
 }
 
 int gqa_varlen_prefill(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t batch,
                        int32_t total_tokens, int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
-                       int32_t head_dim, float scale, int32_t causal, pgqa_dtype dtype, void* out,
-                       void* stream) {
-    if (batch < 0 || total_tokens < 0 || max_seqlen < 0 || num_q_heads <= 0 || num_kv_heads <= 0)
+                       int32_t head_dim, float scale, int32_t causal, int32_t window, pgqa_dtype dtype,
+                       void* out, void* stream) {
+    if (batch < 0 || total_tokens < 0 || max_seqlen < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || window < 0)
         return PGQA_EINVAL;
+    if (window > 0 && !causal) return PGQA_EINVAL;
     if (num_q_heads % num_kv_heads) return PGQA_EINVAL;
     if (dtype != PGQA_BF16 && dtype != PGQA_F32) return PGQA_ENOTSUP;
     if (dtype != PGQA_BF16) return PGQA_ENOTSUP;
@@ -167,7 +168,7 @@ int gqa_varlen_prefill(const void* q, const void* k, const void* v, const int32_
     if (check_index_ptr(cu_seqlens)) return PGQA_EINVAL;
     if (batch == 0 || total_tokens == 0 || max_seqlen == 0) return PGQA_OK;
     pgqa::PrefillLaunch L{q, k, v, cu_seqlens, out, batch, total_tokens, max_seqlen, num_q_heads, num_kv_heads,
-                          head_dim, causal ? 1 : 0, scale};
+                          head_dim, causal ? 1 : 0, scale, window};
     return hip_status(pgqa::launch_prefill(L, (hipStream_t)stream));
 }
 
@@ -175,9 +176,9 @@ int gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_cache, co
                      const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
                      int32_t batch, int32_t total_q, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
                      int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_context_len, float scale,
-                     pgqa_dtype dtype, void* out, void* stream) {
+                     int32_t window, pgqa_dtype dtype, void* out, void* stream) {
     if (batch < 0 || total_q < 0 || max_q_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
-        max_blocks_per_seq <= 0 || max_context_len < 0)
+        max_blocks_per_seq <= 0 || max_context_len < 0 || window < 0)
         return PGQA_EINVAL;
     if (num_q_heads % num_kv_heads) return PGQA_EINVAL;
     if (dtype != PGQA_BF16) return PGQA_ENOTSUP;
@@ -198,7 +199,7 @@ int gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_cache, co
     if (batch == 0 || total_q == 0 || max_q_len == 0) return PGQA_OK;
     pgqa::ExtendLaunch L{q, k_cache, v_cache, cu_q, block_table, context_lens, out, batch, total_q, max_q_len,
                          max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, lg, num_blocks,
-                         max_context_len, scale};
+                         max_context_len, scale, window};
     return hip_status(pgqa::launch_extend(L, (hipStream_t)stream));
 }
 

@@ -41,8 +41,9 @@
 //    only when a running max grows by more than 8, which keeps every weight
 //    <= 256 and is exact because the final o / l uses the same reference max.
 //  * Masking selects (never multiplies) and only on the ragged last tile of a
-//    sequence: scores past the context become -inf and V rows past the context
-//    are zeroed, so NaN in unused slots cannot leak.
+//    sequence (and, under a local-attention window, its first tile): scores
+//    outside [lo, ctx) become -inf and those V rows are zeroed, so NaN in
+//    unused slots (or in pages dropped before the window) cannot leak.
 //  * Large groups (G >= 16) use G/8 waves per workgroup sharing one ring; each
 //    wave owns 8 query heads.
 #include "device_common.hpp"
@@ -80,6 +81,7 @@ struct DecodeArgs {
     int32_t ctx_cap;     // max_context_len: device context lengths are clamped to it
     int32_t num_splits;  // requested shares == gridDim.x of the split kernel
     float scale_log2;    // scale * log2(e): scores live in log2 units, weights use exp2
+    int32_t window;      // > 0: only the newest `window` positions are attended to
 };
 
 constexpr int kStages = PGQA_DECODE_STAGES;   // ring depth (tiles) of the split kernel
@@ -188,9 +190,16 @@ __device__ __forceinline__ float group_bcast(float x, int lane) {
     }
 }
 
-__device__ __forceinline__ int tiles_of(int ctx, int cap, int tt) {
+// A sequence's segment covers positions [lo, ctx) with lo = ctx - window under
+// local attention ("Modern LLM Inference", section 4.4: a token attends only to
+// the most recent positions) and lo = 0 otherwise; its tiles are the TT-token
+// tiles from the one holding lo to the one holding ctx - 1, so pages wholly
+// before the window are never read.
+__device__ __forceinline__ int window_lo(int ctx, int window) { return (window > 0 && ctx > window) ? ctx - window : 0; }
+
+__device__ __forceinline__ int tiles_of(int ctx, int cap, int tt, int window) {
     ctx = clampi(ctx, 0, cap);
-    return (ctx + tt - 1) / tt;
+    return ctx > 0 ? (ctx + tt - 1) / tt - window_lo(ctx, window) / tt : 0;
 }
 
 // q . k for one lane's 16-byte slices (fp32 accumulation).
@@ -347,11 +356,11 @@ __device__ __forceinline__ void bcast_heads(const float* vals, float* out, int l
 }
 
 // One tile: scores, online-softmax update and P.V for this wave's GW heads.
-// FULL: every token of the tile is inside the context (no masking needed).
+// FULL: every token of the tile is inside [lo, ctx) (no masking needed).
 template <bool FULL, int ES, int D, int GW>
 __device__ __forceinline__ void tile_compute(const PGQA_LDS char* kb, const PGQA_LDS char* vb, const u32x4* qv,
-                                             float* m, float* l, float (*o)[16 / ES], int tok0, int ctx, float c,
-                                             int lane) {
+                                             float* m, float* l, float (*o)[16 / ES], int tok0, int ctx, int lo,
+                                             float c, int lane) {
     using Gm = Geo<ES, D>;
     using S = Scatter<Gm::LPT, GW>;
     constexpr int EPL = Gm::EPL, RPT = Gm::RPT, TPR = Gm::TPR, VPL = S::VPL;
@@ -364,7 +373,7 @@ __device__ __forceinline__ void tile_compute(const PGQA_LDS char* kb, const PGQA
 #pragma unroll
         for (int g = 0; g < GW; ++g) v[g] = slice_dot<ES>(qv[g], kx);
         scatter_steps<Gm::LPT / 2, GW>(v, lane);
-        const bool valid = FULL || (tok0 + r * TPR < ctx);
+        const bool valid = FULL || (tok0 + r * TPR < ctx && tok0 + r * TPR >= lo);
 #pragma unroll
         for (int k = 0; k < VPL; ++k) s[r][k] = valid ? v[k] : -INFINITY;
     }
@@ -417,8 +426,8 @@ __device__ __forceinline__ void tile_compute(const PGQA_LDS char* kb, const PGQA
             u32x4 v0 = lds_read_16(vb + r * Gm::ROWB);
             u32x4 v1 = lds_read_16(vb + (r + 1) * Gm::ROWB);
             if (!FULL) {
-                if (tok0 + r * TPR >= ctx) v0 = u32x4{0, 0, 0, 0};
-                if (tok0 + (r + 1) * TPR >= ctx) v1 = u32x4{0, 0, 0, 0};
+                if (tok0 + r * TPR >= ctx || tok0 + r * TPR < lo) v0 = u32x4{0, 0, 0, 0};
+                if (tok0 + (r + 1) * TPR >= ctx || tok0 + (r + 1) * TPR < lo) v1 = u32x4{0, 0, 0, 0};
             }
             const u32 w0[4] = {v0.x, v0.y, v0.z, v0.w};
             const u32 w1[4] = {v1.x, v1.y, v1.z, v1.w};
@@ -447,7 +456,7 @@ __device__ __forceinline__ void tile_compute(const PGQA_LDS char* kb, const PGQA
             const u32x4 vx = lds_read_16(vb + r * Gm::ROWB);
             float vf[EPL];
             unpack16<ES>(vx, vf);
-            if (!FULL && tok0 + r * TPR >= ctx) {
+            if (!FULL && (tok0 + r * TPR >= ctx || tok0 + r * TPR < lo)) {
 #pragma unroll
                 for (int x = 0; x < EPL; ++x) vf[x] = 0.0f;
             }
@@ -488,7 +497,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         int carry = 0;
         for (int base = 0; base < B; base += 64) {
             const int b = base + lane;
-            int x = b < B ? tiles_of(a.context_lens[b], a.ctx_cap, TT) : 0;
+            int x = b < B ? tiles_of(a.context_lens[b], a.ctx_cap, TT, a.window) : 0;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const int y = __shfl_up(x, off);
@@ -544,12 +553,14 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         const int n = (int)min((int64_t)(tiles_b - t0), X1 - X);   // tiles in this piece
         const bool whole = (t0 == 0) && (n == tiles_b);
         const int ctx = clampi(a.context_lens[b], 0, a.ctx_cap);
+        const int lo = window_lo(ctx, a.window);
+        const int tf = lo / TT + t0;   // sequence tile index of the piece's first tile
         const int qh0 = h * G + wave * GW;
         PageWin win;
         win.bt_row = a.block_table + (int64_t)b * a.max_blocks_per_seq;
         win.last_page = (ctx - 1) >> a.bs_log2;
         win.num_blocks = a.num_blocks;
-        if (Gm::TPR <= (1 << a.bs_log2)) win.load((t0 * TT) >> a.bs_log2, lane);
+        if (Gm::TPR <= (1 << a.bs_log2)) win.load((tf * TT) >> a.bs_log2, lane);
 
         // This wave's query slices: GW heads x 16 bytes.
         u32x4 qv[GW];
@@ -572,33 +583,41 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         // Prologue: fill the first kStages-1 ring slots.
 #pragma unroll
         for (int i = 0; i < kStages - 1; ++i)
-            if (i < n) issue_tile<ES, D, W>(a, ring, i, t0 + i, h, ctx, win, wave, lane);
+            if (i < n) issue_tile<ES, D, W>(a, ring, i, tf + i, h, ctx, win, wave, lane);
 
-        // Tiles of the piece: every tile but the piece's last is full (only a
-        // sequence's last tile can be ragged), so the loop body is one path
-        // and the last tile is peeled off with the masked path if it needs it.
+        // Tiles of the piece: every tile but a segment's first (under a window)
+        // and last is full, so the loop body is one path and those two are
+        // peeled off with the masked path if they need it.
         auto step = [&](int it) {
             const int slot = it % kStages;
             // This wave's loads issued after this tile's: at most kStages-2 tiles of lpw each.
             wait_vmcnt_dyn<(kStages - 2) * LPW_MAX>(lpw * min(kStages - 2, n - 1 - it));
             if constexpr (W > 1) __syncthreads();
             if (it + kStages - 1 < n)
-                issue_tile<ES, D, W>(a, ring, (it + kStages - 1) % kStages, t0 + it + kStages - 1, h, ctx,
+                issue_tile<ES, D, W>(a, ring, (it + kStages - 1) % kStages, tf + it + kStages - 1, h, ctx,
                                      win, wave, lane);
             return ring + slot * Gm::TILEB + lane * 16;
         };
-        for (int it = 0; it < n - 1; ++it) {
+        int it0 = 0;
+        if (n > 1 && tf * TT < lo) {
+            const PGQA_LDS char* kb = step(0);
+            tile_compute<false, ES, D, GW>(kb, kb + RPT * Gm::ROWB, qv, m, l, o, tf * TT + tg, ctx, lo, cs, lane);
+            it0 = 1;
+        }
+        for (int it = it0; it < n - 1; ++it) {
             const PGQA_LDS char* kb = step(it);
-            tile_compute<true, ES, D, GW>(kb, kb + RPT * Gm::ROWB, qv, m, l, o, (t0 + it) * TT + tg, ctx, cs, lane);
+            tile_compute<true, ES, D, GW>(kb, kb + RPT * Gm::ROWB, qv, m, l, o, (tf + it) * TT + tg, ctx, lo, cs,
+                                          lane);
         }
         {
             const int it = n - 1;
             const PGQA_LDS char* kb = step(it);
-            const int tile = t0 + it;
-            if ((tile + 1) * TT <= ctx)
-                tile_compute<true, ES, D, GW>(kb, kb + RPT * Gm::ROWB, qv, m, l, o, tile * TT + tg, ctx, cs, lane);
+            const int tile = tf + it;
+            if (tile * TT >= lo && (tile + 1) * TT <= ctx)
+                tile_compute<true, ES, D, GW>(kb, kb + RPT * Gm::ROWB, qv, m, l, o, tile * TT + tg, ctx, lo, cs, lane);
             else
-                tile_compute<false, ES, D, GW>(kb, kb + RPT * Gm::ROWB, qv, m, l, o, tile * TT + tg, ctx, cs, lane);
+                tile_compute<false, ES, D, GW>(kb, kb + RPT * Gm::ROWB, qv, m, l, o, tile * TT + tg, ctx, lo, cs,
+                                               lane);
         }
 
         // ---- per-head (m, l) to every lane, then merge the TPR token groups ----
@@ -684,7 +703,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tt)
 
     int before = 0, all = 0;
     for (int i = tid; i < a.batch; i += 256) {
-        const int t = tiles_of(a.context_lens[i], a.ctx_cap, tt);
+        const int t = tiles_of(a.context_lens[i], a.ctx_cap, tt, a.window);
         all += t;
         if (i < b) before += t;
     }
@@ -700,7 +719,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tt)
     before = red[0][0] + red[0][1] + red[0][2] + red[0][3];
     all = red[1][0] + red[1][1] + red[1][2] + red[1][3];
 
-    const int tiles_b = tiles_of(a.context_lens[b], a.ctx_cap, tt);
+    const int tiles_b = tiles_of(a.context_lens[b], a.ctx_cap, tt, a.window);
     if (tiles_b == 0) return;   // zero-filled by the split kernel
     const int64_t total = (int64_t)Hkv * all;
     const int64_t nw = min((int64_t)a.num_splits, total);
@@ -849,6 +868,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     a.bs_log2 = L.block_size_log2;
     a.ctx_cap = L.max_context_len;
     a.scale_log2 = (float)((double)L.scale * 1.4426950408889634);
+    a.window = L.window;
 
     const int threads = 64 * e.waves;
     // ring + tile prefix sums [batch + 1]

@@ -63,6 +63,7 @@ struct DecodeLaunch {
     int32_t num_splits;   // 0 = choose
     int32_t is_bf16;
     float scale;
+    int32_t window;       // 0: none; > 0: the newest `window` positions only
 };
 
 // Largest number of splits (workgroups of the split-KV kernel) the library picks itself.
@@ -94,6 +95,7 @@ struct PrefillLaunch {
     int32_t head_dim;
     int32_t causal;
     float scale;
+    int32_t window;   // 0: none; > 0: keys i - window + 1 .. i (causal only)
 };
 
 bool prefill_supported(int32_t head_dim, int32_t group);
@@ -119,6 +121,7 @@ struct ExtendLaunch {
     int32_t num_blocks;
     int32_t max_context_len;
     float scale;
+    int32_t window;   // 0: none; > 0: keys p - window + 1 .. p for a row at position p
 };
 
 // Is there a paged multi-token kernel for this (head_dim, group size, block size)?

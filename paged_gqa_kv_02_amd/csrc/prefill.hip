@@ -84,6 +84,7 @@ struct PrefillArgs {
     int32_t num_blocks;
     int32_t bs_log2;
     int32_t ctx_cap;         // host-side bound of context_lens
+    int32_t window;          // > 0: row i sees only its newest `window` keys (local attention)
 };
 
 // Block-table rows are read through the constant address space, which makes
@@ -156,17 +157,18 @@ __device__ __forceinline__ void dma_lane_init(DmaLane<D>& dl, int wave, int lane
 }
 
 
-// DMA of one tile of key block kb: waves 0 and 1 fetch K(kb) into K slot
-// kb % 2, waves 2 and 3 fetch V(kb) into V slot kb % 2 (LDS: K slots, then V
-// slots).
+// DMA of one tile of key block kb: waves 0 and 1 fetch K(kb) into K slot par,
+// waves 2 and 3 fetch V(kb) into V slot par (LDS: K slots, then V slots; par is
+// the parity of the block's index in the workgroup's stream).
 template <int D>
 __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const DmaLane<D>& dl, uint32_t ring, int kb,
-                                           int seq0, int L, int kvh, int wave, int lane, int64_t kvstride) {
+                                           int par, int seq0, int L, int kvh, int wave, int lane,
+                                           int64_t kvstride) {
     using P = PGeo<D>;
     constexpr int NPW = DmaLane<D>::NPW;
     const bool isv = wave >= 2;
     const char* base = (isv ? a.v : a.k) + (int64_t)(seq0 + kb * BN) * kvstride + (int64_t)kvh * P::ROWB;
-    const uint32_t dst = ring + (isv ? 2 * P::TILEB : 0) + (kb & 1) * P::TILEB + (wave & 1) * NPW * 1024;
+    const uint32_t dst = ring + (isv ? 2 * P::TILEB : 0) + par * P::TILEB + (wave & 1) * NPW * 1024;
     if (kb * BN + BN <= L) {
         constexpr int JP = DmaLane<D>::JP;
 #pragma unroll
@@ -232,12 +234,12 @@ __device__ __forceinline__ void paged_load_ids(PagedSrc<D>& ps, int kb, int wave
 // last row (in bounds; those keys are masked).
 template <int D>
 __device__ __forceinline__ void issue_tile_paged(const PagedSrc<D>& ps, const DmaLane<D>& dl, uint32_t ring,
-                                                 int kb, int wave, int lane) {
+                                                 int kb, int par, int wave, int lane) {
     using P = PGeo<D>;
     constexpr int NPW = DmaLane<D>::NPW;
     constexpr int JP = DmaLane<D>::JP;
     const bool isv = wave >= 2;
-    const uint32_t dst = ring + (isv ? 2 * P::TILEB : 0) + (kb & 1) * P::TILEB + (wave & 1) * NPW * 1024;
+    const uint32_t dst = ring + (isv ? 2 * P::TILEB : 0) + par * P::TILEB + (wave & 1) * NPW * 1024;
     const int bs_mask = (1 << ps.lbs) - 1;
     auto base_of = [&](int j, int rb) {
         return ps.pool + (int64_t)ps.id[j] * ps.blk_bytes + ps.head_off + (int64_t)(rb & bs_mask) * P::ROWB;
@@ -316,6 +318,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const bool active = i0 < Lq;
     const int last_key = a.causal ? min(Lk, koff + min(i0 + BQ, Lq)) - 1 : Lk - 1;
     const int last_kb = last_key >= 0 ? last_key / BN : -1;
+    // Local attention (window > 0, causal only): row i also drops keys below
+    // koff + i - window + 1.  The workgroup streams key blocks kb0 .. nkb-1, kb0
+    // set by its first row; every wave computes from kb0 (the blocks before its
+    // own rows' windows are fully masked) to its last block.  Ring slots and the
+    // block loop run on the index relative to kb0.
+    const int win = a.window;
+    const int kb0 = (win > 0 && nkb > 0) ? max(0, koff + tok0 - win + 1) / BN : 0;
+    const int nrel = nkb - kb0;
     const float cs = a.scale_log2;
 
     const int64_t qstride = (int64_t)a.num_q_heads * D * 2;   // bytes per packed Q row
@@ -334,20 +344,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         ps.blk_bytes = ((int64_t)a.num_kv_heads << a.bs_log2) * P::ROWB;
         ps.last = Lk - 1;
         ps.nb = a.num_blocks;
-        if (nkb > 0) {
-            paged_load_ids<D>(ps, 0, wave);
-            issue_tile_paged<D>(ps, dl, ring_addr, 0, wave, lane);
-            if (wave < 2 && nkb > 1) {
-                paged_load_ids<D>(ps, 1, wave);
-                issue_tile_paged<D>(ps, dl, ring_addr, 1, wave, lane);
+        if (nrel > 0) {
+            paged_load_ids<D>(ps, kb0, wave);
+            issue_tile_paged<D>(ps, dl, ring_addr, kb0, 0, wave, lane);
+            if (wave < 2 && nrel > 1) {
+                paged_load_ids<D>(ps, kb0 + 1, wave);
+                issue_tile_paged<D>(ps, dl, ring_addr, kb0 + 1, 1, wave, lane);
             }
             const int nt = wave < 2 ? 2 : 1;
-            if (nt < nkb) paged_load_ids<D>(ps, nt, wave);
+            if (nt < nrel) paged_load_ids<D>(ps, kb0 + nt, wave);
         }
     } else {
         dma_lane_init<D>(dl, wave, lane, kvstride);
-        issue_tile<D>(a, dl, ring_addr, 0, seq0, Lk, kvh, wave, lane, kvstride);
-        if (wave < 2 && nkb > 1) issue_tile<D>(a, dl, ring_addr, 1, seq0, Lk, kvh, wave, lane, kvstride);
+        issue_tile<D>(a, dl, ring_addr, kb0, 0, seq0, Lk, kvh, wave, lane, kvstride);
+        if (wave < 2 && nrel > 1) issue_tile<D>(a, dl, ring_addr, kb0 + 1, 1, seq0, Lk, kvh, wave, lane, kvstride);
     }
 
     // Q^T operand: lane holds row (i0 + l32), d = 16*kk + 8*half .. +8.
@@ -400,20 +410,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
     // One key block: softmax of the block's scores `cur`, overlapped with the
     // next block's scores into `nxt` (when HAS_NEXT), then O^T += V^T P^T.
-    auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], int kb, auto par, auto has_next) {
-        constexpr int PAR = decltype(par)::value;   // kb % 2
-        const int j0 = kb * BN;
-        // Masking (last block of the sequence, or a block crossing the
-        // diagonal): key j0 + off is kept iff off <= lim, with
-        // off = 32*kb2 + 8*(i/4) + i%4 and the lane's 4*half folded into lim.
-        if ((j0 + BN > Lk) || (a.causal && j0 + BN - 1 > koff + i0)) {
+    auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], int kr, auto par, auto has_next) {
+        constexpr int PAR = decltype(par)::value;   // kr % 2
+        const int j0 = (kb0 + kr) * BN;
+        // Masking (last block of the sequence, a block crossing the diagonal,
+        // or one crossing the window's lower edge): key j0 + off is kept iff
+        // llim <= off <= lim, with off = 32*kb2 + 8*(i/4) + i%4 and the lane's
+        // 4*half folded into both bounds.
+        if ((j0 + BN > Lk) || (a.causal && j0 + BN - 1 > koff + i0) || (win > 0 && j0 < koff + i0 + BQ - win)) {
             const int lim = (a.causal ? min(koff + i0 + l32, Lk - 1) : Lk - 1) - j0 - 4 * half;
+            const int llim = (win > 0 ? koff + i0 + l32 - win + 1 : -(1 << 30)) - j0 - 4 * half;
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int off = 32 * kb2 + 8 * (i >> 2) + (i & 3);
-                    cur[kb2][i] = off <= lim ? cur[kb2][i] : -INFINITY;
+                    cur[kb2][i] = (off <= lim && off >= llim) ? cur[kb2][i] : -INFINITY;
                 }
         }
         float mt = cur[0][0];
@@ -486,21 +498,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // Top of block kb: every wave's DMA has landed (K(kb+1), V(kb)) and every
     // wave is done with K(kb) and V(kb-1), so their slots are refilled with
     // K(kb+2) and V(kb+1).
-    auto top = [&](int kb) {
+    auto top = [&](int kr) {
         wait_vmcnt<0>();
         __syncthreads();
-        const int tb = wave < 2 ? kb + 2 : kb + 1;
-        if (tb < nkb) {
+        const int tb = wave < 2 ? kr + 2 : kr + 1;
+        if (tb < nrel) {
             if constexpr (PAGED) {
-                issue_tile_paged<D>(ps, dl, ring_addr, tb, wave, lane);
-                if (tb + 1 < nkb) paged_load_ids<D>(ps, tb + 1, wave);
+                issue_tile_paged<D>(ps, dl, ring_addr, kb0 + tb, tb & 1, wave, lane);
+                if (tb + 1 < nrel) paged_load_ids<D>(ps, kb0 + tb + 1, wave);
             } else {
-                issue_tile<D>(a, dl, ring_addr, tb, seq0, Lk, kvh, wave, lane, kvstride);
+                issue_tile<D>(a, dl, ring_addr, kb0 + tb, tb & 1, seq0, Lk, kvh, wave, lane, kvstride);
             }
         }
     };
-    // Blocks 0 .. kend are computed (kend = last_kb, or -1 for a wave with no
-    // rows); each but the last overlaps the next block's scores.  The two score
+    // Blocks kb0 .. kb0 + kend are computed (kend = last_kb - kb0, or -1 for a
+    // wave with no rows or no keys); each but the last overlaps the next block's
+    // scores.  The two score
     // buffers alternate, so the loop runs two blocks per trip and every block
     // fully rewrites the buffer it fills; the ring parity is a compile-time
     // constant in each copy.  Waves past their last block keep the workgroup's
@@ -510,7 +523,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     f32x16 sa[2], sb[2];
     wait_vmcnt<0>();
     __syncthreads();
-    const int kend = active ? last_kb : -1;
+    const int kend = active && last_kb >= 0 ? last_kb - kb0 : -1;
     if (kend >= 0) scores(sa, I0{});
     int kb = 0;
     for (; kb + 2 <= kend; kb += 2) {
@@ -530,7 +543,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         step(sa, sb, kb, I0{}, std::false_type{});
         kb += 1;
     }
-    for (; kb < nkb; ++kb) top(kb);
+    for (; kb < nrel; ++kb) top(kb);
 
     // Epilogue: O / l rounded to bf16, staged through the idle ring so that
     // each output row is written whole.  The wave's 32 x D tile goes to LDS
@@ -629,6 +642,7 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
     a.causal = L.causal;
     a.scale_log2 = (float)((double)L.scale * 1.4426950408889634);
     a.batch = L.batch;
+    a.window = L.window;
     return launch(fn, a, hg, group, L.max_seqlen, L.head_dim, stream);
 }
 
@@ -656,6 +670,7 @@ hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream) {
     a.num_blocks = L.num_blocks;
     a.bs_log2 = L.block_size_log2;
     a.ctx_cap = L.max_context_len;
+    a.window = L.window;
     return launch(fn, a, hg, group, L.max_q_len, L.head_dim, stream);
 }
 

@@ -88,8 +88,9 @@ def decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: 
 def gqa_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
                      context_lens: torch.Tensor, max_context_len: int, scale: Optional[float] = None,
                      out: Optional[torch.Tensor] = None, num_splits: int = 0,
-                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Decode attention: q [B, Hq, d] over paged K/V -> out [B, Hq, d]."""
+                     workspace: Optional[torch.Tensor] = None, window: int = 0) -> torch.Tensor:
+    """Decode attention: q [B, Hq, d] over paged K/V -> out [B, Hq, d] (window > 0: the newest
+    `window` positions only)."""
     B, hq, d = q.shape
     nb, hkv, bs, d2 = k_cache.shape
     if d2 != d:
@@ -104,7 +105,8 @@ def gqa_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     _i32(block_table, context_lens)
     st = lib().gqa_paged_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
                                 block_table.shape[1], context_lens.data_ptr(), B, hq, hkv, d, bs, nb,
-                                int(max_context_len), float(scale), _dtype(q), out.data_ptr(), int(num_splits),
+                                int(max_context_len), float(scale), int(window), _dtype(q), out.data_ptr(),
+                                int(num_splits),
                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream())
     check("gqa_paged_decode", st)
     return out
@@ -112,7 +114,7 @@ def gqa_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
 
 def gqa_varlen_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
                        max_seqlen: int, scale: Optional[float] = None, causal: bool = True,
-                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                       out: Optional[torch.Tensor] = None, window: int = 0) -> torch.Tensor:
     """Packed varlen prefill: q [T, Hq, d], k / v [T, Hkv, d] -> out [T, Hq, d]."""
     T, hq, d = q.shape
     hkv = k.shape[1]
@@ -124,14 +126,15 @@ def gqa_varlen_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seq
     _i32(cu_seqlens)
     st = lib().gqa_varlen_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
                                   cu_seqlens.numel() - 1, T, int(max_seqlen), hq, hkv, d, float(scale),
-                                  int(bool(causal)), _dtype(q), out.data_ptr(), _stream())
+                                  int(bool(causal)), int(window), _dtype(q), out.data_ptr(), _stream())
     check("gqa_varlen_prefill", st)
     return out
 
 
 def gqa_paged_extend(q: torch.Tensor, cu_q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                      block_table: torch.Tensor, context_lens: torch.Tensor, max_q_len: int, max_context_len: int,
-                     scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                     window: int = 0) -> torch.Tensor:
     """Several new tokens per sequence over its paged cache (chunked prefill on a cached
     prefix, draft verification): q [total_q, Hq, d] -> out [total_q, Hq, d].  The new
     tokens' K/V must already be in the pages; context_lens counts them."""
@@ -148,7 +151,7 @@ def gqa_paged_extend(q: torch.Tensor, cu_q: torch.Tensor, k_cache: torch.Tensor,
     st = lib().gqa_paged_extend(q.data_ptr(), cu_q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                 block_table.data_ptr(), block_table.shape[1], context_lens.data_ptr(),
                                 cu_q.numel() - 1, T, int(max_q_len), hq, hkv, d, bs, nb, int(max_context_len),
-                                float(scale), _dtype(q), out.data_ptr(), _stream())
+                                float(scale), int(window), _dtype(q), out.data_ptr(), _stream())
     check("gqa_paged_extend", st)
     return out
 

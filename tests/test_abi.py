@@ -66,11 +66,11 @@ def test_write_validation(lib):
 
 def _decode(lib, **kw):
     a = dict(q=P[0], kc=P[1], vc=P[2], bt=P[3], maxb=4, cl=P[4], batch=2, hq=8, hkv=2, d=128, bs=16, nb=8,
-             maxctx=64, scale=0.125, dt=BF16, out=P[5], splits=0, ws=P[6], wsb=1 << 30)
+             maxctx=64, scale=0.125, win=0, dt=BF16, out=P[5], splits=0, ws=P[6], wsb=1 << 30)
     a.update(kw)
     return lib.gqa_paged_decode(a["q"], a["kc"], a["vc"], a["bt"], a["maxb"], a["cl"], a["batch"], a["hq"],
-                                a["hkv"], a["d"], a["bs"], a["nb"], a["maxctx"], a["scale"], a["dt"], a["out"],
-                                a["splits"], a["ws"], a["wsb"], None)
+                                a["hkv"], a["d"], a["bs"], a["nb"], a["maxctx"], a["scale"], a["win"], a["dt"],
+                                a["out"], a["splits"], a["ws"], a["wsb"], None)
 
 
 def test_decode_validation(lib):
@@ -81,6 +81,7 @@ def test_decode_validation(lib):
     assert _decode(lib, q=P[0] + 8) == EINVAL
     assert _decode(lib, splits=-1) == EINVAL
     assert _decode(lib, scale=float("nan")) == EINVAL
+    assert _decode(lib, win=-1) == EINVAL
     assert _decode(lib, d=80) == ENOTSUP
     assert _decode(lib, hq=24, hkv=2) == ENOTSUP       # group 12 not built
     assert _decode(lib, hq=256, hkv=2) == ENOTSUP      # group 128 not built
@@ -104,10 +105,10 @@ def test_workspace_size_formula(lib):
 
 def _prefill(lib, **kw):
     a = dict(q=P[0], k=P[1], v=P[2], cu=P[3], batch=3, T=17, maxs=9, hq=32, hkv=8, d=128, scale=0.088,
-             causal=1, dt=BF16, out=P[4])
+             causal=1, win=0, dt=BF16, out=P[4])
     a.update(kw)
     return lib.gqa_varlen_prefill(a["q"], a["k"], a["v"], a["cu"], a["batch"], a["T"], a["maxs"], a["hq"],
-                                  a["hkv"], a["d"], a["scale"], a["causal"], a["dt"], a["out"], None)
+                                  a["hkv"], a["d"], a["scale"], a["causal"], a["win"], a["dt"], a["out"], None)
 
 
 def test_prefill_validation(lib):
@@ -115,6 +116,8 @@ def test_prefill_validation(lib):
     assert _prefill(lib, T=-1) == EINVAL
     assert _prefill(lib, cu=None) == EINVAL
     assert _prefill(lib, out=P[4] + 2) == EINVAL
+    assert _prefill(lib, win=-3) == EINVAL
+    assert _prefill(lib, causal=0, win=8) == EINVAL     # a window needs the causal mask
     assert _prefill(lib, dt=F32) == ENOTSUP             # bf16 MFMA path only
     assert _prefill(lib, d=32) == ENOTSUP
     assert _prefill(lib, hq=24, hkv=8) == ENOTSUP       # group 3
@@ -124,11 +127,11 @@ def test_prefill_validation(lib):
 
 def _extend(lib, **kw):
     a = dict(q=P[0], cu=P[1], kc=P[2], vc=P[3], bt=P[4], maxb=4, cl=P[5], batch=2, T=12, maxq=9, hq=32, hkv=8,
-             d=128, bs=16, nb=8, maxctx=64, scale=0.088, dt=BF16, out=P[6])
+             d=128, bs=16, nb=8, maxctx=64, scale=0.088, win=0, dt=BF16, out=P[6])
     a.update(kw)
     return lib.gqa_paged_extend(a["q"], a["cu"], a["kc"], a["vc"], a["bt"], a["maxb"], a["cl"], a["batch"],
                                 a["T"], a["maxq"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["maxctx"],
-                                a["scale"], a["dt"], a["out"], None)
+                                a["scale"], a["win"], a["dt"], a["out"], None)
 
 
 def test_extend_validation(lib):
@@ -141,6 +144,7 @@ def test_extend_validation(lib):
     assert _extend(lib, cl=P[5] + 2) == EINVAL
     assert _extend(lib, out=P[6] + 2) == EINVAL
     assert _extend(lib, scale=float("inf")) == EINVAL
+    assert _extend(lib, win=-1) == EINVAL
     assert _extend(lib, dt=F32) == ENOTSUP              # bf16 MFMA path only
     assert _extend(lib, d=32) == ENOTSUP
     assert _extend(lib, hq=24, hkv=8) == ENOTSUP        # group 3
