@@ -18,7 +18,8 @@ previous one.  Secondary line items: the packed varlen causal prefill workload
 cache (chunked prefill of 512-token chunks on cached prefixes, and checking 4
 draft tokens per sequence), each with the roofline its arithmetic intensity
 puts it under; decode of 64 samples over the pages of one shared prompt
-(prefix sharing with copy-on-write), against the same samples unshared; and
+(prefix sharing with copy-on-write), against the same samples unshared;
+local-attention decode (4096-token window) on the long-context workload; and
 the fp64 CPU oracle on the same decode batch as a reported baseline.
 """
 
@@ -46,6 +47,7 @@ def _args():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill line item")
     ap.add_argument("--no-extend", action="store_true", help="skip the multi-token (extend) line items")
     ap.add_argument("--no-shared", action="store_true", help="skip the shared-prefix decode line item")
+    ap.add_argument("--no-window", action="store_true", help="skip the sliding-window decode line item")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle timing budget")
     ap.add_argument("--decode-workload", default="llama3_8b_decode",
                     choices=["llama3_8b_decode", "long_ctx_decode", "mqa_decode", "tiny_f32"],
@@ -54,6 +56,8 @@ def _args():
                     help="decode work shares (0 = the library's choice)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step as a captured HIP graph instead of launching its kernels one by one")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_counters.json from two rocprofv3 --pmc runs (no GPU needed)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (scale for HBM byte counters)")
     return ap.parse_args()
@@ -88,6 +92,64 @@ def recorded_traffic(path: str):
         out[part] = int(sum(k["fetch_kib"] * 1024 * cal["fetch_factor"] + k["write_kib"] * 1024 * cal["write_factor"]
                             for k in r["kernels"].values()))
     return out
+
+
+TRAFFIC_PARTS = {
+    # part -> (kernels whose FETCH_SIZE / WRITE_SIZE add up to one call, sources they are built from)
+    "decode": (["decode_split_kernel<2,128,4,1>", "decode_merge_kernel<2,128,4>"],
+               ["paged_gqa_kv_02_amd/csrc/decode.hip", "paged_gqa_kv_02_amd/csrc/device_common.hpp",
+                "paged_gqa_kv_02_amd/csrc/launch.hpp"]),
+    "prefill": (["prefill_kernel<128,4,false>"],
+                ["paged_gqa_kv_02_amd/csrc/prefill.hip", "paged_gqa_kv_02_amd/csrc/device_common.hpp",
+                 "paged_gqa_kv_02_amd/csrc/launch.hpp"]),
+}
+
+
+def _kernel_short(name: str) -> str:
+    n = name.replace("void ", "").replace("pgqa::", "").replace("(anonymous namespace)::", "")
+    return n.split("(")[0].replace(" ", "")
+
+
+def record_traffic(fetch_dir: str, write_dir: str, path: str) -> dict:
+    """Write the per-dispatch FETCH_SIZE / WRITE_SIZE means (KiB) of the decode and
+    prefill kernels from two rocprofv3 --pmc runs of this script into `path`, with
+    the hash of the sources they belong to (the copy calibration already there is
+    kept).  Run on the output of
+      rocprofv3 --pmc FETCH_SIZE -d FETCH_DIR -o pmc -- python3 bench.py --steps 20 --warmup 4
+          --no-cpu-baseline --no-extend --no-shared --no-window
+    and the same with WRITE_SIZE."""
+    import csv
+    import hashlib
+    from collections import defaultdict
+    here = os.path.dirname(os.path.abspath(__file__))
+
+    def means(d, counter):
+        per = defaultdict(float)
+        with open(os.path.join(d, "pmc_counter_collection.csv")) as f:
+            for x in csv.DictReader(f):
+                if x["Counter_Name"] == counter:
+                    per[(_kernel_short(x["Kernel_Name"]), int(x["Dispatch_Id"]))] += float(x["Counter_Value"])
+        agg = defaultdict(list)
+        for (k, _), v in per.items():
+            agg[k].append(v)
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+
+    fetch, write = means(fetch_dir, "FETCH_SIZE"), means(write_dir, "WRITE_SIZE")
+    with open(path) as f:
+        rec = json.load(f)
+    for part, (kernels, sources) in TRAFFIC_PARTS.items():
+        h = hashlib.sha256()
+        for src in sources:
+            with open(os.path.join(here, src), "rb") as fh:
+                h.update(fh.read())
+        rec[part] = {"workload": rec.get(part, {}).get("workload", ""), "sources": sources,
+                     "sha256_16": h.hexdigest()[:16],
+                     "kernels": {k: {"fetch_kib": round(fetch[k], 2), "write_kib": round(write[k], 2)}
+                                 for k in kernels}}
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
 
 
 def log(msg):
@@ -356,6 +418,51 @@ def shared_prefix_leg(args, torch, pg, W, T):
     }
 
 
+def window_leg(args, torch, pg, W, T, window=4096):
+    """Local-attention decode on the long-context workload (B = 8, ctx 32768,
+    Hq 64, Hkv 8): each sequence attends to its newest `window` positions only,
+    so the pages before the window are never read.  Bytes = the K/V inside the
+    windows; the full-attention call on the same pools is timed for comparison."""
+    case = W.make_workload("long_ctx_decode")
+    B, hq, hkv, d, bs = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size
+    table, ctx = T.to_dev(case.block_table), T.to_dev(case.context_lens)
+    kc = T.nan_pool_dev(case.num_blocks, hkv, bs, d, case.dtype)
+    vc = T.nan_pool_dev(case.num_blocks, hkv, bs, d, case.dtype)
+    pg.paged_kv_write(T.to_dev(case.k), T.to_dev(case.v), T.to_dev(case.cu_ctx), T.to_dev(case.start_pos), table,
+                      kc, vc)
+    q, out = T.to_dev(case.q), None
+    out = torch.empty_like(q)
+    ws = pg.decode_workspace(B, hq, hkv, d, 0, q.device)
+    scale, maxctx = float(case.scale), case.max_context_len
+
+    def run(win):
+        f = lambda: pg.gqa_paged_decode(q, kc, vc, table, ctx, maxctx, scale=scale, out=out, workspace=ws,
+                                        window=win)
+        for _ in range(5):
+            f()
+        torch.cuda.synchronize()
+        n = max(20, args.steps // 2)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            evs[i][0].record()
+            f()
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]) * 1e3)
+
+    us_w, us_full = run(window), run(0)
+    row = hkv * d * 2 * 2
+    kv_w = int(np.minimum(case.context_lens, window).astype(np.int64).sum()) * row
+    gbs = kv_w / (us_w * 1e-6) / 1e9
+    return {
+        "workload": "long_ctx_decode", "window": window, "kv_bytes_in_window": kv_w, "decode_us_mean": us_w,
+        "full_attention_us_mean": us_full, "full_attention_kv_gbs": case.kv_bytes() / (us_full * 1e-6) / 1e9,
+        "kv_gbs": gbs,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None},
+    }
+
+
 def cpu_baseline(args, case, W):
     """The fp64 oracle, as it stands, on the same decode step (write + decode),
     repeated until at least --cpu-seconds of host time have been spent."""
@@ -391,6 +498,11 @@ def main():
               file=sys.stderr)
         return 2
     here = os.path.dirname(os.path.abspath(__file__))
+    if args.record_traffic:
+        rec = record_traffic(args.record_traffic[0], args.record_traffic[1],
+                             os.path.join(here, "profiles", "traffic_counters.json"))
+        print(json.dumps({k: rec[k] for k in TRAFFIC_PARTS}), flush=True)
+        return 0
     sys.path.insert(0, here)
     sys.path.insert(0, os.path.join(here, "tests"))
     import torch
@@ -445,6 +557,9 @@ def main():
         for key in ("chunked_prefill", "spec_verify"):
             log(f"extend leg {key}")
             line["extend"][key] = extend_leg(key, args, torch, pg, W, T)
+    if not args.no_window:
+        log("sliding window leg")
+        line["window"] = window_leg(args, torch, pg, W, T)
     if not args.no_shared:
         log("shared prefix leg")
         line["shared_prefix"] = shared_prefix_leg(args, torch, pg, W, T)
