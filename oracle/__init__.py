@@ -15,7 +15,7 @@ import numpy as np
 
 from .build import LIB, build
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 OK, EINVAL, ERANGE = 0, 1, 2
 
 _P = C.c_void_p
@@ -36,7 +36,12 @@ def _bind(lib: C.CDLL) -> C.CDLL:
     lib.oracle_gqa_paged_extend.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _D, _I, _I,
                                             _P, _I, _P, _I]
     lib.oracle_paged_kv_copy_blocks.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I]
+    lib.oracle_fp8_e4m3_decode.argtypes = [_P, C.c_int64, _P]
+    lib.oracle_fp8_e4m3_encode.argtypes = [_P, C.c_int64, _P]
+    lib.oracle_paged_kv_write_fp8.argtypes = [_P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I]
+    lib.oracle_dequantize_fp8.argtypes = [_P, _P, C.c_int64, _I, _P]
     for f in ("oracle_paged_kv_write", "oracle_paged_kv_gather", "oracle_paged_kv_copy_blocks", "oracle_gqa_paged_decode",
+              "oracle_fp8_e4m3_decode", "oracle_fp8_e4m3_encode", "oracle_paged_kv_write_fp8", "oracle_dequantize_fp8",
               "oracle_gqa_varlen_prefill", "oracle_gqa_paged_extend", "oracle_max_threads"):
         getattr(lib, f).restype = C.c_int
     return lib
@@ -55,6 +60,8 @@ class Oracle:
     # -- helpers -------------------------------------------------------------
     @staticmethod
     def _dtype(arr: np.ndarray) -> int:
+        if arr.dtype == np.float64:
+            return F64
         if arr.dtype == np.uint16:
             return BF16
         if arr.dtype == np.float32:
@@ -91,6 +98,44 @@ class Oracle:
                                             self._ptr(bt), bt.shape[1], self._ptr(k_cache),
                                             self._ptr(v_cache), len(cu) - 1, nb, bs, hkv, d, dt)
         self._check(rc, "oracle_paged_kv_write")
+
+    # -- low-precision pages (FP8 E4M3 codes + one fp32 scale per (token, KV head) row) --
+    def fp8_decode(self, codes):
+        c = self._c(codes, np.uint8)
+        out = np.empty(c.shape, dtype=np.float64)
+        self._check(self.lib.oracle_fp8_e4m3_decode(self._ptr(c), c.size, self._ptr(out)), "oracle_fp8_e4m3_decode")
+        return out
+
+    def fp8_encode(self, x):
+        x = self._c(x, np.float32)
+        out = np.empty(x.shape, dtype=np.uint8)
+        self._check(self.lib.oracle_fp8_e4m3_encode(self._ptr(x), x.size, self._ptr(out)), "oracle_fp8_e4m3_encode")
+        return out
+
+    def paged_kv_write_fp8(self, k, v, cu_seqlens, start_pos, block_table, k_cache, v_cache, k_scale, v_scale):
+        """Quantising paged write in place: uint8 code pools [nb, Hkv, bs, d], fp32 scale pools [nb, Hkv, bs]."""
+        k, v = self._c(k), self._c(v)
+        dt = self._dtype(k)
+        for a in (k_cache, v_cache, k_scale, v_scale):
+            assert a.flags.c_contiguous
+        assert k_cache.dtype == np.uint8 and k_scale.dtype == np.float32
+        cu, sp = self._c(cu_seqlens, np.int32), self._c(start_pos, np.int32)
+        bt = self._c(block_table, np.int32)
+        nb, hkv, bs, d = k_cache.shape
+        rc = self.lib.oracle_paged_kv_write_fp8(self._ptr(k), self._ptr(v), self._ptr(cu), self._ptr(sp),
+                                                self._ptr(bt), bt.shape[1], self._ptr(k_cache), self._ptr(v_cache),
+                                                self._ptr(k_scale), self._ptr(v_scale), len(cu) - 1, nb, bs, hkv, d,
+                                                dt)
+        self._check(rc, "oracle_paged_kv_write_fp8")
+
+    def dequantize_fp8(self, codes, scales):
+        """fp64 values of a code pool [..., d] with its scale pool [...]."""
+        c, s = self._c(codes, np.uint8), self._c(scales, np.float32)
+        assert c.shape[:-1] == s.shape
+        out = np.empty(c.shape, dtype=np.float64)
+        rc = self.lib.oracle_dequantize_fp8(self._ptr(c), self._ptr(s), s.size, c.shape[-1], self._ptr(out))
+        self._check(rc, "oracle_dequantize_fp8")
+        return out
 
     def paged_kv_copy_blocks(self, k_cache, v_cache, src, dst):
         """Copy blocks src[i] -> dst[i] (all KV heads, K and V) in place, in order."""

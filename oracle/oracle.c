@@ -56,12 +56,40 @@ static double elem(const void* base, int64_t idx, int32_t dtype) {
         memcpy(&f, &u, sizeof f);
         return (double)f;
     }
+    if (dtype == ORACLE_F64) return ((const double*)base)[idx];
     return (double)((const float*)base)[idx];
 }
 
-static int elem_size(int32_t dtype) { return dtype == ORACLE_BF16 ? 2 : 4; }
+static int elem_size(int32_t dtype) { return dtype == ORACLE_BF16 ? 2 : (dtype == ORACLE_F64 ? 8 : 4); }
 
-static int dtype_ok(int32_t dtype) { return dtype == ORACLE_F32 || dtype == ORACLE_BF16; }
+static int dtype_ok(int32_t dtype) { return dtype == ORACLE_F32 || dtype == ORACLE_BF16 || dtype == ORACLE_F64; }
+
+/*
+ * FP8 E4M3 in the OCP 8-bit floating point layout ("E4M3FN"): bit 7 sign, bits
+ * 6..3 exponent (bias 7), bits 2..0 mantissa.  Exponent field e > 0 gives
+ * (1 + m/8) * 2^(e-7); e = 0 gives the subnormals (m/8) * 2^-6; the codes
+ * S.1111.111 are NaN, and there is no infinity, so the largest finite
+ * magnitude is 1.75 * 2^8 = 448 (code 0x7E).
+ */
+static double e4m3_value(uint8_t code) {
+    const int sign = code >> 7, e = (code >> 3) & 0xF, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double mag = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* Nearest E4M3 code to x (|x| <= 448), ties to the code with an even mantissa:
+ * a plain search over the 127 non-negative finite codes, which are increasing
+ * in value. */
+static uint8_t e4m3_encode(float x) {
+    const double a = fabs((double)x);
+    int best = 0;
+    for (int c = 1; c <= 0x7E; ++c) {
+        const double dc = fabs(e4m3_value((uint8_t)c) - a), db = fabs(e4m3_value((uint8_t)best) - a);
+        if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+    }
+    return (uint8_t)(best | ((x < 0.0f || (x == 0.0f && signbit(x))) ? 0x80 : 0));
+}
 
 int oracle_max_threads(void) {
 #ifdef _OPENMP
@@ -168,6 +196,75 @@ int oracle_paged_kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src
                 memmove((char*)k_cache + to * es, (const char*)k_cache + from * es, row_bytes);
                 memmove((char*)v_cache + to * es, (const char*)v_cache + from * es, row_bytes);
             }
+    return ORACLE_OK;
+}
+
+int oracle_fp8_e4m3_decode(const uint8_t* codes, int64_t n, double* out) {
+    if (n < 0 || (n > 0 && (!codes || !out))) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < n; ++i) out[i] = e4m3_value(codes[i]);
+    return ORACLE_OK;
+}
+
+int oracle_fp8_e4m3_encode(const float* x, int64_t n, uint8_t* codes) {
+    if (n < 0 || (n > 0 && (!x || !codes))) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < n; ++i) {
+        if (!(fabsf(x[i]) <= 448.0f)) return ORACLE_ERANGE;
+        codes[i] = e4m3_encode(x[i]);
+    }
+    return ORACLE_OK;
+}
+
+int oracle_paged_kv_write_fp8(const void* k, const void* v, const int32_t* cu_seqlens,
+                              const int32_t* start_pos, const int32_t* block_table,
+                              int32_t max_blocks_per_seq, uint8_t* k_cache, uint8_t* v_cache,
+                              float* k_scale, float* v_scale, int32_t batch, int32_t num_blocks,
+                              int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype) {
+    if (!k || !v || !cu_seqlens || !start_pos || !block_table || !k_cache || !v_cache || !k_scale || !v_scale)
+        return ORACLE_EINVAL;
+    if (batch < 0 || num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0) return ORACLE_EINVAL;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return ORACLE_EINVAL;
+    for (int32_t b = 0; b < batch; ++b) {
+        if (cu_seqlens[b + 1] < cu_seqlens[b] || start_pos[b] < 0) return ORACLE_ERANGE;
+        for (int64_t t = cu_seqlens[b]; t < cu_seqlens[b + 1]; ++t) {
+            const int64_t pos = (int64_t)start_pos[b] + (t - cu_seqlens[b]);
+            const int64_t blk = block_of(block_table, max_blocks_per_seq, num_blocks, b, pos, block_size);
+            if (blk < 0) return ORACLE_ERANGE;
+            const int64_t slot = pos % block_size;
+            for (int32_t h = 0; h < num_kv_heads; ++h) {
+                const int64_t src = (t * num_kv_heads + h) * (int64_t)head_dim;
+                const int64_t dst = page_offset(blk, h, slot, num_kv_heads, block_size, head_dim);
+                const int64_t srow = (blk * num_kv_heads + h) * block_size + slot;
+                for (int pool = 0; pool < 2; ++pool) {
+                    const void* x = pool ? v : k;
+                    uint8_t* codes = pool ? v_cache : k_cache;
+                    /* The row's scale maps its largest magnitude onto 448; both
+                     * the scale and x / scale are single-precision operations,
+                     * the precision the codes are decided in. */
+                    float amax = 0.0f;
+                    for (int32_t i = 0; i < head_dim; ++i) {
+                        const float a = fabsf((float)elem(x, src + i, dtype));
+                        if (a > amax) amax = a;
+                    }
+                    const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+                    for (int32_t i = 0; i < head_dim; ++i) {
+                        float y = (float)elem(x, src + i, dtype) / sc;
+                        if (y > 448.0f) y = 448.0f;
+                        if (y < -448.0f) y = -448.0f;
+                        codes[dst + i] = e4m3_encode(y);
+                    }
+                    (pool ? v_scale : k_scale)[srow] = sc;
+                }
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+int oracle_dequantize_fp8(const uint8_t* codes, const float* scales, int64_t rows, int32_t head_dim, double* out) {
+    if (rows < 0 || head_dim <= 0 || (rows > 0 && (!codes || !scales || !out))) return ORACLE_EINVAL;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int32_t i = 0; i < head_dim; ++i)
+            out[r * head_dim + i] = e4m3_value(codes[r * head_dim + i]) * (double)scales[r];
     return ORACLE_OK;
 }
 

@@ -5,9 +5,10 @@
  * benchmark's CPU-baseline leg may load this library.  The HIP library never
  * links, includes or calls it, and this file shares no code with it.
  *
- * All pointers are HOST pointers owned by the caller.  Element data is either
- * fp32 (dtype ORACLE_F32) or raw bf16 bit patterns (ORACLE_BF16, uint16 per
- * element); every value is widened exactly to double before any arithmetic.
+ * All pointers are HOST pointers owned by the caller.  Element data is fp32
+ * (dtype ORACLE_F32), raw bf16 bit patterns (ORACLE_BF16, uint16 per element)
+ * or fp64 (ORACLE_F64, for pools dequantised from fp8); every value is widened
+ * exactly to double before any arithmetic.
  *
  * Layouts (row-major, innermost last):
  *   packed K/V        [T, Hkv, d]        T = total tokens, sequences concatenated
@@ -30,7 +31,7 @@
 extern "C" {
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
 enum { ORACLE_OK = 0, ORACLE_EINVAL = 1, ORACLE_ERANGE = 2 };
 
 /* Scatter packed K/V of each sequence's new tokens into the page pools.
@@ -50,6 +51,32 @@ int oracle_paged_kv_gather(const void* k_cache, const void* v_cache, const int32
                            void* k_out, void* v_out, int32_t batch, int32_t num_blocks,
                            int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
                            int32_t dtype);
+
+/* Low-precision KV pages (the Ultimate Guide, section "KV Cache Compression":
+ * KV memory shrinks with fewer bits per value; the pages give the motivation and
+ * byte sizes only, so the format here is a reading): codes are FP8 E4M3 in the
+ * OCP layout (bias 7, largest finite 448, no infinity) and every (token, KV
+ * head) row of d values has its own fp32 scale, stored in a scale pool laid out
+ * like the pages, [num_blocks, Hkv, block_size].  Quantising a row: amax =
+ * max |x|, scale = amax / 448 (1 for an all-zero row), code = the nearest E4M3
+ * value to x / scale (ties to even), the division and the scale in single
+ * precision.  The row's values are then code * scale.
+ *
+ * oracle_fp8_e4m3_decode / _encode: the value of each code (NaN for the NaN
+ * codes) and the nearest code of each value (|x| <= 448, else ORACLE_ERANGE).
+ * oracle_paged_kv_write_fp8: paged_kv_write that quantises (K/V input fp32 or
+ * bf16), writing codes into the uint8 pools and the row scales.
+ * oracle_dequantize_fp8: out[r][i] = value(codes[r][i]) * scales[r] in fp64 for
+ * rows flattened row-major (e.g. a whole pool and its scale pool); attention
+ * over fp8 pages is attention over these fp64 pools (dtype ORACLE_F64). */
+int oracle_fp8_e4m3_decode(const uint8_t* codes, int64_t n, double* out);
+int oracle_fp8_e4m3_encode(const float* x, int64_t n, uint8_t* codes);
+int oracle_paged_kv_write_fp8(const void* k, const void* v, const int32_t* cu_seqlens,
+                              const int32_t* start_pos, const int32_t* block_table,
+                              int32_t max_blocks_per_seq, uint8_t* k_cache, uint8_t* v_cache,
+                              float* k_scale, float* v_scale, int32_t batch, int32_t num_blocks,
+                              int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype);
+int oracle_dequantize_fp8(const uint8_t* codes, const float* scales, int64_t rows, int32_t head_dim, double* out);
 
 /* Copy-on-write block copy (the lecture notes, section 8.2 "Prefix Sharing": when
  * sequences diverge only the modified block is copied).  For i = 0 .. num_pairs-1

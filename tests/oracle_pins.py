@@ -584,6 +584,93 @@ def pin_window_weights_outside_are_zero(orc):
     assert np.allclose(probs[0].sum(-1), 1.0, rtol=1e-12) and np.allclose(probs[1, :, :4].sum(-1), 1.0, rtol=1e-12)
 
 
+def _torch_fp8_values(codes: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def pin_fp8_codes(orc):
+    """Every E4M3 code against torch's float8_e4m3fn and the format's closed form."""
+    codes = np.arange(256, dtype=np.uint8)
+    got, ref = orc.fp8_decode(codes), _torch_fp8_values(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2 and np.array_equal(got[~nan], ref[~nan])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6 and got[0x38] == 1.0
+    assert got[0xB8] == -1.0 and got[0x80] == 0.0
+
+
+def pin_fp8_rounding(orc):
+    """Nearest-even encoding against torch's conversion, on random values, every code
+    value and every midpoint between neighbouring codes (the ties)."""
+    vals = orc.fp8_decode(np.arange(256, dtype=np.uint8))
+    fin = np.sort(vals[~np.isnan(vals)])
+    x = np.concatenate([np.random.default_rng(77).uniform(-448, 448, 20000), fin, (fin[1:] + fin[:-1]) / 2,
+                        np.random.default_rng(78).normal(0, 0.01, 5000)]).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(orc.fp8_encode(x), want)
+
+
+def _fp8_pools(orc, c):
+    kc = np.full((c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim), 0x7F, dtype=np.uint8)
+    vc = kc.copy()
+    ks = np.full((c.num_blocks, c.num_kv_heads, c.block_size), np.nan, dtype=np.float32)
+    vs = ks.copy()
+    orc.paged_kv_write_fp8(c.k, c.v, c.cu_ctx, c.start_pos, c.block_table, kc, vc, ks, vs)
+    return kc, vc, ks, vs
+
+
+def pin_fp8_write(orc):
+    """The quantising write: each row's scale is its largest magnitude over 448 (fp32),
+    its codes are torch's nearest-even conversion of x / scale, the values are within
+    half a code step of the inputs, and slots no token reaches keep the sentinel."""
+    c = W.make_decode_case([9, 30, 4], 4, 2, 16, 4, W.BF16, 79)
+    c.k[3, 1] = 0                                   # an all-zero row: scale 1, codes 0
+    kc, vc, ks, vs = _fp8_pools(orc, c)
+    x = {"k": f64(c.k).astype(np.float32), "v": f64(c.v).astype(np.float32)}
+    used = np.zeros((c.num_blocks, c.block_size), dtype=bool)
+    for b in range(c.batch):
+        for pos in range(int(c.context_lens[b])):
+            t = int(c.cu_ctx[b]) + pos
+            blk, slot = c.block_table[b, pos // 4], pos % 4
+            used[blk, slot] = True
+            for h in range(2):
+                for name, codes, scales in (("k", kc, ks), ("v", vc, vs)):
+                    row = x[name][t, h]
+                    amax = np.float32(np.abs(row).max())
+                    sc = amax / np.float32(448.0) if amax > 0 else np.float32(1.0)
+                    assert scales[blk, h, slot] == sc
+                    y = np.clip(row / sc, np.float32(-448), np.float32(448)).astype(np.float32)
+                    want = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+                    assert np.array_equal(codes[blk, h, slot], want)
+                    deq = _torch_fp8_values(codes[blk, h, slot]) * float(sc)
+                    bound = np.maximum(2.0 ** -4 * np.abs(row), 2.0 ** -10 * float(sc)) * (1 + 1e-6)
+                    assert np.all(np.abs(deq - row) <= bound)
+    assert np.all(kc.transpose(0, 2, 1, 3)[~used] == 0x7F) and np.all(np.isnan(ks.transpose(0, 2, 1)[~used]))
+    assert ks[c.block_table[0, 0], 1, 3] == 1.0 and not kc[c.block_table[0, 0], 1, 3].any()
+
+
+def pin_fp8_decode_is_attention_over_dequantized(orc):
+    """Decode over fp8 pages = attention over the values code * scale, here rebuilt
+    with torch's fp8 conversion and checked against SDPA on dense K/V."""
+    c = W.make_decode_case([13, 1, 40], 8, 2, 16, 4, W.BF16, 80)
+    kc, vc, ks, vs = _fp8_pools(orc, c)
+    got = orc.gqa_paged_decode(f64(c.q), orc.dequantize_fp8(kc, ks), orc.dequantize_fp8(vc, vs), c.block_table,
+                               c.context_lens, c.scale)
+    q = f64(c.q)
+    for b in range(c.batch):
+        n = int(c.context_lens[b])
+        kk = np.zeros((n, 2, 16))
+        vv = np.zeros((n, 2, 16))
+        for pos in range(n):
+            blk, slot = c.block_table[b, pos // 4], pos % 4
+            kk[pos] = _torch_fp8_values(kc[blk, :, slot]) * ks[blk, :, slot, None].astype(np.float64)
+            vv[pos] = _torch_fp8_values(vc[blk, :, slot]) * vs[blk, :, slot, None].astype(np.float64)
+        r = F.scaled_dot_product_attention(torch.from_numpy(q[b][:, None]), torch.from_numpy(kk.transpose(1, 0, 2).copy()),
+                                           torch.from_numpy(vv.transpose(1, 0, 2).copy()), scale=float(c.scale),
+                                           enable_gqa=True)
+        close(got[b], r[:, 0].numpy(), rel=1e-12, what=f"fp8 decode seq {b}")
+
+
 def extend_pages(orc, case: W.ExtendCase):
     kc = W.nan_pool(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)
     vc = W.nan_pool(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)

@@ -53,6 +53,13 @@ MUTANTS = [
      "if (window > 0 && i - window > first) first = i - window;"),
     ("extend_window_ignored", "const int64_t lo = (window > 0 && n > window) ? n - window : 0;   /* newest",
      "const int64_t lo = 0;   /* newest"),
+    ("fp8_ties_to_odd", "if (dc < db || (dc == db && (c & 1) == 0)) best = c;",
+     "if (dc < db || (dc == db && (c & 1) == 1)) best = c;"),
+    ("fp8_scale_over_127", "const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;",
+     "const float sc = amax > 0.0f ? amax / 127.0f : 1.0f;"),
+    ("fp8_subnormal_exponent", "ldexp((double)m / 8.0, -6)", "ldexp((double)m / 8.0, -7)"),
+    ("fp8_dequant_ignores_scale", "out[r * head_dim + i] = e4m3_value(codes[r * head_dim + i]) * (double)scales[r];",
+     "out[r * head_dim + i] = e4m3_value(codes[r * head_dim + i]);"),
     ("copy_skips_v", "memmove((char*)v_cache + to * es, (const char*)v_cache + from * es, row_bytes);", ""),
     ("copy_head_zero", "const int64_t from = page_offset(src[i], h, slot,", "const int64_t from = page_offset(src[i], 0, slot,"),
 ]
