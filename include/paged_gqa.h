@@ -236,6 +236,43 @@ int gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_cache, co
                      float scale, int32_t window, pgqa_dtype dtype, void* out, void* stream);
 
 /*
+ * Low-precision KV pages.  The pages give only the byte sizes (bf16 2 bytes,
+ * int8 1 byte: the lecture notes, section 6) and the motivation (a smaller KV
+ * cache: the Ultimate Guide, section "KV Cache Compression"); the format is
+ * this library's choice: FP8 E4M3 codes (OCP layout: bias 7, largest finite
+ * 448, no infinity), one byte per value, in code pools laid out like the bf16
+ * pools, [num_blocks, Hkv, block_size, d] uint8, and one fp32 scale per
+ * (token, KV head) row in scale pools [num_blocks, Hkv, block_size].  A row x
+ * is stored as codes c = nearest-even E4M3(x / s), s = max|x| / 448 (1 for an
+ * all-zero row), both single-precision operations, and stands for c * s.  A
+ * token's scale is fixed when it is written, so appending tokens never
+ * re-quantises a page.
+ *
+ * paged_kv_write_fp8 -- paged_kv_write that quantises bf16 K/V rows into code
+ * and scale pools (same positions, same skipping rules).  Errors as for
+ * paged_kv_write; PGQA_ENOTSUP for an input dtype other than bf16.
+ *
+ * gqa_paged_decode_fp8 -- gqa_paged_decode over FP8 pages: the same result as
+ * gqa_paged_decode over the values code * scale (bf16 q and out, fp32
+ * accumulation; the K scale multiplies each score and the V scale each weight,
+ * the codes are converted to bf16 exactly).  Same arguments, workspace
+ * (gqa_paged_decode_workspace_size) and window as gqa_paged_decode, plus the
+ * scale pools.  PGQA_ENOTSUP unless head_dim is 64 or 128 and block_size >= 16.
+ */
+int paged_kv_write_fp8(const void* k, const void* v, const int32_t* cu_seqlens, const int32_t* start_pos,
+                       const int32_t* block_table, int32_t max_blocks_per_seq, void* k_cache, void* v_cache,
+                       float* k_scale, float* v_scale, int32_t batch, int32_t total_tokens, int32_t num_blocks,
+                       int32_t block_size, int32_t num_kv_heads, int32_t head_dim, pgqa_dtype dtype,
+                       void* stream);
+
+int gqa_paged_decode_fp8(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                         const float* v_scale, const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+                         float scale, int32_t window, void* out, int32_t num_splits, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
  * paged_kv_copy_blocks -- the device half of copy-on-write (the lecture notes,
  * section 8.2, "Prefix Sharing (Copy-on-Write)": when sequences sharing prefix
  * blocks diverge, only the block being modified is copied).  For every pair p,

@@ -78,15 +78,32 @@ static double e4m3_value(uint8_t code) {
     return sign ? -mag : mag;
 }
 
+/* Values of the 127 non-negative finite codes 0x00 .. 0x7E, which increase
+ * with the code (filled once, before any parallel region). */
+static double e4m3_table[0x7F];
+static int e4m3_table_ready = 0;
+
+static void e4m3_init(void) {
+    if (e4m3_table_ready) return;
+    for (int c = 0; c <= 0x7E; ++c) e4m3_table[c] = e4m3_value((uint8_t)c);
+    e4m3_table_ready = 1;
+}
+
 /* Nearest E4M3 code to x (|x| <= 448), ties to the code with an even mantissa:
- * a plain search over the 127 non-negative finite codes, which are increasing
- * in value. */
+ * lo = the largest code whose value is <= |x| (binary search in the increasing
+ * table), then the nearer of lo and lo + 1. */
 static uint8_t e4m3_encode(float x) {
     const double a = fabs((double)x);
-    int best = 0;
-    for (int c = 1; c <= 0x7E; ++c) {
-        const double dc = fabs(e4m3_value((uint8_t)c) - a), db = fabs(e4m3_value((uint8_t)best) - a);
-        if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+    int lo = 0, hi = 0x7E;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (e4m3_table[mid] <= a) lo = mid;
+        else hi = mid - 1;
+    }
+    int best = lo;
+    if (lo < 0x7E) {
+        const double dl = a - e4m3_table[lo], du = e4m3_table[lo + 1] - a;
+        if (du < dl || (du == dl && ((lo + 1) & 1) == 0)) best = lo + 1;
     }
     return (uint8_t)(best | ((x < 0.0f || (x == 0.0f && signbit(x))) ? 0x80 : 0));
 }
@@ -207,6 +224,7 @@ int oracle_fp8_e4m3_decode(const uint8_t* codes, int64_t n, double* out) {
 
 int oracle_fp8_e4m3_encode(const float* x, int64_t n, uint8_t* codes) {
     if (n < 0 || (n > 0 && (!x || !codes))) return ORACLE_EINVAL;
+    e4m3_init();
     for (int64_t i = 0; i < n; ++i) {
         if (!(fabsf(x[i]) <= 448.0f)) return ORACLE_ERANGE;
         codes[i] = e4m3_encode(x[i]);
@@ -223,12 +241,21 @@ int oracle_paged_kv_write_fp8(const void* k, const void* v, const int32_t* cu_se
         return ORACLE_EINVAL;
     if (batch < 0 || num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0) return ORACLE_EINVAL;
     if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return ORACLE_EINVAL;
+    e4m3_init();
+    /* Contract check first (serial), so the parallel part cannot fail. */
     for (int32_t b = 0; b < batch; ++b) {
         if (cu_seqlens[b + 1] < cu_seqlens[b] || start_pos[b] < 0) return ORACLE_ERANGE;
+        for (int64_t t = cu_seqlens[b]; t < cu_seqlens[b + 1]; ++t)
+            if (block_of(block_table, max_blocks_per_seq, num_blocks, b, (int64_t)start_pos[b] + (t - cu_seqlens[b]),
+                         block_size) < 0)
+                return ORACLE_ERANGE;
+    }
+    /* Rows are independent (a written slot belongs to one token). */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t b = 0; b < batch; ++b) {
         for (int64_t t = cu_seqlens[b]; t < cu_seqlens[b + 1]; ++t) {
             const int64_t pos = (int64_t)start_pos[b] + (t - cu_seqlens[b]);
             const int64_t blk = block_of(block_table, max_blocks_per_seq, num_blocks, b, pos, block_size);
-            if (blk < 0) return ORACLE_ERANGE;
             const int64_t slot = pos % block_size;
             for (int32_t h = 0; h < num_kv_heads; ++h) {
                 const int64_t src = (t * num_kv_heads + h) * (int64_t)head_dim;
@@ -262,6 +289,7 @@ int oracle_paged_kv_write_fp8(const void* k, const void* v, const int32_t* cu_se
 
 int oracle_dequantize_fp8(const uint8_t* codes, const float* scales, int64_t rows, int32_t head_dim, double* out) {
     if (rows < 0 || head_dim <= 0 || (rows > 0 && (!codes || !scales || !out))) return ORACLE_EINVAL;
+#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r)
         for (int32_t i = 0; i < head_dim; ++i)
             out[r * head_dim + i] = e4m3_value(codes[r * head_dim + i]) * (double)scales[r];

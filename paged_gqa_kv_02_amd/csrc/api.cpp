@@ -141,7 +141,56 @@ int gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache, co
     if (workspace_bytes < need) return PGQA_ENOSPC;
     pgqa::DecodeLaunch L{q, k_cache, v_cache, block_table, context_lens, out, workspace, max_blocks_per_seq,
                          batch, num_q_heads, num_kv_heads, head_dim, lg, num_blocks, max_context_len,
-                         num_splits, dtype == PGQA_BF16 ? 1 : 0, scale, window};
+                         num_splits, dtype == PGQA_BF16 ? 1 : 0, scale, window, nullptr, nullptr};
+    return hip_status(pgqa::launch_decode(L, (hipStream_t)stream));
+}
+
+int paged_kv_write_fp8(const void* k, const void* v, const int32_t* cu_seqlens, const int32_t* start_pos,
+                       const int32_t* block_table, int32_t max_blocks_per_seq, void* k_cache, void* v_cache,
+                       float* k_scale, float* v_scale, int32_t batch, int32_t total_tokens, int32_t num_blocks,
+                       int32_t block_size, int32_t num_kv_heads, int32_t head_dim, pgqa_dtype dtype, void* stream) {
+    int32_t lg = 0;
+    const int rc = check_copy_args(k, v, cu_seqlens, start_pos, block_table, max_blocks_per_seq, k_cache, v_cache,
+                                   batch, total_tokens, num_blocks, block_size, num_kv_heads, head_dim, dtype, &lg);
+    if (rc != PGQA_OK) return rc;
+    if (dtype != PGQA_BF16) return PGQA_ENOTSUP;
+    if (check_index_ptr(k_scale) || check_index_ptr(v_scale)) return PGQA_EINVAL;
+    if (batch == 0 || total_tokens == 0) return PGQA_OK;
+    pgqa::KvCopyLaunch L{k, v, k_cache, v_cache, cu_seqlens, start_pos, block_table, max_blocks_per_seq,
+                         batch, total_tokens, num_blocks, lg, num_kv_heads, head_dim, 2};
+    return hip_status(pgqa::launch_kv_write_fp8(L, k_scale, v_scale, (hipStream_t)stream));
+}
+
+int gqa_paged_decode_fp8(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                         const float* v_scale, const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+                         float scale, int32_t window, void* out, int32_t num_splits, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
+        max_context_len < 0 || num_splits < 0 || window < 0)
+        return PGQA_EINVAL;
+    if (num_q_heads % num_kv_heads) return PGQA_EINVAL;
+    int32_t lg = 0;
+    if (!pow2_log2(block_size, &lg) || block_size > 256) return PGQA_ENOTSUP;
+    if (!pgqa::decode_fp8_supported(head_dim, num_q_heads / num_kv_heads, block_size)) return PGQA_ENOTSUP;
+    if (batch > kMaxDecodeBatch) return PGQA_ENOTSUP;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PGQA_EINVAL;
+    if ((int64_t)batch * max_blocks_per_seq > INT32_MAX) return PGQA_EINVAL;
+    if ((int64_t)batch * num_kv_heads * (int64_t)max_context_len > INT32_MAX) return PGQA_EINVAL;
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff()) return PGQA_EINVAL;
+    if (check_elem_ptr(q) || check_elem_ptr(k_cache) || check_elem_ptr(v_cache) || check_elem_ptr(out))
+        return PGQA_EINVAL;
+    if (check_index_ptr(k_scale) || check_index_ptr(v_scale) || check_index_ptr(block_table) ||
+        check_index_ptr(context_lens))
+        return PGQA_EINVAL;
+    if (batch == 0) return PGQA_OK;
+    const size_t need = gqa_paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, num_splits);
+    if (!workspace || !aligned(workspace, 16)) return workspace_bytes < need ? PGQA_ENOSPC : PGQA_EINVAL;
+    if (workspace_bytes < need) return PGQA_ENOSPC;
+    pgqa::DecodeLaunch L{q, k_cache, v_cache, block_table, context_lens, out, workspace, max_blocks_per_seq,
+                         batch, num_q_heads, num_kv_heads, head_dim, lg, num_blocks, max_context_len,
+                         num_splits, 1, scale, window, k_scale, v_scale};
     return hip_status(pgqa::launch_decode(L, (hipStream_t)stream));
 }
 

@@ -22,7 +22,7 @@
 //    (Merging inside the split kernel by the last-arriving share needs
 //    device-scope release fences, which write back every XCD's L2 and cost far
 //    more than the second launch.)
-//  * Streaming: a tile is RPT 1 KB rows of K plus RPT rows of V, moved with
+//  * Streaming: a tile is DRPT 1 KB rows of K plus DRPT rows of V, moved with
 //    16-byte-per-lane global->LDS DMA (global_load_lds_dwordx4) into a ring of
 //    kStages tiles, so loads for later tiles are in flight while the current
 //    one is computed and no VGPRs are tied up by the prefetch.
@@ -44,6 +44,12 @@
 //    sequence (and, under a local-attention window, its first tile): scores
 //    outside [lo, ctx) become -inf and those V rows are zeroed, so NaN in
 //    unused slots (or in pages dropped before the window) cannot leak.
+//  * Low-precision pages (FP8 E4M3 codes, one fp32 scale per token and KV head
+//    row): the same kernel with KES = 1.  A tile moves the same 16 KB of codes
+//    (twice the tokens), plus the tile's row scales by 4-byte-per-lane DMA;
+//    each lane converts its 8 codes of a row to bf16 right after the LDS read
+//    (one instruction per pair, exact), so the scores and P.V are the bf16
+//    path's; the K scale multiplies a token's score and the V scale its weight.
 //  * Large groups (G >= 16) use G/8 waves per workgroup sharing one ring; each
 //    wave owns 8 query heads.
 #include "device_common.hpp"
@@ -82,6 +88,8 @@ struct DecodeArgs {
     int32_t num_splits;  // requested shares == gridDim.x of the split kernel
     float scale_log2;    // scale * log2(e): scores live in log2 units, weights use exp2
     int32_t window;      // > 0: only the newest `window` positions are attended to
+    const float* k_scale;   // FP8 pages: row scales [num_blocks, Hkv, block_size]
+    const float* v_scale;
 };
 
 constexpr int kStages = PGQA_DECODE_STAGES;   // ring depth (tiles) of the split kernel
@@ -89,16 +97,31 @@ constexpr int kRows = PGQA_DECODE_RPT;        // 1 KB wave rows per tile, for K 
 static_assert(kStages >= 2 && kStages <= 6, "ring depth");
 static_assert(kRows == 1 || kRows == 2 || kRows == 4 || kRows == 8 || kRows == 16, "rows per tile");
 
-template <int ES, int D>
+// Tile geometry.  ES = bytes of a q / compute element (4 fp32, 2 bf16); KES =
+// bytes of a cached K/V element (= ES, or 1 for FP8 pages, whose codes are
+// converted to bf16 right after the LDS read, so the compute side is the bf16
+// one).  A compute row is 64 lanes x 16 bytes of compute elements: TPR tokens,
+// LPT lanes per token.  K/V move in 1 KB DMA rows of TPRD tokens; an FP8 tile
+// has twice the compute rows of a bf16 one so that it moves the same bytes.
+template <int ES, int D, int KES = ES>
 struct Geo {
-    static constexpr int EPL = 16 / ES;          // elements per lane per 16-byte load
-    static constexpr int LPT = D / EPL;          // lanes per token row
-    static constexpr int TPR = kWave / LPT;      // tokens per 1 KB wave row
-    static constexpr int RPT = kRows;            // wave rows per tile
-    static constexpr int TT = RPT * TPR;         // tokens per tile
-    static constexpr int ROWB = 1024;
-    static constexpr int TILEB = 2 * RPT * ROWB; // bytes of K + V per tile
+    static constexpr int EPL = 16 / ES;            // compute elements per lane
+    static constexpr int LPT = D / EPL;            // lanes per token
+    static constexpr int TPR = kWave / LPT;        // tokens per compute row
+    static constexpr int RPT = kRows * ES / KES;   // compute rows per tile
+    static constexpr int TT = RPT * TPR;           // tokens per tile
+    static constexpr int ROWB = 1024;              // bytes per DMA row
+    static constexpr int CROWB = TPR * D * KES;    // LDS bytes of one compute row (per pool)
+    static constexpr int LB = CROWB / kWave;       // LDS bytes a lane reads per compute row
+    static constexpr int TPRD = ROWB / (D * KES);  // tokens per DMA row
+    static constexpr int LPTD = kWave / TPRD;      // lanes per token in a DMA row
+    static constexpr int DRPT = RPT * CROWB / ROWB;   // DMA rows per tile, per pool
+    static constexpr int KVB = DRPT * ROWB;        // bytes of K (or V) per tile
+    static constexpr int SCL = KES == ES ? 0 : TT / kWave;   // 4-byte-per-lane scale loads per pool
+    static constexpr int NL = 2 * DRPT + 2 * SCL;  // loads per tile
+    static constexpr int TILEB = 2 * KVB + 2 * SCL * kWave * 4;
     static_assert(LPT >= 2 && LPT <= 32 && TPR * LPT == kWave, "unsupported head_dim / dtype");
+    static_assert(DRPT * ROWB == RPT * CROWB && TPRD * LPTD == kWave, "unsupported head_dim / KV dtype");
 };
 
 constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
@@ -266,66 +289,98 @@ struct PageWin {
         if (page - base >= kWave) load(page, lane);
         return __builtin_amdgcn_readlane(reg, page - base);
     }
+    // Make pages first .. last (last - first < 64) readable by every lane.
+    __device__ __forceinline__ void cover(int first, int last, int lane) {
+        if (first < base || last - base >= kWave) load(first, lane);
+    }
 };
 
-// Issue the global->LDS loads of one tile (token rows of K, then of V) into
-// ring slot `slot`.  Wave `wave` issues the loads li with li % W == wave (the
-// wait counts rely on the per-wave count being fixed).
-template <int ES, int D, int W>
+// Issue the global->LDS loads of one tile (DMA rows of K, then of V, then for
+// FP8 pages the row scales of K and of V) into ring slot `slot`.  Wave `wave`
+// issues the loads li with li % W == wave (the wait counts rely on the per-wave
+// count being fixed).
+template <int ES, int D, int W, int KES>
 __device__ __forceinline__ void issue_tile(const DecodeArgs& a, PGQA_LDS char* ring, int slot, int tile,
                                            int h, int ctx, PageWin& win, int wave, int lane) {
-    using Gm = Geo<ES, D>;
-    const int tg = lane / Gm::LPT;
+    using Gm = Geo<ES, D, KES>;
+    constexpr int DRPT = Gm::DRPT, TPRD = Gm::TPRD;
+    const int tg = lane / Gm::LPTD;
     const int bs_mask = (1 << a.bs_log2) - 1;
     const int tile_tok = tile * Gm::TT;
     PGQA_LDS char* dst = ring + slot * Gm::TILEB;
-    if (Gm::TPR <= (1 << a.bs_log2)) {
-        // Every 1 KB row (TPR tokens) lies in one page, so row r is one
+    if constexpr (Gm::SCL > 0) {
+        // Every block id the scale loads need must sit in the window (at most
+        // TT / block_size + 1 pages; FP8 pages are at least 16 tokens).
+        win.cover(tile_tok >> a.bs_log2, min(tile_tok + Gm::TT - 1, ctx - 1) >> a.bs_log2, lane);
+    }
+    if (TPRD <= (1 << a.bs_log2)) {
+        // Every 1 KB row (TPRD tokens) lies in one page, so row r is one
         // contiguous run of that page.  Row starts are clamped to the last row
-        // holding a context token (TPR-aligned): rows past the context re-read
+        // holding a context token (TPRD-aligned): rows past the context re-read
         // that row (in bounds) and are masked in compute.
-        const int last_row_tok = (ctx - 1) & ~(Gm::TPR - 1);
-        int64_t run[Gm::RPT];
+        const int last_row_tok = (ctx - 1) & ~(TPRD - 1);
+        int64_t run[DRPT];
         if (Gm::TT <= (1 << a.bs_log2)) {
             // The whole tile is in one page (it starts before the context end).
             const int bid = win.get(tile_tok >> a.bs_log2, lane);
-            const int64_t base = ((((int64_t)bid * a.num_kv_heads + h) << a.bs_log2) + (tile_tok & bs_mask)) * (D * ES);
+            const int64_t base = ((((int64_t)bid * a.num_kv_heads + h) << a.bs_log2) + (tile_tok & bs_mask)) * (D * KES);
 #pragma unroll
-            for (int r = 0; r < Gm::RPT; ++r) run[r] = base + r * Gm::ROWB + lane * 16;
+            for (int r = 0; r < DRPT; ++r) run[r] = base + r * Gm::ROWB + lane * 16;
         } else {
 #pragma unroll
-            for (int r = 0; r < Gm::RPT; ++r) {
-                const int tok = min(tile_tok + r * Gm::TPR, last_row_tok);
+            for (int r = 0; r < DRPT; ++r) {
+                const int tok = min(tile_tok + r * TPRD, last_row_tok);
                 const int bid = win.get(tok >> a.bs_log2, lane);
-                run[r] = ((((int64_t)bid * a.num_kv_heads + h) << a.bs_log2) + (tok & bs_mask)) * (D * ES) + lane * 16;
+                run[r] = ((((int64_t)bid * a.num_kv_heads + h) << a.bs_log2) + (tok & bs_mask)) * (D * KES) + lane * 16;
             }
         }
 #pragma unroll
-        for (int li = 0; li < 2 * Gm::RPT; ++li) {
+        for (int li = 0; li < 2 * DRPT; ++li) {
             if (li % W != wave) continue;
-            const int r = li % Gm::RPT;
-            const bool isv = li >= Gm::RPT;
+            const int r = li % DRPT;
+            const bool isv = li >= DRPT;
             load_lds_16((isv ? a.v_cache : a.k_cache) + run[r], dst + li * Gm::ROWB);
         }
     } else {
         // Pages smaller than a row: each lane looks up its own token's page
         // (positions clamped to the context so every table read is in range).
-        const int c = lane % Gm::LPT;
-        int blk[Gm::RPT];
-        int tok[Gm::RPT];
+        const int c = lane % Gm::LPTD;
+        int blk[DRPT];
+        int tok[DRPT];
 #pragma unroll
-        for (int r = 0; r < Gm::RPT; ++r) {
-            tok[r] = min(tile_tok + r * Gm::TPR + tg, ctx - 1);
+        for (int r = 0; r < DRPT; ++r) {
+            tok[r] = min(tile_tok + r * TPRD + tg, ctx - 1);
             blk[r] = clampi(win.bt_row[tok[r] >> a.bs_log2], 0, a.num_blocks - 1);
         }
 #pragma unroll
-        for (int li = 0; li < 2 * Gm::RPT; ++li) {
+        for (int li = 0; li < 2 * DRPT; ++li) {
             if (li % W != wave) continue;
-            const int r = li % Gm::RPT;
-            const bool isv = li >= Gm::RPT;
+            const int r = li % DRPT;
+            const bool isv = li >= DRPT;
             const int64_t prow = (((int64_t)blk[r] * a.num_kv_heads + h) << a.bs_log2) + (tok[r] & bs_mask);
-            const char* src = (isv ? a.v_cache : a.k_cache) + prow * (D * ES) + c * 16;
+            const char* src = (isv ? a.v_cache : a.k_cache) + prow * (D * KES) + c * 16;
             load_lds_16(src, dst + li * Gm::ROWB);
+        }
+    }
+    if constexpr (Gm::SCL > 0) {
+        // Row scales, 4 bytes per lane: lane l of load j fetches the scale of the
+        // token that compute lane group g = p / RPT meets in compute row
+        // r = p % RPT (p = 64 j + l), so each group's RPT scales are contiguous
+        // in LDS.  Tokens past the context re-read the last one (masked).
+        constexpr int RPT = Gm::RPT;
+#pragma unroll
+        for (int j = 0; j < Gm::SCL; ++j) {
+            const int p = j * kWave + lane;
+            const int tok = min(tile_tok + (p % RPT) * Gm::TPR + p / RPT, ctx - 1);
+            const int blk = __builtin_amdgcn_ds_bpermute(((tok >> a.bs_log2) - win.base) << 2, win.reg);
+            const int64_t srow = (((int64_t)blk * a.num_kv_heads + h) << a.bs_log2) + (tok & bs_mask);
+#pragma unroll
+            for (int pool = 0; pool < 2; ++pool) {
+                const int li = 2 * DRPT + pool * Gm::SCL + j;
+                if (li % W != wave) continue;
+                __builtin_amdgcn_global_load_lds((pool ? a.v_scale : a.k_scale) + srow,
+                                                 dst + 2 * Gm::KVB + (pool * Gm::SCL + j) * kWave * 4, 4, 0, 0);
+            }
         }
     }
 }
@@ -355,25 +410,56 @@ __device__ __forceinline__ void bcast_heads(const float* vals, float* out, int l
     }
 }
 
+// 8 FP8 E4M3 codes -> 8 bf16 values (exact: every E4M3 value is a bf16 value),
+// in the order of a bf16 compute slice.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 w) {
+    return u32x4{__builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false)),
+                 __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true)),
+                 __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false)),
+                 __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true))};
+}
+
+// This lane's slice of compute row r of a K or V tile (bf16 / fp32 as stored,
+// or FP8 codes converted to bf16).
+template <int ES, int D, int KES>
+__device__ __forceinline__ u32x4 kv_slice(const PGQA_LDS char* base, int r) {
+    using Gm = Geo<ES, D, KES>;
+    if constexpr (KES == ES) return lds_read_16(base + r * Gm::CROWB);
+    else return fp8x8_to_bf16(lds_read_8(base + r * Gm::CROWB));
+}
+
 // One tile: scores, online-softmax update and P.V for this wave's GW heads.
 // FULL: every token of the tile is inside [lo, ctx) (no masking needed).
-template <bool FULL, int ES, int D, int GW>
-__device__ __forceinline__ void tile_compute(const PGQA_LDS char* kb, const PGQA_LDS char* vb, const u32x4* qv,
-                                             float* m, float* l, float (*o)[16 / ES], int tok0, int ctx, int lo,
-                                             float c, int lane) {
-    using Gm = Geo<ES, D>;
+// tb is the tile's ring slot.  FP8 pages: the row scale of K multiplies the
+// token's score, that of V its weight in P.V (the softmax sum keeps the plain
+// weight), so the codes are used as they are.
+template <bool FULL, int ES, int D, int GW, int KES>
+__device__ __forceinline__ void tile_compute(const PGQA_LDS char* tb, const u32x4* qv, float* m, float* l,
+                                             float (*o)[16 / ES], int tok0, int ctx, int lo, float c, int lane) {
+    using Gm = Geo<ES, D, KES>;
     using S = Scatter<Gm::LPT, GW>;
     constexpr int EPL = Gm::EPL, RPT = Gm::RPT, TPR = Gm::TPR, VPL = S::VPL;
+    constexpr bool Q8 = KES != ES;
+    const PGQA_LDS char* kb = tb + lane * Gm::LB;
+    const PGQA_LDS char* vb = kb + Gm::KVB;
+    // Row scales of this lane's tokens (FP8): group g's RPT scales are contiguous.
+    const PGQA_LDS float* ksc = (const PGQA_LDS float*)(tb + 2 * Gm::KVB) + (lane / Gm::LPT) * RPT;
+    const PGQA_LDS float* vsc = ksc + Gm::SCL * kWave;
 
     float s[RPT][VPL];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-        const u32x4 kx = lds_read_16(kb + r * Gm::ROWB);
+        const u32x4 kx = kv_slice<ES, D, KES>(kb, r);
         float v[GW];
 #pragma unroll
         for (int g = 0; g < GW; ++g) v[g] = slice_dot<ES>(qv[g], kx);
         scatter_steps<Gm::LPT / 2, GW>(v, lane);
         const bool valid = FULL || (tok0 + r * TPR < ctx && tok0 + r * TPR >= lo);
+        if constexpr (Q8) {
+            const float ks = ksc[r];
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) v[k] *= ks;
+        }
 #pragma unroll
         for (int k = 0; k < VPL; ++k) s[r][k] = valid ? v[k] : -INFINITY;
     }
@@ -413,21 +499,29 @@ __device__ __forceinline__ void tile_compute(const PGQA_LDS char* kb, const PGQA
         static_assert(RPT % 2 == 0, "bf16 P.V pairs token rows");
 #pragma unroll
         for (int r = 0; r < RPT; r += 2) {
+            const bool ok0 = FULL || (tok0 + r * TPR < ctx && tok0 + r * TPR >= lo);
+            const bool ok1 = FULL || (tok0 + (r + 1) * TPR < ctx && tok0 + (r + 1) * TPR >= lo);
+            float vs0 = 1.0f, vs1 = 1.0f;
+            if constexpr (Q8) {
+                vs0 = ok0 ? vsc[r] : 0.0f;
+                vs1 = ok1 ? vsc[r + 1] : 0.0f;
+            }
             u32 pk[VPL];
 #pragma unroll
             for (int k = 0; k < VPL; ++k) {
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r][k], c, -m[k]));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1][k], c, -m[k]));
                 l[k] += p0 + p1;
-                pk[k] = pack_bf16x2_rne_hw(p0, p1);
+                if constexpr (Q8) pk[k] = pack_bf16x2_rne_hw(p0 * vs0, p1 * vs1);
+                else pk[k] = pack_bf16x2_rne_hw(p0, p1);
             }
             u32 pg[GW];
             bcast_heads_u32<Gm::LPT, GW>(pk, pg, lane);
-            u32x4 v0 = lds_read_16(vb + r * Gm::ROWB);
-            u32x4 v1 = lds_read_16(vb + (r + 1) * Gm::ROWB);
+            u32x4 v0 = kv_slice<ES, D, KES>(vb, r);
+            u32x4 v1 = kv_slice<ES, D, KES>(vb, r + 1);
             if (!FULL) {
-                if (tok0 + r * TPR >= ctx || tok0 + r * TPR < lo) v0 = u32x4{0, 0, 0, 0};
-                if (tok0 + (r + 1) * TPR >= ctx || tok0 + (r + 1) * TPR < lo) v1 = u32x4{0, 0, 0, 0};
+                if (!ok0) v0 = u32x4{0, 0, 0, 0};
+                if (!ok1) v1 = u32x4{0, 0, 0, 0};
             }
             const u32 w0[4] = {v0.x, v0.y, v0.z, v0.w};
             const u32 w1[4] = {v1.x, v1.y, v1.z, v1.w};
@@ -453,7 +547,7 @@ __device__ __forceinline__ void tile_compute(const PGQA_LDS char* kb, const PGQA
             }
             float pg[GW];
             bcast_heads<Gm::LPT, GW>(p, pg, lane);
-            const u32x4 vx = lds_read_16(vb + r * Gm::ROWB);
+            const u32x4 vx = kv_slice<ES, D, KES>(vb, r);
             float vf[EPL];
             unpack16<ES>(vx, vf);
             if (!FULL && (tok0 + r * TPR >= ctx || tok0 + r * TPR < lo)) {
@@ -474,14 +568,14 @@ __device__ __forceinline__ int64_t share_of(int64_t X, int64_t total, int64_t nw
     return ((X + 1) * nw - 1) / total;
 }
 
-template <int ES, int D, int GW, int W>
+template <int ES, int D, int GW, int W, int KES>
 __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
-    using Gm = Geo<ES, D>;
+    using Gm = Geo<ES, D, KES>;
     using S = Scatter<Gm::LPT, GW>;
-    constexpr int EPL = Gm::EPL, LPT = Gm::LPT, RPT = Gm::RPT, TT = Gm::TT, VPL = S::VPL;
+    constexpr int EPL = Gm::EPL, LPT = Gm::LPT, TT = Gm::TT, VPL = S::VPL;
     constexpr int G = GW * W;
-    // Loads per tile: 2*RPT rows, wave w issues rows li with li % W == w.
-    constexpr int LPW_MAX = (2 * RPT + W - 1) / W;
+    // Loads per tile: NL, wave w issues loads li with li % W == w.
+    constexpr int LPW_MAX = (Gm::NL + W - 1) / W;
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
     PGQA_LDS char* ring = (PGQA_LDS char*)smem;
@@ -547,7 +641,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     const int c = lane % LPT;
     const int tg = lane / LPT;
     const float cs = a.scale_log2;
-    const int lpw = wave < 2 * RPT ? (2 * RPT - wave + W - 1) / W : 0;   // this wave's loads per tile
+    const int lpw = wave < Gm::NL ? (Gm::NL - wave + W - 1) / W : 0;   // this wave's loads per tile
 
     while (X < X1) {
         const int n = (int)min((int64_t)(tiles_b - t0), X1 - X);   // tiles in this piece
@@ -560,7 +654,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         win.bt_row = a.block_table + (int64_t)b * a.max_blocks_per_seq;
         win.last_page = (ctx - 1) >> a.bs_log2;
         win.num_blocks = a.num_blocks;
-        if (Gm::TPR <= (1 << a.bs_log2)) win.load((tf * TT) >> a.bs_log2, lane);
+        if (Gm::TPRD <= (1 << a.bs_log2)) win.load((tf * TT) >> a.bs_log2, lane);
 
         // This wave's query slices: GW heads x 16 bytes.
         u32x4 qv[GW];
@@ -583,7 +677,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         // Prologue: fill the first kStages-1 ring slots.
 #pragma unroll
         for (int i = 0; i < kStages - 1; ++i)
-            if (i < n) issue_tile<ES, D, W>(a, ring, i, tf + i, h, ctx, win, wave, lane);
+            if (i < n) issue_tile<ES, D, W, KES>(a, ring, i, tf + i, h, ctx, win, wave, lane);
 
         // Tiles of the piece: every tile but a segment's first (under a window)
         // and last is full, so the loop body is one path and those two are
@@ -594,30 +688,28 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
             wait_vmcnt_dyn<(kStages - 2) * LPW_MAX>(lpw * min(kStages - 2, n - 1 - it));
             if constexpr (W > 1) __syncthreads();
             if (it + kStages - 1 < n)
-                issue_tile<ES, D, W>(a, ring, (it + kStages - 1) % kStages, tf + it + kStages - 1, h, ctx,
-                                     win, wave, lane);
-            return ring + slot * Gm::TILEB + lane * 16;
+                issue_tile<ES, D, W, KES>(a, ring, (it + kStages - 1) % kStages, tf + it + kStages - 1, h, ctx,
+                                          win, wave, lane);
+            return ring + slot * Gm::TILEB;
         };
         int it0 = 0;
         if (n > 1 && tf * TT < lo) {
             const PGQA_LDS char* kb = step(0);
-            tile_compute<false, ES, D, GW>(kb, kb + RPT * Gm::ROWB, qv, m, l, o, tf * TT + tg, ctx, lo, cs, lane);
+            tile_compute<false, ES, D, GW, KES>(kb, qv, m, l, o, tf * TT + tg, ctx, lo, cs, lane);
             it0 = 1;
         }
         for (int it = it0; it < n - 1; ++it) {
             const PGQA_LDS char* kb = step(it);
-            tile_compute<true, ES, D, GW>(kb, kb + RPT * Gm::ROWB, qv, m, l, o, (tf + it) * TT + tg, ctx, lo, cs,
-                                          lane);
+            tile_compute<true, ES, D, GW, KES>(kb, qv, m, l, o, (tf + it) * TT + tg, ctx, lo, cs, lane);
         }
         {
             const int it = n - 1;
             const PGQA_LDS char* kb = step(it);
             const int tile = tf + it;
             if (tile * TT >= lo && (tile + 1) * TT <= ctx)
-                tile_compute<true, ES, D, GW>(kb, kb + RPT * Gm::ROWB, qv, m, l, o, tile * TT + tg, ctx, lo, cs, lane);
+                tile_compute<true, ES, D, GW, KES>(kb, qv, m, l, o, tile * TT + tg, ctx, lo, cs, lane);
             else
-                tile_compute<false, ES, D, GW>(kb, kb + RPT * Gm::ROWB, qv, m, l, o, tile * TT + tg, ctx, lo, cs,
-                                               lane);
+                tile_compute<false, ES, D, GW, KES>(kb, qv, m, l, o, tile * TT + tg, ctx, lo, cs, lane);
         }
 
         // ---- per-head (m, l) to every lane, then merge the TPR token groups ----
@@ -765,29 +857,29 @@ struct Entry {
     int tt;
 };
 
-template <int ES, int D, int G>
+template <int ES, int D, int G, int KES>
 Entry make_entry() {
     constexpr int GW = G <= 8 ? G : 8;
     constexpr int W = G / GW;
     Entry e;
-    e.split = decode_split_kernel<ES, D, GW, W>;
+    e.split = decode_split_kernel<ES, D, GW, W, KES>;
     e.merge = decode_merge_kernel<ES, D, G>;
     e.waves = W;
-    e.tile_bytes = Geo<ES, D>::TILEB;
-    e.tt = Geo<ES, D>::TT;
+    e.tile_bytes = Geo<ES, D, KES>::TILEB;
+    e.tt = Geo<ES, D, KES>::TT;
     return e;
 }
 
-template <int ES, int D>
+template <int ES, int D, int KES = ES>
 bool pick_g(int group, Entry* e) {
     switch (group) {
-        case 1: *e = make_entry<ES, D, 1>(); return true;
-        case 2: *e = make_entry<ES, D, 2>(); return true;
-        case 4: *e = make_entry<ES, D, 4>(); return true;
-        case 8: *e = make_entry<ES, D, 8>(); return true;
-        case 16: *e = make_entry<ES, D, 16>(); return true;
-        case 32: *e = make_entry<ES, D, 32>(); return true;
-        case 64: *e = make_entry<ES, D, 64>(); return true;
+        case 1: *e = make_entry<ES, D, 1, KES>(); return true;
+        case 2: *e = make_entry<ES, D, 2, KES>(); return true;
+        case 4: *e = make_entry<ES, D, 4, KES>(); return true;
+        case 8: *e = make_entry<ES, D, 8, KES>(); return true;
+        case 16: *e = make_entry<ES, D, 16, KES>(); return true;
+        case 32: *e = make_entry<ES, D, 32, KES>(); return true;
+        case 64: *e = make_entry<ES, D, 64, KES>(); return true;
         default: return false;
     }
 }
@@ -799,6 +891,15 @@ bool pick_d(int head_dim, int group, Entry* e) {
         case 32: return pick_g<ES, 32>(group, e);
         case 64: return pick_g<ES, 64>(group, e);
         case 128: return pick_g<ES, 128>(group, e);
+        default: return false;
+    }
+}
+
+// FP8 pages with bf16 queries: head_dim 64 or 128.
+bool pick_fp8(int head_dim, int group, Entry* e) {
+    switch (head_dim) {
+        case 64: return pick_g<2, 64, 1>(group, e);
+        case 128: return pick_g<2, 128, 1>(group, e);
         default: return false;
     }
 }
@@ -846,11 +947,16 @@ bool decode_supported(int32_t elem_bytes, int32_t head_dim, int32_t group) {
     return pick(elem_bytes, head_dim, group, &e);
 }
 
+bool decode_fp8_supported(int32_t head_dim, int32_t group, int32_t block_size) {
+    Entry e;
+    return pick_fp8(head_dim, group, &e) && block_size >= 16 && block_size <= 256;
+}
+
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     const int es = L.is_bf16 ? 2 : 4;
     const int group = L.num_q_heads / L.num_kv_heads;
     Entry e;
-    if (!pick(es, L.head_dim, group, &e)) return hipErrorInvalidValue;
+    if (L.k_scale ? !pick_fp8(L.head_dim, group, &e) : !pick(es, L.head_dim, group, &e)) return hipErrorInvalidValue;
     if (L.batch == 0) return hipSuccess;
 
     DecodeArgs a;
@@ -869,6 +975,8 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     a.ctx_cap = L.max_context_len;
     a.scale_log2 = (float)((double)L.scale * 1.4426950408889634);
     a.window = L.window;
+    a.k_scale = (const float*)L.k_scale;
+    a.v_scale = (const float*)L.v_scale;
 
     const int threads = 64 * e.waves;
     // ring + tile prefix sums [batch + 1]

@@ -142,6 +142,10 @@ __device__ __forceinline__ u32x4 lds_read_16(const PGQA_LDS void* p) {
     return *(const PGQA_LDS u32x4*)p;
 }
 
+__device__ __forceinline__ u32x2 lds_read_8(const PGQA_LDS void* p) {
+    return *(const PGQA_LDS u32x2*)p;
+}
+
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 }  // namespace pgqa

@@ -29,6 +29,10 @@ struct KvCopyLaunch {
 // to_pages = true: packed -> pages; false: pages -> packed.
 hipError_t launch_kv_copy(const KvCopyLaunch& L, bool to_pages, hipStream_t stream);
 
+// Quantising write of bf16 rows into FP8 E4M3 code pools (dst_k / dst_v) and fp32
+// row-scale pools [num_blocks, Hkv, block_size]; head_dim in {16, 32, 64, 128}.
+hipError_t launch_kv_write_fp8(const KvCopyLaunch& L, void* k_scale, void* v_scale, hipStream_t stream);
+
 struct BlockCopyLaunch {
     void* k_cache;
     void* v_cache;
@@ -64,6 +68,8 @@ struct DecodeLaunch {
     int32_t is_bf16;
     float scale;
     int32_t window;       // 0: none; > 0: the newest `window` positions only
+    const void* k_scale;  // non-null: FP8 E4M3 pages with fp32 row scales (bf16 q / out)
+    const void* v_scale;
 };
 
 // Largest number of splits (workgroups of the split-KV kernel) the library picks itself.
@@ -74,6 +80,9 @@ int32_t decode_tile_tokens(int32_t elem_bytes, int32_t head_dim);
 
 // Is there a decode kernel for this (dtype, head_dim, group size)?
 bool decode_supported(int32_t elem_bytes, int32_t head_dim, int32_t group);
+
+// ... for FP8 pages with bf16 queries?
+bool decode_fp8_supported(int32_t head_dim, int32_t group, int32_t block_size);
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
 

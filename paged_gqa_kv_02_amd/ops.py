@@ -168,3 +168,71 @@ def paged_kv_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src_block
                                     dst_blocks.data_ptr(), src_blocks.numel(), nb, bs, hkv, d, _dtype(k_cache),
                                     _stream())
     check("paged_kv_copy_blocks", st)
+
+
+def fp8_pools(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, device=None):
+    """Empty FP8 page pools: (k_codes, v_codes) uint8 [nb, Hkv, bs, d], (k_scale, v_scale) fp32 [nb, Hkv, bs]."""
+    shape = (num_blocks, num_kv_heads, block_size, head_dim)
+    dev = device or "cuda"
+    return (torch.empty(shape, dtype=torch.uint8, device=dev), torch.empty(shape, dtype=torch.uint8, device=dev),
+            torch.empty(shape[:3], dtype=torch.float32, device=dev),
+            torch.empty(shape[:3], dtype=torch.float32, device=dev))
+
+
+def _u8(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if t.dtype != torch.uint8:
+            raise TypeError(f"FP8 code pools are uint8, got {t.dtype}")
+
+
+def _f32(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if t.dtype != torch.float32:
+            raise TypeError(f"scale pools are float32, got {t.dtype}")
+
+
+def paged_kv_write_fp8(k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, start_pos: torch.Tensor,
+                       block_table: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       k_scale: torch.Tensor, v_scale: torch.Tensor) -> None:
+    """Quantise packed bf16 k, v [T, Hkv, d] into FP8 code pools and fp32 row-scale pools in place."""
+    _dev(k, v, cu_seqlens, start_pos, block_table, k_cache, v_cache, k_scale, v_scale)
+    _i32(cu_seqlens, start_pos, block_table)
+    _u8(k_cache, v_cache)
+    _f32(k_scale, v_scale)
+    nb, hkv, bs, d = k_cache.shape
+    st = lib().paged_kv_write_fp8(k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), start_pos.data_ptr(),
+                                  block_table.data_ptr(), block_table.shape[1], k_cache.data_ptr(), v_cache.data_ptr(),
+                                  k_scale.data_ptr(), v_scale.data_ptr(), cu_seqlens.numel() - 1, k.shape[0], nb, bs,
+                                  hkv, d, _dtype(k), _stream())
+    check("paged_kv_write_fp8", st)
+
+
+def gqa_paged_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+                         v_scale: torch.Tensor, block_table: torch.Tensor, context_lens: torch.Tensor,
+                         max_context_len: int, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                         num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
+                         window: int = 0) -> torch.Tensor:
+    """Decode attention over FP8 pages: bf16 q [B, Hq, d] -> bf16 out [B, Hq, d]."""
+    B, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    if d2 != d:
+        raise ValueError("head_dim mismatch")
+    if q.dtype != torch.bfloat16:
+        raise TypeError("queries over FP8 pages are bfloat16")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = decode_workspace(B, hq, hkv, d, num_splits, q.device)
+    _dev(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, out, workspace)
+    _i32(block_table, context_lens)
+    _u8(k_cache, v_cache)
+    _f32(k_scale, v_scale)
+    st = lib().gqa_paged_decode_fp8(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), k_scale.data_ptr(),
+                                    v_scale.data_ptr(), block_table.data_ptr(), block_table.shape[1],
+                                    context_lens.data_ptr(), B, hq, hkv, d, bs, nb, int(max_context_len),
+                                    float(scale), int(window), out.data_ptr(), int(num_splits), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream())
+    check("gqa_paged_decode_fp8", st)
+    return out

@@ -174,3 +174,40 @@ def test_copy_blocks_validation(lib):
     assert _copy(lib, bs=24) == ENOTSUP
     assert _copy(lib, dt=9) == ENOTSUP
     assert _copy(lib, n=0) == 0
+
+
+def _decode8(lib, **kw):
+    a = dict(q=P[0], kc=P[1], vc=P[2], ks=P[7], vs=P[8], bt=P[3], maxb=4, cl=P[4], batch=2, hq=8, hkv=2, d=128,
+             bs=16, nb=8, maxctx=64, scale=0.125, win=0, out=P[5], splits=0, ws=P[6], wsb=1 << 30)
+    a.update(kw)
+    return lib.gqa_paged_decode_fp8(a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["bt"], a["maxb"], a["cl"],
+                                    a["batch"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["maxctx"], a["scale"],
+                                    a["win"], a["out"], a["splits"], a["ws"], a["wsb"], None)
+
+
+def test_fp8_decode_validation(lib):
+    assert _decode8(lib, hq=6, hkv=4) == EINVAL
+    assert _decode8(lib, ks=None) == EINVAL
+    assert _decode8(lib, vs=P[8] + 2) == EINVAL
+    assert _decode8(lib, maxctx=65) == EINVAL
+    assert _decode8(lib, win=-1) == EINVAL
+    assert _decode8(lib, d=32) == ENOTSUP              # FP8 pages: head_dim 64 or 128
+    assert _decode8(lib, bs=8, maxctx=32) == ENOTSUP   # FP8 pages: block_size >= 16
+    assert _decode8(lib, hq=24, hkv=2) == ENOTSUP
+    assert _decode8(lib, wsb=16) == ENOSPC
+    assert _decode8(lib, batch=0) == 0
+
+
+def test_fp8_write_validation(lib):
+    def w(**kw):
+        a = dict(k=P[0], v=P[1], cu=P[2], sp=P[3], bt=P[4], maxb=4, kc=P[5], vc=P[6], ks=P[7], vs=P[8], batch=2,
+                 T=10, nb=8, bs=16, hkv=2, d=128, dt=BF16)
+        a.update(kw)
+        return lib.paged_kv_write_fp8(a["k"], a["v"], a["cu"], a["sp"], a["bt"], a["maxb"], a["kc"], a["vc"],
+                                      a["ks"], a["vs"], a["batch"], a["T"], a["nb"], a["bs"], a["hkv"], a["d"],
+                                      a["dt"], None)
+    assert w(ks=None) == EINVAL
+    assert w(k=P[0] + 4) == EINVAL
+    assert w(dt=F32) == ENOTSUP
+    assert w(d=96) == ENOTSUP
+    assert w(batch=0) == 0

@@ -53,8 +53,8 @@ MUTANTS = [
      "if (window > 0 && i - window > first) first = i - window;"),
     ("extend_window_ignored", "const int64_t lo = (window > 0 && n > window) ? n - window : 0;   /* newest",
      "const int64_t lo = 0;   /* newest"),
-    ("fp8_ties_to_odd", "if (dc < db || (dc == db && (c & 1) == 0)) best = c;",
-     "if (dc < db || (dc == db && (c & 1) == 1)) best = c;"),
+    ("fp8_ties_to_odd", "if (du < dl || (du == dl && ((lo + 1) & 1) == 0)) best = lo + 1;",
+     "if (du < dl || (du == dl && ((lo + 1) & 1) == 1)) best = lo + 1;"),
     ("fp8_scale_over_127", "const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;",
      "const float sc = amax > 0.0f ? amax / 127.0f : 1.0f;"),
     ("fp8_subnormal_exponent", "ldexp((double)m / 8.0, -6)", "ldexp((double)m / 8.0, -7)"),
