@@ -19,7 +19,8 @@ cache (chunked prefill of 512-token chunks on cached prefixes, and checking 4
 draft tokens per sequence), each with the roofline its arithmetic intensity
 puts it under; decode of 64 samples over the pages of one shared prompt
 (prefix sharing with copy-on-write), against the same samples unshared;
-local-attention decode (4096-token window) on the long-context workload; and
+local-attention decode (4096-token window) on the long-context workload;
+decode of the headline batch over FP8 pages (quantising write + FP8 decode); and
 the fp64 CPU oracle on the same decode batch as a reported baseline.
 """
 
@@ -48,6 +49,7 @@ def _args():
     ap.add_argument("--no-extend", action="store_true", help="skip the multi-token (extend) line items")
     ap.add_argument("--no-shared", action="store_true", help="skip the shared-prefix decode line item")
     ap.add_argument("--no-window", action="store_true", help="skip the sliding-window decode line item")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-page decode line item")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle timing budget")
     ap.add_argument("--decode-workload", default="llama3_8b_decode",
                     choices=["llama3_8b_decode", "long_ctx_decode", "mqa_decode", "tiny_f32"],
@@ -463,6 +465,64 @@ def window_leg(args, torch, pg, W, T, window=4096):
     }
 
 
+def fp8_leg(args, torch, pg, W, T):
+    """Decode of the headline workload over FP8 pages (codes + one fp32 scale per
+    token and KV head), written by the quantising paged write.  Step = quantising
+    write of the 64 newest tokens + FP8 decode; the decode call is event-timed.
+    Bytes = codes + row scales actually stored (264 B per token and KV head for
+    d 128, against 512 B in bf16); tokens/s is compared with the bf16 decode."""
+    case = W.make_workload(args.decode_workload)
+    B, hq, hkv, d, bs = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size
+    table, ctx = T.to_dev(case.block_table), T.to_dev(case.context_lens)
+    pools = []
+    for _ in range(COPIES):
+        kc, vc, ks, vs = pg.fp8_pools(case.num_blocks, hkv, bs, d)
+        pg.paged_kv_write_fp8(T.to_dev(case.k), T.to_dev(case.v), T.to_dev(case.cu_ctx), T.to_dev(case.start_pos),
+                              table, kc, vc, ks, vs)
+        pools.append((kc, vc, ks, vs))
+    last = case.cu_ctx[1:] - 1
+    k_new, v_new = T.to_dev(np.ascontiguousarray(case.k[last])), T.to_dev(np.ascontiguousarray(case.v[last]))
+    cu_new = T.to_dev(np.arange(B + 1, dtype=np.int32))
+    sp_new = T.to_dev((case.context_lens - 1).astype(np.int32))
+    q = T.to_dev(case.q)
+    out = torch.empty_like(q)
+    ws = pg.decode_workspace(B, hq, hkv, d, 0, q.device)
+    scale, maxctx = float(case.scale), case.max_context_len
+
+    def step(i, ev=None):
+        kc, vc, ks, vs = pools[i % COPIES]
+        pg.paged_kv_write_fp8(k_new, v_new, cu_new, sp_new, table, kc, vc, ks, vs)
+        if ev is not None:
+            ev[0].record()
+        pg.gqa_paged_decode_fp8(q, kc, vc, ks, vs, table, ctx, maxctx, scale=scale, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs]) * 1e3)
+    tokens = int(case.context_lens.astype(np.int64).sum())
+    stored = tokens * hkv * 2 * (d + 4)
+    gbs = stored / (us * 1e-6) / 1e9
+    return {
+        "workload": args.decode_workload, "kv_format": "fp8 e4m3 + fp32 row scale", "bytes_per_call": stored,
+        "bf16_equivalent_bytes": case.kv_bytes(), "decode_us_mean": us, "ms_per_step": ms_step, "kv_gbs": gbs,
+        "bf16_equivalent_gbs": case.kv_bytes() / (us * 1e-6) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None},
+    }
+
+
 def cpu_baseline(args, case, W):
     """The fp64 oracle, as it stands, on the same decode step (write + decode),
     repeated until at least --cpu-seconds of host time have been spent."""
@@ -557,6 +617,10 @@ def main():
         for key in ("chunked_prefill", "spec_verify"):
             log(f"extend leg {key}")
             line["extend"][key] = extend_leg(key, args, torch, pg, W, T)
+    if not args.no_fp8:
+        log("fp8 pages leg")
+        line["fp8"] = fp8_leg(args, torch, pg, W, T)
+        line["fp8"]["speedup_vs_bf16_call"] = round(line["decode_call_us"]["mean"] / line["fp8"]["decode_us_mean"], 3)
     if not args.no_window:
         log("sliding window leg")
         line["window"] = window_leg(args, torch, pg, W, T)

@@ -64,6 +64,9 @@
 #ifndef PGQA_DECODE_RPT
 #define PGQA_DECODE_RPT 8
 #endif
+#ifndef PGQA_DECODE_RPT8
+#define PGQA_DECODE_RPT8 16
+#endif
 
 namespace pgqa {
 
@@ -94,6 +97,7 @@ struct DecodeArgs {
 
 constexpr int kStages = PGQA_DECODE_STAGES;   // ring depth (tiles) of the split kernel
 constexpr int kRows = PGQA_DECODE_RPT;        // 1 KB wave rows per tile, for K and for V
+constexpr int kRows8 = PGQA_DECODE_RPT8;      // compute rows per tile over FP8 pages
 static_assert(kStages >= 2 && kStages <= 6, "ring depth");
 static_assert(kRows == 1 || kRows == 2 || kRows == 4 || kRows == 8 || kRows == 16, "rows per tile");
 
@@ -108,7 +112,7 @@ struct Geo {
     static constexpr int EPL = 16 / ES;            // compute elements per lane
     static constexpr int LPT = D / EPL;            // lanes per token
     static constexpr int TPR = kWave / LPT;        // tokens per compute row
-    static constexpr int RPT = kRows * ES / KES;   // compute rows per tile
+    static constexpr int RPT = KES == ES ? kRows : kRows8;   // compute rows per tile
     static constexpr int TT = RPT * TPR;           // tokens per tile
     static constexpr int ROWB = 1024;              // bytes per DMA row
     static constexpr int CROWB = TPR * D * KES;    // LDS bytes of one compute row (per pool)
@@ -117,11 +121,12 @@ struct Geo {
     static constexpr int LPTD = kWave / TPRD;      // lanes per token in a DMA row
     static constexpr int DRPT = RPT * CROWB / ROWB;   // DMA rows per tile, per pool
     static constexpr int KVB = DRPT * ROWB;        // bytes of K (or V) per tile
-    static constexpr int SCL = KES == ES ? 0 : TT / kWave;   // 4-byte-per-lane scale loads per pool
-    static constexpr int NL = 2 * DRPT + 2 * SCL;  // loads per tile
-    static constexpr int TILEB = 2 * KVB + 2 * SCL * kWave * 4;
+    static constexpr int NSL = KES == ES ? 0 : 2 * TT / kWave;   // 4-byte-per-lane loads of K then V row scales
+    static constexpr int NL = 2 * DRPT + NSL;      // loads per tile
+    static constexpr int TILEB = 2 * KVB + NSL * kWave * 4;
     static_assert(LPT >= 2 && LPT <= 32 && TPR * LPT == kWave, "unsupported head_dim / dtype");
     static_assert(DRPT * ROWB == RPT * CROWB && TPRD * LPTD == kWave, "unsupported head_dim / KV dtype");
+    static_assert(KES == ES || NSL * kWave == 2 * TT, "scale loads cover K and V scales of the tile");
 };
 
 constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
@@ -308,7 +313,7 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, PGQA_LDS char* r
     const int bs_mask = (1 << a.bs_log2) - 1;
     const int tile_tok = tile * Gm::TT;
     PGQA_LDS char* dst = ring + slot * Gm::TILEB;
-    if constexpr (Gm::SCL > 0) {
+    if constexpr (Gm::NSL > 0) {
         // Every block id the scale loads need must sit in the window (at most
         // TT / block_size + 1 pages; FP8 pages are at least 16 tokens).
         win.cover(tile_tok >> a.bs_log2, min(tile_tok + Gm::TT - 1, ctx - 1) >> a.bs_log2, lane);
@@ -362,25 +367,24 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, PGQA_LDS char* r
             load_lds_16(src, dst + li * Gm::ROWB);
         }
     }
-    if constexpr (Gm::SCL > 0) {
-        // Row scales, 4 bytes per lane: lane l of load j fetches the scale of the
-        // token that compute lane group g = p / RPT meets in compute row
-        // r = p % RPT (p = 64 j + l), so each group's RPT scales are contiguous
-        // in LDS.  Tokens past the context re-read the last one (masked).
-        constexpr int RPT = Gm::RPT;
+    if constexpr (Gm::NSL > 0) {
+        // Row scales, 4 bytes per lane, K scales then V scales: entry p = 64 j + l
+        // of load j is pool p / TT, position q = p % TT, the scale of the token
+        // that compute lane group g = q / RPT meets in compute row r = q % RPT,
+        // so each group's RPT scales are contiguous in LDS.  Tokens past the
+        // context re-read the last one (masked).
+        constexpr int RPT = Gm::RPT, TT = Gm::TT;
 #pragma unroll
-        for (int j = 0; j < Gm::SCL; ++j) {
+        for (int j = 0; j < Gm::NSL; ++j) {
+            const int li = 2 * DRPT + j;
+            if (li % W != wave) continue;
             const int p = j * kWave + lane;
-            const int tok = min(tile_tok + (p % RPT) * Gm::TPR + p / RPT, ctx - 1);
+            const int qq = p % TT;
+            const int tok = min(tile_tok + (qq % RPT) * Gm::TPR + qq / RPT, ctx - 1);
             const int blk = __builtin_amdgcn_ds_bpermute(((tok >> a.bs_log2) - win.base) << 2, win.reg);
             const int64_t srow = (((int64_t)blk * a.num_kv_heads + h) << a.bs_log2) + (tok & bs_mask);
-#pragma unroll
-            for (int pool = 0; pool < 2; ++pool) {
-                const int li = 2 * DRPT + pool * Gm::SCL + j;
-                if (li % W != wave) continue;
-                __builtin_amdgcn_global_load_lds((pool ? a.v_scale : a.k_scale) + srow,
-                                                 dst + 2 * Gm::KVB + (pool * Gm::SCL + j) * kWave * 4, 4, 0, 0);
-            }
+            __builtin_amdgcn_global_load_lds((p >= TT ? a.v_scale : a.k_scale) + srow,
+                                             dst + 2 * Gm::KVB + j * kWave * 4, 4, 0, 0);
         }
     }
 }
@@ -444,7 +448,7 @@ __device__ __forceinline__ void tile_compute(const PGQA_LDS char* tb, const u32x
     const PGQA_LDS char* vb = kb + Gm::KVB;
     // Row scales of this lane's tokens (FP8): group g's RPT scales are contiguous.
     const PGQA_LDS float* ksc = (const PGQA_LDS float*)(tb + 2 * Gm::KVB) + (lane / Gm::LPT) * RPT;
-    const PGQA_LDS float* vsc = ksc + Gm::SCL * kWave;
+    const PGQA_LDS float* vsc = ksc + Gm::TT;
 
     float s[RPT][VPL];
 #pragma unroll
