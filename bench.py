@@ -98,7 +98,7 @@ def recorded_traffic(path: str):
 
 TRAFFIC_PARTS = {
     # part -> (kernels whose FETCH_SIZE / WRITE_SIZE add up to one call, sources they are built from)
-    "decode": (["decode_split_kernel<2,128,4,1>", "decode_merge_kernel<2,128,4>"],
+    "decode": (["decode_split_kernel<2,128,4,1,2>", "decode_merge_kernel<2,128,4>"],
                ["paged_gqa_kv_02_amd/csrc/decode.hip", "paged_gqa_kv_02_amd/csrc/device_common.hpp",
                 "paged_gqa_kv_02_amd/csrc/launch.hpp"]),
     "prefill": (["prefill_kernel<128,4,false>"],

@@ -24,7 +24,7 @@ def _pmc(dirpath: Path, counter: str, rows):
 
 
 def test_record_then_read_traffic(tmp_path):
-    split = "void pgqa::(anonymous namespace)::decode_split_kernel<2, 128, 4, 1>(pgqa::(anonymous namespace)::DecodeArgs)"
+    split = "void pgqa::(anonymous namespace)::decode_split_kernel<2, 128, 4, 1, 2>(pgqa::(anonymous namespace)::DecodeArgs)"
     merge = "void pgqa::(anonymous namespace)::decode_merge_kernel<2, 128, 4>(pgqa::(anonymous namespace)::DecodeArgs, int)"
     pre = "void pgqa::(anonymous namespace)::prefill_kernel<128, 4, false>(pgqa::(anonymous namespace)::PrefillArgs)"
     # two counter instances per dispatch are summed; dispatches are averaged
@@ -35,7 +35,7 @@ def test_record_then_read_traffic(tmp_path):
     shutil.copy(ROOT / "profiles" / "traffic_counters.json", rec_path)
     rec = bench.record_traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(rec_path))
     k = rec["decode"]["kernels"]
-    assert k["decode_split_kernel<2,128,4,1>"] == {"fetch_kib": 160.0, "write_kib": 4.0}
+    assert k["decode_split_kernel<2,128,4,1,2>"] == {"fetch_kib": 160.0, "write_kib": 4.0}
     assert k["decode_merge_kernel<2,128,4>"] == {"fetch_kib": 10.0, "write_kib": 1.0}
     got = bench.recorded_traffic(str(rec_path))
     cal = rec["copy_calibration"]
