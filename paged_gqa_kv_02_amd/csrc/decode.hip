@@ -784,16 +784,22 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     }
 }
 
-// One 256-thread workgroup per (sequence, KV head) segment: nothing when one
-// share covered the whole segment (or it is empty), else the log-sum-exp merge
-// of the segment's partials in share order (deterministic).  Every thread owns
-// (head, dim) outputs; the loads of successive shares are independent.
+// kMergeSlices 256-thread workgroups per (sequence, KV head) segment, each
+// owning 256 of its G x D outputs: nothing when one share covered the whole
+// segment (or it is empty), else the log-sum-exp merge of the segment's partials
+// in share order (deterministic).  The loads of successive shares are
+// independent.
+template <int G, int D>
+constexpr int merge_slices() { return (G * D + 255) / 256; }
+
 template <int ES, int D, int G>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tt) {
     __shared__ int red[2][4];
+    constexpr int NS = merge_slices<G, D>();
     const int tid = threadIdx.x;
     const int Hkv = a.num_kv_heads;
-    const int seg = blockIdx.x;
+    const int seg = blockIdx.x / NS;
+    const int e = (blockIdx.x % NS) * 256 + tid;
     const int b = seg / Hkv;
     const int h = seg % Hkv;
 
@@ -824,7 +830,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tt)
     const int64_t w1 = share_of(xs + tiles_b - 1, total, nw);
     if (w0 == w1) return;
 
-    for (int e = tid; e < G * D; e += 256) {
+    if (e < G * D) {
         const int g = e / D;
         const int x = e % D;
         float M = -INFINITY, L = 0.0f, acc = 0.0f;
@@ -859,6 +865,7 @@ struct Entry {
     int waves;
     int tile_bytes;
     int tt;
+    int merge_slices;
 };
 
 template <int ES, int D, int G, int KES>
@@ -871,6 +878,7 @@ Entry make_entry() {
     e.waves = W;
     e.tile_bytes = Geo<ES, D, KES>::TILEB;
     e.tt = Geo<ES, D, KES>::TT;
+    e.merge_slices = merge_slices<G, D>();
     return e;
 }
 
@@ -998,7 +1006,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     hipLaunchKernelGGL(e.split, dim3(nw), dim3(threads), lds, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(e.merge, dim3(L.batch * L.num_kv_heads), dim3(256), 0, stream, a, e.tt);
+    hipLaunchKernelGGL(e.merge, dim3(L.batch * L.num_kv_heads * e.merge_slices), dim3(256), 0, stream, a, e.tt);
     return hipGetLastError();
 }
 
