@@ -223,6 +223,9 @@ int gqa_varlen_prefill(const void* q, const void* k, const void* v,
  *   max_q_len    host-side upper bound of the q_len of every sequence
  *   max_context_len  host-side upper bound of context_lens;
  *                    must be <= max_blocks_per_seq * block_size
+ *   workspace    NULL, or device memory (16-byte aligned) of workspace_bytes for
+ *                the key split (gqa_paged_extend_workspace_size); its contents
+ *                need no initialisation; calls that may run at once must not share it
  * Errors: PGQA_EINVAL (bad sizes or pointers, or a grid past 2^31 workgroups),
  * PGQA_ENOTSUP (fp32; head_dim other than 64 / 128; group size not 1, 2 or a
  * multiple of 4 up to 64; block_size below 4 for head_dim 128 or below 8 for
@@ -233,7 +236,21 @@ int gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_cache, co
                      int32_t batch, int32_t total_q, int32_t max_q_len,
                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                      int32_t block_size, int32_t num_blocks, int32_t max_context_len,
-                     float scale, int32_t window, pgqa_dtype dtype, void* out, void* stream);
+                     float scale, int32_t window, pgqa_dtype dtype, void* out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace gqa_paged_extend can use for these sizes (0 when it
+ * would not split): when the call has too few (query tile, sequence, KV head)
+ * pieces to balance the GPU (short queries, e.g. a few draft tokens per
+ * sequence), the library cuts long key ranges into chunks handled by separate
+ * workgroups, which write fp32 partials (running max, sum and unnormalised
+ * output per row and query head) that a second kernel merges exactly (log-sum-
+ * exp, in chunk order; deterministic).  A smaller (or NULL) workspace only
+ * means fewer (or no) chunks.  Returns 0 for invalid sizes.
+ */
+size_t gqa_paged_extend_workspace_size(int32_t batch, int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len);
 
 /*
  * Low-precision KV pages.  The pages give only the byte sizes (bf16 2 bytes,

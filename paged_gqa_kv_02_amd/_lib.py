@@ -27,7 +27,8 @@ _SIGNATURES = {
                                    _P, _Z, _P]),
     "gqa_varlen_prefill": (C.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P]),
     "gqa_paged_extend": (C.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
-                                   _I, _P, _P]),
+                                   _I, _P, _P, _Z, _P]),
+    "gqa_paged_extend_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "paged_kv_copy_blocks": (C.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "paged_kv_write_fp8": (C.c_int, [_P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "gqa_paged_decode_fp8": (C.c_int, [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _I,

@@ -145,6 +145,15 @@ int gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache, co
     return hip_status(pgqa::launch_decode(L, (hipStream_t)stream));
 }
 
+size_t gqa_paged_extend_workspace_size(int32_t batch, int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len) {
+    if (batch <= 0 || total_q <= 0 || max_q_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0)
+        return 0;
+    if (num_q_heads % num_kv_heads) return 0;
+    return pgqa::extend_workspace_bytes(batch, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                                        max_context_len);
+}
+
 int paged_kv_write_fp8(const void* k, const void* v, const int32_t* cu_seqlens, const int32_t* start_pos,
                        const int32_t* block_table, int32_t max_blocks_per_seq, void* k_cache, void* v_cache,
                        float* k_scale, float* v_scale, int32_t batch, int32_t total_tokens, int32_t num_blocks,
@@ -225,7 +234,8 @@ int gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_cache, co
                      const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
                      int32_t batch, int32_t total_q, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
                      int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_context_len, float scale,
-                     int32_t window, pgqa_dtype dtype, void* out, void* stream) {
+                     int32_t window, pgqa_dtype dtype, void* out, void* workspace, size_t workspace_bytes,
+                     void* stream) {
     if (batch < 0 || total_q < 0 || max_q_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
         max_blocks_per_seq <= 0 || max_context_len < 0 || window < 0)
         return PGQA_EINVAL;
@@ -245,10 +255,11 @@ int gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_cache, co
     if (check_elem_ptr(q) || check_elem_ptr(k_cache) || check_elem_ptr(v_cache) || check_elem_ptr(out))
         return PGQA_EINVAL;
     if (check_index_ptr(cu_q) || check_index_ptr(block_table) || check_index_ptr(context_lens)) return PGQA_EINVAL;
+    if (workspace && !aligned(workspace, 16)) return PGQA_EINVAL;
     if (batch == 0 || total_q == 0 || max_q_len == 0) return PGQA_OK;
     pgqa::ExtendLaunch L{q, k_cache, v_cache, cu_q, block_table, context_lens, out, batch, total_q, max_q_len,
                          max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, lg, num_blocks,
-                         max_context_len, scale, window};
+                         max_context_len, scale, window, workspace, workspace ? workspace_bytes : 0};
     return hip_status(pgqa::launch_extend(L, (hipStream_t)stream));
 }
 

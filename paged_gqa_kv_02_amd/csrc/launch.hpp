@@ -131,7 +131,13 @@ struct ExtendLaunch {
     int32_t max_context_len;
     float scale;
     int32_t window;   // 0: none; > 0: keys p - window + 1 .. p for a row at position p
+    void* workspace;  // key-split partials (may be null: no split)
+    size_t workspace_bytes;
 };
+
+// Workspace bytes for the library's key split of a paged multi-token call (0: none).
+size_t extend_workspace_bytes(int32_t batch, int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len);
 
 // Is there a paged multi-token kernel for this (head_dim, group size, block size)?
 bool extend_supported(int32_t head_dim, int32_t group, int32_t block_size);

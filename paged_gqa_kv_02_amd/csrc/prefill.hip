@@ -85,6 +85,13 @@ struct PrefillArgs {
     int32_t bs_log2;
     int32_t ctx_cap;         // host-side bound of context_lens
     int32_t window;          // > 0: row i sees only its newest `window` keys (local attention)
+    // Key split (paged only): a pair's key range is cut into chunks of kchunk
+    // blocks, nchunk per pair at most; a sequence whose keys span more than one
+    // chunk gets fp32 partials per (row, head, chunk), merged afterwards.
+    int32_t nchunk;          // 1 = no split
+    int32_t kchunk;          // key blocks per chunk
+    float* part_o;           // [total_tokens, Hq, nchunk, D]
+    float* part_ml;          // [total_tokens, Hq, nchunk, 2]  (m in log2 units, l)
 };
 
 // Block-table rows are read through the constant address space, which makes
@@ -287,9 +294,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // heaviest-first (query tiles from the last), the head groups sharing the
     // pair's K/V side by side.
     const int id = blockIdx.x;
-    const int per_pair = a.nqt * groups;
+    const int per_pair = a.nqt * groups * a.nchunk;
     const int kq = (id >> 3) / per_pair;                 // the XCD's kq-th pair
-    const int r2 = (id >> 3) - kq * per_pair;
+    const int r3 = (id >> 3) - kq * per_pair;
+    const int r2 = r3 / a.nchunk;
+    const int chunk = r3 - r2 * a.nchunk;                // key chunk (0 without a split)
     const int level = r2 / groups;
     const int grp = r2 - level * groups;
     const int pair = (id & 7) + 8 * kq;
@@ -309,6 +318,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int qtile = a.nqt - 1 - level;
     const int tok0 = qtile * TB * BQ;
     if (tok0 >= Lq) return;
+    // Chunks past the sequence's keys do not exist (chunk 0 always does).
+    const int ckeys = a.kchunk * BN;
+    if (chunk > 0 && chunk * ckeys >= Lk) return;
+    const bool split = Lk > ckeys;                       // partials instead of the output
     const int head = kvh * G + grp * HG + (wave % HG);
     const int i0 = tok0 + (wave / HG) * BQ;          // this wave's first query row (sequence-local)
 
@@ -324,8 +337,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // own rows' windows are fully masked) to its last block.  Ring slots and the
     // block loop run on the index relative to kb0.
     const int win = a.window;
-    const int kb0 = (win > 0 && nkb > 0) ? max(0, koff + tok0 - win + 1) / BN : 0;
-    const int nrel = nkb - kb0;
+    const int kbw = (win > 0 && nkb > 0) ? max(0, koff + tok0 - win + 1) / BN : 0;
+    // This workgroup's key blocks: the window's range cut to its chunk.
+    const int kb0 = max(kbw, chunk * a.kchunk);
+    const int kb1 = min(nkb, chunk * a.kchunk + a.kchunk);
+    const int nrel = max(0, kb1 - kb0);
     const float cs = a.scale_log2;
 
     const int64_t qstride = (int64_t)a.num_q_heads * D * 2;   // bytes per packed Q row
@@ -523,7 +539,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     f32x16 sa[2], sb[2];
     wait_vmcnt<0>();
     __syncthreads();
-    const int kend = active && last_kb >= 0 ? last_kb - kb0 : -1;
+    const int kend = active && last_kb >= 0 ? min(last_kb, kb1 - 1) - kb0 : -1;
     if (kend >= 0) scores(sa, I0{});
     int kb = 0;
     for (; kb + 2 <= kend; kb += 2) {
@@ -552,6 +568,23 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     __syncthreads();   // every wave is done with the ring
     if (!active) return;
     lsum += shfl_xor_f32(lsum, 32);
+    if (split) {
+        // Partial of this key chunk: unnormalised O, running max m and sum l
+        // (both halves of the wave hold the row's m); a row with no key in the
+        // chunk leaves O = 0, l = 0.
+        if (i0 + l32 < Lq) {
+            const int64_t prow = ((int64_t)(seq0 + i0 + l32) * a.num_q_heads + head) * a.nchunk + chunk;
+            float* po = a.part_o + prow * D + 4 * half;
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd)
+                    *(f32x4*)(po + 32 * db + 8 * qd) = f32x4{o[db][4 * qd], o[db][4 * qd + 1], o[db][4 * qd + 2],
+                                                            o[db][4 * qd + 3]};
+            if (half == 0) *(float2*)(a.part_ml + prow * 2) = make_float2(m, lsum);
+        }
+        return;
+    }
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
     PGQA_LDS char* ot = ring + wave * (BQ * P::ROWB);
 #pragma unroll
@@ -571,6 +604,40 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         const u32x4 val = lds_read_16(ot + swz<D>(r, c));
         if (i0 + r < Lq)
             *(u32x4*)(a.out + (int64_t)(seq0 + i0 + r) * qstride + (int64_t)head * D * 2 + c * 16) = val;
+    }
+}
+
+// Merge of the key-chunk partials of split sequences: one workgroup per query
+// row (its sequence found once), each thread a set of (head, dim) outputs; the
+// log-sum-exp of the chunks in chunk order (deterministic).  Rows of sequences
+// that fit one chunk were written by the attention kernel.
+template <int D>
+__global__ __launch_bounds__(256) void extend_merge_kernel(PrefillArgs a) {
+    const int row = blockIdx.x;
+    int lo = 0, hi = a.batch - 1;                          // the sequence holding the row
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (__builtin_amdgcn_readfirstlane(a.cu_seqlens[mid]) <= row) lo = mid;
+        else hi = mid - 1;
+    }
+    const int Lk = __builtin_amdgcn_readfirstlane(clampi(a.context_lens[lo], 0, a.ctx_cap));
+    const int ckeys = a.kchunk * BN;
+    const int nc = Lk > ckeys ? (Lk + ckeys - 1) / ckeys : 1;
+    if (nc <= 1) return;
+    for (int e = threadIdx.x; e < a.num_q_heads * D; e += 256) {
+        const int64_t rh = (int64_t)row * a.num_q_heads + e / D;
+        const float* ml = a.part_ml + rh * a.nchunk * 2;
+        const float* po = a.part_o + rh * a.nchunk * D + e % D;
+        float M = -INFINITY;
+        for (int c = 0; c < nc; ++c) M = fmaxf(M, ml[2 * c]);
+        float acc = 0.0f, L = 0.0f;
+        for (int c = 0; c < nc; ++c) {
+            const float w = __builtin_amdgcn_exp2f(ml[2 * c] - M);
+            acc = fmaf(w, po[(int64_t)c * D], acc);
+            L = fmaf(w, ml[2 * c + 1], L);
+        }
+        const float r = L > 0.0f ? acc / L : 0.0f;
+        *(uint16_t*)(a.out + (rh * D + e % D) * 2) = (uint16_t)f32_to_bf16_bits(r);
     }
 }
 
@@ -599,13 +666,52 @@ size_t lds_bytes(int head_dim) { return head_dim == 128 ? 4 * PGeo<128>::TILEB :
 
 int rows_per_load(int head_dim) { return head_dim == 128 ? PGeo<128>::RPL : PGeo<64>::RPL; }
 
+int cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 256;
+    return n;
+}
+
+constexpr int kNoSplit = 1 << 24;   // key blocks per chunk when nothing is split
+
+// Key split of a paged multi-token call.  Without it there is one workgroup per
+// (query tile, head group, sequence, KV head); when that grid cannot even fill
+// the GPU's workgroup slots (two per CU) the long contexts run on a few CUs, so
+// key ranges are cut into chunks (at least 4 blocks) for about two workgroups
+// per slot.  (A grid that fills the slots once is left alone: shorter chunks
+// cost more in per-workgroup start-up than they recover in balance.)
+// max_chunks (from the caller's workspace) caps the count.
+void extend_split(int64_t wgs_unsplit, int max_context_len, int64_t max_chunks, int* nchunk, int* kchunk) {
+    *nchunk = 1;
+    *kchunk = kNoSplit;
+    const int64_t slots = 2 * (int64_t)cu_count();
+    const int blocks = (max_context_len + BN - 1) / BN;
+    if (wgs_unsplit >= slots || blocks < 8 || max_chunks < 2) return;
+    int64_t nc = (2 * slots + wgs_unsplit - 1) / wgs_unsplit;
+    if (nc > max_chunks) nc = max_chunks;
+    int kc = (int)((blocks + nc - 1) / nc);
+    if (kc < 4) kc = 4;
+    nc = (blocks + kc - 1) / kc;
+    if (nc <= 1) return;
+    *nchunk = (int)nc;
+    *kchunk = kc;
+}
+
 // Tile levels, XCD packing and grid size shared by both entry points.
-hipError_t launch(PrefillFn fn, PrefillArgs& a, int hg, int group, int max_q_rows, int head_dim,
-                  hipStream_t stream) {
+void grid_dims(PrefillArgs& a, int hg, int group, int max_q_rows) {
     const int rows_per_wg = (4 / hg) * BQ;
     a.nqt = (max_q_rows + rows_per_wg - 1) / rows_per_wg;
     a.pairs_per_xcd = (int)(((int64_t)a.batch * a.num_kv_heads + 7) / 8);
-    const int64_t wgs = 8 * (int64_t)a.nqt * a.pairs_per_xcd * (group / hg);
+    (void)group;
+}
+
+int64_t grid_size(const PrefillArgs& a, int hg, int group) {
+    return 8 * (int64_t)a.nqt * a.pairs_per_xcd * (group / hg) * a.nchunk;
+}
+
+hipError_t launch(PrefillFn fn, PrefillArgs& a, int hg, int group, int head_dim, hipStream_t stream) {
+    const int64_t wgs = grid_size(a, hg, group);
     if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(256), lds_bytes(head_dim), stream, a);
     return hipGetLastError();
@@ -643,7 +749,10 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
     a.scale_log2 = (float)((double)L.scale * 1.4426950408889634);
     a.batch = L.batch;
     a.window = L.window;
-    return launch(fn, a, hg, group, L.max_seqlen, L.head_dim, stream);
+    a.nchunk = 1;
+    a.kchunk = kNoSplit;
+    grid_dims(a, hg, group, L.max_seqlen);
+    return launch(fn, a, hg, group, L.head_dim, stream);
 }
 
 hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream) {
@@ -671,7 +780,36 @@ hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream) {
     a.bs_log2 = L.block_size_log2;
     a.ctx_cap = L.max_context_len;
     a.window = L.window;
-    return launch(fn, a, hg, group, L.max_q_len, L.head_dim, stream);
+    grid_dims(a, hg, group, L.max_q_len);
+    a.nchunk = 1;
+    const int64_t per_chunk = (int64_t)L.total_q * L.num_q_heads * (L.head_dim + 2) * 4;
+    const int64_t max_chunks = (L.workspace && per_chunk > 0) ? (int64_t)(L.workspace_bytes / per_chunk) : 0;
+    extend_split(grid_size(a, hg, group), L.max_context_len, max_chunks, &a.nchunk, &a.kchunk);
+    a.part_o = (float*)L.workspace;
+    a.part_ml = a.part_o + (int64_t)L.total_q * L.num_q_heads * a.nchunk * L.head_dim;
+    hipError_t err = launch(fn, a, hg, group, L.head_dim, stream);
+    if (err != hipSuccess || a.nchunk == 1) return err;
+    if (L.head_dim == 128)
+        hipLaunchKernelGGL(extend_merge_kernel<128>, dim3((unsigned)L.total_q), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(extend_merge_kernel<64>, dim3((unsigned)L.total_q), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+size_t extend_workspace_bytes(int32_t batch, int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len) {
+    const int group = num_q_heads / num_kv_heads;
+    PrefillFn fn;
+    int hg;
+    if (!pick<true>(head_dim, group, &fn, &hg)) return 0;
+    PrefillArgs a = {};
+    a.batch = batch;
+    a.num_kv_heads = num_kv_heads;
+    a.nchunk = 1;
+    grid_dims(a, hg, group, max_q_len);
+    int nc = 1, kc = kNoSplit;
+    extend_split(grid_size(a, hg, group), max_context_len, 1 << 20, &nc, &kc);
+    return nc > 1 ? (size_t)total_q * num_q_heads * nc * (head_dim + 2) * 4 : 0;
 }
 
 }  // namespace pgqa

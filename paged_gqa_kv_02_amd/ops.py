@@ -131,10 +131,24 @@ def gqa_varlen_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seq
     return out
 
 
+def gqa_paged_extend_workspace_size(batch: int, total_q: int, max_q_len: int, num_q_heads: int,
+                                    num_kv_heads: int, head_dim: int, max_context_len: int) -> int:
+    return int(lib().gqa_paged_extend_workspace_size(batch, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                                                     max_context_len))
+
+
+def extend_workspace(batch: int, total_q: int, max_q_len: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                     max_context_len: int, device=None) -> torch.Tensor:
+    """Device workspace for gqa_paged_extend's key split (contents need no initialisation)."""
+    n = gqa_paged_extend_workspace_size(batch, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                                        max_context_len)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device or "cuda")
+
+
 def gqa_paged_extend(q: torch.Tensor, cu_q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                      block_table: torch.Tensor, context_lens: torch.Tensor, max_q_len: int, max_context_len: int,
                      scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                     window: int = 0) -> torch.Tensor:
+                     window: int = 0, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Several new tokens per sequence over its paged cache (chunked prefill on a cached
     prefix, draft verification): q [total_q, Hq, d] -> out [total_q, Hq, d].  The new
     tokens' K/V must already be in the pages; context_lens counts them."""
@@ -146,12 +160,15 @@ def gqa_paged_extend(q: torch.Tensor, cu_q: torch.Tensor, k_cache: torch.Tensor,
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
-    _dev(q, cu_q, k_cache, v_cache, block_table, context_lens, out)
+    if workspace is None:
+        workspace = extend_workspace(cu_q.numel() - 1, T, int(max_q_len), hq, hkv, d, int(max_context_len), q.device)
+    _dev(q, cu_q, k_cache, v_cache, block_table, context_lens, out, workspace)
     _i32(cu_q, block_table, context_lens)
     st = lib().gqa_paged_extend(q.data_ptr(), cu_q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                 block_table.data_ptr(), block_table.shape[1], context_lens.data_ptr(),
                                 cu_q.numel() - 1, T, int(max_q_len), hq, hkv, d, bs, nb, int(max_context_len),
-                                float(scale), int(window), _dtype(q), out.data_ptr(), _stream())
+                                float(scale), int(window), _dtype(q), out.data_ptr(), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream())
     check("gqa_paged_extend", st)
     return out
 

@@ -127,11 +127,11 @@ def test_prefill_validation(lib):
 
 def _extend(lib, **kw):
     a = dict(q=P[0], cu=P[1], kc=P[2], vc=P[3], bt=P[4], maxb=4, cl=P[5], batch=2, T=12, maxq=9, hq=32, hkv=8,
-             d=128, bs=16, nb=8, maxctx=64, scale=0.088, win=0, dt=BF16, out=P[6])
+             d=128, bs=16, nb=8, maxctx=64, scale=0.088, win=0, dt=BF16, out=P[6], ws=None, wsb=0)
     a.update(kw)
     return lib.gqa_paged_extend(a["q"], a["cu"], a["kc"], a["vc"], a["bt"], a["maxb"], a["cl"], a["batch"],
                                 a["T"], a["maxq"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["maxctx"],
-                                a["scale"], a["win"], a["dt"], a["out"], None)
+                                a["scale"], a["win"], a["dt"], a["out"], a["ws"], a["wsb"], None)
 
 
 def test_extend_validation(lib):
@@ -145,6 +145,7 @@ def test_extend_validation(lib):
     assert _extend(lib, out=P[6] + 2) == EINVAL
     assert _extend(lib, scale=float("inf")) == EINVAL
     assert _extend(lib, win=-1) == EINVAL
+    assert _extend(lib, ws=P[7] + 8, wsb=1024) == EINVAL    # misaligned workspace
     assert _extend(lib, dt=F32) == ENOTSUP              # bf16 MFMA path only
     assert _extend(lib, d=32) == ENOTSUP
     assert _extend(lib, hq=24, hkv=8) == ENOTSUP        # group 3
@@ -211,3 +212,16 @@ def test_fp8_write_validation(lib):
     assert w(dt=F32) == ENOTSUP
     assert w(d=96) == ENOTSUP
     assert w(batch=0) == 0
+
+
+def test_extend_workspace_size(lib):
+    # 8 sequences x 8 KV heads of 4 query tokens: far fewer pieces than the GPU has slots,
+    # so the long contexts are split
+    n = lib.gqa_paged_extend_workspace_size(8, 32, 4, 64, 8, 128, 32768)
+    assert n > 0 and n % (32 * 64 * 130 * 4) == 0
+    # 64 x 8 pieces fill the slots once: no split
+    assert lib.gqa_paged_extend_workspace_size(64, 256, 4, 32, 8, 128, 4096) == 0
+    # 16 sequences x 512 query tokens fill the GPU without a split
+    assert lib.gqa_paged_extend_workspace_size(16, 8192, 512, 32, 8, 128, 3584) == 0
+    assert lib.gqa_paged_extend_workspace_size(64, 256, 4, 32, 8, 128, 200) == 0   # short contexts
+    assert lib.gqa_paged_extend_workspace_size(2, 8, 4, 30, 8, 128, 4096) == 0     # Hq % Hkv != 0

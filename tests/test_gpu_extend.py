@@ -147,3 +147,41 @@ def test_workload_sampled_rows(orc, key):
     ref = oracle_extend(orc, c, rows=rows)
     e = assert_close(out[rows], ref, W.BF16, f"{key} rows")
     say(f"extend {key}: {e}")
+
+
+@pytest.mark.parametrize("q_len,window,hq,hkv", [(4, 0, 32, 8), (1, 0, 32, 8), (40, 0, 32, 8), (7, 300, 8, 2),
+                                                 (4, 0, 64, 1), (33, 1000, 16, 4)])
+def test_key_split(orc, q_len, window, hq, hkv):
+    """Few query tokens over long contexts: the library splits key ranges into
+    chunks (fp32 partials + merge).  Checked against the oracle, and against the
+    same call with no workspace (no split)."""
+    prefix = [3000, 17, 1024 - q_len, 1025 - q_len, 2048, 4000, 64, 2500]
+    hkv_pairs = hkv if hkv <= 2 else 2           # few (sequence, KV head) pairs, so the call splits
+    hq = hq // hkv * hkv_pairs
+    hkv = hkv_pairs
+    c = W.make_extend_case(prefix, [q_len] * len(prefix), hq, hkv, 128, 16, W.BF16, seed=900 + q_len + window + hq)
+    n = pg.gqa_paged_extend_workspace_size(c.batch, c.total_q, c.max_q_len, hq, hkv, 128, c.max_context_len)
+    assert n > 0, "this shape is meant to split"
+    say(f"extend key split q_len={q_len} window={window} {hq}/{hkv}")
+    dev = DevExtend(c)
+    args = (dev.q, dev.cu_q, dev.kc, dev.vc, dev.table, dev.ctx, c.max_q_len, c.max_context_len)
+    split = pg.gqa_paged_extend(*args, scale=float(c.scale), window=window)
+    plain = pg.gqa_paged_extend(*args, scale=float(c.scale), window=window,
+                                workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    kc = W.nan_pool(c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim, c.dtype)
+    vc = W.nan_pool(c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim, c.dtype)
+    orc.paged_kv_write(c.k, c.v, c.cu_ctx, c.start_pos, c.block_table, kc, vc)
+    ref = orc.gqa_paged_extend(c.q, c.cu_q, kc, vc, c.block_table, c.context_lens, c.scale, window=window)
+    assert_close(to_f64(split), ref, W.BF16, "split")
+    assert_close(to_f64(plain), ref, W.BF16, "no split")
+
+
+def test_key_split_is_deterministic():
+    c = W.make_extend_case([32000, 9000, 20000, 100], [4] * 4, 64, 8, 128, 16, W.BF16, seed=950)
+    assert pg.gqa_paged_extend_workspace_size(c.batch, c.total_q, c.max_q_len, 64, 8, 128, c.max_context_len) > 0
+    dev = DevExtend(c)
+    say("extend key split twice")
+    a = dev.extend()
+    b = dev.extend()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
