@@ -132,9 +132,10 @@ class DevExtend:
                                    int(self.ctx_np.max()) if c.batch else 0, scale=float(c.scale))
 
 
-def oracle_extend(orc, case: W.ExtendCase, rows=None, context_lens=None) -> np.ndarray:
+def oracle_extend(orc, case: W.ExtendCase, rows=None, context_lens=None, window: int = 0) -> np.ndarray:
     kc = W.nan_pool(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)
     vc = W.nan_pool(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim, case.dtype)
     orc.paged_kv_write(case.k, case.v, case.cu_ctx, case.start_pos, case.block_table, kc, vc)
     ctx = case.context_lens if context_lens is None else np.asarray(context_lens, np.int32)
-    return orc.gqa_paged_extend(case.q, case.cu_q, kc, vc, case.block_table, ctx, case.scale, rows=rows)
+    return orc.gqa_paged_extend(case.q, case.cu_q, kc, vc, case.block_table, ctx, case.scale, rows=rows,
+                                window=window)
