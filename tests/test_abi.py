@@ -225,3 +225,13 @@ def test_extend_workspace_size(lib):
     assert lib.gqa_paged_extend_workspace_size(16, 8192, 512, 32, 8, 128, 3584) == 0
     assert lib.gqa_paged_extend_workspace_size(64, 256, 4, 32, 8, 128, 200) == 0   # short contexts
     assert lib.gqa_paged_extend_workspace_size(2, 8, 4, 30, 8, 128, 4096) == 0     # Hq % Hkv != 0
+
+
+def test_build_entry_point(monkeypatch, built_lib):
+    """__graft_entry__.build() runs end to end: the HIP build step is replaced by
+    the library already built (hipcc takes minutes), the oracle is really
+    compiled, and the package imports and loads the library."""
+    import __graft_entry__ as entry
+    from paged_gqa_kv_02_amd import build as hip_build
+    monkeypatch.setattr(hip_build, "build", lambda jobs=0: hip_build.LIB)
+    entry.build()
