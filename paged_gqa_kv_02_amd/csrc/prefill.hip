@@ -462,6 +462,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                     for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
             }
         }
+        // The MFMA + softmax interleave runs at raised wave priority, so of the
+        // two workgroups sharing a SIMD the one in this phase issues first and
+        // the other's P.V products fill the matrix pipe around it.
+        __builtin_amdgcn_s_setprio(3);
         if constexpr (decltype(has_next)::value) scores(nxt, std::integral_constant<int, 1 - PAR>{});
         // P^T operand for 16-key step kk: keys 16kk + 8*(jj/4) + 4*half + jj%4,
         // i.e. accumulator entries 8*(kk%2) .. +7 of half kk/2.  The row sum
@@ -491,6 +495,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
         // O^T += V^T P^T: A = V^T for dims 32*db + l32, keys {16kk + 4*half + 0..3, +8 ..}.
         const PGQA_LDS char* vt = ring + (2 + PAR) * P::TILEB;
 #pragma unroll
