@@ -117,6 +117,15 @@ struct PGeo {
     static_assert((2 * LOADS) % 4 == 0, "loads split over 4 waves");
 };
 
+// The lane's index, produced afresh where it is needed.  The kernel re-derives
+// its lane values after the prologue instead of keeping them live across the
+// key loop, where every register is taken (kept, they are spilled to scratch).
+__device__ __forceinline__ int lane_now() {
+    int x;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+    return x;
+}
+
 // Row r's swizzle key.  LDS has 64 banks of 4 bytes; a 16-byte-per-lane read
 // is served 16 lanes at a time and an 8-byte transposed read 32 lanes at a
 // time, so a read is conflict-free when every lane of a phase hits its own
@@ -434,8 +443,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         // llim <= off <= lim, with off = 32*kb2 + 8*(i/4) + i%4 and the lane's
         // 4*half folded into both bounds.
         if ((j0 + BN > Lk) || (a.causal && j0 + BN - 1 > koff + i0) || (win > 0 && j0 < koff + i0 + BQ - win)) {
-            const int lim = (a.causal ? min(koff + i0 + l32, Lk - 1) : Lk - 1) - j0 - 4 * half;
-            const int llim = (win > 0 ? koff + i0 + l32 - win + 1 : -(1 << 30)) - j0 - 4 * half;
+            const int ln = lane_now();
+            const int lrow = koff + i0 + (ln & 31);
+            const int lim = (a.causal ? min(lrow, Lk - 1) : Lk - 1) - j0 - 4 * (ln >> 5);
+            const int llim = (win > 0 ? lrow - win + 1 : -(1 << 30)) - j0 - 4 * (ln >> 5);
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -525,10 +536,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         const int tb = wave < 2 ? kr + 2 : kr + 1;
         if (tb < nrel) {
             if constexpr (PAGED) {
-                issue_tile_paged<D>(ps, dl, ring_addr, kb0 + tb, tb & 1, wave, lane);
+                issue_tile_paged<D>(ps, dl, ring_addr, kb0 + tb, tb & 1, wave, lane_now());
                 if (tb + 1 < nrel) paged_load_ids<D>(ps, kb0 + tb + 1, wave);
             } else {
-                issue_tile<D>(a, dl, ring_addr, kb0 + tb, tb & 1, seq0, Lk, kvh, wave, lane, kvstride);
+                issue_tile<D>(a, dl, ring_addr, kb0 + tb, tb & 1, seq0, Lk, kvh, wave, lane_now(), kvstride);
             }
         }
     };
@@ -572,21 +583,24 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // one row, CPR consecutive lanes per row.
     __syncthreads();   // every wave is done with the ring
     if (!active) return;
+    const int lane_e = lane_now();
+    const int half_e = lane_e >> 5;
+    const int l32_e = lane_e & 31;
     lsum += shfl_xor_f32(lsum, 32);
     if (split) {
         // Partial of this key chunk: unnormalised O, running max m and sum l
         // (both halves of the wave hold the row's m); a row with no key in the
         // chunk leaves O = 0, l = 0.
-        if (i0 + l32 < Lq) {
-            const int64_t prow = ((int64_t)(seq0 + i0 + l32) * a.num_q_heads + head) * a.nchunk + chunk;
-            float* po = a.part_o + prow * D + 4 * half;
+        if (i0 + l32_e < Lq) {
+            const int64_t prow = ((int64_t)(seq0 + i0 + l32_e) * a.num_q_heads + head) * a.nchunk + chunk;
+            float* po = a.part_o + prow * D + 4 * half_e;
 #pragma unroll
             for (int db = 0; db < DBLK; ++db)
 #pragma unroll
                 for (int qd = 0; qd < 4; ++qd)
                     *(f32x4*)(po + 32 * db + 8 * qd) = f32x4{o[db][4 * qd], o[db][4 * qd + 1], o[db][4 * qd + 2],
                                                             o[db][4 * qd + 3]};
-            if (half == 0) *(float2*)(a.part_ml + prow * 2) = make_float2(m, lsum);
+            if (half_e == 0) *(float2*)(a.part_ml + prow * 2) = make_float2(m, lsum);
         }
         return;
     }
@@ -596,16 +610,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
-            // dims 32*db + 8*qd + 4*half .. +3 of row l32: chunk 4*db + qd, byte 8*half
+            // dims 32*db + 8*qd + 4*half_e .. +3 of row l32_e: chunk 4*db + qd, byte 8*half_e
             u32x2 w;
             w.x = pack_bf16x2_rne_hw(o[db][4 * qd + 0] * inv, o[db][4 * qd + 1] * inv);
             w.y = pack_bf16x2_rne_hw(o[db][4 * qd + 2] * inv, o[db][4 * qd + 3] * inv);
-            *(PGQA_LDS u32x2*)(ot + swz<D>(l32, 4 * db + qd) + 8 * half) = w;
+            *(PGQA_LDS u32x2*)(ot + swz<D>(l32_e, 4 * db + qd) + 8 * half_e) = w;
         }
-    const int c = lane % P::CPR;
+    const int c = lane_e % P::CPR;
 #pragma unroll
     for (int t = 0; t < BQ / P::RPL; ++t) {
-        const int r = t * P::RPL + lane / P::CPR;
+        const int r = t * P::RPL + lane_e / P::CPR;
         const u32x4 val = lds_read_16(ot + swz<D>(r, c));
         if (i0 + r < Lq)
             *(u32x4*)(a.out + (int64_t)(seq0 + i0 + r) * qstride + (int64_t)head * D * 2 + c * 16) = val;
