@@ -434,10 +434,13 @@ __device__ __forceinline__ u32x4 kv_slice(const PGQA_LDS char* base, int r) {
 
 // One tile: scores, online-softmax update and P.V for this wave's GW heads.
 // FULL: every token of the tile is inside [lo, ctx) (no masking needed).
+// PF: all K and V slices of the tile are read from LDS up front, so their
+// latency is paid once per tile instead of once per row pair (off where the
+// extra registers would spill: 8-wave groups and head_dim 16).
 // tb is the tile's ring slot.  FP8 pages: the row scale of K multiplies the
 // token's score, that of V its weight in P.V (the softmax sum keeps the plain
 // weight), so the codes are used as they are.
-template <bool FULL, int ES, int D, int GW, int KES>
+template <bool FULL, int ES, int D, int GW, int KES, bool PF>
 __device__ __forceinline__ void tile_compute(const PGQA_LDS char* tb, const u32x4* qv, float* m, float* l,
                                              float (*o)[16 / ES], int tok0, int ctx, int lo, float c, int lane) {
     using Gm = Geo<ES, D, KES>;
@@ -450,10 +453,18 @@ __device__ __forceinline__ void tile_compute(const PGQA_LDS char* tb, const u32x
     const PGQA_LDS float* ksc = (const PGQA_LDS float*)(tb + 2 * Gm::KVB) + (lane / Gm::LPT) * RPT;
     const PGQA_LDS float* vsc = ksc + Gm::TT;
 
+    u32x4 kxs[PF ? RPT : 1], vxs[PF ? RPT : 1];
+    if constexpr (PF) {
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) kxs[r] = kv_slice<ES, D, KES>(kb, r);
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) vxs[r] = kv_slice<ES, D, KES>(vb, r);
+        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the arithmetic
+    }
     float s[RPT][VPL];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-        const u32x4 kx = kv_slice<ES, D, KES>(kb, r);
+        const u32x4 kx = PF ? kxs[PF ? r : 0] : kv_slice<ES, D, KES>(kb, r);
         float v[GW];
 #pragma unroll
         for (int g = 0; g < GW; ++g) v[g] = slice_dot<ES>(qv[g], kx);
@@ -521,8 +532,8 @@ __device__ __forceinline__ void tile_compute(const PGQA_LDS char* tb, const u32x
             }
             u32 pg[GW];
             bcast_heads_u32<Gm::LPT, GW>(pk, pg, lane);
-            u32x4 v0 = kv_slice<ES, D, KES>(vb, r);
-            u32x4 v1 = kv_slice<ES, D, KES>(vb, r + 1);
+            u32x4 v0 = PF ? vxs[PF ? r : 0] : kv_slice<ES, D, KES>(vb, r);
+            u32x4 v1 = PF ? vxs[PF ? r + 1 : 0] : kv_slice<ES, D, KES>(vb, r + 1);
             if (!FULL) {
                 if (!ok0) v0 = u32x4{0, 0, 0, 0};
                 if (!ok1) v1 = u32x4{0, 0, 0, 0};
@@ -551,7 +562,7 @@ __device__ __forceinline__ void tile_compute(const PGQA_LDS char* tb, const u32x
             }
             float pg[GW];
             bcast_heads<Gm::LPT, GW>(p, pg, lane);
-            const u32x4 vx = kv_slice<ES, D, KES>(vb, r);
+            const u32x4 vx = PF ? vxs[PF ? r : 0] : kv_slice<ES, D, KES>(vb, r);
             float vf[EPL];
             unpack16<ES>(vx, vf);
             if (!FULL && (tok0 + r * TPR >= ctx || tok0 + r * TPR < lo)) {
@@ -578,6 +589,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
     using S = Scatter<Gm::LPT, GW>;
     constexpr int EPL = Gm::EPL, LPT = Gm::LPT, TT = Gm::TT, VPL = S::VPL;
     constexpr int G = GW * W;
+    constexpr bool kPF = W <= 4 && D >= 32;   // read a tile's K/V slices up front
     // Loads per tile: NL, wave w issues loads li with li % W == w.
     constexpr int LPW_MAX = (Gm::NL + W - 1) / W;
 
@@ -699,21 +711,21 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         int it0 = 0;
         if (n > 1 && tf * TT < lo) {
             const PGQA_LDS char* kb = step(0);
-            tile_compute<false, ES, D, GW, KES>(kb, qv, m, l, o, tf * TT + tg, ctx, lo, cs, lane);
+            tile_compute<false, ES, D, GW, KES, kPF>(kb, qv, m, l, o, tf * TT + tg, ctx, lo, cs, lane);
             it0 = 1;
         }
         for (int it = it0; it < n - 1; ++it) {
             const PGQA_LDS char* kb = step(it);
-            tile_compute<true, ES, D, GW, KES>(kb, qv, m, l, o, (tf + it) * TT + tg, ctx, lo, cs, lane);
+            tile_compute<true, ES, D, GW, KES, kPF>(kb, qv, m, l, o, (tf + it) * TT + tg, ctx, lo, cs, lane);
         }
         {
             const int it = n - 1;
             const PGQA_LDS char* kb = step(it);
             const int tile = tf + it;
             if (tile * TT >= lo && (tile + 1) * TT <= ctx)
-                tile_compute<true, ES, D, GW, KES>(kb, qv, m, l, o, tile * TT + tg, ctx, lo, cs, lane);
+                tile_compute<true, ES, D, GW, KES, kPF>(kb, qv, m, l, o, tile * TT + tg, ctx, lo, cs, lane);
             else
-                tile_compute<false, ES, D, GW, KES>(kb, qv, m, l, o, tile * TT + tg, ctx, lo, cs, lane);
+                tile_compute<false, ES, D, GW, KES, kPF>(kb, qv, m, l, o, tile * TT + tg, ctx, lo, cs, lane);
         }
 
         // ---- per-head (m, l) to every lane, then merge the TPR token groups ----
