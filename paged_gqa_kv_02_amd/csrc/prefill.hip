@@ -77,6 +77,7 @@ struct PrefillArgs {
     int32_t batch;
     int32_t nqt;             // query-tile levels (tiles of the longest sequence)
     int32_t pairs_per_xcd;   // ceil(batch * num_kv_heads / 8)
+    int32_t dense;           // 1: each XCD's list holds only existing query tiles (pairs_per_xcd <= 64)
     // Paged K/V only (k, v are then the pools [num_blocks, Hkv, block_size, d]).
     const int32_t* block_table;
     const int32_t* context_lens;
@@ -302,10 +303,41 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // is that of one or two pairs, which its L2 holds), and a pair's tiles
     // heaviest-first (query tiles from the last), the head groups sharing the
     // pair's K/V side by side.
+    //
+    // Dense lists (up to 64 pairs per XCD): XCD x's list holds, pair after
+    // pair, only the query tiles that exist (ceil(Lq / rows) per pair, found by
+    // a wave-wide scan of the pairs' lengths), so no workgroup is launched for
+    // the tiles short sequences lack.  Otherwise every pair gets nqt levels
+    // (the longest sequence's tile count) and levels past a sequence's end exit.
     const int id = blockIdx.x;
-    const int per_pair = a.nqt * groups * a.nchunk;
-    const int kq = (id >> 3) / per_pair;                 // the XCD's kq-th pair
-    const int r3 = (id >> 3) - kq * per_pair;
+    const int per_tile = groups * a.nchunk;
+    int kq, r3, ntiles;
+    if (a.dense) {
+        const int j = id >> 3;
+        const int p = (id & 7) + 8 * lane;
+        int nt = 0;
+        if (lane < a.pairs_per_xcd && p < a.batch * a.num_kv_heads) {
+            const int sq = p / a.num_kv_heads;
+            const int b0 = clampi(a.cu_seqlens[sq], 0, a.total_tokens);
+            nt = (clampi(a.cu_seqlens[sq + 1], b0, a.total_tokens) - b0 + TB * BQ - 1) / (TB * BQ);
+        }
+        int pre = nt * per_tile;                          // inclusive scan of the list lengths
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(pre, off);
+            if (lane >= off) pre += y;
+        }
+        // Pairs whose list ends at or before j come first (pre is non-decreasing).
+        kq = __builtin_amdgcn_readfirstlane(__popcll(__ballot(pre <= j)));
+        if (kq >= a.pairs_per_xcd) return;
+        r3 = j - (kq > 0 ? __builtin_amdgcn_readfirstlane(__shfl(pre, kq - 1)) : 0);
+        ntiles = __builtin_amdgcn_readfirstlane(__shfl(nt, kq));
+    } else {
+        const int per_pair = a.nqt * per_tile;
+        kq = (id >> 3) / per_pair;                       // the XCD's kq-th pair
+        r3 = (id >> 3) - kq * per_pair;
+        ntiles = a.nqt;
+    }
     const int r2 = r3 / a.nchunk;
     const int chunk = r3 - r2 * a.nchunk;                // key chunk (0 without a split)
     const int level = r2 / groups;
@@ -324,7 +356,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int Lq = __builtin_amdgcn_readfirstlane(clampi(a.cu_seqlens[s + 1], seq0, a.total_tokens)) - seq0;
     const int Lk = PAGED ? __builtin_amdgcn_readfirstlane(clampi(a.context_lens[s], 0, a.ctx_cap)) : Lq;
     const int koff = PAGED ? Lk - Lq : 0;
-    const int qtile = a.nqt - 1 - level;
+    const int qtile = ntiles - 1 - level;
     const int tok0 = qtile * TB * BQ;
     if (tok0 >= Lq) return;
     // Chunks past the sequence's keys do not exist (chunk 0 always does).
@@ -729,8 +761,21 @@ int64_t grid_size(const PrefillArgs& a, int hg, int group) {
     return 8 * (int64_t)a.nqt * a.pairs_per_xcd * (group / hg) * a.nchunk;
 }
 
+// Launched grid: with dense lists, 8 x the longest XCD list, bounded by the
+// rows: an XCD holds at most ceil(Hkv / 8) pairs of any one sequence, so its
+// list has at most ceil(Hkv/8) * T / rows + pairs_per_xcd tiles per head group
+// and chunk (T = packed query rows).  Workgroups past their XCD's list exit.
+int64_t launch_grid(PrefillArgs& a, int hg, int group, int64_t total_rows) {
+    const int rows_per_wg = (4 / hg) * BQ;
+    a.dense = a.pairs_per_xcd <= 64 ? 1 : 0;
+    if (!a.dense) return grid_size(a, hg, group);
+    const int64_t per_kv = ((int64_t)a.num_kv_heads + 7) / 8;
+    const int64_t tiles = min((int64_t)a.nqt * a.pairs_per_xcd, per_kv * total_rows / rows_per_wg + a.pairs_per_xcd);
+    return 8 * tiles * (group / hg) * a.nchunk;
+}
+
 hipError_t launch(PrefillFn fn, PrefillArgs& a, int hg, int group, int head_dim, hipStream_t stream) {
-    const int64_t wgs = grid_size(a, hg, group);
+    const int64_t wgs = launch_grid(a, hg, group, a.total_tokens);
     if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(256), lds_bytes(head_dim), stream, a);
     return hipGetLastError();
