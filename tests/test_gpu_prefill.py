@@ -80,3 +80,20 @@ def test_decode_equals_last_prefill_row(orc):
     ref = orc.gqa_varlen_prefill(p.q, p.k, p.v, p.cu_seqlens, p.scale, rows=last.astype(np.int32))
     assert_close(dec, ref, W.BF16, "decode of last rows")
     assert_close(pre[last], ref, W.BF16, "prefill last rows")
+
+
+@pytest.mark.parametrize("batch", [64, 65])
+def test_tile_list_boundary(orc, batch):
+    """64 (sequence, KV head) pairs per XCD is the largest batch whose query tiles are
+    listed densely per XCD (a wave-wide scan of the pairs' lengths); 65 falls back to
+    one level per query tile of the longest sequence.  Ragged, empty and one-row
+    sequences on both sides of that boundary."""
+    rng = np.random.default_rng(batch)
+    lens = rng.integers(0, 200, size=batch)
+    lens[::7] = 0
+    lens[3::11] = 1
+    p = W.make_prefill_case(lens.tolist(), 16, 8, 64, 16, W.BF16, seed=batch)
+    say(f"prefill tile-list boundary B={batch}")
+    out = to_f64(_gpu_prefill(p))
+    ref = orc.gqa_varlen_prefill(p.q, p.k, p.v, p.cu_seqlens, p.scale)
+    assert_close(out, ref, W.BF16, f"tile-list boundary B={batch}")
