@@ -56,13 +56,15 @@
 #include "launch.hpp"
 
 #include <math.h>
+
+#include <algorithm>
 #include <mutex>
 
 #ifndef PGQA_DECODE_STAGES
 #define PGQA_DECODE_STAGES 2
 #endif
 #ifndef PGQA_DECODE_RPT
-#define PGQA_DECODE_RPT 8
+#define PGQA_DECODE_RPT 4
 #endif
 #ifndef PGQA_DECODE_RPT8
 #define PGQA_DECODE_RPT8 16
@@ -949,6 +951,19 @@ int occupancy(SplitFn fn, int threads, size_t lds) {
     return occ;
 }
 
+// LDS bytes per CU (cached).
+size_t lds_per_cu() {
+    static size_t bytes = 0;
+    if (bytes == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess || n < 1)
+            n = 160 * 1024;
+        bytes = (size_t)n;
+    }
+    return bytes;
+}
+
 int cu_count() {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -1004,7 +1019,12 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
 
     const int threads = 64 * e.waves;
     // ring + tile prefix sums [batch + 1]
-    const size_t lds = (size_t)kStages * e.tile_bytes + (((size_t)L.batch + 1) * 4 + 15) / 16 * 16;
+    size_t lds = (size_t)kStages * e.tile_bytes + (((size_t)L.batch + 1) * 4 + 15) / 16 * 16;
+    // One-wave workgroups: ask for a quarter of the CU's LDS so that exactly one
+    // runs per SIMD.  More of them (a second wave on some SIMDs) leave those
+    // SIMDs twice as long on the same shares: measured 5 per CU at 177 us
+    // against 122 us for 4 on the Llama-3-8B-shaped batch.
+    if (e.waves == 1) lds = std::max(lds, lds_per_cu() / 4);
     int nw = L.num_splits;
     if (nw <= 0) {
         nw = occupancy(e.split, threads, lds) * cu_count();
