@@ -312,14 +312,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int id = blockIdx.x;
     const int per_tile = groups * a.nchunk;
     int kq, r3, ntiles;
+    int d_seq0 = 0, d_lq = 0, d_lk = 0;   // the chosen pair's rows and keys, from the scan's loads
     if (a.dense) {
         const int j = id >> 3;
         const int p = (id & 7) + 8 * lane;
-        int nt = 0;
+        int nt = 0, b0 = 0, lq = 0, lk = 0;
         if (lane < a.pairs_per_xcd && p < a.batch * a.num_kv_heads) {
             const int sq = p / a.num_kv_heads;
-            const int b0 = clampi(a.cu_seqlens[sq], 0, a.total_tokens);
-            nt = (clampi(a.cu_seqlens[sq + 1], b0, a.total_tokens) - b0 + TB * BQ - 1) / (TB * BQ);
+            b0 = clampi(a.cu_seqlens[sq], 0, a.total_tokens);
+            lq = clampi(a.cu_seqlens[sq + 1], b0, a.total_tokens) - b0;
+            if constexpr (PAGED) lk = clampi(a.context_lens[sq], 0, a.ctx_cap);
+            nt = (lq + TB * BQ - 1) / (TB * BQ);
         }
         int pre = nt * per_tile;                          // inclusive scan of the list lengths
 #pragma unroll
@@ -332,6 +335,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         if (kq >= a.pairs_per_xcd) return;
         r3 = j - (kq > 0 ? __builtin_amdgcn_readfirstlane(__shfl(pre, kq - 1)) : 0);
         ntiles = __builtin_amdgcn_readfirstlane(__shfl(nt, kq));
+        d_seq0 = __builtin_amdgcn_readfirstlane(__shfl(b0, kq));
+        d_lq = __builtin_amdgcn_readfirstlane(__shfl(lq, kq));
+        if constexpr (PAGED) d_lk = __builtin_amdgcn_readfirstlane(__shfl(lk, kq));
     } else {
         const int per_pair = a.nqt * per_tile;
         kq = (id >> 3) / per_pair;                       // the XCD's kq-th pair
@@ -352,9 +358,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // when causal, sees keys 0 .. koff + i.
     // (Loaded values count as divergent for the compiler: readfirstlane keeps
     // the sizes, and every branch on them, scalar.)
-    const int seq0 = __builtin_amdgcn_readfirstlane(clampi(a.cu_seqlens[s], 0, a.total_tokens));
-    const int Lq = __builtin_amdgcn_readfirstlane(clampi(a.cu_seqlens[s + 1], seq0, a.total_tokens)) - seq0;
-    const int Lk = PAGED ? __builtin_amdgcn_readfirstlane(clampi(a.context_lens[s], 0, a.ctx_cap)) : Lq;
+    // (With dense lists these come from the scan's loads: no second round trip.)
+    const int seq0 = a.dense ? d_seq0 : __builtin_amdgcn_readfirstlane(clampi(a.cu_seqlens[s], 0, a.total_tokens));
+    const int Lq = a.dense ? d_lq
+                           : __builtin_amdgcn_readfirstlane(clampi(a.cu_seqlens[s + 1], seq0, a.total_tokens)) - seq0;
+    const int Lk = PAGED ? (a.dense ? d_lk : __builtin_amdgcn_readfirstlane(clampi(a.context_lens[s], 0, a.ctx_cap)))
+                         : Lq;
     const int koff = PAGED ? Lk - Lq : 0;
     const int qtile = ntiles - 1 - level;
     const int tok0 = qtile * TB * BQ;
