@@ -1022,8 +1022,10 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     size_t lds = (size_t)kStages * e.tile_bytes + (((size_t)L.batch + 1) * 4 + 15) / 16 * 16;
     // One-wave workgroups: ask for a quarter of the CU's LDS so that exactly one
     // runs per SIMD.  More of them (a second wave on some SIMDs) leave those
-    // SIMDs twice as long on the same shares: measured 5 per CU at 177 us
-    // against 122 us for 4 on the Llama-3-8B-shaped batch.
+    // SIMDs twice as long on the same shares: on the Llama-3-8B-shaped batch,
+    // 5 per CU ran 177 us against 128 us for 4 (32-token tiles), and the
+    // 16-token tiles ran 126-129 us at the 9 per CU their LDS allows against
+    // 122 us at 4.
     if (e.waves == 1) lds = std::max(lds, lds_per_cu() / 4);
     int nw = L.num_splits;
     if (nw <= 0) {
