@@ -67,7 +67,7 @@
 #define PGQA_DECODE_RPT 4
 #endif
 #ifndef PGQA_DECODE_RPT8
-#define PGQA_DECODE_RPT8 16
+#define PGQA_DECODE_RPT8 8
 #endif
 
 namespace pgqa {
@@ -1021,12 +1021,15 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     // ring + tile prefix sums [batch + 1]
     size_t lds = (size_t)kStages * e.tile_bytes + (((size_t)L.batch + 1) * 4 + 15) / 16 * 16;
     // One-wave workgroups: ask for a quarter of the CU's LDS so that exactly one
-    // runs per SIMD.  More of them (a second wave on some SIMDs) leave those
-    // SIMDs twice as long on the same shares: on the Llama-3-8B-shaped batch,
-    // 5 per CU ran 177 us against 128 us for 4 (32-token tiles), and the
-    // 16-token tiles ran 126-129 us at the 9 per CU their LDS allows against
-    // 122 us at 4.
-    if (e.waves == 1) lds = std::max(lds, lds_per_cu() / 4);
+    // runs per SIMD (bf16 / fp32 pages), or an eighth for exactly two (FP8
+    // pages, whose code conversion makes the tile arithmetic the bound, so a
+    // second wave per SIMD hides its latencies).  An uneven count (a second
+    // wave on some SIMDs only) leaves those SIMDs twice as long on the same
+    // shares: on the Llama-3-8B-shaped batch, 5 per CU ran 177 us against
+    // 128 us for 4 (32-token tiles), the 16-token tiles 126-129 us at the 9 per
+    // CU their LDS allows against 122 us at 4, and FP8 pages 78-86 us at 8 per
+    // CU (8-row tiles) against 87-93 us at 4 (16-row tiles).
+    if (e.waves == 1) lds = std::max(lds, lds_per_cu() / (L.k_scale ? 8 : 4));
     int nw = L.num_splits;
     if (nw <= 0) {
         nw = occupancy(e.split, threads, lds) * cu_count();
