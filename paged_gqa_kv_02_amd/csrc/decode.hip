@@ -66,6 +66,9 @@
 #ifndef PGQA_DECODE_RPT
 #define PGQA_DECODE_RPT 4
 #endif
+#ifndef PGQA_MQA_CHUNK
+#define PGQA_MQA_CHUNK 16  // 64-key blocks per key chunk on the matrix-core MQA route
+#endif
 #ifndef PGQA_DECODE_RPT8
 #define PGQA_DECODE_RPT8 8
 #endif
@@ -997,6 +1000,44 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     Entry e;
     if (L.k_scale ? !pick_fp8(L.head_dim, group, &e) : !pick(es, L.head_dim, group, &e)) return hipErrorInvalidValue;
     if (L.batch == 0) return hipSuccess;
+
+    // Many query heads on one KV head (MQA, G a multiple of 32): the G heads of a
+    // token are the 32-row tiles of the matrix-core kernel.  q [B, G, d] is read
+    // as B sequences of G rows with one head (the same bytes), every row seeing
+    // all keys [0, ctx) of the sequence's pages; the kernel's key split spreads
+    // the long contexts.  At ~32 FLOP per K/V byte this shape outruns the VALU
+    // dot products of the split kernel (bf16 only; no window; library-chosen
+    // splits, so an explicit split count keeps the split-KV path).
+    if (L.num_kv_heads == 1 && group % 32 == 0 && L.is_bf16 && !L.k_scale && L.window == 0 && L.num_splits == 0 &&
+        (L.head_dim == 64 || L.head_dim == 128) && extend_supported(L.head_dim, 1, 1 << L.block_size_log2) &&
+        (int64_t)L.batch * group <= 0x7fffffff) {
+        ExtendLaunch x{};
+        x.q = L.q;
+        x.k_cache = L.k_cache;
+        x.v_cache = L.v_cache;
+        x.cu_q = nullptr;
+        x.block_table = L.block_table;
+        x.context_lens = L.context_lens;
+        x.out = L.out;
+        x.batch = L.batch;
+        x.total_q = L.batch * group;
+        x.max_q_len = group;
+        x.max_blocks_per_seq = L.max_blocks_per_seq;
+        x.num_q_heads = 1;
+        x.num_kv_heads = 1;
+        x.head_dim = L.head_dim;
+        x.block_size_log2 = L.block_size_log2;
+        x.num_blocks = L.num_blocks;
+        x.max_context_len = L.max_context_len;
+        x.scale = L.scale;
+        x.window = 0;
+        x.workspace = L.workspace;
+        x.workspace_bytes = decode_workspace_bytes(L.batch, L.num_q_heads, L.num_kv_heads, L.head_dim, 0);
+        x.non_causal = 1;
+        x.fixed_qlen = group;
+        x.chunk_blocks = PGQA_MQA_CHUNK;
+        return launch_extend(x, stream);
+    }
 
     DecodeArgs a;
     a.q = (const char*)L.q;

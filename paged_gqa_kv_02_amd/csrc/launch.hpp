@@ -133,6 +133,9 @@ struct ExtendLaunch {
     int32_t window;   // 0: none; > 0: keys p - window + 1 .. p for a row at position p
     void* workspace;  // key-split partials (may be null: no split)
     size_t workspace_bytes;
+    int32_t non_causal;  // 1: every row sees all keys [0, ctx) (rows = query heads of one token)
+    int32_t fixed_qlen;  // > 0: sequence s holds rows [s * fixed_qlen, (s + 1) * fixed_qlen); cu_q unused
+    int32_t chunk_blocks;  // > 0: key chunks of this many 64-key blocks (0: the library's choice)
 };
 
 // Workspace bytes for the library's key split of a paged multi-token call (0: none).

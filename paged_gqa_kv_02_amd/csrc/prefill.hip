@@ -78,6 +78,7 @@ struct PrefillArgs {
     int32_t nqt;             // query-tile levels (tiles of the longest sequence)
     int32_t pairs_per_xcd;   // ceil(batch * num_kv_heads / 8)
     int32_t dense;           // 1: each XCD's list holds only existing query tiles (pairs_per_xcd <= 64)
+    int32_t fixed_qlen;      // > 0: sequence s holds rows [s * fixed_qlen, +fixed_qlen) (cu_seqlens unused)
     // Paged K/V only (k, v are then the pools [num_blocks, Hkv, block_size, d]).
     const int32_t* block_table;
     const int32_t* context_lens;
@@ -319,8 +320,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         int nt = 0, b0 = 0, lq = 0, lk = 0;
         if (lane < a.pairs_per_xcd && p < a.batch * a.num_kv_heads) {
             const int sq = p / a.num_kv_heads;
-            b0 = clampi(a.cu_seqlens[sq], 0, a.total_tokens);
-            lq = clampi(a.cu_seqlens[sq + 1], b0, a.total_tokens) - b0;
+            if (a.fixed_qlen > 0) {
+                b0 = min(sq * a.fixed_qlen, a.total_tokens);
+                lq = min(b0 + a.fixed_qlen, a.total_tokens) - b0;
+            } else {
+                b0 = clampi(a.cu_seqlens[sq], 0, a.total_tokens);
+                lq = clampi(a.cu_seqlens[sq + 1], b0, a.total_tokens) - b0;
+            }
             if constexpr (PAGED) lk = clampi(a.context_lens[sq], 0, a.ctx_cap);
             nt = (lq + TB * BQ - 1) / (TB * BQ);
         }
@@ -359,9 +365,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // (Loaded values count as divergent for the compiler: readfirstlane keeps
     // the sizes, and every branch on them, scalar.)
     // (With dense lists these come from the scan's loads: no second round trip.)
-    const int seq0 = a.dense ? d_seq0 : __builtin_amdgcn_readfirstlane(clampi(a.cu_seqlens[s], 0, a.total_tokens));
+    const int seq0 = a.dense ? d_seq0
+                     : a.fixed_qlen > 0 ? min(s * a.fixed_qlen, a.total_tokens)
+                     : __builtin_amdgcn_readfirstlane(clampi(a.cu_seqlens[s], 0, a.total_tokens));
     const int Lq = a.dense ? d_lq
-                           : __builtin_amdgcn_readfirstlane(clampi(a.cu_seqlens[s + 1], seq0, a.total_tokens)) - seq0;
+                   : a.fixed_qlen > 0 ? min(seq0 + a.fixed_qlen, a.total_tokens) - seq0
+                   : __builtin_amdgcn_readfirstlane(clampi(a.cu_seqlens[s + 1], seq0, a.total_tokens)) - seq0;
     const int Lk = PAGED ? (a.dense ? d_lk : __builtin_amdgcn_readfirstlane(clampi(a.context_lens[s], 0, a.ctx_cap)))
                          : Lq;
     const int koff = PAGED ? Lk - Lq : 0;
@@ -675,10 +684,14 @@ template <int D>
 __global__ __launch_bounds__(256) void extend_merge_kernel(PrefillArgs a) {
     const int row = blockIdx.x;
     int lo = 0, hi = a.batch - 1;                          // the sequence holding the row
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (__builtin_amdgcn_readfirstlane(a.cu_seqlens[mid]) <= row) lo = mid;
-        else hi = mid - 1;
+    if (a.fixed_qlen > 0) {
+        lo = min(row / a.fixed_qlen, hi);
+    } else {
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (__builtin_amdgcn_readfirstlane(a.cu_seqlens[mid]) <= row) lo = mid;
+            else hi = mid - 1;
+        }
     }
     const int Lk = __builtin_amdgcn_readfirstlane(clampi(a.context_lens[lo], 0, a.ctx_cap));
     const int ckeys = a.kchunk * BN;
@@ -843,7 +856,8 @@ hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream) {
     a.total_tokens = L.total_q;
     a.num_q_heads = L.num_q_heads;
     a.num_kv_heads = L.num_kv_heads;
-    a.causal = 1;
+    a.causal = L.non_causal ? 0 : 1;
+    a.fixed_qlen = L.fixed_qlen;
     a.scale_log2 = (float)((double)L.scale * 1.4426950408889634);
     a.batch = L.batch;
     a.block_table = L.block_table;
@@ -857,7 +871,26 @@ hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream) {
     a.nchunk = 1;
     const int64_t per_chunk = (int64_t)L.total_q * L.num_q_heads * (L.head_dim + 2) * 4;
     const int64_t max_chunks = (L.workspace && per_chunk > 0) ? (int64_t)(L.workspace_bytes / per_chunk) : 0;
-    extend_split(grid_size(a, hg, group), L.max_context_len, max_chunks, &a.nchunk, &a.kchunk);
+    a.kchunk = kNoSplit;
+    if (L.chunk_blocks > 0) {
+        // Caller-chosen chunk length (few query rows per sequence: every
+        // workgroup is bound by its ring's one-block-ahead DMA latency, so many
+        // short chunks beat a few long ones), capped by the workspace.
+        const int blocks = (L.max_context_len + BN - 1) / BN;
+        int kc = L.chunk_blocks;
+        int64_t nc = (blocks + kc - 1) / kc;
+        if (nc > max_chunks) {
+            nc = max_chunks > 0 ? max_chunks : 1;
+            kc = (int)((blocks + nc - 1) / nc);
+            nc = (blocks + kc - 1) / kc;
+        }
+        if (nc > 1) {
+            a.nchunk = (int)nc;
+            a.kchunk = kc;
+        }
+    } else {
+        extend_split(grid_size(a, hg, group), L.max_context_len, max_chunks, &a.nchunk, &a.kchunk);
+    }
     a.part_o = (float*)L.workspace;
     a.part_ml = a.part_o + (int64_t)L.total_q * L.num_q_heads * a.nchunk * L.head_dim;
     hipError_t err = launch(fn, a, hg, group, L.head_dim, stream);
