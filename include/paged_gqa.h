@@ -148,6 +148,11 @@ size_t gqa_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads,
  * (0 = library choice, which fills the GPU); the partials of a sequence cut
  * across shares are merged exactly (log-sum-exp, in share order) by a second
  * kernel.  The result is deterministic for a given num_splits.
+ * With one KV head and Hq a multiple of 32 (bf16, head_dim 64 or 128, block_size
+ * >= 8 for d 64 / >= 4 for d 128, window 0, num_splits 0), the call runs on the
+ * matrix cores instead: the Hq query heads of a token are the rows of the MFMA
+ * tile, the keys are cut into chunks of 1024 merged by log-sum-exp (partials in
+ * the same workspace); the result is deterministic as well.
  *   q            [batch, Hq, d]
  *   k_cache, v_cache [num_blocks, Hkv, block_size, d]
  *   block_table  [batch, max_blocks_per_seq]; entries past ceil(ctx/bs) never read
