@@ -139,3 +139,29 @@ def test_workspace_reuse(orc):
         torch.cuda.synchronize()
         assert_close(to_f64(out), ref, W.BF16, f"reuse splits={splits}")
         assert_close(to_f64(out_s), ref_s, W.BF16, f"reuse small splits={splits}")
+
+
+@pytest.mark.parametrize("hq,d,bs", [(32, 128, 16), (32, 64, 8), (64, 128, 4), (32, 128, 256)])
+def test_one_kv_head_matrix_core_route(orc, hq, d, bs):
+    """One KV head and Hq a multiple of 32 run on the matrix cores (query heads as
+    tile rows, keys in chunks of 1024): empty, one-token, page- and chunk-edge and
+    long contexts against the oracle, sharpened queries too, deterministic, and
+    within tolerance of the split-KV kernel (an explicit split count keeps that path)."""
+    lens = [0, 1, bs - 1, bs, bs + 1, 1023, 1024, 1025, 3000, 5000]
+    case = W.make_decode_case(lens, hq, 1, d, bs, W.BF16, seed=hq * 7 + d + bs)
+    say(f"decode one KV head hq={hq} d{d} bs{bs}")
+    dev = DevDecode(case)
+    out = dev.decode()
+    again = dev.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16)), "not deterministic"
+    ref = oracle_decode(orc, case)
+    assert_close(to_f64(out), ref, W.BF16, f"one KV head hq={hq} d{d} bs{bs}")
+    assert not to_f64(out)[0].any(), "empty context must give zeros"
+    split = dev.decode(num_splits=97)
+    torch.cuda.synchronize()
+    assert_close(to_f64(split), ref, W.BF16, "split-KV path")
+    q4 = W.f32_to_bf16_bits(W.bf16_bits_to_f32(case.q) * np.float32(4.0))
+    case.q = q4
+    sharp = to_f64(DevDecode(case).decode())
+    assert_close(sharp, oracle_decode(orc, case), W.BF16, "sharpened")
