@@ -954,17 +954,21 @@ int occupancy(SplitFn fn, int threads, size_t lds) {
     return occ;
 }
 
-// LDS bytes per CU (cached).
+// LDS bytes per CU of the current device (cached per device).
 size_t lds_per_cu() {
-    static size_t bytes = 0;
-    if (bytes == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess || n < 1)
+    static std::mutex mu;
+    static size_t bytes[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    const int slot = dev < 64 ? dev : 63;
+    std::lock_guard<std::mutex> lock(mu);
+    if (bytes[slot] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess || n < 1)
             n = 160 * 1024;
-        bytes = (size_t)n;
+        bytes[slot] = (size_t)n;
     }
-    return bytes;
+    return bytes[slot];
 }
 
 int cu_count() {
