@@ -50,6 +50,7 @@ def _args():
     ap.add_argument("--no-shared", action="store_true", help="skip the shared-prefix decode line item")
     ap.add_argument("--no-window", action="store_true", help="skip the sliding-window decode line item")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-page decode line item")
+    ap.add_argument("--no-mqa", action="store_true", help="skip the one-KV-head (MQA) decode line item")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle timing budget")
     ap.add_argument("--decode-workload", default="llama3_8b_decode",
                     choices=["llama3_8b_decode", "long_ctx_decode", "mqa_decode", "tiny_f32"],
@@ -523,6 +524,61 @@ def fp8_leg(args, torch, pg, W, T):
     }
 
 
+def mqa_leg(args, torch, pg, W, T):
+    """MQA decode (B = 256, lognormal contexts, 32 query heads on one KV head,
+    bs 32).  With one KV head and a group of 32 the library routes the call to
+    the matrix-core multi-token kernel (the query heads form the rows of the
+    32-row MFMA tile, contexts cut into key chunks merged afterwards); the VALU
+    split kernel on the same pools (forced by an explicit 1,024-share split) is
+    timed beside it.  Calls rotate over COPIES pools so that the K/V (~180 MB per
+    copy) is not served from the last call's cache.  Bytes = the K/V read."""
+    case = W.make_workload("mqa_decode")
+    B, hq, hkv, d, bs = case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size
+    table, ctx = T.to_dev(case.block_table), T.to_dev(case.context_lens)
+    k_all, v_all = T.to_dev(case.k), T.to_dev(case.v)
+    cu_all, sp0 = T.to_dev(case.cu_ctx), T.to_dev(case.start_pos)
+    pools = []
+    for _ in range(COPIES):
+        kc = T.nan_pool_dev(case.num_blocks, hkv, bs, d, case.dtype)
+        vc = T.nan_pool_dev(case.num_blocks, hkv, bs, d, case.dtype)
+        pg.paged_kv_write(k_all, v_all, cu_all, sp0, table, kc, vc)
+        pools.append((kc, vc))
+    del k_all, v_all
+    q = T.to_dev(case.q)
+    out = torch.empty_like(q)
+    ws = pg.decode_workspace(B, hq, hkv, d, 0, q.device)
+    scale, maxctx = float(case.scale), case.max_context_len
+
+    def run(splits):
+        def f(i):
+            kc, vc = pools[i % COPIES]
+            pg.gqa_paged_decode(q, kc, vc, table, ctx, maxctx, scale=scale, out=out, workspace=ws,
+                                num_splits=splits)
+        for i in range(5):
+            f(i)
+        torch.cuda.synchronize()
+        n = max(20, args.steps // 2)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            evs[i][0].record()
+            f(i)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]) * 1e3)
+
+    us, us_split = run(0), run(1024)
+    kvb = case.kv_bytes()
+    gbs = kvb / (us * 1e-6) / 1e9
+    return {
+        "workload": "mqa_decode", "batch": B, "num_q_heads": hq, "num_kv_heads": hkv, "block_size": bs,
+        "kv_bytes_per_call": kvb, "route": "matrix-core multi-token kernel (query heads as MFMA tile rows)",
+        "decode_us_mean": us, "kv_gbs": gbs, "split_kernel_us_mean": us_split,
+        "speedup_vs_split_kernel": round(us_split / us, 3),
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None},
+    }
+
+
 def cpu_baseline(args, case, W):
     """The fp64 oracle, as it stands, on the same decode step (write + decode),
     repeated until at least --cpu-seconds of host time have been spent."""
@@ -627,6 +683,9 @@ def main():
     if not args.no_shared:
         log("shared prefix leg")
         line["shared_prefix"] = shared_prefix_leg(args, torch, pg, W, T)
+    if not args.no_mqa:
+        log("mqa decode leg")
+        line["mqa"] = mqa_leg(args, torch, pg, W, T)
     if not args.no_cpu_baseline:
         log("cpu baseline leg (oracle)")
         ref, cb = cpu_baseline(args, case, W)
