@@ -676,13 +676,29 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
 }
 
-// Merge of the key-chunk partials of split sequences: one workgroup per query
-// row (its sequence found once), each thread a set of (head, dim) outputs; the
-// log-sum-exp of the chunks in chunk order (deterministic).  Rows of sequences
-// that fit one chunk were written by the attention kernel.
+// Merge of the key-chunk partials of split sequences: a query row's Hq x D
+// outputs go to one thread each, a 256-thread workgroup taking 256 / (Hq x D)
+// rows when a row has fewer outputs than that (one wave or more per row, so
+// each wave belongs to one row and finds its sequence once), else one row and a
+// loop over its outputs.  Log-sum-exp of the chunks in chunk order with a
+// running maximum (deterministic; the loads of successive chunks do not wait on
+// one another).  A chunk in which a row sees no key holds m = -1e30 (finite),
+// l = 0, O = 0 and so adds nothing.  Rows of sequences that fit one chunk were
+// written by the attention kernel.
+template <int D>
+int merge_rows_per_wg(int num_q_heads) {
+    const int per = num_q_heads * D;
+    return per >= 256 ? 1 : 256 / per;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void extend_merge_kernel(PrefillArgs a) {
-    const int row = blockIdx.x;
+    const int per = a.num_q_heads * D;
+    const int rpw = per >= 256 ? 1 : 256 / per;
+    const int sub = rpw > 1 ? (int)threadIdx.x / per : 0;
+    if (sub >= rpw) return;                                 // threads past the last whole row
+    const int row = (int)blockIdx.x * rpw + sub;
+    if (row >= a.total_tokens) return;
     int lo = 0, hi = a.batch - 1;                          // the sequence holding the row
     if (a.fixed_qlen > 0) {
         lo = min(row / a.fixed_qlen, hi);
@@ -697,17 +713,23 @@ __global__ __launch_bounds__(256) void extend_merge_kernel(PrefillArgs a) {
     const int ckeys = a.kchunk * BN;
     const int nc = Lk > ckeys ? (Lk + ckeys - 1) / ckeys : 1;
     if (nc <= 1) return;
-    for (int e = threadIdx.x; e < a.num_q_heads * D; e += 256) {
+    const int e0 = rpw > 1 ? (int)threadIdx.x - sub * per : (int)threadIdx.x;
+    for (int e = e0; e < per; e += 256) {
         const int64_t rh = (int64_t)row * a.num_q_heads + e / D;
         const float* ml = a.part_ml + rh * a.nchunk * 2;
         const float* po = a.part_o + rh * a.nchunk * D + e % D;
-        float M = -INFINITY;
-        for (int c = 0; c < nc; ++c) M = fmaxf(M, ml[2 * c]);
-        float acc = 0.0f, L = 0.0f;
+        float M = -INFINITY, acc = 0.0f, L = 0.0f;
+#pragma unroll 4
         for (int c = 0; c < nc; ++c) {
-            const float w = __builtin_amdgcn_exp2f(ml[2 * c] - M);
-            acc = fmaf(w, po[(int64_t)c * D], acc);
-            L = fmaf(w, ml[2 * c + 1], L);
+            const float mc = ml[2 * c];
+            const float lc = ml[2 * c + 1];
+            const float oc = po[(int64_t)c * D];
+            const float mn = fmaxf(M, mc);
+            const float sa = __builtin_amdgcn_exp2f(M - mn);
+            const float sb = __builtin_amdgcn_exp2f(mc - mn);
+            acc = acc * sa + oc * sb;
+            L = L * sa + lc * sb;
+            M = mn;
         }
         const float r = L > 0.0f ? acc / L : 0.0f;
         *(uint16_t*)(a.out + (rh * D + e % D) * 2) = (uint16_t)f32_to_bf16_bits(r);
@@ -895,10 +917,15 @@ hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream) {
     a.part_ml = a.part_o + (int64_t)L.total_q * L.num_q_heads * a.nchunk * L.head_dim;
     hipError_t err = launch(fn, a, hg, group, L.head_dim, stream);
     if (err != hipSuccess || a.nchunk == 1) return err;
-    if (L.head_dim == 128)
-        hipLaunchKernelGGL(extend_merge_kernel<128>, dim3((unsigned)L.total_q), dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL(extend_merge_kernel<64>, dim3((unsigned)L.total_q), dim3(256), 0, stream, a);
+    if (L.head_dim == 128) {
+        const int rpw = merge_rows_per_wg<128>(L.num_q_heads);
+        hipLaunchKernelGGL(extend_merge_kernel<128>, dim3((unsigned)((L.total_q + rpw - 1) / rpw)), dim3(256), 0,
+                           stream, a);
+    } else {
+        const int rpw = merge_rows_per_wg<64>(L.num_q_heads);
+        hipLaunchKernelGGL(extend_merge_kernel<64>, dim3((unsigned)((L.total_q + rpw - 1) / rpw)), dim3(256), 0,
+                           stream, a);
+    }
     return hipGetLastError();
 }
 
