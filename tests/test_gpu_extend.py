@@ -176,6 +176,22 @@ def test_key_split(orc, q_len, window, hq, hkv):
     assert_close(to_f64(plain), ref, W.BF16, "no split")
 
 
+@pytest.mark.parametrize("q_len", [3, 37])
+@pytest.mark.parametrize("hq,hkv,d", [(1, 1, 128), (1, 1, 64), (2, 1, 64), (2, 2, 64)])
+def test_key_split_short_rows(orc, q_len, hq, hkv, d):
+    """Key split where a query row has 64 or 128 outputs (Hq x d), so one merge
+    workgroup takes 2 or 4 rows; odd query lengths make those rows belong to
+    different sequences."""
+    prefix = [3000, 17, 1024 - q_len, 1025 - q_len, 2048, 4000, 64, 2500, 0, 7000]
+    c = W.make_extend_case(prefix, [q_len] * len(prefix), hq, hkv, d, 16, W.BF16, seed=970 + q_len + hq + d)
+    n = pg.gqa_paged_extend_workspace_size(c.batch, c.total_q, c.max_q_len, hq, hkv, d, c.max_context_len)
+    assert n > 0, "this shape is meant to split"
+    say(f"extend key split, short rows: q_len={q_len} {hq}/{hkv} d={d}")
+    dev = DevExtend(c)
+    out = to_f64(dev.extend())
+    assert_close(out, oracle_extend(orc, c), W.BF16, f"short rows {hq}/{hkv} d{d}")
+
+
 def test_key_split_is_deterministic():
     c = W.make_extend_case([32000, 9000, 20000, 100], [4] * 4, 64, 8, 128, 16, W.BF16, seed=950)
     assert pg.gqa_paged_extend_workspace_size(c.batch, c.total_q, c.max_q_len, 64, 8, 128, c.max_context_len) > 0
