@@ -610,7 +610,7 @@ def cpu_baseline(args, case, W):
 def main():
     args = _args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         return 2
     here = os.path.dirname(os.path.abspath(__file__))
