@@ -79,6 +79,7 @@ struct PrefillArgs {
     int32_t pairs_per_xcd;   // ceil(batch * num_kv_heads / 8)
     int32_t dense;           // 1: each XCD's list holds only existing query tiles (pairs_per_xcd <= 64)
     int32_t fixed_qlen;      // > 0: sequence s holds rows [s * fixed_qlen, +fixed_qlen) (cu_seqlens unused)
+    int32_t chunk_lpt;       // 1: dense lists of key chunks, full chunks first (one query tile and head group per pair)
     // Paged K/V only (k, v are then the pools [num_blocks, Hkv, block_size, d]).
     const int32_t* block_table;
     const int32_t* context_lens;
@@ -330,16 +331,47 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
             if constexpr (PAGED) lk = clampi(a.context_lens[sq], 0, a.ctx_cap);
             nt = (lq + TB * BQ - 1) / (TB * BQ);
         }
-        int pre = nt * per_tile;                          // inclusive scan of the list lengths
+        if (a.chunk_lpt) {
+            // Key chunks longest first: every pair's full chunks (pair after
+            // pair), then every pair's last, shorter chunk.  A batch whose chunks
+            // outnumber the workgroup slots then leaves short chunks, not full
+            // ones, for the second round.  Only the chunks that exist are listed
+            // (a pair with no keys keeps one chunk, which writes its zero rows).
+            const int ck = a.kchunk * BN;
+            const int fa = nt > 0 ? lk / ck : 0;
+            const int tb = (nt > 0 && (lk == 0 || lk % ck != 0)) ? 1 : 0;
+            int pa = fa, pb = tb;                        // inclusive scans
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(pre, off);
-            if (lane >= off) pre += y;
+            for (int off = 1; off < 64; off <<= 1) {
+                const int ya = __shfl_up(pa, off);
+                const int yb = __shfl_up(pb, off);
+                if (lane >= off) {
+                    pa += ya;
+                    pb += yb;
+                }
+            }
+            const int tot_a = __builtin_amdgcn_readfirstlane(__shfl(pa, 63));
+            if (j < tot_a) {
+                kq = __builtin_amdgcn_readfirstlane(__popcll(__ballot(pa <= j)));
+                if (kq >= a.pairs_per_xcd) return;
+                r3 = j - (kq > 0 ? __builtin_amdgcn_readfirstlane(__shfl(pa, kq - 1)) : 0);
+            } else {
+                kq = __builtin_amdgcn_readfirstlane(__popcll(__ballot(pb <= j - tot_a)));
+                if (kq >= a.pairs_per_xcd) return;
+                r3 = __builtin_amdgcn_readfirstlane(__shfl(fa, kq));   // the last chunk's index
+            }
+        } else {
+            int pre = nt * per_tile;                      // inclusive scan of the list lengths
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(pre, off);
+                if (lane >= off) pre += y;
+            }
+            // Pairs whose list ends at or before j come first (pre is non-decreasing).
+            kq = __builtin_amdgcn_readfirstlane(__popcll(__ballot(pre <= j)));
+            if (kq >= a.pairs_per_xcd) return;
+            r3 = j - (kq > 0 ? __builtin_amdgcn_readfirstlane(__shfl(pre, kq - 1)) : 0);
         }
-        // Pairs whose list ends at or before j come first (pre is non-decreasing).
-        kq = __builtin_amdgcn_readfirstlane(__popcll(__ballot(pre <= j)));
-        if (kq >= a.pairs_per_xcd) return;
-        r3 = j - (kq > 0 ? __builtin_amdgcn_readfirstlane(__shfl(pre, kq - 1)) : 0);
         ntiles = __builtin_amdgcn_readfirstlane(__shfl(nt, kq));
         d_seq0 = __builtin_amdgcn_readfirstlane(__shfl(b0, kq));
         d_lq = __builtin_amdgcn_readfirstlane(__shfl(lq, kq));
@@ -909,6 +941,9 @@ hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream) {
         if (nc > 1) {
             a.nchunk = (int)nc;
             a.kchunk = kc;
+            // One query tile and one head group per pair: list the chunks
+            // longest first (the kernel does so with dense lists).
+            a.chunk_lpt = (L.fixed_qlen > 0 && group == hg && a.nqt == 1) ? 1 : 0;
         }
     } else {
         extend_split(grid_size(a, hg, group), L.max_context_len, max_chunks, &a.nchunk, &a.kchunk);
