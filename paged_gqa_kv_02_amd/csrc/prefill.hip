@@ -941,13 +941,13 @@ hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream) {
         if (nc > 1) {
             a.nchunk = (int)nc;
             a.kchunk = kc;
-            // One query tile and one head group per pair: list the chunks
-            // longest first (the kernel does so with dense lists).
-            a.chunk_lpt = (L.fixed_qlen > 0 && group == hg && a.nqt == 1) ? 1 : 0;
         }
     } else {
         extend_split(grid_size(a, hg, group), L.max_context_len, max_chunks, &a.nchunk, &a.kchunk);
     }
+    // One query tile and one head group per pair: list the key chunks longest
+    // first (the kernel does so with dense lists).
+    a.chunk_lpt = (a.nchunk > 1 && group == hg && a.nqt == 1) ? 1 : 0;
     a.part_o = (float*)L.workspace;
     a.part_ml = a.part_o + (int64_t)L.total_q * L.num_q_heads * a.nchunk * L.head_dim;
     hipError_t err = launch(fn, a, hg, group, L.head_dim, stream);
