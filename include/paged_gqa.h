@@ -36,8 +36,13 @@
  * Conventions shared by every call (the pgqa_bm_* block manager below is
  * host-only and documented on its own)
  *   - Every array argument is a DEVICE pointer owned by the caller; the
- *     library never allocates, frees or keeps device memory, never
- *     synchronises, and keeps no state between calls (thread-safe).
+ *     library never allocates, frees or keeps device memory and never
+ *     synchronises.  Its only state between calls is a per-device cache of
+ *     launch facts read from the HIP runtime (compute units, LDS per compute
+ *     unit, kernel occupancy), guarded by a lock, so the calls are thread-safe.
+ *   - `scale` (the attention calls) may be any finite float: the result is
+ *     softmax(scale * q.k) for that value, a zero scale giving every visible
+ *     key the same weight.  NaN or infinite scales are PGQA_EINVAL.
  *   - Element arrays hold PGQA_F32 (float) or PGQA_BF16 (bfloat16 bit
  *     patterns, 2 bytes each); out has the dtype of q.  Index arrays are int32.
  *   - Element pointers and the workspace must be 16-byte aligned.
@@ -159,7 +164,7 @@ size_t gqa_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads,
  *   context_lens [batch]
  *   max_context_len  host-side upper bound of context_lens;
  *                    must be <= max_blocks_per_seq * block_size
- *   scale        softmax scale, normally 1/sqrt(head_dim)
+ *   scale        softmax scale, normally 1/sqrt(head_dim); any finite value
  *   window       0, or > 0 for local attention: only positions
  *                [ctx - window, ctx) are attended to (see "Local attention" above);
  *                tiles wholly before the window are not read

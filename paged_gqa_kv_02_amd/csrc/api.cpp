@@ -113,19 +113,20 @@ size_t gqa_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32
     return pgqa::decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, num_splits);
 }
 
-int gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
-                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
-                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                     int32_t max_context_len, float scale, int32_t window, pgqa_dtype dtype, void* out,
-                     int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+// Host-side checks of gqa_paged_decode's arguments other than the workspace;
+// block_size's log2 in *lg.
+static int check_decode_args(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t max_context_len, float scale, int32_t window,
+                             pgqa_dtype dtype, const void* out, int32_t num_splits, int32_t* lg) {
     if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
         max_context_len < 0 || num_splits < 0 || window < 0)
         return PGQA_EINVAL;
     if (num_q_heads % num_kv_heads) return PGQA_EINVAL;
     const int es = elem_bytes(dtype);
     if (es == 0 || !head_dim_ok(head_dim)) return PGQA_ENOTSUP;
-    int32_t lg = 0;
-    if (!pow2_log2(block_size, &lg) || block_size > 256) return PGQA_ENOTSUP;
+    if (!pow2_log2(block_size, lg) || block_size > 256) return PGQA_ENOTSUP;
     if (!pgqa::decode_supported(es, head_dim, num_q_heads / num_kv_heads)) return PGQA_ENOTSUP;
     if (batch > kMaxDecodeBatch) return PGQA_ENOTSUP;
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PGQA_EINVAL;
@@ -135,6 +136,19 @@ int gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache, co
     if (check_elem_ptr(q) || check_elem_ptr(k_cache) || check_elem_ptr(v_cache) || check_elem_ptr(out))
         return PGQA_EINVAL;
     if (check_index_ptr(block_table) || check_index_ptr(context_lens)) return PGQA_EINVAL;
+    return PGQA_OK;
+}
+
+int gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                     int32_t max_context_len, float scale, int32_t window, pgqa_dtype dtype, void* out,
+                     int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+    int32_t lg = 0;
+    const int rc = check_decode_args(q, k_cache, v_cache, block_table, max_blocks_per_seq, context_lens, batch,
+                                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len,
+                                     scale, window, dtype, out, num_splits, &lg);
+    if (rc != PGQA_OK) return rc;
     if (batch == 0) return PGQA_OK;
     const size_t need = gqa_paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, num_splits);
     if (!workspace || !aligned(workspace, 16)) return workspace_bytes < need ? PGQA_ENOSPC : PGQA_EINVAL;

@@ -37,7 +37,10 @@
 //    lane instead of 4).  The weights are then broadcast back across the row
 //    (DPP row_newbcast) for the P.V accumulation in fp32.
 //  * Online softmax in log2 units with the scale folded into the exponent,
-//    p = exp2(s * scale*log2e - m), and a lazy rescale: o and l are rescaled
+//    p = exp2(s * scale*log2e - m) (a negative or zero scale is applied as the
+//    sign of the query bits, so the folded factor is always positive), each
+//    weight rounded to bf16 once and the same rounded weight added to the sum
+//    and used in P.V (bf16 pages), and a lazy rescale: o and l are rescaled
 //    only when a running max grows by more than 8, which keeps every weight
 //    <= 256 and is exact because the final o / l uses the same reference max.
 //  * Masking selects (never multiplies) and only on the ragged last tile of a
@@ -94,7 +97,9 @@ struct DecodeArgs {
     int32_t bs_log2;
     int32_t ctx_cap;     // max_context_len: device context lengths are clamped to it
     int32_t num_splits;  // requested shares == gridDim.x of the split kernel
-    float scale_log2;    // scale * log2(e): scores live in log2 units, weights use exp2
+    float scale_log2;    // |scale| * log2(e): scores live in log2 units, weights use exp2
+    u32 q_and;           // the scale's sign, applied to the query bits as they are loaded
+    u32 q_xor;
     int32_t window;      // > 0: only the newest `window` positions are attended to
     const float* k_scale;   // FP8 pages: row scales [num_blocks, Hkv, block_size]
     const float* v_scale;
@@ -531,9 +536,14 @@ __device__ __forceinline__ void tile_compute(const PGQA_LDS char* tb, const u32x
             for (int k = 0; k < VPL; ++k) {
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r][k], c, -m[k]));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1][k], c, -m[k]));
-                l[k] += p0 + p1;
-                if constexpr (Q8) pk[k] = pack_bf16x2_rne_hw(p0 * vs0, p1 * vs1);
-                else pk[k] = pack_bf16x2_rne_hw(p0, p1);
+                if constexpr (Q8) {
+                    l[k] += p0 + p1;
+                    pk[k] = pack_bf16x2_rne_hw(p0 * vs0, p1 * vs1);
+                } else {
+                    // The sum adds the bf16-rounded weights, exactly the ones P.V uses.
+                    pk[k] = pack_bf16x2_rne_hw(p0, p1);
+                    l[k] = dot2_bf16(pk[k], 0x3F803F80u, l[k]);
+                }
             }
             u32 pg[GW];
             bcast_heads_u32<Gm::LPT, GW>(pk, pg, lane);
@@ -681,7 +691,8 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         u32x4 qv[GW];
 #pragma unroll
         for (int g = 0; g < GW; ++g)
-            qv[g] = *(const u32x4*)(a.q + ((int64_t)(b * a.num_q_heads + qh0 + g) * D + c * EPL) * ES);
+            qv[g] = (*(const u32x4*)(a.q + ((int64_t)(b * a.num_q_heads + qh0 + g) * D + c * EPL) * ES) & a.q_and) ^
+                    a.q_xor;
 
         // Running max / sum of the heads this lane owns; o for all GW heads.
         float m[VPL], l[VPL], o[GW][EPL];
@@ -1057,7 +1068,10 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     a.num_blocks = L.num_blocks;
     a.bs_log2 = L.block_size_log2;
     a.ctx_cap = L.max_context_len;
-    a.scale_log2 = (float)((double)L.scale * 1.4426950408889634);
+    const ScaleFold sf = fold_scale(L.scale, L.is_bf16 || L.k_scale);
+    a.scale_log2 = sf.cs;
+    a.q_and = sf.q_and;
+    a.q_xor = sf.q_xor;
     a.window = L.window;
     a.k_scale = (const float*)L.k_scale;
     a.v_scale = (const float*)L.v_scale;

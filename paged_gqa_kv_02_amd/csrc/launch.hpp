@@ -8,6 +8,27 @@
 
 namespace pgqa {
 
+// The softmax scale as the attention kernels apply it.  They take the running
+// maximum of the raw dot products and fold the scale into the exponent,
+// exp2(s * cs - m * cs), which needs cs > 0.  Any finite scale is reduced to that
+// case exactly: s * scale = (sign(scale) q) . k * |scale|, and the kernels apply
+// the sign to the query bits when they load them (q_and clears, q_xor flips the
+// sign bit of every element; a zero scale zeroes the query, so every visible key
+// gets the same weight).  cs = |scale| * log2(e) (log2(e) for a zero scale).
+struct ScaleFold {
+    float cs;
+    uint32_t q_and;
+    uint32_t q_xor;
+};
+
+inline ScaleFold fold_scale(float scale, bool bf16) {
+    const double log2e = 1.4426950408889634;
+    const uint32_t sign = bf16 ? 0x80008000u : 0x80000000u;
+    if (scale > 0.0f) return {(float)((double)scale * log2e), 0xffffffffu, 0u};
+    if (scale < 0.0f) return {(float)(-(double)scale * log2e), 0xffffffffu, sign};
+    return {(float)log2e, 0u, 0u};
+}
+
 struct KvCopyLaunch {
     const void* src_k;
     const void* src_v;

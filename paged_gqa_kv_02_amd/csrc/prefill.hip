@@ -73,7 +73,9 @@ struct PrefillArgs {
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t causal;
-    float scale_log2;
+    float scale_log2;        // |scale| * log2(e)
+    u32 q_and;               // the scale's sign, applied to the query bits as they are loaded
+    u32 q_xor;
     int32_t batch;
     int32_t nqt;             // query-tile levels (tiles of the longest sequence)
     int32_t pairs_per_xcd;   // ceil(batch * num_kv_heads / 8)
@@ -473,7 +475,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         const int row = min(i0 + l32, Lq - 1);
         const char* qp = a.q + (int64_t)(seq0 + row) * qstride + (int64_t)head * D * 2 + half * 16;
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) qreg[kk] = *(const u32x4*)(qp + kk * 32);
+        for (int kk = 0; kk < KSTEPS; ++kk) qreg[kk] = (*(const u32x4*)(qp + kk * 32) & a.q_and) ^ a.q_xor;
     }
 
     float m = kMaxInit, lsum = 0.0f;
@@ -886,7 +888,10 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
     a.num_q_heads = L.num_q_heads;
     a.num_kv_heads = L.num_kv_heads;
     a.causal = L.causal;
-    a.scale_log2 = (float)((double)L.scale * 1.4426950408889634);
+    const ScaleFold sf = fold_scale(L.scale, true);
+    a.scale_log2 = sf.cs;
+    a.q_and = sf.q_and;
+    a.q_xor = sf.q_xor;
     a.batch = L.batch;
     a.window = L.window;
     a.nchunk = 1;
@@ -912,7 +917,10 @@ hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream) {
     a.num_kv_heads = L.num_kv_heads;
     a.causal = L.non_causal ? 0 : 1;
     a.fixed_qlen = L.fixed_qlen;
-    a.scale_log2 = (float)((double)L.scale * 1.4426950408889634);
+    const ScaleFold sf = fold_scale(L.scale, true);
+    a.scale_log2 = sf.cs;
+    a.q_and = sf.q_and;
+    a.q_xor = sf.q_xor;
     a.batch = L.batch;
     a.block_table = L.block_table;
     a.context_lens = L.context_lens;

@@ -8,7 +8,6 @@ in the HIP kernels of libpaged_gqa.so; torch only owns memory and streams.
 
 from __future__ import annotations
 
-import math
 from typing import Optional, Tuple
 
 import torch
@@ -42,12 +41,60 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+def _same_dtype(what: str, ref: torch.Tensor, *ts: torch.Tensor) -> None:
+    for t in ts:
+        if t.dtype != ref.dtype:
+            raise TypeError(f"{what}: dtype {t.dtype} differs from {ref.dtype}")
+
+
+def _shape(what: str, t: torch.Tensor, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _rank(what: str, t: torch.Tensor, n: int) -> None:
+    if t.dim() != n:
+        raise ValueError(f"{what}: expected {n} dimensions, got shape {tuple(t.shape)}")
+
+
+def _rows(what: str, t: torch.Tensor, n: int) -> None:
+    if t.dim() < 1 or t.shape[0] != n:
+        raise ValueError(f"{what}: expected {n} rows, got shape {tuple(t.shape)}")
+
+
+def _table(block_table: torch.Tensor, batch: int) -> None:
+    _rank("block_table", block_table, 2)
+    _rows("block_table", block_table, batch)
+
+
+def _pools(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    _rank("k_cache", k_cache, 4)
+    _shape("v_cache", v_cache, k_cache.shape)
+    _same_dtype("v_cache", k_cache, v_cache)
+    return k_cache.shape
+
+
+def _out(out: Optional[torch.Tensor], q: torch.Tensor) -> torch.Tensor:
+    if out is None:
+        return torch.empty_like(q)
+    _shape("out", out, q.shape)
+    _same_dtype("out", q, out)
+    return out
+
+
 def paged_kv_write(k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, start_pos: torch.Tensor,
                    block_table: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
     """Scatter packed k, v [T, Hkv, d] into k_cache, v_cache [num_blocks, Hkv, bs, d] in place."""
+    nb, hkv, bs, d = _pools(k_cache, v_cache)
+    _rank("k", k, 3)
+    _shape("k", k, (k.shape[0], hkv, d))
+    _shape("v", v, k.shape)
+    _same_dtype("k / v against the cache", k_cache, k, v)
+    batch = start_pos.numel()
+    _rows("cu_seqlens", cu_seqlens, batch + 1)
+    _table(block_table, batch)
     _dev(k, v, cu_seqlens, start_pos, block_table, k_cache, v_cache)
     _i32(cu_seqlens, start_pos, block_table)
-    nb, hkv, bs, d = k_cache.shape
     st = lib().paged_kv_write(k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), start_pos.data_ptr(),
                               block_table.data_ptr(), block_table.shape[1], k_cache.data_ptr(), v_cache.data_ptr(),
                               cu_seqlens.numel() - 1, k.shape[0], nb, bs, hkv, d, _dtype(k), _stream())
@@ -59,11 +106,17 @@ def paged_kv_gather(k_cache: torch.Tensor, v_cache: torch.Tensor, cu_seqlens: to
                     k_out: Optional[torch.Tensor] = None,
                     v_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Inverse of paged_kv_write: packed [total_tokens, Hkv, d] copies of the cached rows."""
-    nb, hkv, bs, d = k_cache.shape
+    nb, hkv, bs, d = _pools(k_cache, v_cache)
+    batch = start_pos.numel()
+    _rows("cu_seqlens", cu_seqlens, batch + 1)
+    _table(block_table, batch)
     if k_out is None:
         k_out = torch.empty((total_tokens, hkv, d), dtype=k_cache.dtype, device=k_cache.device)
     if v_out is None:
         v_out = torch.empty((total_tokens, hkv, d), dtype=k_cache.dtype, device=k_cache.device)
+    _shape("k_out", k_out, (total_tokens, hkv, d))
+    _shape("v_out", v_out, (total_tokens, hkv, d))
+    _same_dtype("k_out / v_out against the cache", k_cache, k_out, v_out)
     _dev(k_cache, v_cache, cu_seqlens, start_pos, block_table, k_out, v_out)
     _i32(cu_seqlens, start_pos, block_table)
     st = lib().paged_kv_gather(k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens.data_ptr(), start_pos.data_ptr(),
@@ -86,19 +139,20 @@ def decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: 
 
 
 def gqa_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
-                     context_lens: torch.Tensor, max_context_len: int, scale: Optional[float] = None,
+                     context_lens: torch.Tensor, max_context_len: int, scale: float,
                      out: Optional[torch.Tensor] = None, num_splits: int = 0,
                      workspace: Optional[torch.Tensor] = None, window: int = 0) -> torch.Tensor:
     """Decode attention: q [B, Hq, d] over paged K/V -> out [B, Hq, d] (window > 0: the newest
-    `window` positions only)."""
+    `window` positions only).  scale is the softmax scale (normally 1/sqrt(d))."""
+    _rank("q", q, 3)
     B, hq, d = q.shape
-    nb, hkv, bs, d2 = k_cache.shape
+    nb, hkv, bs, d2 = _pools(k_cache, v_cache)
     if d2 != d:
         raise ValueError("head_dim mismatch")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
+    _same_dtype("k_cache / v_cache against q", q, k_cache)
+    _table(block_table, B)
+    _shape("context_lens", context_lens, (B,))
+    out = _out(out, q)
     if workspace is None:
         workspace = decode_workspace(B, hq, hkv, d, num_splits, q.device)
     _dev(q, k_cache, v_cache, block_table, context_lens, out, workspace)
@@ -113,15 +167,18 @@ def gqa_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
 
 
 def gqa_varlen_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
-                       max_seqlen: int, scale: Optional[float] = None, causal: bool = True,
+                       max_seqlen: int, scale: float, causal: bool = True,
                        out: Optional[torch.Tensor] = None, window: int = 0) -> torch.Tensor:
     """Packed varlen prefill: q [T, Hq, d], k / v [T, Hkv, d] -> out [T, Hq, d]."""
+    _rank("q", q, 3)
+    _rank("k", k, 3)
     T, hq, d = q.shape
     hkv = k.shape[1]
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
+    _shape("k", k, (T, hkv, d))
+    _shape("v", v, k.shape)
+    _same_dtype("k / v against q", q, k, v)
+    _rank("cu_seqlens", cu_seqlens, 1)
+    out = _out(out, q)
     _dev(q, k, v, cu_seqlens, out)
     _i32(cu_seqlens)
     st = lib().gqa_varlen_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
@@ -147,19 +204,22 @@ def extend_workspace(batch: int, total_q: int, max_q_len: int, num_q_heads: int,
 
 def gqa_paged_extend(q: torch.Tensor, cu_q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                      block_table: torch.Tensor, context_lens: torch.Tensor, max_q_len: int, max_context_len: int,
-                     scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                     scale: float, out: Optional[torch.Tensor] = None,
                      window: int = 0, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Several new tokens per sequence over its paged cache (chunked prefill on a cached
     prefix, draft verification): q [total_q, Hq, d] -> out [total_q, Hq, d].  The new
     tokens' K/V must already be in the pages; context_lens counts them."""
+    _rank("q", q, 3)
     T, hq, d = q.shape
-    nb, hkv, bs, d2 = k_cache.shape
+    nb, hkv, bs, d2 = _pools(k_cache, v_cache)
     if d2 != d:
         raise ValueError("head_dim mismatch")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
+    _same_dtype("k_cache / v_cache against q", q, k_cache)
+    _rank("cu_q", cu_q, 1)
+    batch = cu_q.numel() - 1
+    _table(block_table, batch)
+    _shape("context_lens", context_lens, (batch,))
+    out = _out(out, q)
     if workspace is None:
         workspace = extend_workspace(cu_q.numel() - 1, T, int(max_q_len), hq, hkv, d, int(max_context_len), q.device)
     _dev(q, cu_q, k_cache, v_cache, block_table, context_lens, out, workspace)
@@ -176,11 +236,11 @@ def gqa_paged_extend(q: torch.Tensor, cu_q: torch.Tensor, k_cache: torch.Tensor,
 def paged_kv_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src_blocks: torch.Tensor,
                          dst_blocks: torch.Tensor) -> None:
     """Copy whole blocks src_blocks[p] -> dst_blocks[p] (all heads, K and V) in place."""
-    _dev(k_cache, v_cache, src_blocks, dst_blocks)
-    _i32(src_blocks, dst_blocks)
+    nb, hkv, bs, d = _pools(k_cache, v_cache)
     if src_blocks.numel() != dst_blocks.numel():
         raise ValueError("src_blocks and dst_blocks differ in length")
-    nb, hkv, bs, d = k_cache.shape
+    _dev(k_cache, v_cache, src_blocks, dst_blocks)
+    _i32(src_blocks, dst_blocks)
     st = lib().paged_kv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), src_blocks.data_ptr(),
                                     dst_blocks.data_ptr(), src_blocks.numel(), nb, bs, hkv, d, _dtype(k_cache),
                                     _stream())
@@ -212,11 +272,21 @@ def paged_kv_write_fp8(k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tenso
                        block_table: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                        k_scale: torch.Tensor, v_scale: torch.Tensor) -> None:
     """Quantise packed bf16 k, v [T, Hkv, d] into FP8 code pools and fp32 row-scale pools in place."""
-    _dev(k, v, cu_seqlens, start_pos, block_table, k_cache, v_cache, k_scale, v_scale)
-    _i32(cu_seqlens, start_pos, block_table)
     _u8(k_cache, v_cache)
     _f32(k_scale, v_scale)
-    nb, hkv, bs, d = k_cache.shape
+    nb, hkv, bs, d = _pools(k_cache, v_cache)
+    _shape("k_scale", k_scale, (nb, hkv, bs))
+    _shape("v_scale", v_scale, (nb, hkv, bs))
+    _rank("k", k, 3)
+    _shape("k", k, (k.shape[0], hkv, d))
+    _shape("v", v, k.shape)
+    if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("rows quantised into FP8 pages are bfloat16")
+    batch = start_pos.numel()
+    _rows("cu_seqlens", cu_seqlens, batch + 1)
+    _table(block_table, batch)
+    _dev(k, v, cu_seqlens, start_pos, block_table, k_cache, v_cache, k_scale, v_scale)
+    _i32(cu_seqlens, start_pos, block_table)
     st = lib().paged_kv_write_fp8(k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), start_pos.data_ptr(),
                                   block_table.data_ptr(), block_table.shape[1], k_cache.data_ptr(), v_cache.data_ptr(),
                                   k_scale.data_ptr(), v_scale.data_ptr(), cu_seqlens.numel() - 1, k.shape[0], nb, bs,
@@ -226,26 +296,28 @@ def paged_kv_write_fp8(k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tenso
 
 def gqa_paged_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
                          v_scale: torch.Tensor, block_table: torch.Tensor, context_lens: torch.Tensor,
-                         max_context_len: int, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                         max_context_len: int, scale: float, out: Optional[torch.Tensor] = None,
                          num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
                          window: int = 0) -> torch.Tensor:
     """Decode attention over FP8 pages: bf16 q [B, Hq, d] -> bf16 out [B, Hq, d]."""
+    _rank("q", q, 3)
     B, hq, d = q.shape
-    nb, hkv, bs, d2 = k_cache.shape
+    _u8(k_cache, v_cache)
+    _f32(k_scale, v_scale)
+    nb, hkv, bs, d2 = _pools(k_cache, v_cache)
     if d2 != d:
         raise ValueError("head_dim mismatch")
     if q.dtype != torch.bfloat16:
         raise TypeError("queries over FP8 pages are bfloat16")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
+    _shape("k_scale", k_scale, (nb, hkv, bs))
+    _shape("v_scale", v_scale, (nb, hkv, bs))
+    _table(block_table, B)
+    _shape("context_lens", context_lens, (B,))
+    out = _out(out, q)
     if workspace is None:
         workspace = decode_workspace(B, hq, hkv, d, num_splits, q.device)
     _dev(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, out, workspace)
     _i32(block_table, context_lens)
-    _u8(k_cache, v_cache)
-    _f32(k_scale, v_scale)
     st = lib().gqa_paged_decode_fp8(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), k_scale.data_ptr(),
                                     v_scale.data_ptr(), block_table.data_ptr(), block_table.shape[1],
                                     context_lens.data_ptr(), B, hq, hkv, d, bs, nb, int(max_context_len),

@@ -782,4 +782,42 @@ def pin_contract_errors(orc):
         assert str(EINVAL) in str(e)
 
 
+def pin_zero_scale_gives_mean(orc):
+    """scale = 0 makes every score 0: each output is the plain mean of the values its
+    row sees (decode: the whole context; causal prefill: the prefix up to the row)."""
+    c = W.make_decode_case([7, 19, 1], 8, 2, 16, 4, W.F32, 37, scale=0.0)
+    out = decode(orc, c)
+    G = c.num_q_heads // c.num_kv_heads
+    v = f64(c.v)
+    for b in range(c.batch):
+        a, e = c.cu_ctx[b], c.cu_ctx[b + 1]
+        close(out[b], np.repeat(v[a:e].mean(axis=0), G, axis=0), rel=1e-14, what="zero-scale decode")
+    p = W.make_prefill_case([5, 12], 4, 2, 8, 4, W.F32, 38, scale=0.0)
+    pre = orc.gqa_varlen_prefill(p.q, p.k, p.v, p.cu_seqlens, 0.0, causal=True)
+    vv = f64(p.v)
+    for s_ in range(p.batch):
+        a, e = int(p.cu_seqlens[s_]), int(p.cu_seqlens[s_ + 1])
+        for i in range(a, e):
+            close(pre[i], np.repeat(vv[a:i + 1].mean(axis=0), 2, axis=0), rel=1e-14, what="zero-scale prefill")
+
+
+def pin_negative_scale_matches_library(orc):
+    """A negative scale is an ordinary softmax of scale * q.k.  The library routine
+    takes the square root of its scale, so it is asked for the same scores written
+    as |scale| * (-q).k (negating a bf16 query flips its sign bit: exact)."""
+    def flipped(case):
+        import copy
+        g = copy.copy(case)
+        g.q = case.q ^ np.uint16(0x8000)
+        g.scale = -case.scale
+        return g
+    for lens, hq, hkv, d, seed in [([9, 33], 8, 2, 16, 39), ([1, 70], 4, 4, 32, 40)]:
+        c = W.make_decode_case(lens, hq, hkv, d, 4, W.BF16, seed, scale=-0.75)
+        close(decode(orc, c), sdpa_decode(flipped(c)), what="negative-scale decode")
+    p = W.make_prefill_case([6, 31], 8, 2, 16, 4, W.BF16, 41, scale=-0.4)
+    for causal in (True, False):
+        close(orc.gqa_varlen_prefill(p.q, p.k, p.v, p.cu_seqlens, p.scale, causal=causal),
+              sdpa_prefill(flipped(p), causal), what="negative-scale prefill")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

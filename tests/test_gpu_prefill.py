@@ -51,20 +51,16 @@ def test_empty_sequences_in_batch(orc):
     assert_close(out, ref, W.BF16, "empty sequences")
 
 
-def test_workload_sampled_rows(orc):
-    """The full varlen prefill workload, checked on sampled rows (first, last and
-    random rows of every sequence) that the oracle evaluates one by one."""
+def test_workload_every_output(orc):
+    """The full varlen prefill workload (32 sequences, 16K packed rows) in the
+    benchmark's launch configuration, every output element against the oracle."""
     p = W.make_workload("varlen_prefill")
     say(f"prefill workload T={p.total_tokens}")
     out = to_f64(_gpu_prefill(p))
-    rng = np.random.default_rng(0)
-    rows = []
-    for s in range(p.batch):
-        a, e = int(p.cu_seqlens[s]), int(p.cu_seqlens[s + 1])
-        rows += [a, e - 1] + rng.integers(a, e, size=6).tolist()
-    rows = np.array(sorted(set(rows)), dtype=np.int32)
-    ref = orc.gqa_varlen_prefill(p.q, p.k, p.v, p.cu_seqlens, p.scale, rows=rows)
-    assert_close(out[rows], ref, W.BF16, "prefill workload rows")
+    torch.cuda.synchronize()
+    ref = orc.gqa_varlen_prefill(p.q, p.k, p.v, p.cu_seqlens, p.scale)
+    e = assert_close(out, ref, W.BF16, "prefill workload")
+    say(f"prefill workload: {e}")
 
 
 def test_decode_equals_last_prefill_row(orc):
