@@ -36,8 +36,9 @@
  * Conventions shared by every call (the pgqa_bm_* block manager below is
  * host-only and documented on its own)
  *   - Every array argument is a DEVICE pointer owned by the caller; the
- *     library never allocates, frees or keeps device memory and never
- *     synchronises.  Its only state between calls is a per-device cache of
+ *     library never allocates, frees or keeps device memory (the one
+ *     exception, gqa_paged_decode_noalloc's scratch, is documented with it) and
+ *     never synchronises.  Its only state between calls is a per-device cache of
  *     launch facts read from the HIP runtime (compute units, LDS per compute
  *     unit, kernel occupancy), guarded by a lock, so the calls are thread-safe.
  *   - `scale` (the attention calls) may be any finite float: the result is
@@ -180,6 +181,29 @@ int gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                      int32_t max_context_len, float scale, int32_t window, pgqa_dtype dtype,
                      void* out, int32_t num_splits,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gqa_paged_decode_noalloc -- gqa_paged_decode for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, result and errors
+ * as gqa_paged_decode (bit-identical output for the same num_splits) without
+ * the workspace: the split-KV partials go to a scratch array of 128 MiB that the
+ * library holds on each GPU it runs on until the process ends (its device address
+ * is looked up once per device, at the first call there).  The call allocates
+ * nothing.  Sizes whose workspace, gqa_paged_decode_workspace_size(batch, Hq,
+ * Hkv, head_dim, num_splits), exceeds 128 MiB return PGQA_ENOSPC (from about
+ * 7,560 sequences with Hq 32, Hkv 8, head_dim 128).  The scratch needs no
+ * initialisation, and every call on one GPU shares it: calls that may overlap on
+ * one GPU (different streams, or host threads) race and give wrong results; the
+ * caller serialises them.  PGQA_EHIP if the scratch cannot be located.
+ */
+int gqa_paged_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens,
+                             int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                             int32_t max_context_len, float scale, int32_t window, pgqa_dtype dtype,
+                             void* out, int32_t num_splits, void* stream);
 
 /*
  * gqa_varlen_prefill -- packed variable-length prefill with a block-diagonal

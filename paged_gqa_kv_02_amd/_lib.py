@@ -25,6 +25,8 @@ _SIGNATURES = {
     "gqa_paged_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
     "gqa_paged_decode": (C.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _I,
                                    _P, _Z, _P]),
+    "gqa_paged_decode_noalloc": (C.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _I,
+                                           _P]),
     "gqa_varlen_prefill": (C.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P]),
     "gqa_paged_extend": (C.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                                    _I, _P, _P, _Z, _P]),

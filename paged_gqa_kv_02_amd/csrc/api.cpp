@@ -159,6 +159,28 @@ int gqa_paged_decode(const void* q, const void* k_cache, const void* v_cache, co
     return hip_status(pgqa::launch_decode(L, (hipStream_t)stream));
 }
 
+int gqa_paged_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t max_context_len, float scale, int32_t window,
+                             pgqa_dtype dtype, void* out, int32_t num_splits, void* stream) {
+    int32_t lg = 0;
+    const int rc = check_decode_args(q, k_cache, v_cache, block_table, max_blocks_per_seq, context_lens, batch,
+                                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len,
+                                     scale, window, dtype, out, num_splits, &lg);
+    if (rc != PGQA_OK) return rc;
+    if (batch == 0) return PGQA_OK;
+    // The same partials gqa_paged_decode would need, in the library's own scratch.
+    const size_t need = gqa_paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, num_splits);
+    if (need > pgqa::kDecodeScratchBytes) return PGQA_ENOSPC;
+    void* scratch = pgqa::decode_scratch();
+    if (!scratch) return PGQA_EHIP;
+    pgqa::DecodeLaunch L{q, k_cache, v_cache, block_table, context_lens, out, scratch, max_blocks_per_seq,
+                         batch, num_q_heads, num_kv_heads, head_dim, lg, num_blocks, max_context_len,
+                         num_splits, dtype == PGQA_BF16 ? 1 : 0, scale, window, nullptr, nullptr};
+    return hip_status(pgqa::launch_decode(L, (hipStream_t)stream));
+}
+
 size_t gqa_paged_extend_workspace_size(int32_t batch, int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
                                        int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len) {
     if (batch <= 0 || total_q <= 0 || max_q_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0)

@@ -1106,6 +1106,27 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Scratch of the allocation-free decode entry point: a file-scope device array,
+// one copy per GPU (held until the process ends).  Host code never passes the
+// array's name to a kernel (on the host that name is only a stand-in for the
+// symbol); it looks up the device address on each device once and passes that.
+// Every call on one GPU shares the array: calls that may overlap on that GPU race.
+static __device__ __attribute__((aligned(256))) char scratch[kDecodeScratchBytes];
+
+void* decode_scratch() {
+    static std::mutex mu;
+    static void* addr[64] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
 size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                               int32_t num_splits) {
     const int64_t splits = num_splits > 0 ? num_splits : kDecodeMaxSplits;

@@ -111,6 +111,14 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
 size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                               int32_t num_splits);
 
+// Size of the library's own device scratch, which takes the place of the
+// caller's workspace in the allocation-free decode entry point.
+constexpr size_t kDecodeScratchBytes = (size_t)128 << 20;
+
+// Device address of that scratch on the current device (looked up once per
+// device); null if the lookup fails.
+void* decode_scratch();
+
 struct PrefillLaunch {
     const void* q;
     const void* k;

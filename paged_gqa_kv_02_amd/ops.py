@@ -166,6 +166,31 @@ def gqa_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     return out
 
 
+def gqa_paged_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                             block_table: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                             scale: float, out: torch.Tensor, num_splits: int = 0, window: int = 0) -> torch.Tensor:
+    """gqa_paged_decode without a workspace (the library's own per-GPU scratch holds the
+    split partials; calls that may overlap on one GPU race).  out is required: nothing
+    is allocated."""
+    _rank("q", q, 3)
+    B, hq, d = q.shape
+    nb, hkv, bs, d2 = _pools(k_cache, v_cache)
+    if d2 != d:
+        raise ValueError("head_dim mismatch")
+    _same_dtype("k_cache / v_cache against q", q, k_cache)
+    _table(block_table, B)
+    _shape("context_lens", context_lens, (B,))
+    out = _out(out, q)
+    _dev(q, k_cache, v_cache, block_table, context_lens, out)
+    _i32(block_table, context_lens)
+    st = lib().gqa_paged_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+                                        block_table.shape[1], context_lens.data_ptr(), B, hq, hkv, d, bs, nb,
+                                        int(max_context_len), float(scale), int(window), _dtype(q), out.data_ptr(),
+                                        int(num_splits), _stream())
+    check("gqa_paged_decode_noalloc", st)
+    return out
+
+
 def gqa_varlen_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
                        max_seqlen: int, scale: float, causal: bool = True,
                        out: Optional[torch.Tensor] = None, window: int = 0) -> torch.Tensor:

@@ -24,6 +24,7 @@ def test_header_declares_the_calls():
     names = L.header_functions()
     for n in ("paged_kv_write", "paged_kv_gather", "gqa_paged_decode", "gqa_paged_decode_workspace_size",
               "gqa_varlen_prefill", "gqa_paged_extend", "paged_kv_copy_blocks", "pgqa_bm_create", "pgqa_bm_append",
+              "gqa_paged_decode_noalloc",
               "pgqa_bm_fork", "pgqa_bm_free_sequence", "pgqa_status_string"):
         assert n in names
 
@@ -93,6 +94,32 @@ def test_decode_validation(lib):
     assert _decode(lib, wsb=need - 1) == ENOSPC
     assert _decode(lib, ws=None, wsb=0) == ENOSPC
     assert _decode(lib, batch=0) == 0
+
+
+def _decode_noalloc(lib, **kw):
+    a = dict(q=P[0], kc=P[1], vc=P[2], bt=P[3], maxb=4, cl=P[4], batch=2, hq=8, hkv=2, d=128, bs=16, nb=8,
+             maxctx=64, scale=0.125, win=0, dt=BF16, out=P[5], splits=0)
+    a.update(kw)
+    return lib.gqa_paged_decode_noalloc(a["q"], a["kc"], a["vc"], a["bt"], a["maxb"], a["cl"], a["batch"], a["hq"],
+                                        a["hkv"], a["d"], a["bs"], a["nb"], a["maxctx"], a["scale"], a["win"],
+                                        a["dt"], a["out"], a["splits"], None)
+
+
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode checks its arguments like gqa_paged_decode, and refuses
+    sizes whose partials would not fit its 128 MiB scratch, before any HIP call."""
+    assert _decode_noalloc(lib, hq=6, hkv=4) == EINVAL
+    assert _decode_noalloc(lib, out=None) == EINVAL
+    assert _decode_noalloc(lib, scale=float("inf")) == EINVAL
+    assert _decode_noalloc(lib, d=80) == ENOTSUP
+    assert _decode_noalloc(lib, batch=9000) == ENOTSUP
+    assert _decode_noalloc(lib, batch=0) == 0
+    limit = 128 << 20
+    # 8,000 sequences x 8 KV heads, G = 4, d = 128: (4096 + 64000) x 4 x 130 x 4 bytes > 128 MiB
+    assert lib.gqa_paged_decode_workspace_size(8000, 32, 8, 128, 0) > limit
+    assert _decode_noalloc(lib, batch=8000, hq=32, hkv=8, maxb=1, maxctx=16) == ENOSPC
+    assert lib.gqa_paged_decode_workspace_size(7500, 32, 8, 128, 0) <= limit
+    assert _decode_noalloc(lib, splits=200000, hq=32, hkv=8) == ENOSPC
 
 
 def test_workspace_size_formula(lib):
