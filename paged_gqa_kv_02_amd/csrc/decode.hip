@@ -75,6 +75,9 @@
 #ifndef PGQA_DECODE_RPT8
 #define PGQA_DECODE_RPT8 8
 #endif
+#ifndef PGQA_DECODE_LDS_DIV
+#define PGQA_DECODE_LDS_DIV 4   // one-wave workgroups per CU on bf16 / fp32 pages (one per SIMD)
+#endif
 
 namespace pgqa {
 
@@ -394,7 +397,7 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, PGQA_LDS char* r
             const int blk = __builtin_amdgcn_ds_bpermute(((tok >> a.bs_log2) - win.base) << 2, win.reg);
             const int64_t srow = (((int64_t)blk * a.num_kv_heads + h) << a.bs_log2) + (tok & bs_mask);
             __builtin_amdgcn_global_load_lds((p >= TT ? a.v_scale : a.k_scale) + srow,
-                                             dst + 2 * Gm::KVB + j * kWave * 4, 4, 0, 0);
+                                             dst + 2 * Gm::KVB + j * kWave * 4, 4, 0, PGQA_KV_CPOL);
         }
     }
 }
@@ -1088,7 +1091,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     // 128 us for 4 (32-token tiles), the 16-token tiles 126-129 us at the 9 per
     // CU their LDS allows against 122 us at 4, and FP8 pages 78-86 us at 8 per
     // CU (8-row tiles) against 87-93 us at 4 (16-row tiles).
-    if (e.waves == 1) lds = std::max(lds, lds_per_cu() / (L.k_scale ? 8 : 4));
+    if (e.waves == 1) lds = std::max(lds, lds_per_cu() / (L.k_scale ? 8 : PGQA_DECODE_LDS_DIV));
     int nw = L.num_splits;
     if (nw <= 0) {
         nw = occupancy(e.split, threads, lds) * cu_count();

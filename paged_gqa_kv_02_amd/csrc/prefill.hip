@@ -82,6 +82,7 @@ struct PrefillArgs {
     int32_t dense;           // 1: each XCD's list holds only existing query tiles (pairs_per_xcd <= 64)
     int32_t fixed_qlen;      // > 0: sequence s holds rows [s * fixed_qlen, +fixed_qlen) (cu_seqlens unused)
     int32_t chunk_lpt;       // 1: dense lists of key chunks, full chunks first (one query tile and head group per pair)
+    int32_t kv_nt;           // 1: K/V read by one workgroup only (one query tile and head group per pair): non-temporal loads
     // Paged K/V only (k, v are then the pools [num_blocks, Hkv, block_size, d]).
     const int32_t* block_table;
     const int32_t* context_lens;
@@ -193,14 +194,14 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const DmaLane<D
     if (kb * BN + BN <= L) {
         constexpr int JP = DmaLane<D>::JP;
 #pragma unroll
-        for (int j = 0; j < NPW; ++j) dma16(base + (j / JP) * 16 * kvstride, dl.soff[j % JP], dst + j * 1024);
+        for (int j = 0; j < NPW; ++j) dma16(base + (j / JP) * 16 * kvstride, dl.soff[j % JP], dst + j * 1024, a.kv_nt);
     } else {
         const int last = L - 1 - kb * BN;
 #pragma unroll
         for (int j = 0; j < NPW; ++j) {
             const int r = ((wave & 1) * NPW + j) * P::RPL + lane / P::CPR;
             const int c = (lane % P::CPR) ^ swz_key<D>(r);
-            dma16(base, (uint32_t)(min(r, last) * kvstride + c * 16), dst + j * 1024);
+            dma16(base, (uint32_t)(min(r, last) * kvstride + c * 16), dst + j * 1024, a.kv_nt);
         }
     }
 }
@@ -233,6 +234,7 @@ struct PagedSrc {
     int lbs;
     int last;            // last key row of the sequence (ctx - 1)
     int nb;
+    bool nt;             // non-temporal loads
     int id[NPW];
 };
 
@@ -269,7 +271,7 @@ __device__ __forceinline__ void issue_tile_paged(const PagedSrc<D>& ps, const Dm
 #pragma unroll
         for (int j = 0; j < NPW; ++j) {
             const int row0 = paged_row0<D>(kb, wave, j);
-            dma16(base_of(j, row0), dl.soff[j % JP], dst + j * 1024);
+            dma16(base_of(j, row0), dl.soff[j % JP], dst + j * 1024, ps.nt);
         }
     } else {
         const int r = lane / P::CPR;
@@ -279,7 +281,7 @@ __device__ __forceinline__ void issue_tile_paged(const PagedSrc<D>& ps, const Dm
             const int rb = min(row0, ps.last);
             const int rc = min(row0 + r, ps.last);
             const int c = (lane % P::CPR) ^ swz_key<D>((j % JP) * P::RPL + r);
-            dma16(base_of(j, rb), (uint32_t)((rc - rb) * P::ROWB + c * 16), dst + j * 1024);
+            dma16(base_of(j, rb), (uint32_t)((rc - rb) * P::ROWB + c * 16), dst + j * 1024, ps.nt);
         }
     }
 }
@@ -453,6 +455,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         ps.blk_bytes = ((int64_t)a.num_kv_heads << a.bs_log2) * P::ROWB;
         ps.last = Lk - 1;
         ps.nb = a.num_blocks;
+        ps.nt = a.kv_nt != 0;
         if (nrel > 0) {
             paged_load_ids<D>(ps, kb0, wave);
             issue_tile_paged<D>(ps, dl, ring_addr, kb0, 0, wave, lane);
@@ -897,6 +900,7 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
     a.nchunk = 1;
     a.kchunk = kNoSplit;
     grid_dims(a, hg, group, L.max_seqlen);
+    a.kv_nt = (group == hg && a.nqt == 1) ? 1 : 0;
     return launch(fn, a, hg, group, L.head_dim, stream);
 }
 
@@ -956,6 +960,8 @@ hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream) {
     // One query tile and one head group per pair: list the key chunks longest
     // first (the kernel does so with dense lists).
     a.chunk_lpt = (a.nchunk > 1 && group == hg && a.nqt == 1) ? 1 : 0;
+    // One query tile and one head group per pair: each K/V byte goes to one workgroup.
+    a.kv_nt = (group == hg && a.nqt == 1) ? 1 : 0;
     a.part_o = (float*)L.workspace;
     a.part_ml = a.part_o + (int64_t)L.total_q * L.num_q_heads * a.nchunk * L.head_dim;
     hipError_t err = launch(fn, a, hg, group, L.head_dim, stream);
