@@ -52,8 +52,8 @@
 // the causal diagonal is shifted by ctx - q_len (bottom-right alignment).  Each
 // 1 KB wave-load covers 4 (d = 128) or 8 (d = 64) consecutive rows of one
 // page, so its source is one scalar base (block id from a scalar load of the
-// block-table row, fetched one tile ahead) plus the lane's offset, exactly as
-// for packed K/V.
+// block-table row, issued before the block's DMA wait and barrier) plus the
+// lane's offset, exactly as for packed K/V.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -99,6 +99,10 @@ struct PrefillArgs {
     float* part_o;           // [total_tokens, Hq, nchunk, D]
     float* part_ml;          // [total_tokens, Hq, nchunk, 2]  (m in log2 units, l)
 };
+
+#ifndef PGQA_KREADS_AHEAD
+#define PGQA_KREADS_AHEAD 2
+#endif
 
 // Block-table rows are read through the constant address space, which makes
 // the compiler fetch a uniform entry with a scalar load (the table is never
@@ -220,10 +224,11 @@ __device__ __forceinline__ void dma_lane_init_paged(DmaLane<D>& dl, int lane) {
     }
 }
 
-// Paged source of one wave: its pool (K for waves 0-1, V for waves 2-3), the
-// sequence's block-table row and the block ids of the next tile it will fetch
-// (one per wave-load, loaded a tile ahead so the scalar loads are off the
-// critical path).
+// Paged source of one wave: its pool (K for waves 0-1, V for waves 2-3, NPW
+// wave-loads each from wave-load j0 = (wave & 1) * NPW on), the sequence's
+// block-table row and the block ids of the next tile it will fetch (one per
+// wave-load, loaded before the DMA wait and barrier that precede the tile's
+// issue and clamped only at the issue, so their latency hides behind those).
 template <int D>
 struct PagedSrc {
     static constexpr int NPW = DmaLane<D>::NPW;
@@ -235,20 +240,22 @@ struct PagedSrc {
     int last;            // last key row of the sequence (ctx - 1)
     int nb;
     bool nt;             // non-temporal loads
+    bool isv;            // this wave fetches V (else K)
+    int j0;              // first wave-load of the tile this wave issues
     int id[NPW];
 };
 
 // First key row (relative to the sequence) of wave-load j of tile kb.
 template <int D>
-__device__ __forceinline__ int paged_row0(int kb, int wave, int j) {
-    return kb * BN + ((wave & 1) * DmaLane<D>::NPW + j) * PGeo<D>::RPL;
+__device__ __forceinline__ int paged_row0(int kb, int j) {
+    return kb * BN + j * PGeo<D>::RPL;
 }
 
 template <int D>
-__device__ __forceinline__ void paged_load_ids(PagedSrc<D>& ps, int kb, int wave) {
+__device__ __forceinline__ void paged_load_ids(PagedSrc<D>& ps, int kb) {
 #pragma unroll
     for (int j = 0; j < PagedSrc<D>::NPW; ++j)
-        ps.id[j] = clampi(ps.bt[min(paged_row0<D>(kb, wave, j), ps.last) >> ps.lbs], 0, ps.nb - 1);
+        ps.id[j] = ps.bt[min(paged_row0<D>(kb, ps.j0 + j), ps.last) >> ps.lbs];
 }
 
 // DMA of tile kb from the pages (same LDS placement as issue_tile).  A load's
@@ -257,27 +264,27 @@ __device__ __forceinline__ void paged_load_ids(PagedSrc<D>& ps, int kb, int wave
 // last row (in bounds; those keys are masked).
 template <int D>
 __device__ __forceinline__ void issue_tile_paged(const PagedSrc<D>& ps, const DmaLane<D>& dl, uint32_t ring,
-                                                 int kb, int par, int wave, int lane) {
+                                                 int kb, int par, int lane) {
     using P = PGeo<D>;
     constexpr int NPW = DmaLane<D>::NPW;
     constexpr int JP = DmaLane<D>::JP;
-    const bool isv = wave >= 2;
-    const uint32_t dst = ring + (isv ? 2 * P::TILEB : 0) + par * P::TILEB + (wave & 1) * NPW * 1024;
+    const uint32_t dst = ring + (ps.isv ? 2 * P::TILEB : 0) + par * P::TILEB + ps.j0 * 1024;
     const int bs_mask = (1 << ps.lbs) - 1;
     auto base_of = [&](int j, int rb) {
-        return ps.pool + (int64_t)ps.id[j] * ps.blk_bytes + ps.head_off + (int64_t)(rb & bs_mask) * P::ROWB;
+        return ps.pool + (int64_t)clampi(ps.id[j], 0, ps.nb - 1) * ps.blk_bytes + ps.head_off +
+               (int64_t)(rb & bs_mask) * P::ROWB;
     };
     if (kb * BN + BN <= ps.last + 1) {
 #pragma unroll
         for (int j = 0; j < NPW; ++j) {
-            const int row0 = paged_row0<D>(kb, wave, j);
+            const int row0 = paged_row0<D>(kb, ps.j0 + j);
             dma16(base_of(j, row0), dl.soff[j % JP], dst + j * 1024, ps.nt);
         }
     } else {
         const int r = lane / P::CPR;
 #pragma unroll
         for (int j = 0; j < NPW; ++j) {
-            const int row0 = paged_row0<D>(kb, wave, j);
+            const int row0 = paged_row0<D>(kb, ps.j0 + j);
             const int rb = min(row0, ps.last);
             const int rc = min(row0 + r, ps.last);
             const int c = (lane % P::CPR) ^ swz_key<D>((j % JP) * P::RPL + r);
@@ -291,6 +298,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     using P = PGeo<D>;
     constexpr int TB = 4 / HG;               // 32-row token blocks per workgroup
     constexpr int KSTEPS = P::KSTEPS, DBLK = P::DBLK;
+    constexpr int NPW = DmaLane<D>::NPW;   // wave-loads per tile and DMA wave (normal roles)
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
     PGQA_LDS char* ring = (PGQA_LDS char*)smem;
@@ -449,7 +457,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     if constexpr (PAGED) {
         dma_lane_init_paged<D>(dl, lane);
         ps.bt = (ConstI32Ptr)(a.block_table + (int64_t)s * a.max_blocks_per_seq);
-        ps.pool = wave >= 2 ? a.v : a.k;
+        ps.isv = wave >= 2;
+        ps.j0 = (wave & 1) * NPW;
+        ps.pool = ps.isv ? a.v : a.k;
         ps.lbs = a.bs_log2;
         ps.head_off = ((int64_t)kvh << a.bs_log2) * P::ROWB;
         ps.blk_bytes = ((int64_t)a.num_kv_heads << a.bs_log2) * P::ROWB;
@@ -457,14 +467,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         ps.nb = a.num_blocks;
         ps.nt = a.kv_nt != 0;
         if (nrel > 0) {
-            paged_load_ids<D>(ps, kb0, wave);
-            issue_tile_paged<D>(ps, dl, ring_addr, kb0, 0, wave, lane);
-            if (wave < 2 && nrel > 1) {
-                paged_load_ids<D>(ps, kb0 + 1, wave);
-                issue_tile_paged<D>(ps, dl, ring_addr, kb0 + 1, 1, wave, lane);
+            paged_load_ids<D>(ps, kb0);
+            issue_tile_paged<D>(ps, dl, ring_addr, kb0, 0, lane);
+            if (!ps.isv && nrel > 1) {
+                paged_load_ids<D>(ps, kb0 + 1);
+                issue_tile_paged<D>(ps, dl, ring_addr, kb0 + 1, 1, lane);
             }
-            const int nt = wave < 2 ? 2 : 1;
-            if (nt < nrel) paged_load_ids<D>(ps, kb0 + nt, wave);
         }
     } else {
         dma_lane_init<D>(dl, wave, lane, kvstride);
@@ -584,11 +592,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
             // Interleave: per next-block MFMA one K read and a slice of the
             // softmax arithmetic, so the VALU work hides under the matrix pipe
             // and only a few K fragments are live at a time.
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // two K reads ahead
+            __builtin_amdgcn_sched_group_barrier(0x100, PGQA_KREADS_AHEAD, 0);   // K reads ahead
 #pragma unroll
             for (int i = 0; i < 2 * KSTEPS; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                if (i + 2 < 2 * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // K read
+                if (i + PGQA_KREADS_AHEAD < 2 * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // K read
                 __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
             }
         }
@@ -618,13 +626,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // wave is done with K(kb) and V(kb-1), so their slots are refilled with
     // K(kb+2) and V(kb+1).
     auto top = [&](int kr) {
+        const int tb = (PAGED ? !ps.isv : wave < 2) ? kr + 2 : kr + 1;
+        // The block ids of the tile issued below are loaded before the DMA wait
+        // and the barrier, which cover their latency; no scalar load is then in
+        // flight during the block's LDS reads (whose waits would otherwise also
+        // wait for it, scalar loads returning out of order).
+        if constexpr (PAGED)
+            if (tb < nrel) paged_load_ids<D>(ps, kb0 + tb);
         wait_vmcnt<0>();
         __syncthreads();
-        const int tb = wave < 2 ? kr + 2 : kr + 1;
         if (tb < nrel) {
             if constexpr (PAGED) {
-                issue_tile_paged<D>(ps, dl, ring_addr, kb0 + tb, tb & 1, wave, lane_now());
-                if (tb + 1 < nrel) paged_load_ids<D>(ps, kb0 + tb + 1, wave);
+                issue_tile_paged<D>(ps, dl, ring_addr, kb0 + tb, tb & 1, lane_now());
             } else {
                 issue_tile<D>(a, dl, ring_addr, kb0 + tb, tb & 1, seq0, Lk, kvh, wave, lane_now(), kvstride);
             }
