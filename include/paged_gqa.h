@@ -134,7 +134,8 @@ int paged_kv_gather(const void* k_cache, const void* v_cache,
 /*
  * Bytes of device workspace gqa_paged_decode needs for these sizes: fp32
  * split-KV partials (running max, sum and unnormalised output per query head)
- * for at most (num_splits + batch * Hkv) pieces.  num_splits = 0 sizes it for
+ * for at most (num_splits + batch * Hkv) pieces, and the per-sequence tile
+ * counts the merge step reads (batch + 1 int32).  num_splits = 0 sizes it for
  * the library's own choice.  Returns 0 for invalid sizes.  Its contents need no
  * initialisation; two calls that may run at the same time must not share it.
  */

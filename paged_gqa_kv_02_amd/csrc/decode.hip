@@ -92,6 +92,7 @@ struct DecodeArgs {
     char* out;
     float* part_o;       // [slots][G][D]   slots = num_splits + batch * Hkv
     float* part_ml;      // [slots][G][2]   (m, l) in log2 units
+    int32_t* tile_pref;  // [batch + 1] tiles of the sequences before b (written by the split kernel's first share)
     int32_t batch;
     int32_t num_q_heads;
     int32_t num_kv_heads;
@@ -637,6 +638,9 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         if (lane == 0) pref[0] = 0;
     }
     __syncthreads();
+    // The merge kernel reads the same prefix sums (no rescan of every context there).
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i <= B; i += 64 * W) a.tile_pref[i] = pref[i];
 
     // Shares: min(num_splits, total) so that no share is empty and every share
     // of a cut segment writes the partial the merge reads.
@@ -824,8 +828,7 @@ template <int G, int D>
 constexpr int merge_slices() { return (G * D + 255) / 256; }
 
 template <int ES, int D, int G>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tt) {
-    __shared__ int red[2][4];
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     constexpr int NS = merge_slices<G, D>();
     const int tid = threadIdx.x;
     const int Hkv = a.num_kv_heads;
@@ -834,25 +837,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tt)
     const int b = seg / Hkv;
     const int h = seg % Hkv;
 
-    int before = 0, all = 0;
-    for (int i = tid; i < a.batch; i += 256) {
-        const int t = tiles_of(a.context_lens[i], a.ctx_cap, tt, a.window);
-        all += t;
-        if (i < b) before += t;
-    }
-    for (int mk = 32; mk >= 1; mk >>= 1) {
-        before += __shfl_xor(before, mk);
-        all += __shfl_xor(all, mk);
-    }
-    if ((tid & 63) == 0) {
-        red[0][tid >> 6] = before;
-        red[1][tid >> 6] = all;
-    }
-    __syncthreads();
-    before = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-    all = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-
-    const int tiles_b = tiles_of(a.context_lens[b], a.ctx_cap, tt, a.window);
+    // Tiles of the sequences before b, of b, and of all: the split kernel's prefix sums.
+    const int before = __builtin_amdgcn_readfirstlane(a.tile_pref[b]);
+    const int tiles_b = __builtin_amdgcn_readfirstlane(a.tile_pref[b + 1]) - before;
+    const int all = __builtin_amdgcn_readfirstlane(a.tile_pref[a.batch]);
     if (tiles_b == 0) return;   // zero-filled by the split kernel
     const int64_t total = (int64_t)Hkv * all;
     const int64_t nw = min((int64_t)a.num_splits, total);
@@ -888,7 +876,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int tt)
 // ---- dispatch ------------------------------------------------------------------
 
 typedef void (*SplitFn)(DecodeArgs);
-typedef void (*MergeFn)(DecodeArgs, int);
+typedef void (*MergeFn)(DecodeArgs);
 
 struct Entry {
     SplitFn split;
@@ -1101,11 +1089,12 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     const int64_t slots = (int64_t)nw + (int64_t)L.batch * L.num_kv_heads;
     a.part_o = (float*)L.workspace;
     a.part_ml = a.part_o + slots * (L.num_q_heads / L.num_kv_heads) * L.head_dim;
+    a.tile_pref = (int32_t*)(a.part_ml + slots * (L.num_q_heads / L.num_kv_heads) * 2);
 
     hipLaunchKernelGGL(e.split, dim3(nw), dim3(threads), lds, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(e.merge, dim3(L.batch * L.num_kv_heads * e.merge_slices), dim3(256), 0, stream, a, e.tt);
+    hipLaunchKernelGGL(e.merge, dim3(L.batch * L.num_kv_heads * e.merge_slices), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1135,7 +1124,7 @@ size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv
     const int64_t splits = num_splits > 0 ? num_splits : kDecodeMaxSplits;
     const int64_t slots = splits + (int64_t)batch * num_kv_heads;
     const int64_t group = num_q_heads / num_kv_heads;
-    return (size_t)(slots * group * (head_dim + 2) * 4);
+    return (size_t)(slots * group * (head_dim + 2) * 4 + ((int64_t)batch + 1) * 4);
 }
 
 }  // namespace pgqa

@@ -107,7 +107,8 @@ bool decode_fp8_supported(int32_t head_dim, int32_t group, int32_t block_size);
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
 
-// Decode workspace: fp32 partials for (splits + batch * Hkv) pieces x G heads x (head_dim + 2).
+// Decode workspace: fp32 partials for (splits + batch * Hkv) pieces x G heads x (head_dim + 2), then
+// (batch + 1) int32 tile prefix sums.
 size_t decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                               int32_t num_splits);
 

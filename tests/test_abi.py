@@ -123,9 +123,9 @@ def test_decode_noalloc_validation(lib):
 
 
 def test_workspace_size_formula(lib):
-    # (splits + B * Hkv) pieces x G heads x (d + 2) floats
-    assert lib.gqa_paged_decode_workspace_size(64, 32, 8, 128, 100) == (100 + 512) * 4 * 130 * 4
-    assert lib.gqa_paged_decode_workspace_size(8, 64, 8, 128, 0) == (4096 + 64) * 8 * 130 * 4
+    # (splits + B * Hkv) pieces x G heads x (d + 2) floats, then B + 1 int32 tile prefix sums
+    assert lib.gqa_paged_decode_workspace_size(64, 32, 8, 128, 100) == (100 + 512) * 4 * 130 * 4 + 65 * 4
+    assert lib.gqa_paged_decode_workspace_size(8, 64, 8, 128, 0) == (4096 + 64) * 8 * 130 * 4 + 9 * 4
     assert lib.gqa_paged_decode_workspace_size(2, 6, 4, 128, 0) == 0
     assert lib.gqa_paged_decode_workspace_size(-1, 8, 2, 128, 0) == 0
 
