@@ -238,6 +238,7 @@ struct PagedSrc {
     int64_t blk_bytes;   // Hkv * block_size * row bytes
     int lbs;
     int last;            // last key row of the sequence (ctx - 1)
+    int lo;              // first key row the workgroup needs (its first row's window edge, or 0)
     int nb;
     bool nt;             // non-temporal loads
     bool isv;            // this wave fetches V (else K)
@@ -255,13 +256,16 @@ template <int D>
 __device__ __forceinline__ void paged_load_ids(PagedSrc<D>& ps, int kb) {
 #pragma unroll
     for (int j = 0; j < PagedSrc<D>::NPW; ++j)
-        ps.id[j] = ps.bt[min(paged_row0<D>(kb, ps.j0 + j), ps.last) >> ps.lbs];
+        ps.id[j] = ps.bt[min(max(paged_row0<D>(kb, ps.j0 + j), ps.lo), ps.last) >> ps.lbs];
 }
 
 // DMA of tile kb from the pages (same LDS placement as issue_tile).  A load's
 // rows lie in one page (block_size >= rows per load), so its source is a
 // uniform base plus the lane offset; rows past the sequence end re-read its
-// last row (in bounds; those keys are masked).
+// last row, and rows below the first key the workgroup needs (under a window:
+// rows of pages the caller may have released) re-read that key's row (in bounds
+// and written; those keys are masked, and their values are finite, so a zero
+// weight cannot meet a NaN in P.V).
 template <int D>
 __device__ __forceinline__ void issue_tile_paged(const PagedSrc<D>& ps, const DmaLane<D>& dl, uint32_t ring,
                                                  int kb, int par, int lane) {
@@ -274,7 +278,7 @@ __device__ __forceinline__ void issue_tile_paged(const PagedSrc<D>& ps, const Dm
         return ps.pool + (int64_t)clampi(ps.id[j], 0, ps.nb - 1) * ps.blk_bytes + ps.head_off +
                (int64_t)(rb & bs_mask) * P::ROWB;
     };
-    if (kb * BN + BN <= ps.last + 1) {
+    if (kb * BN >= ps.lo && kb * BN + BN <= ps.last + 1) {
 #pragma unroll
         for (int j = 0; j < NPW; ++j) {
             const int row0 = paged_row0<D>(kb, ps.j0 + j);
@@ -285,8 +289,8 @@ __device__ __forceinline__ void issue_tile_paged(const PagedSrc<D>& ps, const Dm
 #pragma unroll
         for (int j = 0; j < NPW; ++j) {
             const int row0 = paged_row0<D>(kb, ps.j0 + j);
-            const int rb = min(row0, ps.last);
-            const int rc = min(row0 + r, ps.last);
+            const int rb = min(max(row0, ps.lo), ps.last);
+            const int rc = min(max(row0 + r, ps.lo), ps.last);
             const int c = (lane % P::CPR) ^ swz_key<D>((j % JP) * P::RPL + r);
             dma16(base_of(j, rb), (uint32_t)((rc - rb) * P::ROWB + c * 16), dst + j * 1024, ps.nt);
         }
@@ -464,6 +468,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         ps.head_off = ((int64_t)kvh << a.bs_log2) * P::ROWB;
         ps.blk_bytes = ((int64_t)a.num_kv_heads << a.bs_log2) * P::ROWB;
         ps.last = Lk - 1;
+        ps.lo = win > 0 ? min(max(0, koff + tok0 - win + 1), Lk - 1) : 0;
         ps.nb = a.num_blocks;
         ps.nt = a.kv_nt != 0;
         if (nrel > 0) {

@@ -105,6 +105,33 @@ def test_extend_windows(orc, window, d, hq, hkv):
     assert_close(out, ref, W.BF16, f"extend window {window} d{d}")
 
 
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_extend_released_pages_are_not_read(orc, bs):
+    """Multi-token queries with a window: pages wholly before every query's window
+    released (table entries outside the pool, blocks NaN); a 64-key block of the
+    kernel can start inside such pages when they are smaller than the block."""
+    window = 100
+    c = W.make_extend_case([3000, 700, 64, 1500, 37], [4, 40, 5, 1, 130], 32, 8, 128, bs, W.BF16, seed=1700 + bs)
+    dev = DevExtend(c)
+    ref = oracle_extend(orc, c, window=window)
+    table = c.block_table.copy()
+    nan_blocks = []
+    for b, ctx in enumerate(c.context_lens):
+        lo = max(0, int(ctx) - int(c.q_lens[b]) - window + 1)   # the first new row's window edge
+        first_kept_page = lo // bs
+        nan_blocks += table[b, :first_kept_page].tolist()
+        table[b, :first_kept_page] = -1
+    assert nan_blocks
+    say(f"extend window with released pages bs{bs}")
+    kc, vc = dev.kc.clone(), dev.vc.clone()
+    idx = torch.tensor(nan_blocks, dtype=torch.long, device="cuda")
+    kc[idx] = float("nan")
+    vc[idx] = float("nan")
+    out = to_f64(pg.gqa_paged_extend(dev.q, dev.cu_q, kc, vc, to_dev(table), dev.ctx, c.max_q_len,
+                                     c.max_context_len, scale=float(c.scale), window=window))
+    assert_close(out, ref, W.BF16, f"extend released pages bs{bs}")
+
+
 def test_window_covering_everything_is_full_attention():
     """A window at least the longest context changes nothing: bit-identical outputs."""
     case = W.make_decode_case(LENS, 32, 8, 128, 16, W.BF16, seed=1600)
