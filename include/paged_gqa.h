@@ -325,6 +325,26 @@ int gqa_paged_decode_fp8(const void* q, const void* k_cache, const void* v_cache
                          size_t workspace_bytes, void* stream);
 
 /*
+ * gqa_paged_extend_fp8 -- gqa_paged_extend over FP8 pages: the same result as
+ * gqa_paged_extend over the values code * scale (bf16 q and out, fp32
+ * accumulation; each tile of codes is converted to bf16 exactly in LDS and the
+ * MFMA products are the bf16 ones; the K scale multiplies each score, the V
+ * scale each weight before its bf16 rounding, and the row sum adds the
+ * unrounded weights).  Same arguments, mask, window and workspace
+ * (gqa_paged_extend_workspace_size) as gqa_paged_extend, plus the scale pools
+ * [num_blocks, Hkv, block_size] fp32 (k_scale, v_scale, both non-NULL).
+ * Errors as for gqa_paged_extend; PGQA_ENOTSUP also for block_size below
+ * 1024 / head_dim (8 for head_dim 128, 16 for 64: the rows one 1 KB load of
+ * codes covers); PGQA_EINVAL also for scale pools of 4 GiB or more.
+ */
+int gqa_paged_extend_fp8(const void* q, const int32_t* cu_q, const void* k_cache, const void* v_cache,
+                         const float* k_scale, const float* v_scale, const int32_t* block_table,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch, int32_t total_q,
+                         int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, int32_t max_context_len, float scale,
+                         int32_t window, void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * paged_kv_copy_blocks -- the device half of copy-on-write (the lecture notes,
  * section 8.2, "Prefix Sharing (Copy-on-Write)": when sequences sharing prefix
  * blocks diverge, only the block being modified is copied).  For every pair p,

@@ -266,12 +266,15 @@ int gqa_varlen_prefill(const void* q, const void* k, const void* v, const int32_
     return hip_status(pgqa::launch_prefill(L, (hipStream_t)stream));
 }
 
-int gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_cache, const void* v_cache,
-                     const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
-                     int32_t batch, int32_t total_q, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
-                     int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_context_len, float scale,
-                     int32_t window, pgqa_dtype dtype, void* out, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+// Shared checks and launch of gqa_paged_extend and gqa_paged_extend_fp8
+// (k_scale / v_scale null: bf16 pages).
+static int extend_call(const void* q, const int32_t* cu_q, const void* k_cache, const void* v_cache,
+                       const float* k_scale, const float* v_scale, const int32_t* block_table,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch, int32_t total_q,
+                       int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t max_context_len, float scale, int32_t window,
+                       pgqa_dtype dtype, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    const bool fp8 = k_scale != nullptr || v_scale != nullptr;
     if (batch < 0 || total_q < 0 || max_q_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
         max_blocks_per_seq <= 0 || max_context_len < 0 || window < 0)
         return PGQA_EINVAL;
@@ -279,8 +282,13 @@ int gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_cache, co
     if (dtype != PGQA_BF16) return PGQA_ENOTSUP;
     int32_t lg = 0;
     if (!pow2_log2(block_size, &lg) || block_size > 256) return PGQA_ENOTSUP;
-    if (!pgqa::extend_supported(head_dim, num_q_heads / num_kv_heads, block_size)) return PGQA_ENOTSUP;
+    if (fp8 ? !pgqa::extend_supported_fp8(head_dim, num_q_heads / num_kv_heads, block_size)
+            : !pgqa::extend_supported(head_dim, num_q_heads / num_kv_heads, block_size))
+        return PGQA_ENOTSUP;
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PGQA_EINVAL;
+    // The kernel addresses a scale pool with 32-bit byte offsets.
+    if (fp8 && (int64_t)num_blocks * num_kv_heads * block_size * 4 > UINT32_MAX) return PGQA_EINVAL;
+    if (fp8 && (check_index_ptr(k_scale) || check_index_ptr(v_scale))) return PGQA_EINVAL;
     if ((int64_t)batch * max_blocks_per_seq > INT32_MAX) return PGQA_EINVAL;
     if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff()) return PGQA_EINVAL;
     if ((int64_t)total_q * num_q_heads * head_dim > ((int64_t)1 << 40)) return PGQA_EINVAL;
@@ -296,7 +304,32 @@ int gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_cache, co
     pgqa::ExtendLaunch L{q, k_cache, v_cache, cu_q, block_table, context_lens, out, batch, total_q, max_q_len,
                          max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, lg, num_blocks,
                          max_context_len, scale, window, workspace, workspace ? workspace_bytes : 0};
+    L.k_scale = k_scale;
+    L.v_scale = v_scale;
     return hip_status(pgqa::launch_extend(L, (hipStream_t)stream));
+}
+
+int gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                     int32_t batch, int32_t total_q, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_context_len, float scale,
+                     int32_t window, pgqa_dtype dtype, void* out, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    return extend_call(q, cu_q, k_cache, v_cache, nullptr, nullptr, block_table, max_blocks_per_seq, context_lens,
+                       batch, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_context_len, scale, window, dtype, out, workspace, workspace_bytes, stream);
+}
+
+int gqa_paged_extend_fp8(const void* q, const int32_t* cu_q, const void* k_cache, const void* v_cache,
+                         const float* k_scale, const float* v_scale, const int32_t* block_table,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch, int32_t total_q,
+                         int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, int32_t max_context_len, float scale,
+                         int32_t window, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!k_scale || !v_scale) return PGQA_EINVAL;
+    return extend_call(q, cu_q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks_per_seq, context_lens,
+                       batch, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_context_len, scale, window, PGQA_BF16, out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -428,15 +428,6 @@ __device__ __forceinline__ void bcast_heads(const float* vals, float* out, int l
     }
 }
 
-// 8 FP8 E4M3 codes -> 8 bf16 values (exact: every E4M3 value is a bf16 value),
-// in the order of a bf16 compute slice.
-__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 w) {
-    return u32x4{__builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false)),
-                 __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true)),
-                 __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false)),
-                 __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true))};
-}
-
 // This lane's slice of compute row r of a K or V tile (bf16 / fp32 as stored,
 // or FP8 codes converted to bf16).
 template <int ES, int D, int KES>

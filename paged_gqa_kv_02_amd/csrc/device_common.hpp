@@ -54,6 +54,15 @@ __device__ __forceinline__ float dot2_bf16(u32 a, u32 b, float acc) {
                                            acc, false);
 }
 
+// 8 FP8 E4M3 codes (little-endian bytes of w) -> 8 bf16 values in the same
+// order, as a bf16 row slice (exact: every E4M3 value is a bf16 value).
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 w) {
+    return u32x4{__builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false)),
+                 __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true)),
+                 __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false)),
+                 __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true))};
+}
+
 // ---- cross-lane ---------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -133,6 +142,21 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t
                      : "memory", "m0");
     else
         asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"((const char*)s),
+                     "s"(__builtin_amdgcn_readfirstlane(lds))
+                     : "memory", "m0");
+}
+// 4 bytes per lane: lane l copies 4 bytes from sbase + voff into LDS at lds + 4*l.
+__device__ __forceinline__ void dma4(const char* sbase, uint32_t voff, uint32_t lds, bool nt) {
+    const uint64_t p = (uint64_t)(uintptr_t)sbase;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint64_t s = ((uint64_t)hi << 32) | (uint64_t)lo;
+    if (nt)
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1 nt" ::"v"(voff), "s"((const char*)s),
+                     "s"(__builtin_amdgcn_readfirstlane(lds))
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"((const char*)s),
                      "s"(__builtin_amdgcn_readfirstlane(lds))
                      : "memory", "m0");
 }

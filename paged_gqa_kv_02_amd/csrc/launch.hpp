@@ -166,6 +166,10 @@ struct ExtendLaunch {
     int32_t non_causal;  // 1: every row sees all keys [0, ctx) (rows = query heads of one token)
     int32_t fixed_qlen;  // > 0: sequence s holds rows [s * fixed_qlen, (s + 1) * fixed_qlen); cu_q unused
     int32_t chunk_blocks;  // > 0: key chunks of this many 64-key blocks (0: the library's choice)
+    // FP8 pages: k_cache / v_cache hold E4M3 codes and these the fp32 row scales
+    // [num_blocks, Hkv, block_size]; null for bf16 pages.
+    const float* k_scale;
+    const float* v_scale;
 };
 
 // Workspace bytes for the library's key split of a paged multi-token call (0: none).
@@ -174,6 +178,7 @@ size_t extend_workspace_bytes(int32_t batch, int32_t total_q, int32_t max_q_len,
 
 // Is there a paged multi-token kernel for this (head_dim, group size, block size)?
 bool extend_supported(int32_t head_dim, int32_t group, int32_t block_size);
+bool extend_supported_fp8(int32_t head_dim, int32_t group, int32_t block_size);
 
 hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream);
 

@@ -98,6 +98,9 @@ struct PrefillArgs {
     int32_t kchunk;          // key blocks per chunk
     float* part_o;           // [total_tokens, Hq, nchunk, D]
     float* part_ml;          // [total_tokens, Hq, nchunk, 2]  (m in log2 units, l)
+    // FP8 pages only (k, v are then code pools [num_blocks, Hkv, block_size, d] uint8).
+    const float* k_scale;    // row scales [num_blocks, Hkv, block_size]
+    const float* v_scale;
 };
 
 #ifndef PGQA_KREADS_AHEAD
@@ -210,6 +213,28 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const DmaLane<D
     }
 }
 
+// FP8 pages (E4M3 codes, one fp32 scale per key row): a tile's codes (BN rows
+// of D bytes) are DMA'd into the upper half of the tile's bf16 ring slot, 1 KB
+// (RPL8 rows of one page) per wave-load, K waves and V waves NPW8 loads each;
+// after they land, all waves convert them into the slot's bf16 layout (exact),
+// so the MFMA code is the bf16 one.  The tile's row scales go to a small LDS
+// area by one 4-byte-per-lane DMA per pool (wave 1: K, wave 3: V).
+template <int D>
+struct Q8Geo {
+    static constexpr int CODEB = BN * D;          // code bytes per tile and pool
+    static constexpr int LOADS = CODEB / 1024;    // 1 KB wave-loads per tile and pool
+    static constexpr int NPW8 = LOADS / 2;        // per DMA wave
+    static constexpr int RPL8 = 1024 / D;         // rows per wave-load
+    static constexpr int NG = BN / RPL8;          // wave-loads (row groups) per tile
+    static constexpr int CPT = CODEB / 16 / 256;  // 16-byte code chunks per thread in the conversion
+    static_assert(CPT >= 1 && NG <= 8, "FP8 tile geometry");
+};
+
+// LDS of the row scales: K scales in three slots (a tile's K scales are used one
+// block after its codes, when its scores are scaled), V scales in two; 64 floats each.
+constexpr int kScaleSlotB = BN * 4;
+constexpr int kScaleB = 5 * kScaleSlotB;
+
 // Paged K/V: the lane's offset inside wave-load j, relative to that load's
 // first row (the swizzle key only depends on the row modulo 16, and loads j and
 // j + JP are 16 rows apart).
@@ -247,16 +272,23 @@ struct PagedSrc {
 };
 
 // First key row (relative to the sequence) of wave-load j of tile kb.
-template <int D>
+template <int D, bool Q8 = false>
 __device__ __forceinline__ int paged_row0(int kb, int j) {
-    return kb * BN + j * PGeo<D>::RPL;
+    return kb * BN + j * (Q8 ? Q8Geo<D>::RPL8 : PGeo<D>::RPL);
 }
 
-template <int D>
+template <int D, bool Q8 = false>
 __device__ __forceinline__ void paged_load_ids(PagedSrc<D>& ps, int kb) {
+    if constexpr (Q8) {
+        // FP8 pages: the ids of every row group of the tile (the scale loads need them all).
 #pragma unroll
-    for (int j = 0; j < PagedSrc<D>::NPW; ++j)
-        ps.id[j] = ps.bt[min(max(paged_row0<D>(kb, ps.j0 + j), ps.lo), ps.last) >> ps.lbs];
+        for (int g = 0; g < Q8Geo<D>::NG; ++g)
+            ps.id[g] = ps.bt[min(max(paged_row0<D, true>(kb, g), ps.lo), ps.last) >> ps.lbs];
+    } else {
+#pragma unroll
+        for (int j = 0; j < PagedSrc<D>::NPW; ++j)
+            ps.id[j] = ps.bt[min(max(paged_row0<D>(kb, ps.j0 + j), ps.lo), ps.last) >> ps.lbs];
+    }
 }
 
 // DMA of tile kb from the pages (same LDS placement as issue_tile).  A load's
@@ -297,8 +329,97 @@ __device__ __forceinline__ void issue_tile_paged(const PagedSrc<D>& ps, const Dm
     }
 }
 
-template <int D, int HG, bool PAGED>
+// DMA of tile kb of FP8 pages: codes into the upper half of ring slot `par`
+// (rows in plain order, D bytes each), and, from wave 1 (K) and wave 3 (V), the
+// tile's 64 row scales into scale slot `ssl`.  Rows outside [lo, last] re-read
+// the nearest of the two (as in issue_tile_paged).
+template <int D>
+__device__ __forceinline__ void issue_tile_paged_q8(const PagedSrc<D>& ps, const float* scale_pool, uint32_t ring,
+                                                    uint32_t scales, int kb, int par, int ssl, int wave, int lane,
+                                                    int kvh, int hkv) {
+    using P = PGeo<D>;
+    using Q = Q8Geo<D>;
+    const uint32_t dst = ring + (ps.isv ? 2 * P::TILEB : 0) + par * P::TILEB + P::TILEB / 2;
+    const int bs_mask = (1 << ps.lbs) - 1;
+    const int64_t row_b = D;                                    // code bytes per row
+    const int64_t blk_b = ((int64_t)hkv << ps.lbs) * row_b;     // code bytes per block
+    const int64_t head_b = ((int64_t)kvh << ps.lbs) * row_b;
+    // (Ids are picked with constant indexes: a runtime index would put the array in scratch.)
+    auto base_of = [&](int id, int rb) {
+        return ps.pool + (int64_t)clampi(id, 0, ps.nb - 1) * blk_b + head_b + (int64_t)(rb & bs_mask) * row_b;
+    };
+    const bool full = kb * BN >= ps.lo && kb * BN + BN <= ps.last + 1;
+    const int r = lane / (D / 16);
+    const int col = (lane % (D / 16)) * 16;
+#pragma unroll
+    for (int j = 0; j < Q::NPW8; ++j) {
+        const int g = (wave & 1) * Q::NPW8 + j;
+        const int id = (wave & 1) ? ps.id[Q::NPW8 + j] : ps.id[j];
+        const int row0 = paged_row0<D, true>(kb, g);
+        if (full) {
+            dma16(base_of(id, row0), (uint32_t)(lane * 16), dst + g * 1024, ps.nt);
+        } else {
+            const int rb = min(max(row0, ps.lo), ps.last);
+            const int rc = min(max(row0 + r, ps.lo), ps.last);
+            dma16(base_of(id, rb), (uint32_t)((rc - rb) * row_b + col), dst + g * 1024, ps.nt);
+        }
+    }
+    if (wave & 1) {
+        // Row scale of key kb*BN + lane (clamped like the codes): its row group's
+        // block id, picked from the wave's uniform ids.
+        const int key = min(max(kb * BN + lane, ps.lo), ps.last);
+        const int g = (key - kb * BN) / Q::RPL8;
+        int id = ps.id[0];
+#pragma unroll
+        for (int gg = 1; gg < Q::NG; ++gg) id = g == gg ? ps.id[gg] : id;
+        id = clampi(id, 0, ps.nb - 1);
+        const uint32_t off = (uint32_t)((((int64_t)id * hkv + kvh) << ps.lbs) + (key & bs_mask)) * 4u;
+        dma4((const char*)scale_pool, off, scales + ssl * kScaleSlotB, ps.nt);
+    }
+}
+
+// Conversion of landed FP8 code tiles into the bf16 ring layout: the K tile of
+// slot kpar (kpar < 0: none) and the V tile of slot vpar.  All 256 threads read
+// their code chunks, wait for every wave (codes and converted rows share the
+// slot's upper half), then write the bf16 rows (swizzled like DMA'd bf16 tiles)
+// and wait again.
+template <int D>
+__device__ __forceinline__ void convert_q8(PGQA_LDS char* ring, int kpar, int vpar) {
+    using P = PGeo<D>;
+    using Q = Q8Geo<D>;
+    const int t = threadIdx.x;
+    u32x4 kc[Q::CPT], vc[Q::CPT];
+#pragma unroll
+    for (int i = 0; i < Q::CPT; ++i) {
+        const int c = t + 256 * i;
+        if (kpar >= 0) kc[i] = lds_read_16(ring + kpar * P::TILEB + P::TILEB / 2 + c * 16);
+        if (vpar >= 0) vc[i] = lds_read_16(ring + (2 + vpar) * P::TILEB + P::TILEB / 2 + c * 16);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < Q::CPT; ++i) {
+        const int c = t + 256 * i;
+        const int row = c / (D / 16);
+        const int c16 = c % (D / 16);
+        const int o0 = row * P::ROWB + (((2 * c16) ^ swz_key<D>(row)) << 4);
+        const int o1 = row * P::ROWB + (((2 * c16 + 1) ^ swz_key<D>(row)) << 4);
+        if (kpar >= 0) {
+            PGQA_LDS char* kt = ring + kpar * P::TILEB;
+            *(PGQA_LDS u32x4*)(kt + o0) = fp8x8_to_bf16(u32x2{kc[i].x, kc[i].y});
+            *(PGQA_LDS u32x4*)(kt + o1) = fp8x8_to_bf16(u32x2{kc[i].z, kc[i].w});
+        }
+        if (vpar >= 0) {
+            PGQA_LDS char* vt = ring + (2 + vpar) * P::TILEB;
+            *(PGQA_LDS u32x4*)(vt + o0) = fp8x8_to_bf16(u32x2{vc[i].x, vc[i].y});
+            *(PGQA_LDS u32x4*)(vt + o1) = fp8x8_to_bf16(u32x2{vc[i].z, vc[i].w});
+        }
+    }
+    __syncthreads();
+}
+
+template <int D, int HG, bool PAGED, bool Q8 = false>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+    static_assert(PAGED || !Q8, "FP8 K/V only from pages");
     using P = PGeo<D>;
     constexpr int TB = 4 / HG;               // 32-row token blocks per workgroup
     constexpr int KSTEPS = P::KSTEPS, DBLK = P::DBLK;
@@ -458,6 +579,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     DmaLane<D> dl;
     PagedSrc<D> ps;
     const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+    // FP8 row scales: K scales of relative tile t in slot t % 3, V scales in slot 3 + t % 2.
+    const uint32_t scale_addr = ring_addr + 4 * P::TILEB;
+    const PGQA_LDS float* scale_lds = (const PGQA_LDS float*)(ring + 4 * P::TILEB);
+    // DMA of relative tile t (key block kb0 + t) of this wave's pool.
+    auto issue_paged = [&](int t, int ln) {
+        if constexpr (Q8)
+            issue_tile_paged_q8<D>(ps, ps.isv ? a.v_scale : a.k_scale, ring_addr, scale_addr, kb0 + t, t & 1,
+                                   ps.isv ? 3 + (t & 1) : t % 3, wave, ln, kvh, a.num_kv_heads);
+        else
+            issue_tile_paged<D>(ps, dl, ring_addr, kb0 + t, t & 1, ln);
+    };
     if constexpr (PAGED) {
         dma_lane_init_paged<D>(dl, lane);
         ps.bt = (ConstI32Ptr)(a.block_table + (int64_t)s * a.max_blocks_per_seq);
@@ -472,11 +604,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         ps.nb = a.num_blocks;
         ps.nt = a.kv_nt != 0;
         if (nrel > 0) {
-            paged_load_ids<D>(ps, kb0);
-            issue_tile_paged<D>(ps, dl, ring_addr, kb0, 0, lane);
+            paged_load_ids<D, Q8>(ps, kb0);
+            issue_paged(0, lane);
             if (!ps.isv && nrel > 1) {
-                paged_load_ids<D>(ps, kb0 + 1);
-                issue_tile_paged<D>(ps, dl, ring_addr, kb0 + 1, 1, lane);
+                paged_load_ids<D, Q8>(ps, kb0 + 1);
+                issue_paged(1, lane);
             }
         }
     } else {
@@ -538,6 +670,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], int kr, auto par, auto has_next) {
         constexpr int PAR = decltype(par)::value;   // kr % 2
         const int j0 = (kb0 + kr) * BN;
+        // FP8 pages: scores times the keys' row scales (key offsets as in the masking below).
+        if constexpr (Q8) {
+            const PGQA_LDS float* ks = scale_lds + (kr % 3) * BN + 4 * (lane_now() >> 5);
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                const f32x4 k4 = *(const PGQA_LDS f32x4*)(ks + 8 * g);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) cur[g >> 2][4 * (g & 3) + t] *= k4[t];
+            }
+        }
         // Masking (last block of the sequence, a block crossing the diagonal,
         // or one crossing the window's lower edge): key j0 + off is kept iff
         // llim <= off <= lim, with off = 32*kb2 + 8*(i/4) + i%4 and the lane's
@@ -587,10 +729,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
             float p[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(cur[kk >> 1][8 * (kk & 1) + j], cs, -m));
+            if constexpr (Q8) {
+                // Weights times the values' row scales (accumulator entry 8*(kk%2) + j
+                // of half kk/2 is key 16*kk + 8*(j/4) + 4*half + j%4); the row sum
+                // takes the plain weights.
+                const PGQA_LDS float* vs = scale_lds + (3 + PAR) * BN + 16 * kk + 4 * (lane_now() >> 5);
+                const f32x4 v0 = *(const PGQA_LDS f32x4*)vs;
+                const f32x4 v1 = *(const PGQA_LDS f32x4*)(vs + 8);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                pb[kk][j] = pack_bf16x2_rne_hw(p[2 * j], p[2 * j + 1]);
-                lsum = dot2_bf16(pb[kk][j], ones_bf16x2, lsum);
+                for (int j = 0; j < 4; ++j) {
+                    lsum += p[2 * j] + p[2 * j + 1];
+                    const f32x4& vv = j < 2 ? v0 : v1;
+                    pb[kk][j] = pack_bf16x2_rne_hw(p[2 * j] * vv[(2 * j) & 3], p[2 * j + 1] * vv[(2 * j + 1) & 3]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pb[kk][j] = pack_bf16x2_rne_hw(p[2 * j], p[2 * j + 1]);
+                    lsum = dot2_bf16(pb[kk][j], ones_bf16x2, lsum);
+                }
             }
         }
         if constexpr (decltype(has_next)::value) {
@@ -637,16 +794,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         // flight during the block's LDS reads (whose waits would otherwise also
         // wait for it, scalar loads returning out of order).
         if constexpr (PAGED)
-            if (tb < nrel) paged_load_ids<D>(ps, kb0 + tb);
+            if (tb < nrel) paged_load_ids<D, Q8>(ps, kb0 + tb);
         wait_vmcnt<0>();
         __syncthreads();
         if (tb < nrel) {
             if constexpr (PAGED) {
-                issue_tile_paged<D>(ps, dl, ring_addr, kb0 + tb, tb & 1, lane_now());
+                issue_paged(tb, lane_now());
             } else {
                 issue_tile<D>(a, dl, ring_addr, kb0 + tb, tb & 1, seq0, Lk, kvh, wave, lane_now(), kvstride);
             }
         }
+        // FP8 pages: the codes of K(kr+1) and V(kr) have landed; into bf16 (the
+        // tiles just issued go to the other slots).
+        if constexpr (Q8) convert_q8<D>(ring, kr + 1 < nrel ? (kr + 1) & 1 : -1, kr & 1);
     };
     // Blocks kb0 .. kb0 + kend are computed (kend = last_kb - kb0, or -1 for a
     // wave with no rows or no keys); each but the last overlaps the next block's
@@ -660,6 +820,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     f32x16 sa[2], sb[2];
     wait_vmcnt<0>();
     __syncthreads();
+    if constexpr (Q8)
+        if (nrel > 0) convert_q8<D>(ring, 0, -1);
     const int kend = active && last_kb >= 0 ? min(last_kb, kb1 - 1) - kb0 : -1;
     if (kend >= 0) scores(sa, I0{});
     int kb = 0;
@@ -793,26 +955,38 @@ __global__ __launch_bounds__(256) void extend_merge_kernel(PrefillArgs a) {
 
 typedef void (*PrefillFn)(PrefillArgs);
 
+template <int D, bool PAGED, bool Q8>
+PrefillFn pick_hg(int h) {
+    if constexpr (!PAGED && Q8) {
+        return nullptr;
+    } else {
+        return h == 4 ? prefill_kernel<D, 4, PAGED, Q8>
+                      : (h == 2 ? prefill_kernel<D, 2, PAGED, Q8> : prefill_kernel<D, 1, PAGED, Q8>);
+    }
+}
+
 template <bool PAGED>
-bool pick(int head_dim, int group, PrefillFn* fn, int* hg) {
+bool pick(int head_dim, int group, PrefillFn* fn, int* hg, bool q8 = false) {
     const int h = group >= 4 ? 4 : group;
     if (group != 1 && group != 2 && group % 4 != 0) return false;
     if (group > 64) return false;
+    if (q8 && !PAGED) return false;
     *hg = h;
     if (head_dim == 128) {
-        *fn = h == 4 ? prefill_kernel<128, 4, PAGED>
-                     : (h == 2 ? prefill_kernel<128, 2, PAGED> : prefill_kernel<128, 1, PAGED>);
+        *fn = q8 ? pick_hg<128, PAGED, true>(h) : pick_hg<128, PAGED, false>(h);
         return true;
     }
     if (head_dim == 64) {
-        *fn = h == 4 ? prefill_kernel<64, 4, PAGED>
-                     : (h == 2 ? prefill_kernel<64, 2, PAGED> : prefill_kernel<64, 1, PAGED>);
+        *fn = q8 ? pick_hg<64, PAGED, true>(h) : pick_hg<64, PAGED, false>(h);
         return true;
     }
     return false;
 }
 
-size_t lds_bytes(int head_dim) { return head_dim == 128 ? 4 * PGeo<128>::TILEB : 4 * PGeo<64>::TILEB; }
+// Ring (two K and two V tiles), plus the row-scale slots with FP8 pages.
+size_t lds_bytes(int head_dim, bool q8) {
+    return (head_dim == 128 ? 4 * PGeo<128>::TILEB : 4 * PGeo<64>::TILEB) + (q8 ? kScaleB : 0);
+}
 
 int rows_per_load(int head_dim) { return head_dim == 128 ? PGeo<128>::RPL : PGeo<64>::RPL; }
 
@@ -876,7 +1050,7 @@ int64_t launch_grid(PrefillArgs& a, int hg, int group, int64_t total_rows) {
 hipError_t launch(PrefillFn fn, PrefillArgs& a, int hg, int group, int head_dim, hipStream_t stream) {
     const int64_t wgs = launch_grid(a, hg, group, a.total_tokens);
     if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(256), lds_bytes(head_dim), stream, a);
+    hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(256), lds_bytes(head_dim, a.k_scale != nullptr), stream, a);
     return hipGetLastError();
 }
 
@@ -892,6 +1066,13 @@ bool extend_supported(int32_t head_dim, int32_t group, int32_t block_size) {
     PrefillFn fn;
     int hg;
     return pick<true>(head_dim, group, &fn, &hg) && block_size >= rows_per_load(head_dim) && block_size <= 256;
+}
+
+bool extend_supported_fp8(int32_t head_dim, int32_t group, int32_t block_size) {
+    PrefillFn fn;
+    int hg;
+    // A 1 KB wave-load of codes (1024 / head_dim rows) must lie in one page.
+    return pick<true>(head_dim, group, &fn, &hg, true) && block_size >= 1024 / head_dim && block_size <= 256;
 }
 
 hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
@@ -926,9 +1107,14 @@ hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream) {
     const int group = L.num_q_heads / L.num_kv_heads;
     PrefillFn fn;
     int hg;
-    if (!extend_supported(L.head_dim, group, 1 << L.block_size_log2)) return hipErrorInvalidValue;
-    pick<true>(L.head_dim, group, &fn, &hg);
+    const bool q8 = L.k_scale != nullptr;
+    if (q8 ? !extend_supported_fp8(L.head_dim, group, 1 << L.block_size_log2)
+           : !extend_supported(L.head_dim, group, 1 << L.block_size_log2))
+        return hipErrorInvalidValue;
+    pick<true>(L.head_dim, group, &fn, &hg, q8);
     PrefillArgs a = {};
+    a.k_scale = L.k_scale;
+    a.v_scale = L.v_scale;
     a.q = (const char*)L.q;
     a.k = (const char*)L.k_cache;
     a.v = (const char*)L.v_cache;

@@ -350,3 +350,38 @@ def gqa_paged_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                                     workspace.numel() * workspace.element_size(), _stream())
     check("gqa_paged_decode_fp8", st)
     return out
+
+
+def gqa_paged_extend_fp8(q: torch.Tensor, cu_q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         k_scale: torch.Tensor, v_scale: torch.Tensor, block_table: torch.Tensor,
+                         context_lens: torch.Tensor, max_q_len: int, max_context_len: int, scale: float,
+                         out: Optional[torch.Tensor] = None, window: int = 0,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gqa_paged_extend over FP8 pages: bf16 q [total_q, Hq, d] -> bf16 out [total_q, Hq, d]."""
+    _rank("q", q, 3)
+    T, hq, d = q.shape
+    _u8(k_cache, v_cache)
+    _f32(k_scale, v_scale)
+    nb, hkv, bs, d2 = _pools(k_cache, v_cache)
+    if d2 != d:
+        raise ValueError("head_dim mismatch")
+    if q.dtype != torch.bfloat16:
+        raise TypeError("queries over FP8 pages are bfloat16")
+    _shape("k_scale", k_scale, (nb, hkv, bs))
+    _shape("v_scale", v_scale, (nb, hkv, bs))
+    _rank("cu_q", cu_q, 1)
+    batch = cu_q.numel() - 1
+    _table(block_table, batch)
+    _shape("context_lens", context_lens, (batch,))
+    out = _out(out, q)
+    if workspace is None:
+        workspace = extend_workspace(batch, T, int(max_q_len), hq, hkv, d, int(max_context_len), q.device)
+    _dev(q, cu_q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, out, workspace)
+    _i32(cu_q, block_table, context_lens)
+    st = lib().gqa_paged_extend_fp8(q.data_ptr(), cu_q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                    k_scale.data_ptr(), v_scale.data_ptr(), block_table.data_ptr(),
+                                    block_table.shape[1], context_lens.data_ptr(), batch, T, int(max_q_len), hq,
+                                    hkv, d, bs, nb, int(max_context_len), float(scale), int(window), out.data_ptr(),
+                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream())
+    check("gqa_paged_extend_fp8", st)
+    return out

@@ -24,7 +24,7 @@ def test_header_declares_the_calls():
     names = L.header_functions()
     for n in ("paged_kv_write", "paged_kv_gather", "gqa_paged_decode", "gqa_paged_decode_workspace_size",
               "gqa_varlen_prefill", "gqa_paged_extend", "paged_kv_copy_blocks", "pgqa_bm_create", "pgqa_bm_append",
-              "gqa_paged_decode_noalloc",
+              "gqa_paged_decode_noalloc", "gqa_paged_extend_fp8", "gqa_paged_decode_fp8", "paged_kv_write_fp8",
               "pgqa_bm_fork", "pgqa_bm_free_sequence", "pgqa_status_string"):
         assert n in names
 
@@ -239,6 +239,35 @@ def test_fp8_write_validation(lib):
     assert w(dt=F32) == ENOTSUP
     assert w(d=96) == ENOTSUP
     assert w(batch=0) == 0
+
+
+def _extend8(lib, **kw):
+    a = dict(q=P[0], cu=P[1], kc=P[2], vc=P[3], ks=P[7], vs=P[8], bt=P[4], maxb=4, cl=P[5], batch=2, T=12, maxq=9,
+             hq=32, hkv=8, d=128, bs=16, nb=8, maxctx=64, scale=0.088, win=0, out=P[6], ws=None, wsb=0)
+    a.update(kw)
+    return lib.gqa_paged_extend_fp8(a["q"], a["cu"], a["kc"], a["vc"], a["ks"], a["vs"], a["bt"], a["maxb"], a["cl"],
+                                    a["batch"], a["T"], a["maxq"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"],
+                                    a["maxctx"], a["scale"], a["win"], a["out"], a["ws"], a["wsb"], None)
+
+
+def test_fp8_extend_validation(lib):
+    assert _extend8(lib, ks=None) == EINVAL
+    assert _extend8(lib, vs=None) == EINVAL
+    assert _extend8(lib, ks=P[7] + 2) == EINVAL
+    assert _extend8(lib, hq=30) == EINVAL
+    assert _extend8(lib, maxctx=65) == EINVAL
+    assert _extend8(lib, cu=None) == EINVAL
+    assert _extend8(lib, out=P[6] + 2) == EINVAL
+    assert _extend8(lib, win=-1) == EINVAL
+    assert _extend8(lib, scale=float("nan")) == EINVAL
+    # Scale pools of 4 GiB or more (32-bit offsets in the kernel).
+    assert _extend8(lib, nb=1 << 19, bs=256, hkv=8, hq=32, maxb=1 << 10, maxctx=64) == EINVAL
+    assert _extend8(lib, d=32) == ENOTSUP
+    assert _extend8(lib, hq=24, hkv=8) == ENOTSUP
+    assert _extend8(lib, bs=4, maxctx=16) == ENOTSUP         # one 1 KB load of 128-byte code rows spans 8 rows
+    assert _extend8(lib, d=64, bs=8, maxctx=32) == ENOTSUP   # 16 rows of 64-byte codes
+    assert _extend8(lib, batch=0) == 0
+    assert _extend8(lib, T=0) == 0
 
 
 def test_extend_workspace_size(lib):

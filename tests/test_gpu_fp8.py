@@ -119,3 +119,138 @@ def test_workload(orc, key):
     out, ref = _decode_case_fp8(orc, c)
     e = assert_close(out, ref, W.BF16, f"fp8 {key}")
     say(f"fp8 {key}: {e}")
+
+
+# ---- several new tokens per sequence over FP8 pages (gqa_paged_extend_fp8) ----
+
+def _extend_case_fp8(orc, c, window=0, context_lens=None, workspace=None):
+    """Device result and the oracle's multi-token attention over the dequantised
+    cache (fp64, bf16 queries widened exactly)."""
+    dev, host = _write_both(orc, c)
+    dk, dv, dks, dvs = dev
+    hk, hv, hks, hvs = host
+    ctx = c.context_lens if context_lens is None else np.asarray(context_lens, np.int32)
+    kw = {} if workspace is None else {"workspace": workspace}
+    out = pg.gqa_paged_extend_fp8(to_dev(c.q), to_dev(c.cu_q), dk, dv, dks, dvs, to_dev(c.block_table),
+                                  to_dev(ctx), c.max_q_len, int(ctx.max()) if len(ctx) else 0,
+                                  scale=float(c.scale), window=window, **kw)
+    qd = (c.q.view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = orc.gqa_paged_extend(qd, c.cu_q, orc.dequantize_fp8(hk, hks), orc.dequantize_fp8(hv, hvs),
+                               c.block_table, ctx, c.scale, window=window)
+    return to_f64(out), ref
+
+
+EXT_PREFIX = [0, 1, 31, 64, 100, 7, 250]
+EXT_QLENS = [1, 33, 64, 5, 129, 40, 16]
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2), (32, 8), (16, 1), (64, 1)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_extend_shapes(orc, hq, hkv, d):
+    c = W.make_extend_case(EXT_PREFIX, EXT_QLENS, hq, hkv, d, 16, W.BF16, seed=2500 + hq * 10 + hkv + d)
+    say(f"fp8 extend {hq}/{hkv} d{d}")
+    out, ref = _extend_case_fp8(orc, c)
+    assert_close(out, ref, W.BF16, f"fp8 extend {hq}/{hkv} d{d}")
+
+
+@pytest.mark.parametrize("d,bs", [(128, 8), (128, 16), (128, 64), (128, 256), (64, 16), (64, 32), (64, 256)])
+def test_extend_block_sizes(orc, d, bs):
+    c = W.make_extend_case([0, bs - 1, bs, 3 * bs + 1, 70], [bs + 1, 1, 2 * bs, 64, 97], 8, 2, d, bs, W.BF16,
+                           seed=2600 + bs + d)
+    say(f"fp8 extend bs{bs} d{d}")
+    out, ref = _extend_case_fp8(orc, c)
+    assert_close(out, ref, W.BF16, f"fp8 extend bs{bs} d{d}")
+
+
+def test_extend_single_token_equals_decode(orc):
+    """q_len = 1 everywhere: FP8 decode over the same pages, both against the oracle."""
+    c = W.make_extend_case([0, 15, 16, 300, 1000, 2047], [1] * 6, 32, 8, 128, 16, W.BF16, seed=2610)
+    say("fp8 extend q_len=1 vs fp8 decode")
+    out, ref = _extend_case_fp8(orc, c)
+    assert_close(out, ref, W.BF16, "fp8 extend q_len=1")
+    dc = W.DecodeCase(name="x", dtype=W.BF16, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                      context_lens=c.context_lens, cu_ctx=c.cu_ctx, q=c.q, k=c.k, v=c.v,
+                      block_table=c.block_table, num_blocks=c.num_blocks, scale=c.scale)
+    dec, dref = _decode_case_fp8(orc, dc)
+    assert np.array_equal(dref, ref)
+    assert_close(dec, ref, W.BF16, "fp8 decode")
+
+
+def test_extend_edges(orc):
+    """Empty sequences, a context shorter than its query count (rows with no key
+    give 0), and a sequence with no context at all."""
+    c = W.make_extend_case([5, 0, 40, 3, 0, 16], [0, 0, 70, 9, 4, 33], 8, 2, 128, 16, W.BF16, seed=2620)
+    ctx = c.context_lens.copy()
+    ctx[3] = 4
+    ctx[4] = 0
+    say("fp8 extend edges")
+    out, ref = _extend_case_fp8(orc, c, context_lens=ctx)
+    qa = int(c.cu_q[3])
+    assert (ref[qa:qa + 5] == 0).all() and (out[qa:qa + 5] == 0).all()
+    assert (out[int(c.cu_q[4]):int(c.cu_q[5])] == 0).all()
+    assert_close(out, ref, W.BF16, "fp8 extend edges")
+
+
+def test_extend_sharpened_queries(orc):
+    c = W.make_extend_case([10, 200, 63], [100, 17, 65], 32, 8, 128, 16, W.BF16, seed=2630)
+    c.q = W.f32_to_bf16_bits(W.bf16_bits_to_f32(c.q) * np.float32(4.0))
+    say("fp8 extend sharpened")
+    out, ref = _extend_case_fp8(orc, c)
+    assert np.abs(ref).max() > 0.5
+    assert_close(out, ref, W.BF16, "fp8 extend sharpened")
+
+
+@pytest.mark.parametrize("q_len,window,d", [(4, 0, 128), (7, 300, 128), (37, 1000, 64), (40, 0, 64)])
+def test_extend_key_split_and_window(orc, q_len, window, d):
+    """Few query tokens over long contexts (the library splits the key range),
+    with and without a window; also with no workspace (no split)."""
+    prefix = [3000, 17, 1024 - q_len, 1025 - q_len, 2048, 4000, 64, 2500]
+    c = W.make_extend_case(prefix, [q_len] * len(prefix), 8, 2, d, 16, W.BF16, seed=2640 + q_len + window + d)
+    assert pg.gqa_paged_extend_workspace_size(c.batch, c.total_q, c.max_q_len, 8, 2, d, c.max_context_len) > 0
+    say(f"fp8 extend key split q_len={q_len} window={window} d{d}")
+    out, ref = _extend_case_fp8(orc, c, window=window)
+    assert_close(out, ref, W.BF16, "fp8 split")
+    out1, _ = _extend_case_fp8(orc, c, window=window, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    assert_close(out1, ref, W.BF16, "fp8 no split")
+
+
+@pytest.mark.parametrize("key", ["chunked_prefill", "spec_verify"])
+def test_extend_workload(orc, key):
+    """The multi-token workloads over FP8 pages in the benchmark's launch
+    configuration, every output against the oracle."""
+    c = W.make_workload(key)
+    say(f"fp8 extend workload {key}")
+    out, ref = _extend_case_fp8(orc, c)
+    e = assert_close(out, ref, W.BF16, f"fp8 extend {key}")
+    say(f"fp8 extend {key}: {e}")
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_extend_released_pages_are_not_read(orc, bs):
+    """A window over FP8 pages with the pages before every query's window released
+    (table entries -1, their codes NaN, their scales NaN)."""
+    window = 100
+    c = W.make_extend_case([3000, 700, 64, 1500, 37], [4, 40, 5, 1, 130], 32, 8, 128, bs, W.BF16, seed=2700 + bs)
+    dev, host = _write_both(orc, c)
+    dk, dv, dks, dvs = dev
+    hk, hv, hks, hvs = host
+    qd = (c.q.view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = orc.gqa_paged_extend(qd, c.cu_q, orc.dequantize_fp8(hk, hks), orc.dequantize_fp8(hv, hvs),
+                               c.block_table, c.context_lens, c.scale, window=window)
+    table = c.block_table.copy()
+    gone = []
+    for b, ctx in enumerate(c.context_lens):
+        lo = max(0, int(ctx) - int(c.q_lens[b]) - window + 1)
+        gone += table[b, :lo // bs].tolist()
+        table[b, :lo // bs] = -1
+    assert gone
+    idx = torch.tensor(gone, dtype=torch.long, device="cuda")
+    for pool in (dk, dv):
+        pool[idx] = 0x7F
+    for pool in (dks, dvs):
+        pool[idx] = float("nan")
+    say(f"fp8 extend window with released pages bs{bs}")
+    out = pg.gqa_paged_extend_fp8(to_dev(c.q), to_dev(c.cu_q), dk, dv, dks, dvs, to_dev(table),
+                                  to_dev(c.context_lens), c.max_q_len, c.max_context_len, scale=float(c.scale),
+                                  window=window)
+    assert_close(to_f64(out), ref, W.BF16, f"fp8 extend released pages bs{bs}")
