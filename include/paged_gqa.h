@@ -90,6 +90,15 @@ enum {
     PGQA_EHIP = 4     /* a HIP launch failed */
 };
 
+/* Flags of pgqa_check_contents (status[0]). */
+enum {
+    PGQA_CHECK_BLOCK_ID = 1,      /* a page the call would touch has a block id outside [0, num_blocks) */
+    PGQA_CHECK_CONTEXT = 2,       /* a context length outside [0, max_context_len] (or a write past the table row) */
+    PGQA_CHECK_ROWS = 4,          /* row offsets not starting at 0, decreasing, not ending at the row
+                                     count, or a sequence with more rows than max_rows */
+    PGQA_CHECK_SHORT_CONTEXT = 8  /* fewer cached positions than new query rows */
+};
+
 /* Supported shapes: head_dim in {16, 32, 64, 128}; block_size a power of two in
  * [1, 256]; Hq / Hkv in {1, 2, 4, 8, 16, 32, 64}. */
 
@@ -410,6 +419,38 @@ int32_t pgqa_bm_num_free_blocks(const pgqa_block_manager* bm);
 
 /* Static, human-readable text of a status code. */
 const char* pgqa_status_string(int status);
+
+/*
+ * pgqa_check_contents -- debugging aid: checks on the device the promises the
+ * calls above take on trust about device array contents (the conventions
+ * section: block ids of every used page inside the pool, which the paging
+ * passages require of a block table; context lengths within the host bound;
+ * row offsets non-decreasing from 0 to the row count, as a packed batch's
+ * offsets are by construction, itinai.com/?p=48087, first paragraph).  It
+ * reads and reports, nothing else; the hot path never runs it.  Pass the
+ * arrays of the call to be checked:
+ *   decode:   block_table, context_lens (cu_rows = start_pos = NULL); with
+ *             window > 0 only pages from ctx - window on are checked
+ *   extend:   block_table, context_lens, cu_rows = cu_q, total_rows = total_q,
+ *             max_rows = max_q_len (pages from the first row's window edge on)
+ *   prefill:  cu_rows = cu_seqlens, total_rows, max_rows = max_seqlen
+ *   KV write: block_table, cu_rows = cu_seqlens, start_pos (the pages of the
+ *             written positions, which the write skips when their id is bad)
+ * NULL arrays are not checked; max_rows < 0 leaves the per-sequence row count
+ * unchecked.  The kernels read only inside the caller's arrays whatever the
+ * contents (a length past the table row is cut to it).
+ *   status   device int32[4], written in stream order: [0] PGQA_CHECK_* flags
+ *            (0: every promise kept), [1] the lowest sequence with a
+ *            violation (INT32_MAX if none), [2] the number of bad block-table
+ *            entries, [3] the number of sequences with a violation.
+ * Errors: PGQA_EINVAL (null or misaligned status, negative sizes, start_pos
+ * without cu_rows, a block table without num_blocks / max_blocks_per_seq > 0),
+ * PGQA_ENOTSUP (block_size not a power of two up to 256), PGQA_EHIP.
+ */
+int pgqa_check_contents(const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        const int32_t* cu_rows, const int32_t* start_pos, int32_t batch, int32_t total_rows,
+                        int32_t max_rows, int32_t num_blocks, int32_t block_size, int32_t max_context_len,
+                        int32_t window, int32_t* status, void* stream);
 
 #ifdef __cplusplus
 }

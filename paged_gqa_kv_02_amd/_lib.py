@@ -37,6 +37,7 @@ _SIGNATURES = {
                                        _P, _Z, _P]),
     "gqa_paged_extend_fp8": (C.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                        _I, _F, _I, _P, _P, _Z, _P]),
+    "pgqa_check_contents": (C.c_int, [_P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "pgqa_bm_create": (_P, [_I, _I]),
     "pgqa_bm_destroy": (None, [_P]),
     "pgqa_bm_new_sequence": (C.c_int, [_P, C.POINTER(_I)]),

@@ -22,7 +22,7 @@ LIB = PKG / "libpaged_gqa.so"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "block_manager.cpp", "kv_copy.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "block_manager.cpp", "kv_copy.hip", "decode.hip", "prefill.hip", "checks.hip"]
 
 # Packed fp32 ops (v_pk_fma_f32 & co.) are switched off for device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -332,4 +332,25 @@ int gqa_paged_extend_fp8(const void* q, const int32_t* cu_q, const void* k_cache
                        max_context_len, scale, window, PGQA_BF16, out, workspace, workspace_bytes, stream);
 }
 
+int pgqa_check_contents(const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        const int32_t* cu_rows, const int32_t* start_pos, int32_t batch, int32_t total_rows,
+                        int32_t max_rows, int32_t num_blocks, int32_t block_size, int32_t max_context_len,
+                        int32_t window, int32_t* status, void* stream) {
+    if (check_index_ptr(status) || batch < 0 || total_rows < 0 || max_context_len < 0 || window < 0)
+        return PGQA_EINVAL;
+    if (start_pos && !cu_rows) return PGQA_EINVAL;
+    int32_t lg = 0;
+    if (block_table) {
+        if (max_blocks_per_seq <= 0 || num_blocks <= 0) return PGQA_EINVAL;
+        if (!pow2_log2(block_size, &lg) || block_size > 256) return PGQA_ENOTSUP;
+        if ((int64_t)batch * max_blocks_per_seq > INT32_MAX) return PGQA_EINVAL;
+    }
+    if ((block_table && check_index_ptr(block_table)) || (context_lens && check_index_ptr(context_lens)) ||
+        (cu_rows && check_index_ptr(cu_rows)) || (start_pos && check_index_ptr(start_pos)))
+        return PGQA_EINVAL;
+    pgqa::CheckLaunch L{block_table, context_lens, cu_rows, start_pos, status, max_blocks_per_seq, batch,
+                        total_rows, max_rows, num_blocks, lg, max_context_len, window};
+    return hip_status(pgqa::launch_check(L, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -1033,6 +1033,9 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
         x.non_causal = 1;
         x.fixed_qlen = group;
         x.chunk_blocks = PGQA_MQA_CHUNK;
+        if (log_enabled())
+            log_line("decode B=%d Hq=%d Hkv=1 d=%d: %d query heads of a token as rows of the matrix-core kernel",
+                     L.batch, L.num_q_heads, L.head_dim, group);
         return launch_extend(x, stream);
     }
 
@@ -1082,6 +1085,12 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     a.part_ml = a.part_o + slots * (L.num_q_heads / L.num_kv_heads) * L.head_dim;
     a.tile_pref = (int32_t*)(a.part_ml + slots * (L.num_q_heads / L.num_kv_heads) * 2);
 
+    if (log_enabled())
+        log_line("decode B=%d Hq=%d Hkv=%d d=%d bs=%d%s window=%d: split-KV kernel, %d workgroups x %d waves "
+                 "(%s splits), LDS %zu B; merge %d workgroups",
+                 L.batch, L.num_q_heads, L.num_kv_heads, L.head_dim, 1 << L.block_size_log2,
+                 L.k_scale ? " fp8" : (L.is_bf16 ? " bf16" : " f32"), L.window, nw, e.waves,
+                 L.num_splits > 0 ? "caller's" : "occupancy", lds, L.batch * L.num_kv_heads * e.merge_slices);
     hipLaunchKernelGGL(e.split, dim3(nw), dim3(threads), lds, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "paged_gqa.h"
+
 namespace pgqa {
 
 // The softmax scale as the attention kernels apply it.  They take the running
@@ -181,5 +183,29 @@ bool extend_supported(int32_t head_dim, int32_t group, int32_t block_size);
 bool extend_supported_fp8(int32_t head_dim, int32_t group, int32_t block_size);
 
 hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream);
+
+// PGQA_LOG=1 in the environment: every attention launch prints its route,
+// grid and key split to stderr.
+bool log_enabled();
+void log_line(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+
+// Debug check of device array contents (pgqa_check_contents).
+struct CheckLaunch {
+    const int32_t* block_table;
+    const int32_t* context_lens;
+    const int32_t* cu;
+    const int32_t* start_pos;
+    int32_t* status;
+    int32_t max_blocks_per_seq;
+    int32_t batch;
+    int32_t total_rows;
+    int32_t max_rows;
+    int32_t num_blocks;
+    int32_t block_size_log2;
+    int32_t max_context_len;
+    int32_t window;
+};
+
+hipError_t launch_check(const CheckLaunch& L, hipStream_t stream);
 
 }  // namespace pgqa

@@ -1050,6 +1050,13 @@ int64_t launch_grid(PrefillArgs& a, int hg, int group, int64_t total_rows) {
 hipError_t launch(PrefillFn fn, PrefillArgs& a, int hg, int group, int head_dim, hipStream_t stream) {
     const int64_t wgs = launch_grid(a, hg, group, a.total_tokens);
     if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (log_enabled())
+        log_line("%s B=%d rows=%d Hq=%d Hkv=%d d=%d%s window=%d: %lld workgroups (%s tile lists, %d query-tile "
+                 "levels, %d pairs per XCD, %d head(s) per wave group), key chunks %d x %d blocks%s, %s K/V loads",
+                 a.block_table ? "extend" : "prefill", a.batch, a.total_tokens, a.num_q_heads, a.num_kv_heads,
+                 head_dim, a.k_scale ? " fp8" : "", a.window, (long long)wgs, a.dense ? "dense" : "full", a.nqt,
+                 a.pairs_per_xcd, hg, a.nchunk, a.nchunk > 1 ? a.kchunk : 0, a.chunk_lpt ? " (longest first)" : "",
+                 a.kv_nt ? "non-temporal" : "cached");
     hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(256), lds_bytes(head_dim, a.k_scale != nullptr), stream, a);
     return hipGetLastError();
 }

@@ -8,11 +8,57 @@ in the HIP kernels of libpaged_gqa.so; torch only owns memory and streams.
 
 from __future__ import annotations
 
+import os
 from typing import Optional, Tuple
 
 import torch
 
 from ._lib import PGQA_BF16, PGQA_F32, check, lib
+
+# PGQA_DEBUG_CHECKS=1: before each call, check the device arrays' contents
+# (block ids, lengths, row offsets) with pgqa_check_contents and raise
+# ContractError on a broken promise.  Each check waits for the GPU.
+DEBUG_CHECKS = os.environ.get("PGQA_DEBUG_CHECKS", "") not in ("", "0")
+
+_CHECK_FLAGS = {1: "block id outside the pool", 2: "context length or write position out of range",
+                4: "bad row offsets", 8: "fewer cached positions than query rows"}
+_INT32_MAX = 2 ** 31 - 1
+
+
+class ContractError(ValueError):
+    """A device array breaks a promise the C ABI takes on trust (found by check_contents)."""
+
+
+def check_contents(batch: int, block_table: Optional[torch.Tensor] = None,
+                   context_lens: Optional[torch.Tensor] = None, cu_rows: Optional[torch.Tensor] = None,
+                   start_pos: Optional[torch.Tensor] = None, total_rows: int = 0, max_rows: int = -1,
+                   num_blocks: int = 0, block_size: int = 1, max_context_len: int = 0, window: int = 0) -> dict:
+    """Run pgqa_check_contents on the given device arrays and return its report
+    (flags, first bad sequence or None, bad block-table entries, bad sequences)."""
+    ts = [t for t in (block_table, context_lens, cu_rows, start_pos) if t is not None]
+    _dev(*ts)
+    _i32(*ts)
+    dev = ts[0].device if ts else torch.device("cuda")
+    status = torch.empty(4, dtype=torch.int32, device=dev)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib().pgqa_check_contents(ptr(block_table), block_table.shape[1] if block_table is not None else 0,
+                                   ptr(context_lens), ptr(cu_rows), ptr(start_pos), int(batch), int(total_rows),
+                                   int(max_rows), int(num_blocks), int(block_size), int(max_context_len),
+                                   int(window), status.data_ptr(), _stream())
+    check("pgqa_check_contents", st)
+    f, first, nbad, nseq = status.cpu().tolist()
+    return {"flags": f, "first_bad_sequence": None if first == _INT32_MAX else first, "bad_block_ids": nbad,
+            "bad_sequences": nseq,
+            "problems": [msg for bit, msg in _CHECK_FLAGS.items() if f & bit]}
+
+
+def _debug(call: str, batch: int, **kw) -> None:
+    if not DEBUG_CHECKS:
+        return
+    r = check_contents(batch, **kw)
+    if r["flags"]:
+        raise ContractError(f"{call}: {', '.join(r['problems'])} ({r['bad_sequences']} sequence(s), first "
+                            f"{r['first_bad_sequence']}; {r['bad_block_ids']} bad block-table entries)")
 
 _DT = {torch.bfloat16: PGQA_BF16, torch.float32: PGQA_F32}
 
@@ -95,6 +141,8 @@ def paged_kv_write(k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, s
     _table(block_table, batch)
     _dev(k, v, cu_seqlens, start_pos, block_table, k_cache, v_cache)
     _i32(cu_seqlens, start_pos, block_table)
+    _debug("paged_kv_write", batch, block_table=block_table, cu_rows=cu_seqlens, start_pos=start_pos,
+           total_rows=k.shape[0], num_blocks=nb, block_size=bs)
     st = lib().paged_kv_write(k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), start_pos.data_ptr(),
                               block_table.data_ptr(), block_table.shape[1], k_cache.data_ptr(), v_cache.data_ptr(),
                               cu_seqlens.numel() - 1, k.shape[0], nb, bs, hkv, d, _dtype(k), _stream())
@@ -119,6 +167,8 @@ def paged_kv_gather(k_cache: torch.Tensor, v_cache: torch.Tensor, cu_seqlens: to
     _same_dtype("k_out / v_out against the cache", k_cache, k_out, v_out)
     _dev(k_cache, v_cache, cu_seqlens, start_pos, block_table, k_out, v_out)
     _i32(cu_seqlens, start_pos, block_table)
+    _debug("paged_kv_gather", batch, block_table=block_table, cu_rows=cu_seqlens, start_pos=start_pos,
+           total_rows=total_tokens, num_blocks=nb, block_size=bs)
     st = lib().paged_kv_gather(k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens.data_ptr(), start_pos.data_ptr(),
                                block_table.data_ptr(), block_table.shape[1], k_out.data_ptr(), v_out.data_ptr(),
                                cu_seqlens.numel() - 1, total_tokens, nb, bs, hkv, d, _dtype(k_cache), _stream())
@@ -157,6 +207,8 @@ def gqa_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
         workspace = decode_workspace(B, hq, hkv, d, num_splits, q.device)
     _dev(q, k_cache, v_cache, block_table, context_lens, out, workspace)
     _i32(block_table, context_lens)
+    _debug("gqa_paged_decode", B, block_table=block_table, context_lens=context_lens, num_blocks=nb, block_size=bs,
+           max_context_len=int(max_context_len), window=int(window))
     st = lib().gqa_paged_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
                                 block_table.shape[1], context_lens.data_ptr(), B, hq, hkv, d, bs, nb,
                                 int(max_context_len), float(scale), int(window), _dtype(q), out.data_ptr(),
@@ -171,7 +223,7 @@ def gqa_paged_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: to
                              scale: float, out: torch.Tensor, num_splits: int = 0, window: int = 0) -> torch.Tensor:
     """gqa_paged_decode without a workspace (the library's own per-GPU scratch holds the
     split partials; calls that may overlap on one GPU race).  out is required: nothing
-    is allocated."""
+    is allocated (so PGQA_DEBUG_CHECKS, whose check needs a status buffer, skips it)."""
     _rank("q", q, 3)
     B, hq, d = q.shape
     nb, hkv, bs, d2 = _pools(k_cache, v_cache)
@@ -206,6 +258,7 @@ def gqa_varlen_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seq
     out = _out(out, q)
     _dev(q, k, v, cu_seqlens, out)
     _i32(cu_seqlens)
+    _debug("gqa_varlen_prefill", cu_seqlens.numel() - 1, cu_rows=cu_seqlens, total_rows=T, max_rows=int(max_seqlen))
     st = lib().gqa_varlen_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
                                   cu_seqlens.numel() - 1, T, int(max_seqlen), hq, hkv, d, float(scale),
                                   int(bool(causal)), int(window), _dtype(q), out.data_ptr(), _stream())
@@ -249,6 +302,9 @@ def gqa_paged_extend(q: torch.Tensor, cu_q: torch.Tensor, k_cache: torch.Tensor,
         workspace = extend_workspace(cu_q.numel() - 1, T, int(max_q_len), hq, hkv, d, int(max_context_len), q.device)
     _dev(q, cu_q, k_cache, v_cache, block_table, context_lens, out, workspace)
     _i32(cu_q, block_table, context_lens)
+    _debug("gqa_paged_extend", batch, block_table=block_table, context_lens=context_lens, cu_rows=cu_q,
+           total_rows=T, max_rows=int(max_q_len), num_blocks=nb, block_size=bs, max_context_len=int(max_context_len),
+           window=int(window))
     st = lib().gqa_paged_extend(q.data_ptr(), cu_q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                 block_table.data_ptr(), block_table.shape[1], context_lens.data_ptr(),
                                 cu_q.numel() - 1, T, int(max_q_len), hq, hkv, d, bs, nb, int(max_context_len),
@@ -312,6 +368,8 @@ def paged_kv_write_fp8(k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tenso
     _table(block_table, batch)
     _dev(k, v, cu_seqlens, start_pos, block_table, k_cache, v_cache, k_scale, v_scale)
     _i32(cu_seqlens, start_pos, block_table)
+    _debug("paged_kv_write_fp8", batch, block_table=block_table, cu_rows=cu_seqlens, start_pos=start_pos,
+           total_rows=k.shape[0], num_blocks=nb, block_size=bs)
     st = lib().paged_kv_write_fp8(k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(), start_pos.data_ptr(),
                                   block_table.data_ptr(), block_table.shape[1], k_cache.data_ptr(), v_cache.data_ptr(),
                                   k_scale.data_ptr(), v_scale.data_ptr(), cu_seqlens.numel() - 1, k.shape[0], nb, bs,
@@ -343,6 +401,8 @@ def gqa_paged_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
         workspace = decode_workspace(B, hq, hkv, d, num_splits, q.device)
     _dev(q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, out, workspace)
     _i32(block_table, context_lens)
+    _debug("gqa_paged_decode_fp8", B, block_table=block_table, context_lens=context_lens, num_blocks=nb,
+           block_size=bs, max_context_len=int(max_context_len), window=int(window))
     st = lib().gqa_paged_decode_fp8(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), k_scale.data_ptr(),
                                     v_scale.data_ptr(), block_table.data_ptr(), block_table.shape[1],
                                     context_lens.data_ptr(), B, hq, hkv, d, bs, nb, int(max_context_len),
@@ -378,6 +438,9 @@ def gqa_paged_extend_fp8(q: torch.Tensor, cu_q: torch.Tensor, k_cache: torch.Ten
         workspace = extend_workspace(batch, T, int(max_q_len), hq, hkv, d, int(max_context_len), q.device)
     _dev(q, cu_q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, out, workspace)
     _i32(cu_q, block_table, context_lens)
+    _debug("gqa_paged_extend_fp8", batch, block_table=block_table, context_lens=context_lens, cu_rows=cu_q,
+           total_rows=T, max_rows=int(max_q_len), num_blocks=nb, block_size=bs, max_context_len=int(max_context_len),
+           window=int(window))
     st = lib().gqa_paged_extend_fp8(q.data_ptr(), cu_q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                     k_scale.data_ptr(), v_scale.data_ptr(), block_table.data_ptr(),
                                     block_table.shape[1], context_lens.data_ptr(), batch, T, int(max_q_len), hq,

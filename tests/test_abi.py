@@ -24,7 +24,7 @@ def test_header_declares_the_calls():
     names = L.header_functions()
     for n in ("paged_kv_write", "paged_kv_gather", "gqa_paged_decode", "gqa_paged_decode_workspace_size",
               "gqa_varlen_prefill", "gqa_paged_extend", "paged_kv_copy_blocks", "pgqa_bm_create", "pgqa_bm_append",
-              "gqa_paged_decode_noalloc", "gqa_paged_extend_fp8", "gqa_paged_decode_fp8", "paged_kv_write_fp8",
+              "gqa_paged_decode_noalloc", "gqa_paged_extend_fp8", "pgqa_check_contents", "gqa_paged_decode_fp8", "paged_kv_write_fp8",
               "pgqa_bm_fork", "pgqa_bm_free_sequence", "pgqa_status_string"):
         assert n in names
 
@@ -291,3 +291,22 @@ def test_build_entry_point(monkeypatch, built_lib):
     from paged_gqa_kv_02_amd import build as hip_build
     monkeypatch.setattr(hip_build, "build", lambda jobs=0: hip_build.LIB)
     entry.build()
+
+
+def test_check_contents_validation(lib):
+    def c(**kw):
+        a = dict(bt=P[0], maxb=4, cl=P[1], cu=None, sp=None, batch=2, T=0, maxr=-1, nb=8, bs=16, maxctx=64, win=0,
+                 st=P[2])
+        a.update(kw)
+        return lib.pgqa_check_contents(a["bt"], a["maxb"], a["cl"], a["cu"], a["sp"], a["batch"], a["T"], a["maxr"],
+                                       a["nb"], a["bs"], a["maxctx"], a["win"], a["st"], None)
+    assert c(st=None) == EINVAL
+    assert c(st=P[2] + 2) == EINVAL
+    assert c(batch=-1) == EINVAL
+    assert c(win=-1) == EINVAL
+    assert c(sp=P[3]) == EINVAL            # a write check needs the row offsets
+    assert c(nb=0) == EINVAL
+    assert c(maxb=0) == EINVAL
+    assert c(cl=P[1] + 1) == EINVAL
+    assert c(bs=12) == ENOTSUP
+    assert c(bs=512) == ENOTSUP
