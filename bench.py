@@ -46,7 +46,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 COPIES = 4
 
-LEGS = ["decode", "tiny", "long_ctx", "window", "mqa", "prefill", "chunked_prefill", "spec_verify", "fp8", "shared"]
+LEGS = ["decode", "tiny", "long_ctx", "window", "mqa", "prefill", "chunked_prefill", "spec_verify", "fp8",
+        "fp8_spec", "shared"]
 
 _DECODE_SRC = ["paged_gqa_kv_02_amd/csrc/decode.hip", "paged_gqa_kv_02_amd/csrc/device_common.hpp",
                "paged_gqa_kv_02_amd/csrc/launch.hpp"]
@@ -63,11 +64,12 @@ TRAFFIC_PARTS = {
                  _DECODE_SRC),
     "window": ("long_ctx_decode, window 4096",
                ["decode_split_kernel<2,128,8,1,2>", "decode_merge_kernel<2,128,8>"], _DECODE_SRC),
-    "mqa": ("mqa_decode", ["prefill_kernel<128,1,true>", "extend_merge_kernel<128>"],
+    "mqa": ("mqa_decode", ["prefill_kernel<128,1,true,false>", "extend_merge_kernel<128>"],
             _DECODE_SRC + _PREFILL_SRC[:1]),
-    "prefill": ("varlen_prefill", ["prefill_kernel<128,4,false>"], _PREFILL_SRC),
-    "chunked_prefill": ("chunked_prefill", ["prefill_kernel<128,4,true>"], _PREFILL_SRC),
-    "spec_verify": ("spec_verify", ["prefill_kernel<128,4,true>"], _PREFILL_SRC),
+    "prefill": ("varlen_prefill", ["prefill_kernel<128,4,false,false>"], _PREFILL_SRC),
+    "chunked_prefill": ("chunked_prefill", ["prefill_kernel<128,4,true,false>"], _PREFILL_SRC),
+    "spec_verify": ("spec_verify", ["prefill_kernel<128,4,true,false>"], _PREFILL_SRC),
+    "fp8_spec": ("spec_verify over FP8 pages", ["prefill_kernel<128,4,true,true>"], _PREFILL_SRC),
     "fp8": ("llama3_8b_decode over FP8 pages", ["decode_split_kernel<2,128,4,1,1>", "decode_merge_kernel<2,128,4>"],
             _DECODE_SRC),
     "shared": ("shared_prefix_decode", ["decode_split_kernel<2,128,4,1,2>", "decode_merge_kernel<2,128,4>"],
@@ -453,15 +455,23 @@ def prefill_leg(args, torch, pg, W, T, traffic=None):
     }
 
 
-def extend_leg(key, args, torch, pg, W, T, traffic=None):
+def extend_leg(key, args, torch, pg, W, T, traffic=None, fp8=False):
     """One multi-token step on a named workload: write the new tokens' K/V into
     their pages, then gqa_paged_extend over prefix + new tokens.  HIP events
-    bracket the extend call; two pool copies alternate between steps."""
+    bracket the extend call; two pool copies alternate between steps.  fp8: the
+    same over FP8 pages (quantising write, gqa_paged_extend_fp8); bytes are then
+    the codes and row scales stored."""
     c = W.make_workload(key)
     q, cu_q = T.to_dev(c.q), T.to_dev(c.cu_q)
     table, ctx = T.to_dev(c.block_table), T.to_dev(c.context_lens)
     pools = []
     for _ in range(2):
+        if fp8:
+            p4 = pg.fp8_pools(c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
+            pg.paged_kv_write_fp8(T.to_dev(c.k), T.to_dev(c.v), T.to_dev(c.cu_ctx), T.to_dev(c.start_pos), table,
+                                  *p4)
+            pools.append(p4)
+            continue
         kc = T.nan_pool_dev(c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim, c.dtype)
         vc = T.nan_pool_dev(c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim, c.dtype)
         pg.paged_kv_write(T.to_dev(c.k), T.to_dev(c.v), T.to_dev(c.cu_ctx), T.to_dev(c.start_pos), table, kc, vc)
@@ -474,11 +484,17 @@ def extend_leg(key, args, torch, pg, W, T, traffic=None):
     scale = float(c.scale)
 
     def step(i, ev=None):
-        kc, vc = pools[i % 2]
-        pg.paged_kv_write(k_new, v_new, cu_q, sp_new, table, kc, vc)
+        pool = pools[i % 2]
+        if fp8:
+            pg.paged_kv_write_fp8(k_new, v_new, cu_q, sp_new, table, *pool)
+        else:
+            pg.paged_kv_write(k_new, v_new, cu_q, sp_new, table, *pool)
         if ev is not None:
             ev[0].record()
-        pg.gqa_paged_extend(q, cu_q, kc, vc, table, ctx, c.max_q_len, c.max_context_len, scale=scale, out=out)
+        if fp8:
+            pg.gqa_paged_extend_fp8(q, cu_q, *pool, table, ctx, c.max_q_len, c.max_context_len, scale=scale, out=out)
+        else:
+            pg.gqa_paged_extend(q, cu_q, *pool, table, ctx, c.max_q_len, c.max_context_len, scale=scale, out=out)
         if ev is not None:
             ev[1].record()
 
@@ -494,10 +510,13 @@ def extend_leg(key, args, torch, pg, W, T, traffic=None):
     wall = time.perf_counter() - t0
     us = float(np.mean([a.elapsed_time(b) for a, b in evs]) * 1e3)
     flops, kv = c.flops(), c.kv_bytes()
+    if fp8:
+        kv = kv // (2 * c.head_dim) * (c.head_dim + 4)   # per token and KV head: d code bytes + a 4-byte scale
     # Bound by arithmetic intensity against the ridge point (peak FLOP/s / peak B/s).
     mfma = flops / kv > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     return {
-        "workload": key, "batch": c.batch, "query_tokens": c.total_q, "flops_per_call": flops,
+        "workload": key, "kv_format": "fp8 e4m3 + fp32 row scale" if fp8 else "bf16", "batch": c.batch,
+        "query_tokens": c.total_q, "flops_per_call": flops,
         "kv_bytes_per_call": kv, "call_us_mean": round(us, 2), "ms_per_step": wall * 1e3 / n,
         "tflops": round(flops / (us * 1e-6) / 1e12, 2), "kv_gbs": round(kv / (us * 1e-6) / 1e9, 2),
         "query_tokens_per_s": round(c.total_q / (us * 1e-6), 1),
@@ -802,6 +821,9 @@ def main(argv=None):
         line["fp8"] = fp8_leg(args, torch, pg, W, T, traffic["fp8"])
         if "decode_call_us" in line:
             line["fp8"]["speedup_vs_bf16_call"] = round(line["decode_call_us"]["mean"] / line["fp8"]["call_us_mean"], 3)
+    if "fp8_spec" in legs:
+        log("fp8 pages, multi-token leg")
+        line["fp8_spec_verify"] = extend_leg("spec_verify", args, torch, pg, W, T, traffic["fp8_spec"], fp8=True)
     if "shared" in legs:
         log("shared prefix leg")
         line["shared_prefix"] = shared_prefix_leg(args, torch, pg, W, T, traffic["shared"])

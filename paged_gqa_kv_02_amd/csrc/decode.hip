@@ -69,6 +69,9 @@
 #ifndef PGQA_DECODE_RPT
 #define PGQA_DECODE_RPT 4
 #endif
+#ifndef PGQA_MQA_PACK
+#define PGQA_MQA_PACK 1
+#endif
 #ifndef PGQA_MQA_CHUNK
 #define PGQA_MQA_CHUNK 16  // 64-key blocks per key chunk on the matrix-core MQA route
 #endif
@@ -999,8 +1002,9 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     if (L.batch == 0) return hipSuccess;
 
     // Many query heads on one KV head (MQA, G a multiple of 32): the G heads of a
-    // token are the 32-row tiles of the matrix-core kernel.  q [B, G, d] is read
-    // as B sequences of G rows with one head (the same bytes), every row seeing
+    // token are rows of the matrix-core kernel (G = 32: the packed rows of one
+    // tile, two waves sharing every key block; larger G: q [B, G, d] read as B
+    // sequences of G tokens with one head, the same bytes), every row seeing
     // all keys [0, ctx) of the sequence's pages; the kernel's key split spreads
     // the long contexts.  At ~32 FLOP per K/V byte this shape outruns the VALU
     // dot products of the split kernel (bf16 only; no window; library-chosen
@@ -1017,10 +1021,14 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
         x.context_lens = L.context_lens;
         x.out = L.out;
         x.batch = L.batch;
-        x.total_q = L.batch * group;
-        x.max_q_len = group;
+        // G = 32: one token per sequence whose 32 heads are the packed rows of
+        // one tile (its position ctx - 1 sees every key).  Otherwise the G heads
+        // are read as G tokens of one head, all seeing every key.
+        const bool packed = PGQA_MQA_PACK && group == 32;
+        x.total_q = packed ? L.batch : L.batch * group;
+        x.max_q_len = packed ? 1 : group;
+        x.num_q_heads = packed ? group : 1;
         x.max_blocks_per_seq = L.max_blocks_per_seq;
-        x.num_q_heads = 1;
         x.num_kv_heads = 1;
         x.head_dim = L.head_dim;
         x.block_size_log2 = L.block_size_log2;
@@ -1030,8 +1038,8 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
         x.window = 0;
         x.workspace = L.workspace;
         x.workspace_bytes = decode_workspace_bytes(L.batch, L.num_q_heads, L.num_kv_heads, L.head_dim, 0);
-        x.non_causal = 1;
-        x.fixed_qlen = group;
+        x.non_causal = packed ? 0 : 1;
+        x.fixed_qlen = packed ? 1 : group;
         x.chunk_blocks = PGQA_MQA_CHUNK;
         if (log_enabled())
             log_line("decode B=%d Hq=%d Hkv=1 d=%d: %d query heads of a token as rows of the matrix-core kernel",

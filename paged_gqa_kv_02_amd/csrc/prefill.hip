@@ -83,6 +83,7 @@ struct PrefillArgs {
     int32_t fixed_qlen;      // > 0: sequence s holds rows [s * fixed_qlen, +fixed_qlen) (cu_seqlens unused)
     int32_t chunk_lpt;       // 1: dense lists of key chunks, full chunks first (one query tile and head group per pair)
     int32_t kv_nt;           // 1: K/V read by one workgroup only (one query tile and head group per pair): non-temporal loads
+    int32_t pack;            // host side: the packed-rows kernel was chosen
     // Paged K/V only (k, v are then the pools [num_blocks, Hkv, block_size, d]).
     const int32_t* block_table;
     const int32_t* context_lens;
@@ -213,12 +214,14 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const DmaLane<D
     }
 }
 
-// FP8 pages (E4M3 codes, one fp32 scale per key row): a tile's codes (BN rows
-// of D bytes) are DMA'd into the upper half of the tile's bf16 ring slot, 1 KB
-// (RPL8 rows of one page) per wave-load, K waves and V waves NPW8 loads each;
-// after they land, all waves convert them into the slot's bf16 layout (exact),
-// so the MFMA code is the bf16 one.  The tile's row scales go to a small LDS
-// area by one 4-byte-per-lane DMA per pool (wave 1: K, wave 3: V).
+// FP8 pages (E4M3 codes, one fp32 scale per key row).  LDS holds one bf16 K
+// tile and one bf16 V tile (swizzled as above), then two stages of K codes and
+// two of V codes (BN rows of D bytes each, plain order), so the ring's size is
+// unchanged.  A tile's codes are DMA'd 1 KB (RPL8 rows of one page) per
+// wave-load, K waves and V waves NPW8 loads each; once they land, every thread
+// converts its share into the bf16 tile (exact), so the MFMA code is the bf16
+// one.  The tile's row scales go to a small LDS area by one 4-byte-per-lane
+// DMA per pool (wave 1: K, wave 3: V).
 template <int D>
 struct Q8Geo {
     static constexpr int CODEB = BN * D;          // code bytes per tile and pool
@@ -329,7 +332,7 @@ __device__ __forceinline__ void issue_tile_paged(const PagedSrc<D>& ps, const Dm
     }
 }
 
-// DMA of tile kb of FP8 pages: codes into the upper half of ring slot `par`
+// DMA of tile kb of FP8 pages: codes into code stage `par` of the wave's pool
 // (rows in plain order, D bytes each), and, from wave 1 (K) and wave 3 (V), the
 // tile's 64 row scales into scale slot `ssl`.  Rows outside [lo, last] re-read
 // the nearest of the two (as in issue_tile_paged).
@@ -339,7 +342,7 @@ __device__ __forceinline__ void issue_tile_paged_q8(const PagedSrc<D>& ps, const
                                                     int kvh, int hkv) {
     using P = PGeo<D>;
     using Q = Q8Geo<D>;
-    const uint32_t dst = ring + (ps.isv ? 2 * P::TILEB : 0) + par * P::TILEB + P::TILEB / 2;
+    const uint32_t dst = ring + 2 * P::TILEB + ((ps.isv ? 2 : 0) + par) * Q::CODEB;
     const int bs_mask = (1 << ps.lbs) - 1;
     const int64_t row_b = D;                                    // code bytes per row
     const int64_t blk_b = ((int64_t)hkv << ps.lbs) * row_b;     // code bytes per block
@@ -378,24 +381,23 @@ __device__ __forceinline__ void issue_tile_paged_q8(const PagedSrc<D>& ps, const
     }
 }
 
-// Conversion of landed FP8 code tiles into the bf16 ring layout: the K tile of
-// slot kpar (kpar < 0: none) and the V tile of slot vpar.  All 256 threads read
-// their code chunks, wait for every wave (codes and converted rows share the
-// slot's upper half), then write the bf16 rows (swizzled like DMA'd bf16 tiles)
-// and wait again.
+// Conversion of landed FP8 code tiles into the bf16 tiles: the K codes of
+// stage kpar (kpar < 0: none) and the V codes of stage vpar (vpar < 0: none).
+// Every thread converts its own code chunks into bf16 rows (swizzled like
+// DMA'd bf16 tiles); a barrier then publishes them.
 template <int D>
 __device__ __forceinline__ void convert_q8(PGQA_LDS char* ring, int kpar, int vpar) {
     using P = PGeo<D>;
     using Q = Q8Geo<D>;
     const int t = threadIdx.x;
     u32x4 kc[Q::CPT], vc[Q::CPT];
+    const PGQA_LDS char* codes = ring + 2 * P::TILEB;
 #pragma unroll
     for (int i = 0; i < Q::CPT; ++i) {
         const int c = t + 256 * i;
-        if (kpar >= 0) kc[i] = lds_read_16(ring + kpar * P::TILEB + P::TILEB / 2 + c * 16);
-        if (vpar >= 0) vc[i] = lds_read_16(ring + (2 + vpar) * P::TILEB + P::TILEB / 2 + c * 16);
+        if (kpar >= 0) kc[i] = lds_read_16(codes + kpar * Q::CODEB + c * 16);
+        if (vpar >= 0) vc[i] = lds_read_16(codes + (2 + vpar) * Q::CODEB + c * 16);
     }
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < Q::CPT; ++i) {
         const int c = t + 256 * i;
@@ -404,12 +406,12 @@ __device__ __forceinline__ void convert_q8(PGQA_LDS char* ring, int kpar, int vp
         const int o0 = row * P::ROWB + (((2 * c16) ^ swz_key<D>(row)) << 4);
         const int o1 = row * P::ROWB + (((2 * c16 + 1) ^ swz_key<D>(row)) << 4);
         if (kpar >= 0) {
-            PGQA_LDS char* kt = ring + kpar * P::TILEB;
+            PGQA_LDS char* kt = ring;
             *(PGQA_LDS u32x4*)(kt + o0) = fp8x8_to_bf16(u32x2{kc[i].x, kc[i].y});
             *(PGQA_LDS u32x4*)(kt + o1) = fp8x8_to_bf16(u32x2{kc[i].z, kc[i].w});
         }
         if (vpar >= 0) {
-            PGQA_LDS char* vt = ring + (2 + vpar) * P::TILEB;
+            PGQA_LDS char* vt = ring + P::TILEB;
             *(PGQA_LDS u32x4*)(vt + o0) = fp8x8_to_bf16(u32x2{vc[i].x, vc[i].y});
             *(PGQA_LDS u32x4*)(vt + o1) = fp8x8_to_bf16(u32x2{vc[i].z, vc[i].w});
         }
@@ -417,10 +419,19 @@ __device__ __forceinline__ void convert_q8(PGQA_LDS char* ring, int kpar, int vp
     __syncthreads();
 }
 
-template <int D, int HG, bool PAGED, bool Q8 = false>
+// PACK (paged calls with at most 32 query rows per KV head and sequence: q_len
+// x G <= 32, e.g. decode of many heads on one KV head, or draft verification):
+// the rows of a workgroup are the (token, head) pairs of one sequence and KV
+// head, row r = token r / G, head r % G of the KV head's group, so a few tokens
+// fill one 32-row MFMA tile instead of G mostly empty ones.  Waves 0 and 1 then
+// share every key block, each taking one 32-key half with its own running max,
+// sum and output, merged through LDS at the end; waves 2 and 3 only fetch V.
+template <int D, int HG, bool PAGED, bool Q8 = false, bool PACK = false>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     static_assert(PAGED || !Q8, "FP8 K/V only from pages");
+    static_assert(!PACK || (PAGED && HG == 1), "packed rows: paged, one workgroup per KV head");
     using P = PGeo<D>;
+    constexpr int NH = PACK ? 1 : 2;          // 32-key halves of a block each wave computes
     constexpr int TB = 4 / HG;               // 32-row token blocks per workgroup
     constexpr int KSTEPS = P::KSTEPS, DBLK = P::DBLK;
     constexpr int NPW = DmaLane<D>::NPW;   // wave-loads per tile and DMA wave (normal roles)
@@ -433,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int half = lane >> 5;
     const int l32 = lane & 31;
     const int G = a.num_q_heads / a.num_kv_heads;
-    const int groups = G / HG;
+    const int groups = PACK ? 1 : G / HG;
 
     // Work mapping.  Workgroups are dealt to the 8 XCDs round-robin by linear
     // id and every XCD has its own L2, so all tiles of one (sequence, KV head)
@@ -551,7 +562,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     if (chunk > 0 && chunk * ckeys >= Lk) return;
     const bool split = Lk > ckeys;                       // partials instead of the output
     const int head = kvh * G + grp * HG + (wave % HG);
-    const int i0 = tok0 + (wave / HG) * BQ;          // this wave's first query row (sequence-local)
+    // This wave's first query row (sequence-local); packed: token 0 for waves 0, 1.
+    const int i0 = PACK ? (wave < 2 ? 0 : 1 << 30) : tok0 + (wave / HG) * BQ;
+    const int hoff = PACK ? (wave & 1) : 0;          // packed: the wave's key half
+    const int prows = PACK ? Lq * G : 0;             // packed rows (<= 32)
 
     const int wg_rows_end = min(Lq, tok0 + TB * BQ);
     const int keys = a.causal ? min(Lk, koff + wg_rows_end) : Lk;   // keys the workgroup reads
@@ -622,6 +636,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     {
         const int row = min(i0 + l32, Lq - 1);
         const char* qp = a.q + (int64_t)(seq0 + row) * qstride + (int64_t)head * D * 2 + half * 16;
+        if constexpr (PACK) {
+            const int r = min(l32, prows - 1);
+            qp = a.q + (int64_t)(seq0 + r / G) * qstride + (int64_t)(kvh * G + r % G) * D * 2 + half * 16;
+        }
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) qreg[kk] = (*(const u32x4*)(qp + kk * 32) & a.q_and) ^ a.q_xor;
     }
@@ -652,15 +670,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // S^T = K Q^T for key block kb (K slot kb % 2): per 32-key half kb2, lane
     // (l32, half) gets row l32, keys 32*kb2 + 8*(i/4) + 4*half + i%4.
     auto scores = [&](f32x16 (&st)[2], auto slot) {
-        const PGQA_LDS char* kt = ring + decltype(slot)::value * P::TILEB;
+        // (FP8 pages: the one bf16 K tile.)
+        const PGQA_LDS char* kt = ring + (Q8 ? 0 : decltype(slot)::value * P::TILEB);
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
+        for (int kb2 = 0; kb2 < NH; ++kb2) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) st[kb2][i] = 0.0f;
 #pragma unroll
             for (int kk = 0; kk < KSTEPS; ++kk)
                 st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, lds_read_16(kt + 32 * kb2 * P::ROWB + (kx ^ (kk << 5)))),
+                    __builtin_bit_cast(bf16x8, lds_read_16(kt + 32 * (kb2 + hoff) * P::ROWB + (kx ^ (kk << 5)))),
                     __builtin_bit_cast(bf16x8, qreg[kk]), st[kb2], 0, 0, 0);
         }
     };
@@ -672,9 +691,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         const int j0 = (kb0 + kr) * BN;
         // FP8 pages: scores times the keys' row scales (key offsets as in the masking below).
         if constexpr (Q8) {
-            const PGQA_LDS float* ks = scale_lds + (kr % 3) * BN + 4 * (lane_now() >> 5);
+            const PGQA_LDS float* ks = scale_lds + (kr % 3) * BN + 32 * hoff + 4 * (lane_now() >> 5);
 #pragma unroll
-            for (int g = 0; g < 8; ++g) {
+            for (int g = 0; g < 4 * NH; ++g) {
                 const f32x4 k4 = *(const PGQA_LDS f32x4*)(ks + 8 * g);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) cur[g >> 2][4 * (g & 3) + t] *= k4[t];
@@ -686,11 +705,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         // 4*half folded into both bounds.
         if ((j0 + BN > Lk) || (a.causal && j0 + BN - 1 > koff + i0) || (win > 0 && j0 < koff + i0 + BQ - win)) {
             const int ln = lane_now();
-            const int lrow = koff + i0 + (ln & 31);
-            const int lim = (a.causal ? min(lrow, Lk - 1) : Lk - 1) - j0 - 4 * (ln >> 5);
-            const int llim = (win > 0 ? lrow - win + 1 : -(1 << 30)) - j0 - 4 * (ln >> 5);
+            // The lane's row position (packed: its row's token).
+            const int lrow = koff + (PACK ? (ln & 31) / G : i0 + (ln & 31));
+            const int lim = (a.causal ? min(lrow, Lk - 1) : Lk - 1) - j0 - 4 * (ln >> 5) - 32 * hoff;
+            const int llim = (win > 0 ? lrow - win + 1 : -(1 << 30)) - j0 - 4 * (ln >> 5) - 32 * hoff;
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
+            for (int kb2 = 0; kb2 < NH; ++kb2)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int off = 32 * kb2 + 8 * (i >> 2) + (i & 3);
@@ -699,7 +719,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         }
         float mt = cur[0][0];
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < NH; ++kb2)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mt = fmaxf(mt, cur[kb2][i]);
         mt = fmaxf(mt, shfl_xor_f32(mt, 32)) * cs;
@@ -723,9 +743,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         // P^T operand for 16-key step kk: keys 16kk + 8*(jj/4) + 4*half + jj%4,
         // i.e. accumulator entries 8*(kk%2) .. +7 of half kk/2.  The row sum
         // adds the bf16-rounded weights, the same ones the PV product uses.
-        u32x4 pb[4];
+        u32x4 pb[2 * NH];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < 2 * NH; ++kk) {
             float p[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(cur[kk >> 1][8 * (kk & 1) + j], cs, -m));
@@ -733,7 +753,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                 // Weights times the values' row scales (accumulator entry 8*(kk%2) + j
                 // of half kk/2 is key 16*kk + 8*(j/4) + 4*half + j%4); the row sum
                 // takes the plain weights.
-                const PGQA_LDS float* vs = scale_lds + (3 + PAR) * BN + 16 * kk + 4 * (lane_now() >> 5);
+                const PGQA_LDS float* vs = scale_lds + (3 + PAR) * BN + 16 * (kk + 2 * hoff) + 4 * (lane_now() >> 5);
                 const f32x4 v0 = *(const PGQA_LDS f32x4*)vs;
                 const f32x4 v1 = *(const PGQA_LDS f32x4*)(vs + 8);
 #pragma unroll
@@ -756,29 +776,29 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
             // and only a few K fragments are live at a time.
             __builtin_amdgcn_sched_group_barrier(0x100, PGQA_KREADS_AHEAD, 0);   // K reads ahead
 #pragma unroll
-            for (int i = 0; i < 2 * KSTEPS; ++i) {
+            for (int i = 0; i < NH * KSTEPS; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                if (i + PGQA_KREADS_AHEAD < 2 * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // K read
+                if (i + PGQA_KREADS_AHEAD < NH * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // K read
                 __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
             }
         }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         // O^T += V^T P^T: A = V^T for dims 32*db + l32, keys {16kk + 4*half + 0..3, +8 ..}.
-        const PGQA_LDS char* vt = ring + (2 + PAR) * P::TILEB;
+        const PGQA_LDS char* vt = ring + (Q8 ? 1 : 2 + PAR) * P::TILEB;
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
-            u32x4 va[4];
+            u32x4 va[2 * NH];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const PGQA_LDS char* vk = vt + 16 * kk * P::ROWB;
+            for (int kk = 0; kk < 2 * NH; ++kk) {
+                const PGQA_LDS char* vk = vt + 16 * (kk + 2 * hoff) * P::ROWB;
                 const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PGQA_LDS i16x4*)(vk + (vx ^ (db << 6))));
                 const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PGQA_LDS i16x4*)(vk + 8 * P::ROWB + (vx ^ (db << 6) ^ 32)));
                 va[kk] = u32x4{__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
                                __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y};
             }
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
+            for (int kk = 0; kk < 2 * NH; ++kk)
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[kk]),
                                                                 __builtin_bit_cast(bf16x8, pb[kk]), o[db], 0, 0, 0);
         }
@@ -804,8 +824,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                 issue_tile<D>(a, dl, ring_addr, kb0 + tb, tb & 1, seq0, Lk, kvh, wave, lane_now(), kvstride);
             }
         }
-        // FP8 pages: the codes of K(kr+1) and V(kr) have landed; into bf16 (the
-        // tiles just issued go to the other slots).
+        // FP8 pages: the codes of K(kr+1) and V(kr) have landed; into the bf16
+        // tiles, which every wave is done with (the codes just issued go to the
+        // other stages).
         if constexpr (Q8) convert_q8<D>(ring, kr + 1 < nrel ? (kr + 1) & 1 : -1, kr & 1);
     };
     // Blocks kb0 .. kb0 + kend are computed (kend = last_kb - kb0, or -1 for a
@@ -849,17 +870,59 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // (swizzled like the K/V tiles), then each lane writes one 16-byte chunk of
     // one row, CPR consecutive lanes per row.
     __syncthreads();   // every wave is done with the ring
+    if constexpr (PACK) {
+        // The two key halves of the same rows: wave 1's running max, sum and
+        // output go through LDS (value-major, lane-minor: conflict-free) to wave 0,
+        // which rescales both to the larger max and adds them.
+        PGQA_LDS float* xs = (PGQA_LDS float*)(ring + 2 * BQ * P::ROWB);
+        const int ln = lane_now();
+        if (wave == 1 && active) {
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) xs[(16 * db + i) * 64 + ln] = o[db][i];
+            xs[16 * DBLK * 64 + ln] = m;
+            xs[(16 * DBLK + 1) * 64 + ln] = lsum;
+        }
+        __syncthreads();
+        if (wave != 0) return;
+        const float m1 = xs[16 * DBLK * 64 + ln];
+        const float l1 = xs[(16 * DBLK + 1) * 64 + ln];
+        const float mx = fmaxf(m, m1);
+        const float a0 = __builtin_amdgcn_exp2f(m - mx);
+        const float a1 = __builtin_amdgcn_exp2f(m1 - mx);
+        m = mx;
+        lsum = lsum * a0 + l1 * a1;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] = o[db][i] * a0 + xs[(16 * db + i) * 64 + ln] * a1;
+    }
     if (!active) return;
     const int lane_e = lane_now();
     const int half_e = lane_e >> 5;
     const int l32_e = lane_e & 31;
     lsum += shfl_xor_f32(lsum, 32);
+    // Output row of the lane's row l32_e: token and query head (packed: the
+    // row's token and head; else row i0 + l32_e of the wave's head).
+    auto out_row = [&](int r, int& tok, int& hq) {
+        if constexpr (PACK) {
+            tok = r / G;
+            hq = kvh * G + r % G;
+        } else {
+            tok = i0 + r;
+            hq = head;
+        }
+    };
+    const int rows_here = PACK ? prows : Lq - i0;   // valid rows of the wave's tile
     if (split) {
         // Partial of this key chunk: unnormalised O, running max m and sum l
         // (both halves of the wave hold the row's m); a row with no key in the
         // chunk leaves O = 0, l = 0.
-        if (i0 + l32_e < Lq) {
-            const int64_t prow = ((int64_t)(seq0 + i0 + l32_e) * a.num_q_heads + head) * a.nchunk + chunk;
+        if (l32_e < rows_here) {
+            int tok, hq;
+            out_row(l32_e, tok, hq);
+            const int64_t prow = ((int64_t)(seq0 + tok) * a.num_q_heads + hq) * a.nchunk + chunk;
             float* po = a.part_o + prow * D + 4 * half_e;
 #pragma unroll
             for (int db = 0; db < DBLK; ++db)
@@ -888,33 +951,41 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     for (int t = 0; t < BQ / P::RPL; ++t) {
         const int r = t * P::RPL + lane_e / P::CPR;
         const u32x4 val = lds_read_16(ot + swz<D>(r, c));
-        if (i0 + r < Lq)
-            *(u32x4*)(a.out + (int64_t)(seq0 + i0 + r) * qstride + (int64_t)head * D * 2 + c * 16) = val;
+        if (r < rows_here) {
+            int tok, hq;
+            out_row(r, tok, hq);
+            *(u32x4*)(a.out + (int64_t)(seq0 + tok) * qstride + (int64_t)hq * D * 2 + c * 16) = val;
+        }
     }
 }
 
 // Merge of the key-chunk partials of split sequences: a query row's Hq x D
 // outputs go to one thread each, a 256-thread workgroup taking 256 / (Hq x D)
 // rows when a row has fewer outputs than that (one wave or more per row, so
-// each wave belongs to one row and finds its sequence once), else one row and a
-// loop over its outputs.  Log-sum-exp of the chunks in chunk order with a
+// each wave belongs to one row and finds its sequence once), else
+// (Hq x D) / 256 workgroups sharing one row.  Log-sum-exp of the chunks in chunk order with a
 // running maximum (deterministic; the loads of successive chunks do not wait on
 // one another).  A chunk in which a row sees no key holds m = -1e30 (finite),
 // l = 0, O = 0 and so adds nothing.  Rows of sequences that fit one chunk were
 // written by the attention kernel.
+// Merge workgroups of the whole call (a row's outputs, Hq x D, are a multiple
+// of 64; a row with more than 256 of them takes (Hq x D + 255) / 256 workgroups).
 template <int D>
-int merge_rows_per_wg(int num_q_heads) {
+int64_t merge_grid(int total_rows, int num_q_heads) {
     const int per = num_q_heads * D;
-    return per >= 256 ? 1 : 256 / per;
+    if (per >= 256) return (int64_t)total_rows * ((per + 255) / 256);
+    const int rpw = 256 / per;
+    return ((int64_t)total_rows + rpw - 1) / rpw;
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void extend_merge_kernel(PrefillArgs a) {
     const int per = a.num_q_heads * D;
     const int rpw = per >= 256 ? 1 : 256 / per;
+    const int wpr = per > 256 ? (per + 255) / 256 : 1;     // workgroups per row
     const int sub = rpw > 1 ? (int)threadIdx.x / per : 0;
     if (sub >= rpw) return;                                 // threads past the last whole row
-    const int row = (int)blockIdx.x * rpw + sub;
+    const int row = wpr > 1 ? (int)(blockIdx.x / wpr) : (int)blockIdx.x * rpw + sub;
     if (row >= a.total_tokens) return;
     int lo = 0, hi = a.batch - 1;                          // the sequence holding the row
     if (a.fixed_qlen > 0) {
@@ -930,8 +1001,8 @@ __global__ __launch_bounds__(256) void extend_merge_kernel(PrefillArgs a) {
     const int ckeys = a.kchunk * BN;
     const int nc = Lk > ckeys ? (Lk + ckeys - 1) / ckeys : 1;
     if (nc <= 1) return;
-    const int e0 = rpw > 1 ? (int)threadIdx.x - sub * per : (int)threadIdx.x;
-    for (int e = e0; e < per; e += 256) {
+    const int e0 = rpw > 1 ? (int)threadIdx.x - sub * per : (int)(blockIdx.x % wpr) * 256 + (int)threadIdx.x;
+    for (int e = e0; e < per; e += 256 * wpr) {
         const int64_t rh = (int64_t)row * a.num_q_heads + e / D;
         const float* ml = a.part_ml + rh * a.nchunk * 2;
         const float* po = a.part_o + rh * a.nchunk * D + e % D;
@@ -956,28 +1027,43 @@ __global__ __launch_bounds__(256) void extend_merge_kernel(PrefillArgs a) {
 typedef void (*PrefillFn)(PrefillArgs);
 
 template <int D, bool PAGED, bool Q8>
-PrefillFn pick_hg(int h) {
-    if constexpr (!PAGED && Q8) {
-        return nullptr;
+PrefillFn pick_hg(int h, bool pack) {
+    if constexpr (!PAGED) {
+        return Q8 || pack ? nullptr
+                          : (h == 4 ? prefill_kernel<D, 4, false> : (h == 2 ? prefill_kernel<D, 2, false>
+                                                                               : prefill_kernel<D, 1, false>));
     } else {
+        if (pack) return prefill_kernel<D, 1, true, Q8, true>;
         return h == 4 ? prefill_kernel<D, 4, PAGED, Q8>
                       : (h == 2 ? prefill_kernel<D, 2, PAGED, Q8> : prefill_kernel<D, 1, PAGED, Q8>);
     }
 }
 
+#ifndef PGQA_EXT_PACK
+#define PGQA_EXT_PACK 1
+#endif
+
+// Packed rows (paged calls): every sequence's query tokens times the group fit
+// one 32-row tile.
+bool use_pack(int group, int max_q_len) {
+    return PGQA_EXT_PACK && max_q_len > 0 && group <= BQ && (int64_t)max_q_len * group <= BQ;
+}
+
+// Kernel for a head_dim and group size; hg = heads per workgroup (packed: the
+// whole group, one workgroup per KV head).
 template <bool PAGED>
-bool pick(int head_dim, int group, PrefillFn* fn, int* hg, bool q8 = false) {
+bool pick(int head_dim, int group, PrefillFn* fn, int* hg, bool q8 = false, bool pack = false) {
     const int h = group >= 4 ? 4 : group;
     if (group != 1 && group != 2 && group % 4 != 0) return false;
     if (group > 64) return false;
-    if (q8 && !PAGED) return false;
-    *hg = h;
+    if ((q8 || pack) && !PAGED) return false;
+    *hg = pack ? group : h;
     if (head_dim == 128) {
-        *fn = q8 ? pick_hg<128, PAGED, true>(h) : pick_hg<128, PAGED, false>(h);
+        *fn = q8 ? pick_hg<128, PAGED, true>(h, pack) : pick_hg<128, PAGED, false>(h, pack);
         return true;
     }
     if (head_dim == 64) {
-        *fn = q8 ? pick_hg<64, PAGED, true>(h) : pick_hg<64, PAGED, false>(h);
+        *fn = q8 ? pick_hg<64, PAGED, true>(h, pack) : pick_hg<64, PAGED, false>(h, pack);
         return true;
     }
     return false;
@@ -1022,10 +1108,14 @@ void extend_split(int64_t wgs_unsplit, int max_context_len, int64_t max_chunks, 
     *kchunk = kc;
 }
 
+// Query tokens per workgroup: (4 / hg) tiles of 32 rows; packed, 32 / group
+// tokens (every sequence has at most that many).
+int tokens_per_wg(const PrefillArgs& a, int hg, int group) { return a.pack ? max(1, BQ / group) : (4 / hg) * BQ; }
+
 // Tile levels, XCD packing and grid size shared by both entry points.
 void grid_dims(PrefillArgs& a, int hg, int group, int max_q_rows) {
-    const int rows_per_wg = (4 / hg) * BQ;
-    a.nqt = (max_q_rows + rows_per_wg - 1) / rows_per_wg;
+    const int rows_per_wg = tokens_per_wg(a, hg, group);
+    a.nqt = a.pack ? 1 : (max_q_rows + rows_per_wg - 1) / rows_per_wg;
     a.pairs_per_xcd = (int)(((int64_t)a.batch * a.num_kv_heads + 7) / 8);
     (void)group;
 }
@@ -1039,7 +1129,7 @@ int64_t grid_size(const PrefillArgs& a, int hg, int group) {
 // list has at most ceil(Hkv/8) * T / rows + pairs_per_xcd tiles per head group
 // and chunk (T = packed query rows).  Workgroups past their XCD's list exit.
 int64_t launch_grid(PrefillArgs& a, int hg, int group, int64_t total_rows) {
-    const int rows_per_wg = (4 / hg) * BQ;
+    const int rows_per_wg = tokens_per_wg(a, hg, group);
     a.dense = a.pairs_per_xcd <= 64 ? 1 : 0;
     if (!a.dense) return grid_size(a, hg, group);
     const int64_t per_kv = ((int64_t)a.num_kv_heads + 7) / 8;
@@ -1118,8 +1208,10 @@ hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream) {
     if (q8 ? !extend_supported_fp8(L.head_dim, group, 1 << L.block_size_log2)
            : !extend_supported(L.head_dim, group, 1 << L.block_size_log2))
         return hipErrorInvalidValue;
-    pick<true>(L.head_dim, group, &fn, &hg, q8);
+    const bool pack = use_pack(group, L.max_q_len);
+    pick<true>(L.head_dim, group, &fn, &hg, q8, pack);
     PrefillArgs a = {};
+    a.pack = pack ? 1 : 0;
     a.k_scale = L.k_scale;
     a.v_scale = L.v_scale;
     a.q = (const char*)L.q;
@@ -1177,15 +1269,13 @@ hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream) {
     a.part_ml = a.part_o + (int64_t)L.total_q * L.num_q_heads * a.nchunk * L.head_dim;
     hipError_t err = launch(fn, a, hg, group, L.head_dim, stream);
     if (err != hipSuccess || a.nchunk == 1) return err;
-    if (L.head_dim == 128) {
-        const int rpw = merge_rows_per_wg<128>(L.num_q_heads);
-        hipLaunchKernelGGL(extend_merge_kernel<128>, dim3((unsigned)((L.total_q + rpw - 1) / rpw)), dim3(256), 0,
-                           stream, a);
-    } else {
-        const int rpw = merge_rows_per_wg<64>(L.num_q_heads);
-        hipLaunchKernelGGL(extend_merge_kernel<64>, dim3((unsigned)((L.total_q + rpw - 1) / rpw)), dim3(256), 0,
-                           stream, a);
-    }
+    const int64_t mg = L.head_dim == 128 ? merge_grid<128>(L.total_q, L.num_q_heads)
+                                         : merge_grid<64>(L.total_q, L.num_q_heads);
+    if (mg > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (L.head_dim == 128)
+        hipLaunchKernelGGL(extend_merge_kernel<128>, dim3((unsigned)mg), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(extend_merge_kernel<64>, dim3((unsigned)mg), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1194,8 +1284,10 @@ size_t extend_workspace_bytes(int32_t batch, int32_t total_q, int32_t max_q_len,
     const int group = num_q_heads / num_kv_heads;
     PrefillFn fn;
     int hg;
-    if (!pick<true>(head_dim, group, &fn, &hg)) return 0;
+    const bool pack = use_pack(group, max_q_len);
+    if (!pick<true>(head_dim, group, &fn, &hg, false, pack)) return 0;
     PrefillArgs a = {};
+    a.pack = pack ? 1 : 0;
     a.batch = batch;
     a.num_kv_heads = num_kv_heads;
     a.nchunk = 1;

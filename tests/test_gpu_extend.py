@@ -190,3 +190,30 @@ def test_key_split_is_deterministic():
     b = dev.extend()
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("hq,hkv,qlens,window", [
+    (32, 8, [4, 1, 3, 4, 2, 4], 0),      # 4 tokens x 4 heads: 16 packed rows
+    (64, 8, [4, 4, 1, 3, 4, 2], 0),      # 4 x 8 = 32 rows, a full tile
+    (32, 2, [2, 1, 2, 2, 2, 1], 37),     # 2 x 16 rows, window inside the first block
+    (32, 1, [1, 1, 1, 1, 1, 1], 0),      # 32 heads of one token
+    (2, 1, [16, 9, 16, 1, 5, 16], 300),  # 16 x 2 rows, causal across many tokens
+    (8, 8, [32, 17, 32, 32, 1, 8], 0),   # one head per KV head: 32 tokens
+    (8, 8, [33, 17, 32, 32, 1, 8], 0),   # 33 tokens: not packed
+])
+def test_packed_rows(orc, hq, hkv, qlens, window):
+    """Calls whose query tokens times the group fit one 32-row tile run on the
+    packed-rows kernel (rows = (token, head) pairs, two waves splitting each key
+    block): ragged token counts, causal masks between the packed tokens,
+    windows, and long contexts that split into key chunks."""
+    prefix = [3000, 0, 61, 64, 1500, 127 - qlens[5]]
+    c = W.make_extend_case(prefix, qlens, hq, hkv, 128, 16, W.BF16, seed=990 + hq + hkv + sum(qlens) + window)
+    say(f"extend packed rows {hq}/{hkv} q_lens {qlens} window {window}")
+    dev = DevExtend(c)
+    out = to_f64(pg.gqa_paged_extend(dev.q, dev.cu_q, dev.kc, dev.vc, dev.table, dev.ctx, c.max_q_len,
+                                     c.max_context_len, scale=float(c.scale), window=window))
+    assert_close(out, oracle_extend(orc, c, window=window), W.BF16, f"packed {hq}/{hkv}")
+    plain = to_f64(pg.gqa_paged_extend(dev.q, dev.cu_q, dev.kc, dev.vc, dev.table, dev.ctx, c.max_q_len,
+                                       c.max_context_len, scale=float(c.scale), window=window,
+                                       workspace=torch.empty(16, dtype=torch.uint8, device="cuda")))
+    assert_close(plain, oracle_extend(orc, c, window=window), W.BF16, f"packed {hq}/{hkv}, no split")
