@@ -64,12 +64,12 @@ TRAFFIC_PARTS = {
                  _DECODE_SRC),
     "window": ("long_ctx_decode, window 4096",
                ["decode_split_kernel<2,128,8,1,2>", "decode_merge_kernel<2,128,8>"], _DECODE_SRC),
-    "mqa": ("mqa_decode", ["prefill_kernel<128,1,true,false>", "extend_merge_kernel<128>"],
+    "mqa": ("mqa_decode", ["prefill_kernel<128,1,true,false,true>", "extend_merge_kernel<128>"],
             _DECODE_SRC + _PREFILL_SRC[:1]),
-    "prefill": ("varlen_prefill", ["prefill_kernel<128,4,false,false>"], _PREFILL_SRC),
-    "chunked_prefill": ("chunked_prefill", ["prefill_kernel<128,4,true,false>"], _PREFILL_SRC),
-    "spec_verify": ("spec_verify", ["prefill_kernel<128,4,true,false>"], _PREFILL_SRC),
-    "fp8_spec": ("spec_verify over FP8 pages", ["prefill_kernel<128,4,true,true>"], _PREFILL_SRC),
+    "prefill": ("varlen_prefill", ["prefill_kernel<128,4,false,false,false>"], _PREFILL_SRC),
+    "chunked_prefill": ("chunked_prefill", ["prefill_kernel<128,4,true,false,false>"], _PREFILL_SRC),
+    "spec_verify": ("spec_verify", ["prefill_kernel<128,1,true,false,true>"], _PREFILL_SRC),
+    "fp8_spec": ("spec_verify over FP8 pages", ["prefill_kernel<128,1,true,true,true>"], _PREFILL_SRC),
     "fp8": ("llama3_8b_decode over FP8 pages", ["decode_split_kernel<2,128,4,1,1>", "decode_merge_kernel<2,128,4>"],
             _DECODE_SRC),
     "shared": ("shared_prefix_decode", ["decode_split_kernel<2,128,4,1,2>", "decode_merge_kernel<2,128,4>"],
@@ -386,8 +386,9 @@ def window_leg(args, torch, pg, W, T, window=4096, traffic=None):
 def mqa_leg(args, torch, pg, W, T, traffic=None):
     """MQA decode (B = 256, lognormal contexts, 32 query heads on one KV head,
     bs 32).  With one KV head and a group of 32 the library routes the call to
-    the matrix-core multi-token kernel (the query heads form the rows of the
-    32-row MFMA tile, contexts cut into key chunks merged afterwards); the VALU
+    the matrix-core multi-token kernel (the query heads form the packed rows of
+    one 32-row MFMA tile, two waves sharing every key block, contexts cut into
+    key chunks merged afterwards); the VALU
     split kernel on the same pools (forced by an explicit 1,024-share split) is
     timed beside it.  Calls rotate over four pool copies.  Bytes = the K/V read."""
     case = W.make_workload("mqa_decode")
@@ -407,7 +408,7 @@ def mqa_leg(args, torch, pg, W, T, traffic=None):
     return {
         "workload": "mqa_decode", "batch": case.batch, "num_q_heads": case.num_q_heads,
         "num_kv_heads": case.num_kv_heads, "block_size": case.block_size, "kv_bytes_per_call": kvb,
-        "route": "matrix-core multi-token kernel (query heads as MFMA tile rows)",
+        "route": "matrix-core multi-token kernel (query heads as the packed rows of one MFMA tile)",
         "call_us": {k: round(v, 2) for k, v in us.items()}, "split_kernel_us_mean": round(us_split["mean"], 2),
         "speedup_vs_split_kernel": round(us_split["mean"] / us["mean"], 3),
         "tokens_per_s": round(case.batch / (us["mean"] * 1e-6), 1), "roofline": _hbm_roof(kvb, us["mean"], traffic),
@@ -445,10 +446,15 @@ def prefill_leg(args, torch, pg, W, T, traffic=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     us = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    # The same call back to back (no paged write between): the kernel in steady state.
+    b2b = _timed_calls(torch, lambda i: pg.gqa_varlen_prefill(q, k, v, cu, p.max_seqlen, scale=scale, causal=True,
+                                                              out=out), n)
     flops = p.flops()
     return {
         "workload": "varlen_prefill", "tokens": p.total_tokens, "flops_per_call": flops,
         "call_us": {"mean": round(float(us.mean()), 2), "median": round(float(np.median(us)), 2)},
+        "back_to_back_us": {k_: round(v_, 2) for k_, v_ in b2b.items()},
+        "back_to_back_tflops": round(flops / (b2b["mean"] * 1e-6) / 1e12, 2),
         "ms_per_step": wall * 1e3 / n, "tflops": round(flops / (us.mean() * 1e-6) / 1e12, 2),
         "tokens_per_s": round(p.total_tokens / (us.mean() * 1e-6), 1),
         "roofline": _mfma_roof(flops, float(us.mean()), traffic), "out": out,

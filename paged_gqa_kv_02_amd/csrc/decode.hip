@@ -81,6 +81,9 @@
 #ifndef PGQA_DECODE_LDS_DIV
 #define PGQA_DECODE_LDS_DIV 4   // one-wave workgroups per CU on bf16 / fp32 pages (one per SIMD)
 #endif
+#ifndef PGQA_DECODE_LDS_DIV8
+#define PGQA_DECODE_LDS_DIV8 8  // one-wave workgroups per CU on FP8 pages (two per SIMD)
+#endif
 
 namespace pgqa {
 
@@ -1081,7 +1084,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     // 128 us for 4 (32-token tiles), the 16-token tiles 126-129 us at the 9 per
     // CU their LDS allows against 122 us at 4, and FP8 pages 78-86 us at 8 per
     // CU (8-row tiles) against 87-93 us at 4 (16-row tiles).
-    if (e.waves == 1) lds = std::max(lds, lds_per_cu() / (L.k_scale ? 8 : PGQA_DECODE_LDS_DIV));
+    if (e.waves == 1) lds = std::max(lds, lds_per_cu() / (L.k_scale ? PGQA_DECODE_LDS_DIV8 : PGQA_DECODE_LDS_DIV));
     int nw = L.num_splits;
     if (nw <= 0) {
         nw = occupancy(e.split, threads, lds) * cu_count();
