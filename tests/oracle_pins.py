@@ -704,6 +704,32 @@ def sdpa_extend(case: W.ExtendCase) -> np.ndarray:
     return out
 
 
+def pin_fp8_extend_is_attention_over_dequantized(orc):
+    """Multi-token queries over fp8 pages = attention over the values code * scale:
+    the oracle over its dequantised pools against SDPA with a bottom-right mask on
+    dense K/V rebuilt with torch's fp8 conversion."""
+    c = W.make_extend_case([0, 7, 40, 3], [5, 1, 9, 16], 8, 2, 16, 4, W.BF16, 89)
+    kc, vc, ks, vs = _fp8_pools(orc, c)
+    got = orc.gqa_paged_extend(f64(c.q), c.cu_q, orc.dequantize_fp8(kc, ks), orc.dequantize_fp8(vc, vs),
+                               c.block_table, c.context_lens, c.scale)
+    q = f64(c.q)
+    for b in range(c.batch):
+        qa, qe = int(c.cu_q[b]), int(c.cu_q[b + 1])
+        n, ctx = qe - qa, int(c.context_lens[b])
+        kk = np.zeros((ctx, 2, 16))
+        vv = np.zeros((ctx, 2, 16))
+        for pos in range(ctx):
+            blk, slot = c.block_table[b, pos // 4], pos % 4
+            kk[pos] = _torch_fp8_values(kc[blk, :, slot]) * ks[blk, :, slot, None].astype(np.float64)
+            vv[pos] = _torch_fp8_values(vc[blk, :, slot]) * vs[blk, :, slot, None].astype(np.float64)
+        mask = np.arange(ctx)[None, :] <= (ctx - n + np.arange(n))[:, None]
+        r = F.scaled_dot_product_attention(torch.from_numpy(q[qa:qe]).permute(1, 0, 2).unsqueeze(0).contiguous(),
+                                           torch.from_numpy(kk.transpose(1, 0, 2).copy()).unsqueeze(0),
+                                           torch.from_numpy(vv.transpose(1, 0, 2).copy()).unsqueeze(0),
+                                           attn_mask=torch.from_numpy(mask), scale=float(c.scale), enable_gqa=True)
+        close(got[qa:qe], r[0].permute(1, 0, 2).numpy(), rel=1e-12, what=f"fp8 extend seq {b}")
+
+
 def pin_extend_matches_library(orc):
     for dt, seed in ((W.F32, 81), (W.BF16, 82)):
         c = W.make_extend_case([0, 7, 40, 3, 100], [5, 1, 9, 16, 2], 8, 2, 16, 4, dt, seed)
