@@ -200,6 +200,9 @@ def test_key_split_is_deterministic():
     (2, 1, [16, 9, 16, 1, 5, 16], 300),  # 16 x 2 rows, causal across many tokens
     (8, 8, [32, 17, 32, 32, 1, 8], 0),   # one head per KV head: 32 tokens
     (8, 8, [33, 17, 32, 32, 1, 8], 0),   # 33 tokens: not packed
+    (24, 2, [2, 1, 2, 2, 1, 2], 0),      # G = 12: 24 rows, heads not a power of two
+    (24, 1, [1, 1, 1, 1, 1, 1], 100),    # G = 24, one token
+    (40, 2, [1, 1, 1, 1, 1, 1], 0),      # G = 20
 ])
 def test_packed_rows(orc, hq, hkv, qlens, window):
     """Calls whose query tokens times the group fit one 32-row tile run on the

@@ -254,3 +254,14 @@ def test_extend_released_pages_are_not_read(orc, bs):
                                   to_dev(c.context_lens), c.max_q_len, c.max_context_len, scale=float(c.scale),
                                   window=window)
     assert_close(to_f64(out), ref, W.BF16, f"fp8 extend released pages bs{bs}")
+
+
+@pytest.mark.parametrize("hq,hkv,qlens,window", [(24, 2, [2, 1, 2, 2], 0), (32, 1, [1, 1, 1, 1], 0),
+                                                 (8, 2, [8, 3, 8, 1], 70), (2, 2, [32, 5, 17, 32], 0)])
+def test_extend_packed_rows(orc, hq, hkv, qlens, window):
+    """FP8 pages on the packed-rows kernel (query tokens x group <= 32): groups that
+    are not powers of two, one token of 32 heads, windows, full 32-row tiles."""
+    c = W.make_extend_case([3000, 64, 130, 1], qlens, hq, hkv, 128, 16, W.BF16, seed=2800 + hq + hkv + window)
+    say(f"fp8 extend packed {hq}/{hkv} q_lens {qlens} window {window}")
+    out, ref = _extend_case_fp8(orc, c, window=window)
+    assert_close(out, ref, W.BF16, f"fp8 packed {hq}/{hkv}")
