@@ -43,39 +43,40 @@ __global__ __launch_bounds__(256) void check_kernel(CheckArgs a) {
     int flags = 0;
     // Rows of the sequence (its new tokens): offsets start at 0, never decrease,
     // end at total_rows, and no sequence has more than max_rows.
-    int rows = 0;
+    // (Contents may be anything: the arithmetic on them is 64-bit.)
+    int64_t rows = 0;
     if (a.cu) {
-        const int c0 = a.cu[b];
-        const int c1 = a.cu[b + 1];
+        const int64_t c0 = a.cu[b];
+        const int64_t c1 = a.cu[b + 1];
         if ((b == 0 && c0 != 0) || c1 < c0 || (b == a.batch - 1 && c1 != a.total_rows) ||
             (a.max_rows >= 0 && c1 - c0 > a.max_rows))
             flags |= PGQA_CHECK_ROWS;
-        rows = min(max(c1 - c0, 0), 1 << 30);
+        rows = c1 > c0 ? c1 - c0 : 0;
     }
     // Positions whose pages the call reads or writes: [p_lo, p_hi).
-    int p_lo = 0, p_hi = 0;
+    int64_t p_lo = 0, p_hi = 0;
     const int64_t table_pos = (int64_t)a.max_blocks_per_seq << a.bs_log2;
     if (a.context_lens) {
-        const int L = a.context_lens[b];
+        const int64_t L = a.context_lens[b];
         if (L < 0 || L > a.max_context_len) flags |= PGQA_CHECK_CONTEXT;
-        const int q = a.cu ? rows : 1;   // without offsets: one query token (decode)
+        const int64_t q = a.cu ? rows : 1;   // without offsets: one query token (decode)
         if (a.cu && L < rows) flags |= PGQA_CHECK_SHORT_CONTEXT;
         if (!a.cu || rows > 0) {
-            p_hi = (int)min((int64_t)min(max(L, 0), a.max_context_len), table_pos);
+            p_hi = min(min(max(L, (int64_t)0), (int64_t)a.max_context_len), table_pos);
             // Under a window only the first query row's window edge onwards is read.
-            if (a.window > 0) p_lo = max(0, p_hi - q - a.window + 1);
+            if (a.window > 0) p_lo = max((int64_t)0, p_hi - q - a.window + 1);
         }
     } else if (a.start_pos && a.cu) {
-        const int s = a.start_pos[b];
-        if (s < 0 || (int64_t)s + rows > table_pos) flags |= PGQA_CHECK_CONTEXT;
-        p_lo = (int)min((int64_t)max(s, 0), table_pos);
-        p_hi = (int)min((int64_t)max(s, 0) + rows, table_pos);
+        const int64_t s = a.start_pos[b];
+        if (s < 0 || s + rows > table_pos) flags |= PGQA_CHECK_CONTEXT;
+        p_lo = min(max(s, (int64_t)0), table_pos);
+        p_hi = min(max(s, (int64_t)0) + rows, table_pos);
     }
     int bad = 0;
     if (a.block_table && p_hi > p_lo) {
         const int32_t* row = a.block_table + (int64_t)b * a.max_blocks_per_seq;
-        const int pg0 = p_lo >> a.bs_log2;
-        const int pg1 = ((p_hi - 1) >> a.bs_log2) + 1;
+        const int pg0 = (int)(p_lo >> a.bs_log2);
+        const int pg1 = (int)(((p_hi - 1) >> a.bs_log2) + 1);   // <= max_blocks_per_seq
         for (int p = pg0 + (int)threadIdx.x; p < pg1; p += 256) {
             const int id = row[p];
             bad += (id < 0 || id >= a.num_blocks) ? 1 : 0;

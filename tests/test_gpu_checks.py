@@ -142,3 +142,22 @@ def test_launch_log(monkeypatch, capfd):
     pg.gqa_paged_decode(dev.q, dev.kc, dev.vc, dev.table, dev.ctx, c.max_context_len, scale=float(c.scale))
     torch.cuda.synchronize()
     assert "pgqa:" not in capfd.readouterr().err
+
+
+def test_garbage_contents_are_reported_not_followed():
+    """Extreme values in every array: each is reported, and the check reads nothing
+    outside the arrays (lengths are cut to the table row)."""
+    c = W.make_extend_case([0, 31, 64], [5, 33, 1], 8, 2, 128, 16, W.BF16, seed=3007)
+    big = 2 ** 31 - 1
+    ctx = np.array([big, -big - 1, 7], dtype=np.int32)
+    cu = np.array([0, big, 5, 7], dtype=np.int32)
+    t = np.full_like(c.block_table, -7)
+    say("check contents: garbage")
+    r = pg.check_contents(c.batch, block_table=to_dev(t), context_lens=to_dev(ctx), cu_rows=to_dev(cu),
+                          total_rows=c.total_q, max_rows=c.max_q_len, num_blocks=c.num_blocks,
+                          block_size=c.block_size, max_context_len=c.max_context_len, window=big)
+    assert r["flags"] == 1 | 2 | 4 | 8 and r["first_bad_sequence"] == 0 and r["bad_sequences"] == 3
+    sp = np.array([big, -5, 0], dtype=np.int32)
+    r = pg.check_contents(c.batch, block_table=to_dev(t), cu_rows=to_dev(cu), start_pos=to_dev(sp),
+                          total_rows=c.total_q, num_blocks=c.num_blocks, block_size=c.block_size)
+    assert r["flags"] & 2 and r["flags"] & 4 and r["bad_sequences"] == 3
