@@ -73,7 +73,7 @@
 #define PGQA_MQA_PACK 1
 #endif
 #ifndef PGQA_MQA_CHUNK
-#define PGQA_MQA_CHUNK 16  // 64-key blocks per key chunk on the matrix-core MQA route
+#define PGQA_MQA_CHUNK 20  // 64-key blocks per key chunk on the matrix-core MQA route
 #endif
 #ifndef PGQA_DECODE_RPT8
 #define PGQA_DECODE_RPT8 8

@@ -146,10 +146,11 @@ def test_workspace_reuse(orc):
 @pytest.mark.parametrize("hq,d,bs", [(32, 128, 16), (32, 64, 8), (64, 128, 4), (32, 128, 256)])
 def test_one_kv_head_matrix_core_route(orc, hq, d, bs):
     """One KV head and Hq a multiple of 32 run on the matrix cores (query heads as
-    tile rows, keys in chunks of 1024): empty, one-token, page- and chunk-edge and
-    long contexts against the oracle, sharpened queries too, deterministic, and
-    within tolerance of the split-KV kernel (an explicit split count keeps that path)."""
-    lens = [0, 1, bs - 1, bs, bs + 1, 1023, 1024, 1025, 3000, 5000]
+    tile rows, keys in chunks of 1280 = 20 blocks of 64): empty, one-token, page- and
+    chunk-edge and long contexts against the oracle, sharpened queries too,
+    deterministic, and within tolerance of the split-KV kernel (an explicit split
+    count keeps that path)."""
+    lens = [0, 1, bs - 1, bs, bs + 1, 1023, 1024, 1025, 1279, 1280, 1281, 2561, 3000, 5000]
     case = W.make_decode_case(lens, hq, 1, d, bs, W.BF16, seed=hq * 7 + d + bs)
     say(f"decode one KV head hq={hq} d{d} bs{bs}")
     dev = DevDecode(case)
