@@ -88,6 +88,15 @@ __device__ __forceinline__ float shfl_xor_f32(float x, int mask) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
 }
 
+// max(x of this lane, x of lane ^ 32) with gfx950's half-wave swap
+// (v_permlane32_swap: a VALU operation, no LDS round trip).  Swapping the upper
+// half of one copy with the lower half of another leaves the lower halves in the
+// first result and the upper halves in the second, each duplicated over the wave.
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float wave_max(float x) {
     for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, shfl_xor_f32(x, m));
     return x;

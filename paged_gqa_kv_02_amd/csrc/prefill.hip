@@ -708,21 +708,32 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
             // The lane's row position (packed: its row's token).
             const int lrow = koff + (PACK ? (ln & 31) / G : i0 + (ln & 31));
             const int lim = (a.causal ? min(lrow, Lk - 1) : Lk - 1) - j0 - 4 * (ln >> 5) - 32 * hoff;
-            const int llim = (win > 0 ? lrow - win + 1 : -(1 << 30)) - j0 - 4 * (ln >> 5) - 32 * hoff;
+            if (win > 0) {
+                const int llim = lrow - win + 1 - j0 - 4 * (ln >> 5) - 32 * hoff;
 #pragma unroll
-            for (int kb2 = 0; kb2 < NH; ++kb2)
+                for (int kb2 = 0; kb2 < NH; ++kb2)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int off = 32 * kb2 + 8 * (i >> 2) + (i & 3);
-                    cur[kb2][i] = (off <= lim && off >= llim) ? cur[kb2][i] : -INFINITY;
-                }
+                    for (int i = 0; i < 16; ++i) {
+                        const int off = 32 * kb2 + 8 * (i >> 2) + (i & 3);
+                        cur[kb2][i] = (off <= lim && off >= llim) ? cur[kb2][i] : -INFINITY;
+                    }
+            } else {
+                // (No window: one comparison per score.)
+#pragma unroll
+                for (int kb2 = 0; kb2 < NH; ++kb2)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int off = 32 * kb2 + 8 * (i >> 2) + (i & 3);
+                        cur[kb2][i] = off <= lim ? cur[kb2][i] : -INFINITY;
+                    }
+            }
         }
         float mt = cur[0][0];
 #pragma unroll
         for (int kb2 = 0; kb2 < NH; ++kb2)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mt = fmaxf(mt, cur[kb2][i]);
-        mt = fmaxf(mt, shfl_xor_f32(mt, 32)) * cs;
+        mt = max_xor32(mt) * cs;
         const bool need = mt > m + 8.0f;
         if (__builtin_expect(__any(need), 0)) {
             if (need) {
