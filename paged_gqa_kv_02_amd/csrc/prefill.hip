@@ -54,6 +54,7 @@
 // page, so its source is one scalar base (block id from a scalar load of the
 // block-table row, issued before the block's DMA wait and barrier) plus the
 // lane's offset, exactly as for packed K/V.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -84,6 +85,9 @@ struct PrefillArgs {
     int32_t chunk_lpt;       // 1: dense lists of key chunks, full chunks first (one query tile and head group per pair)
     int32_t kv_nt;           // 1: K/V read by one workgroup only (one query tile and head group per pair): non-temporal loads
     int32_t pack;            // host side: the packed-rows kernel was chosen
+    int32_t sk_nw;           // > 0 (packed rows): stream-K shares, one per workgroup
+    int32_t sk_pair_units;   // work units charged per pair on top of its key blocks (its piece's start-up)
+    int32_t* sk_cut;         // [sk_nw][4]: per share, the pair cut at its end (or -1), its units, the total
     // Paged K/V only (k, v are then the pools [num_blocks, Hkv, block_size, d]).
     const int32_t* block_table;
     const int32_t* context_lens;
@@ -97,8 +101,8 @@ struct PrefillArgs {
     // chunk gets fp32 partials per (row, head, chunk), merged afterwards.
     int32_t nchunk;          // 1 = no split
     int32_t kchunk;          // key blocks per chunk
-    float* part_o;           // [total_tokens, Hq, nchunk, D]
-    float* part_ml;          // [total_tokens, Hq, nchunk, 2]  (m in log2 units, l)
+    float* part_o;           // [total_tokens, Hq, nchunk, D]  (stream-K: [2 * sk_nw, 32, D])
+    float* part_ml;          // [total_tokens, Hq, nchunk, 2]  (m in log2 units, l; stream-K: [2 * sk_nw, 32, 2])
     // FP8 pages only (k, v are then code pools [num_blocks, Hkv, block_size, d] uint8).
     const float* k_scale;    // row scales [num_blocks, Hkv, block_size]
     const float* v_scale;
@@ -446,6 +450,541 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int G = a.num_q_heads / a.num_kv_heads;
     const int groups = PACK ? 1 : G / HG;
 
+    // One tile: query tile `qtile` of head group `grp` of pair (s, kvh) (rows
+    // seq0 .. seq0 + Lq - 1 of the packed q / out, Lk keys), over the key blocks
+    // [c_lo, c_hi) cut to those the tile reads.  Its output goes to `out`, or
+    // (split) as partials: of key chunk `chunk`, or in stream-K slot `slot` >= 0.
+    // Query row i sits at key position koff + i (packed prefill: the sequence's
+    // own rows, koff = 0; paged: the cached context, koff = ctx - q_len) and,
+    // when causal, sees keys 0 .. koff + i.
+    auto tile = [&](const int s, const int kvh, const int grp, const int qtile, const int seq0, const int Lq,
+                    const int Lk, const int c_lo, const int c_hi, const bool split, const int chunk,
+                    const int slot) __attribute__((always_inline)) {
+        const int koff = PAGED ? Lk - Lq : 0;
+        const int tok0 = qtile * TB * BQ;
+        const int head = kvh * G + grp * HG + (wave % HG);
+        // This wave's first query row (sequence-local); packed: token 0 for waves 0, 1.
+        const int i0 = PACK ? (wave < 2 ? 0 : 1 << 30) : tok0 + (wave / HG) * BQ;
+        const int hoff = PACK ? (wave & 1) : 0;          // packed: the wave's key half
+        const int prows = PACK ? Lq * G : 0;             // packed rows (<= 32)
+
+        const int wg_rows_end = min(Lq, tok0 + TB * BQ);
+        const int keys = a.causal ? min(Lk, koff + wg_rows_end) : Lk;   // keys the workgroup reads
+        const int nkb = keys > 0 ? (keys + BN - 1) / BN : 0;
+        const bool active = i0 < Lq;
+        const int last_key = a.causal ? min(Lk, koff + min(i0 + BQ, Lq)) - 1 : Lk - 1;
+        const int last_kb = last_key >= 0 ? last_key / BN : -1;
+        // Local attention (window > 0, causal only): row i also drops keys below
+        // koff + i - window + 1.  The workgroup streams key blocks kb0 .. nkb-1, kb0
+        // set by its first row; every wave computes from kb0 (the blocks before its
+        // own rows' windows are fully masked) to its last block.  Ring slots and the
+        // block loop run on the index relative to kb0.
+        const int win = a.window;
+        const int kbw = (win > 0 && nkb > 0) ? max(0, koff + tok0 - win + 1) / BN : 0;
+        // This workgroup's key blocks: the window's range cut to its chunk (or piece).
+        const int kb0 = max(kbw, c_lo);
+        const int kb1 = min(nkb, c_hi);
+        const int nrel = max(0, kb1 - kb0);
+        const float cs = a.scale_log2;
+
+        const int64_t qstride = (int64_t)a.num_q_heads * D * 2;   // bytes per packed Q row
+        const int64_t kvstride = (int64_t)a.num_kv_heads * P::ROWB;
+
+        // Prologue: K(0), V(0) and K(1) in flight while Q is read.
+        DmaLane<D> dl;
+        PagedSrc<D> ps;
+        const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+        // FP8 row scales: K scales of relative tile t in slot t % 3, V scales in slot 3 + t % 2.
+        const uint32_t scale_addr = ring_addr + 4 * P::TILEB;
+        const PGQA_LDS float* scale_lds = (const PGQA_LDS float*)(ring + 4 * P::TILEB);
+        // DMA of relative tile t (key block kb0 + t) of this wave's pool.
+        auto issue_paged = [&](int t, int ln) {
+            if constexpr (Q8)
+                issue_tile_paged_q8<D>(ps, ps.isv ? a.v_scale : a.k_scale, ring_addr, scale_addr, kb0 + t, t & 1,
+                                       ps.isv ? 3 + (t & 1) : t % 3, wave, ln, kvh, a.num_kv_heads);
+            else
+                issue_tile_paged<D>(ps, dl, ring_addr, kb0 + t, t & 1, ln);
+        };
+        if constexpr (PAGED) {
+            dma_lane_init_paged<D>(dl, lane);
+            ps.bt = (ConstI32Ptr)(a.block_table + (int64_t)s * a.max_blocks_per_seq);
+            ps.isv = wave >= 2;
+            ps.j0 = (wave & 1) * NPW;
+            ps.pool = ps.isv ? a.v : a.k;
+            ps.lbs = a.bs_log2;
+            ps.head_off = ((int64_t)kvh << a.bs_log2) * P::ROWB;
+            ps.blk_bytes = ((int64_t)a.num_kv_heads << a.bs_log2) * P::ROWB;
+            ps.last = Lk - 1;
+            ps.lo = win > 0 ? min(max(0, koff + tok0 - win + 1), Lk - 1) : 0;
+            ps.nb = a.num_blocks;
+            ps.nt = a.kv_nt != 0;
+            if (nrel > 0) {
+                paged_load_ids<D, Q8>(ps, kb0);
+                issue_paged(0, lane);
+                if (!ps.isv && nrel > 1) {
+                    paged_load_ids<D, Q8>(ps, kb0 + 1);
+                    issue_paged(1, lane);
+                }
+            }
+        } else {
+            dma_lane_init<D>(dl, wave, lane, kvstride);
+            issue_tile<D>(a, dl, ring_addr, kb0, 0, seq0, Lk, kvh, wave, lane, kvstride);
+            if (wave < 2 && nrel > 1) issue_tile<D>(a, dl, ring_addr, kb0 + 1, 1, seq0, Lk, kvh, wave, lane, kvstride);
+        }
+
+        // Q^T operand: lane holds row (i0 + l32), d = 16*kk + 8*half .. +8.
+        u32x4 qreg[KSTEPS];
+        {
+            const int row = min(i0 + l32, Lq - 1);
+            const char* qp = a.q + (int64_t)(seq0 + row) * qstride + (int64_t)head * D * 2 + half * 16;
+            if constexpr (PACK) {
+                const int r = min(l32, prows - 1);
+                qp = a.q + (int64_t)(seq0 + r / G) * qstride + (int64_t)(kvh * G + r % G) * D * 2 + half * 16;
+            }
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk) qreg[kk] = (*(const u32x4*)(qp + kk * 32) & a.q_and) ^ a.q_xor;
+        }
+
+        float m = kMaxInit, lsum = 0.0f;
+        f32x16 o[DBLK];
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
+
+        // V^T operand addressing (ds_read_b64_tr_b16): in each 16-lane group, lane j
+        // supplies row (key0 + j/4), dims d0 + 4*(j%4) .. +3 of the V tile; lane i
+        // of the group then receives dims d0 + i of keys key0 .. key0+3.
+        const int gl = lane & 15;
+        const int vrow = gl >> 2;                          // + key0
+        const int vdim = 16 * ((lane >> 4) & 1) + 4 * (gl & 3);   // + 32*db
+        // Per-lane LDS offsets, fixed for the whole key loop.  K operand, step kk:
+        // row l32 (+32 per key half, which keeps the swizzle key), chunk 2*kk + half,
+        // i.e. kx ^ (kk << 5).  V operand, dim block db, keys +8h: rows
+        // 4*half + vrow + 8h (+16 per key step, same key), chunk 4*db + vdim/8; the
+        // key of row r + 8 is key(r) ^ 2, so this is (vx ^ (db << 6) ^ (h << 5)) +
+        // 8h rows.  The XORs only touch the chunk field of the offset.
+        const int kx = swz<D>(l32, half);
+        const int vx = swz<D>(4 * half + vrow, vdim >> 3) + ((vdim & 7) << 1);
+        const u32 ones_bf16x2 = 0x3F803F80u;   // (1.0, 1.0) in bf16
+
+        // S^T = K Q^T for key block kb (K slot kb % 2): per 32-key half kb2, lane
+        // (l32, half) gets row l32, keys 32*kb2 + 8*(i/4) + 4*half + i%4.
+        auto scores = [&](f32x16 (&st)[2], auto slot) {
+            // (FP8 pages: the one bf16 K tile.)
+            const PGQA_LDS char* kt = ring + (Q8 ? 0 : decltype(slot)::value * P::TILEB);
+#pragma unroll
+            for (int kb2 = 0; kb2 < NH; ++kb2) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) st[kb2][i] = 0.0f;
+#pragma unroll
+                for (int kk = 0; kk < KSTEPS; ++kk)
+                    st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, lds_read_16(kt + 32 * (kb2 + hoff) * P::ROWB + (kx ^ (kk << 5)))),
+                        __builtin_bit_cast(bf16x8, qreg[kk]), st[kb2], 0, 0, 0);
+            }
+        };
+
+        // One key block: softmax of the block's scores `cur`, overlapped with the
+        // next block's scores into `nxt` (when HAS_NEXT), then O^T += V^T P^T.
+        auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], int kr, auto par, auto has_next) {
+            constexpr int PAR = decltype(par)::value;   // kr % 2
+            const int j0 = (kb0 + kr) * BN;
+            // FP8 pages: scores times the keys' row scales (key offsets as in the masking below).
+            if constexpr (Q8) {
+                const PGQA_LDS float* ks = scale_lds + (kr % 3) * BN + 32 * hoff + 4 * (lane_now() >> 5);
+#pragma unroll
+                for (int g = 0; g < 4 * NH; ++g) {
+                    const f32x4 k4 = *(const PGQA_LDS f32x4*)(ks + 8 * g);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) cur[g >> 2][4 * (g & 3) + t] *= k4[t];
+                }
+            }
+            // Masking (last block of the sequence, a block crossing the diagonal,
+            // or one crossing the window's lower edge): key j0 + off is kept iff
+            // llim <= off <= lim, with off = 32*kb2 + 8*(i/4) + i%4 and the lane's
+            // 4*half folded into both bounds.
+            if ((j0 + BN > Lk) || (a.causal && j0 + BN - 1 > koff + i0) || (win > 0 && j0 < koff + i0 + BQ - win)) {
+                const int ln = lane_now();
+                // The lane's row position (packed: its row's token).
+                const int lrow = koff + (PACK ? (ln & 31) / G : i0 + (ln & 31));
+                const int lim = (a.causal ? min(lrow, Lk - 1) : Lk - 1) - j0 - 4 * (ln >> 5) - 32 * hoff;
+                if (win > 0) {
+                    const int llim = lrow - win + 1 - j0 - 4 * (ln >> 5) - 32 * hoff;
+#pragma unroll
+                    for (int kb2 = 0; kb2 < NH; ++kb2)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int off = 32 * kb2 + 8 * (i >> 2) + (i & 3);
+                            cur[kb2][i] = (off <= lim && off >= llim) ? cur[kb2][i] : -INFINITY;
+                        }
+                } else {
+                    // (No window: one comparison per score.)
+#pragma unroll
+                    for (int kb2 = 0; kb2 < NH; ++kb2)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int off = 32 * kb2 + 8 * (i >> 2) + (i & 3);
+                            cur[kb2][i] = off <= lim ? cur[kb2][i] : -INFINITY;
+                        }
+                }
+            }
+            float mt = cur[0][0];
+#pragma unroll
+            for (int kb2 = 0; kb2 < NH; ++kb2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mt = fmaxf(mt, cur[kb2][i]);
+            mt = max_xor32(mt) * cs;
+            const bool need = mt > m + 8.0f;
+            if (__builtin_expect(__any(need), 0)) {
+                if (need) {
+                    const float alpha = __builtin_amdgcn_exp2f(m - mt);
+                    m = mt;
+                    lsum *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+                }
+            }
+            // The MFMA + softmax interleave runs at raised wave priority, so of the
+            // two workgroups sharing a SIMD the one in this phase issues first and
+            // the other's P.V products fill the matrix pipe around it.
+            __builtin_amdgcn_s_setprio(3);
+            if constexpr (decltype(has_next)::value) scores(nxt, std::integral_constant<int, 1 - PAR>{});
+            // P^T operand for 16-key step kk: keys 16kk + 8*(jj/4) + 4*half + jj%4,
+            // i.e. accumulator entries 8*(kk%2) .. +7 of half kk/2.  The row sum
+            // adds the bf16-rounded weights, the same ones the PV product uses.
+            u32x4 pb[2 * NH];
+#pragma unroll
+            for (int kk = 0; kk < 2 * NH; ++kk) {
+                float p[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(cur[kk >> 1][8 * (kk & 1) + j], cs, -m));
+                if constexpr (Q8) {
+                    // Weights times the values' row scales (accumulator entry 8*(kk%2) + j
+                    // of half kk/2 is key 16*kk + 8*(j/4) + 4*half + j%4); the row sum
+                    // takes the plain weights.
+                    const PGQA_LDS float* vs = scale_lds + (3 + PAR) * BN + 16 * (kk + 2 * hoff) + 4 * (lane_now() >> 5);
+                    const f32x4 v0 = *(const PGQA_LDS f32x4*)vs;
+                    const f32x4 v1 = *(const PGQA_LDS f32x4*)(vs + 8);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        lsum += p[2 * j] + p[2 * j + 1];
+                        const f32x4& vv = j < 2 ? v0 : v1;
+                        pb[kk][j] = pack_bf16x2_rne_hw(p[2 * j] * vv[(2 * j) & 3], p[2 * j + 1] * vv[(2 * j + 1) & 3]);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        pb[kk][j] = pack_bf16x2_rne_hw(p[2 * j], p[2 * j + 1]);
+                        lsum = dot2_bf16(pb[kk][j], ones_bf16x2, lsum);
+                    }
+                }
+            }
+            if constexpr (decltype(has_next)::value) {
+                // Interleave: per next-block MFMA one K read and a slice of the
+                // softmax arithmetic, so the VALU work hides under the matrix pipe
+                // and only a few K fragments are live at a time.
+                __builtin_amdgcn_sched_group_barrier(0x100, PGQA_KREADS_AHEAD, 0);   // K reads ahead
+#pragma unroll
+                for (int i = 0; i < NH * KSTEPS; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                    if (i + PGQA_KREADS_AHEAD < NH * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // K read
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
+            // O^T += V^T P^T: A = V^T for dims 32*db + l32, keys {16kk + 4*half + 0..3, +8 ..}.
+            const PGQA_LDS char* vt = ring + (Q8 ? 1 : 2 + PAR) * P::TILEB;
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) {
+                u32x4 va[2 * NH];
+#pragma unroll
+                for (int kk = 0; kk < 2 * NH; ++kk) {
+                    const PGQA_LDS char* vk = vt + 16 * (kk + 2 * hoff) * P::ROWB;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PGQA_LDS i16x4*)(vk + (vx ^ (db << 6))));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PGQA_LDS i16x4*)(vk + 8 * P::ROWB + (vx ^ (db << 6) ^ 32)));
+                    va[kk] = u32x4{__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
+                                   __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y};
+                }
+#pragma unroll
+                for (int kk = 0; kk < 2 * NH; ++kk)
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[kk]),
+                                                                    __builtin_bit_cast(bf16x8, pb[kk]), o[db], 0, 0, 0);
+            }
+        };
+
+        // Top of block kb: every wave's DMA has landed (K(kb+1), V(kb)) and every
+        // wave is done with K(kb) and V(kb-1), so their slots are refilled with
+        // K(kb+2) and V(kb+1).
+        auto top = [&](int kr) {
+            const int tb = (PAGED ? !ps.isv : wave < 2) ? kr + 2 : kr + 1;
+            // The block ids of the tile issued below are loaded before the DMA wait
+            // and the barrier, which cover their latency; no scalar load is then in
+            // flight during the block's LDS reads (whose waits would otherwise also
+            // wait for it, scalar loads returning out of order).
+            if constexpr (PAGED)
+                if (tb < nrel) paged_load_ids<D, Q8>(ps, kb0 + tb);
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (tb < nrel) {
+                if constexpr (PAGED) {
+                    issue_paged(tb, lane_now());
+                } else {
+                    issue_tile<D>(a, dl, ring_addr, kb0 + tb, tb & 1, seq0, Lk, kvh, wave, lane_now(), kvstride);
+                }
+            }
+            // FP8 pages: the codes of K(kr+1) and V(kr) have landed; into the bf16
+            // tiles, which every wave is done with (the codes just issued go to the
+            // other stages).
+            if constexpr (Q8) convert_q8<D>(ring, kr + 1 < nrel ? (kr + 1) & 1 : -1, kr & 1);
+        };
+        // Blocks kb0 .. kb0 + kend are computed (kend = last_kb - kb0, or -1 for a
+        // wave with no rows or no keys); each but the last overlaps the next block's
+        // scores.  The two score
+        // buffers alternate, so the loop runs two blocks per trip and every block
+        // fully rewrites the buffer it fills; the ring parity is a compile-time
+        // constant in each copy.  Waves past their last block keep the workgroup's
+        // barriers and DMA going to the end.
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        f32x16 sa[2], sb[2];
+        wait_vmcnt<0>();
+        __syncthreads();
+        if constexpr (Q8)
+            if (nrel > 0) convert_q8<D>(ring, 0, -1);
+        const int kend = active && last_kb >= 0 ? min(last_kb, kb1 - 1) - kb0 : -1;
+        if (kend >= 0) scores(sa, I0{});
+        int kb = 0;
+        for (; kb + 2 <= kend; kb += 2) {
+            top(kb);
+            step(sa, sb, kb, I0{}, std::true_type{});
+            top(kb + 1);
+            step(sb, sa, kb + 1, I1{}, std::true_type{});
+        }
+        if (kb + 1 == kend) {
+            top(kb);
+            step(sa, sb, kb, I0{}, std::true_type{});
+            top(kb + 1);
+            step(sb, sa, kb + 1, I1{}, std::false_type{});
+            kb += 2;
+        } else if (kb == kend) {
+            top(kb);
+            step(sa, sb, kb, I0{}, std::false_type{});
+            kb += 1;
+        }
+        for (; kb < nrel; ++kb) top(kb);
+
+        // Epilogue: O / l rounded to bf16, staged through the idle ring so that
+        // each output row is written whole.  The wave's 32 x D tile goes to LDS
+        // (swizzled like the K/V tiles), then each lane writes one 16-byte chunk of
+        // one row, CPR consecutive lanes per row.
+        __syncthreads();   // every wave is done with the ring
+        if constexpr (PACK) {
+            // The two key halves of the same rows: wave 1's running max, sum and
+            // output go through LDS (value-major, lane-minor: conflict-free) to wave 0,
+            // which rescales both to the larger max and adds them.
+            PGQA_LDS float* xs = (PGQA_LDS float*)(ring + 2 * BQ * P::ROWB);
+            const int ln = lane_now();
+            if (wave == 1 && active) {
+#pragma unroll
+                for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) xs[(16 * db + i) * 64 + ln] = o[db][i];
+                xs[16 * DBLK * 64 + ln] = m;
+                xs[(16 * DBLK + 1) * 64 + ln] = lsum;
+            }
+            __syncthreads();
+            if (wave != 0) return;
+            const float m1 = xs[16 * DBLK * 64 + ln];
+            const float l1 = xs[(16 * DBLK + 1) * 64 + ln];
+            const float mx = fmaxf(m, m1);
+            const float a0 = __builtin_amdgcn_exp2f(m - mx);
+            const float a1 = __builtin_amdgcn_exp2f(m1 - mx);
+            m = mx;
+            lsum = lsum * a0 + l1 * a1;
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[db][i] = o[db][i] * a0 + xs[(16 * db + i) * 64 + ln] * a1;
+        }
+        if (!active) return;
+        const int lane_e = lane_now();
+        const int half_e = lane_e >> 5;
+        const int l32_e = lane_e & 31;
+        lsum += shfl_xor_f32(lsum, 32);
+        // Output row of the lane's row l32_e: token and query head (packed: the
+        // row's token and head; else row i0 + l32_e of the wave's head).
+        auto out_row = [&](int r, int& tok, int& hq) {
+            if constexpr (PACK) {
+                tok = r / G;
+                hq = kvh * G + r % G;
+            } else {
+                tok = i0 + r;
+                hq = head;
+            }
+        };
+        const int rows_here = PACK ? prows : Lq - i0;   // valid rows of the wave's tile
+        if (split) {
+            // Partial of this key chunk (or of this piece of a stream-K share, in
+            // its slot): unnormalised O, running max m and sum l (both halves of the
+            // wave hold the row's m); a row with no key in the range leaves O = 0,
+            // l = 0.
+            if (l32_e < rows_here) {
+                int tok, hq;
+                out_row(l32_e, tok, hq);
+                const int64_t prow = slot >= 0 ? (int64_t)slot * BQ + l32_e
+                                               : ((int64_t)(seq0 + tok) * a.num_q_heads + hq) * a.nchunk + chunk;
+                float* po = a.part_o + prow * D + 4 * half_e;
+#pragma unroll
+                for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd)
+                        *(f32x4*)(po + 32 * db + 8 * qd) = f32x4{o[db][4 * qd], o[db][4 * qd + 1], o[db][4 * qd + 2],
+                                                                o[db][4 * qd + 3]};
+                if (half_e == 0) *(float2*)(a.part_ml + prow * 2) = make_float2(m, lsum);
+            }
+            return;
+        }
+        const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+        PGQA_LDS char* ot = ring + wave * (BQ * P::ROWB);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                // dims 32*db + 8*qd + 4*half_e .. +3 of row l32_e: chunk 4*db + qd, byte 8*half_e
+                u32x2 w;
+                w.x = pack_bf16x2_rne_hw(o[db][4 * qd + 0] * inv, o[db][4 * qd + 1] * inv);
+                w.y = pack_bf16x2_rne_hw(o[db][4 * qd + 2] * inv, o[db][4 * qd + 3] * inv);
+                *(PGQA_LDS u32x2*)(ot + swz<D>(l32_e, 4 * db + qd) + 8 * half_e) = w;
+            }
+        const int c = lane_e % P::CPR;
+#pragma unroll
+        for (int t = 0; t < BQ / P::RPL; ++t) {
+            const int r = t * P::RPL + lane_e / P::CPR;
+            const u32x4 val = lds_read_16(ot + swz<D>(r, c));
+            if (r < rows_here) {
+                int tok, hq;
+                out_row(r, tok, hq);
+                *(u32x4*)(a.out + (int64_t)(seq0 + tok) * qstride + (int64_t)hq * D * 2 + c * 16) = val;
+            }
+        }
+    };
+
+    if constexpr (PACK) {
+        if (a.sk_nw > 0) {
+            // Stream-K shares.  A pair's work is counted in units: sk_pair_units
+            // for the start-up of its piece (Q and the first tiles' latency, about
+            // that of a few blocks), then one per key block (those of its window,
+            // as the tile computes them; at least one unit in all, so a pair whose
+            // rows have no key gets the piece that writes its zero rows).  A
+            // piece's blocks are its units past the start-up ones.  The pairs'
+            // units, concatenated in pair order, are cut into
+            // sk_nw equal shares and workgroup w runs the pieces of share w: whole
+            // pairs straight to the output, a pair cut by a share edge as partials
+            // in slot 2w (the share's first piece) or 2w + 1 (its last), which
+            // sk_merge_kernel combines.  Shares are equal in bytes whatever the
+            // context lengths, and share w runs on XCD w % 8, so the XCDs and
+            // workgroups finish together.
+            const int npairs = a.batch * a.num_kv_heads;
+            const int per = (npairs + 255) / 256;              // pairs per thread in the scan
+            const int t = threadIdx.x;
+            auto units = [&](int p, int& b0, int& lq, int& lk, int& kbw) {
+                const int sq = p / a.num_kv_heads;
+                if (a.fixed_qlen > 0) {
+                    b0 = min(sq * a.fixed_qlen, a.total_tokens);
+                    lq = min(b0 + a.fixed_qlen, a.total_tokens) - b0;
+                } else {
+                    b0 = clampi(a.cu_seqlens[sq], 0, a.total_tokens);
+                    lq = clampi(a.cu_seqlens[sq + 1], b0, a.total_tokens) - b0;
+                }
+                lk = clampi(a.context_lens[sq], 0, a.ctx_cap);
+                // Every packed row's keys end at the sequence's last key; a window
+                // starts the reads at the first row's edge.
+                const int nkb = (lk + BN - 1) / BN;
+                kbw = (a.window > 0 && nkb > 0) ? max(0, lk - lq - a.window + 1) / BN : 0;
+                return lq > 0 ? max(1, a.sk_pair_units + nkb - kbw) : 0;
+            };
+            // Block-wide exclusive scan of the per-thread sums (thread t: pairs
+            // t * per .. t * per + per - 1).
+            int sum = 0;
+            for (int i = 0; i < per; ++i) {
+                const int p = t * per + i;
+                int b0, lq, lk, kbw;
+                if (p < npairs) sum += units(p, b0, lq, lk, kbw);
+            }
+            int inc = sum;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(inc, off);
+                if (lane >= off) inc += y;
+            }
+            PGQA_LDS int* sh = (PGQA_LDS int*)ring;
+            if (lane == 63) sh[wave] = inc;
+            __syncthreads();
+            const int wsum0 = sh[0], wsum1 = sh[1], wsum2 = sh[2], wsum3 = sh[3];
+            const int total = wsum0 + wsum1 + wsum2 + wsum3;
+            const int excl = (wave > 0 ? wsum0 : 0) + (wave > 1 ? wsum1 : 0) + (wave > 2 ? wsum2 : 0) + inc - sum;
+            const int w = blockIdx.x;
+            const int lo = (int)((int64_t)w * total / a.sk_nw);
+            const int hi = (int)((int64_t)(w + 1) * total / a.sk_nw);
+            // The pair holding unit lo, found by the thread whose range holds it.
+            if (lo < hi && lo >= excl && lo < excl + sum) {
+                int u0 = excl;
+                for (int i = 0; i < per; ++i) {
+                    const int p = t * per + i;
+                    int b0, lq, lk, kbw;
+                    const int u = p < npairs ? units(p, b0, lq, lk, kbw) : 0;
+                    if (lo < u0 + u) {
+                        sh[4] = p;
+                        sh[5] = u0;
+                        break;
+                    }
+                    u0 += u;
+                }
+            }
+            __syncthreads();
+            int cut_p = -1, cut_u0 = 0, cut_u1 = 0;
+            if (lo < hi) {
+                int p = __builtin_amdgcn_readfirstlane(sh[4]);
+                int U = __builtin_amdgcn_readfirstlane(sh[5]);
+                while (U < hi && p < npairs) {
+                    int b0, lq, lk, kbw;
+                    const int u = __builtin_amdgcn_readfirstlane(units(p, b0, lq, lk, kbw));
+                    if (u > 0) {
+                        b0 = __builtin_amdgcn_readfirstlane(b0);
+                        lq = __builtin_amdgcn_readfirstlane(lq);
+                        lk = __builtin_amdgcn_readfirstlane(lk);
+                        kbw = __builtin_amdgcn_readfirstlane(kbw);
+                        const int plo = max(lo, U) - U;
+                        const int phi = min(hi, U + u) - U;
+                        const bool whole = plo == 0 && phi == u;
+                        const int slot = whole ? -1 : 2 * w + (U <= lo ? 0 : 1);
+                        if (U >= lo && U + u > hi) {   // begins here, ends in a later share
+                            cut_p = p;
+                            cut_u0 = U;
+                            cut_u1 = U + u;
+                        }
+                        const int sq = p / a.num_kv_heads;
+                        // Every wave is done with the ring (the scan's words, the
+                        // previous piece's tiles) before this piece's DMA.
+                        __syncthreads();
+                        const int c0 = a.sk_pair_units;
+                        tile(sq, p - sq * a.num_kv_heads, 0, 0, b0, lq, lk, kbw + max(0, plo - c0), kbw + max(0, phi - c0),
+                             !whole, 0, slot);
+                    }
+                    U += u;
+                    ++p;
+                }
+            }
+            // For the merge: the pair that begins in this share and is cut at its end.
+            if (t == 0) *(int4*)(a.sk_cut + 4 * w) = make_int4(cut_p, cut_u0, cut_u1, total);
+            return;
+        }
+    }
+
     // Work mapping.  Workgroups are dealt to the 8 XCDs round-robin by linear
     // id and every XCD has its own L2, so all tiles of one (sequence, KV head)
     // pair stay on one XCD: pair p = seq * Hkv + kvh lives on XCD p % 8.  Each
@@ -538,10 +1077,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     if (pair >= a.batch * a.num_kv_heads) return;
     const int s = pair / a.num_kv_heads;
     const int kvh = pair - s * a.num_kv_heads;
-    // Query rows seq0 .. seq0 + Lq - 1 of the packed q / out.  Keys: Lk rows;
-    // query row i sits at key position koff + i (packed prefill: the sequence's
-    // own rows, koff = 0; paged: the cached context, koff = ctx - q_len) and,
-    // when causal, sees keys 0 .. koff + i.
+    // The pair's query rows and keys.
     // (Loaded values count as divergent for the compiler: readfirstlane keeps
     // the sizes, and every branch on them, scalar.)
     // (With dense lists these come from the scan's loads: no second round trip.)
@@ -553,7 +1089,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                    : __builtin_amdgcn_readfirstlane(clampi(a.cu_seqlens[s + 1], seq0, a.total_tokens)) - seq0;
     const int Lk = PAGED ? (a.dense ? d_lk : __builtin_amdgcn_readfirstlane(clampi(a.context_lens[s], 0, a.ctx_cap)))
                          : Lq;
-    const int koff = PAGED ? Lk - Lq : 0;
     const int qtile = ntiles - 1 - level;
     const int tok0 = qtile * TB * BQ;
     if (tok0 >= Lq) return;
@@ -561,413 +1096,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int ckeys = a.kchunk * BN;
     if (chunk > 0 && chunk * ckeys >= Lk) return;
     const bool split = Lk > ckeys;                       // partials instead of the output
-    const int head = kvh * G + grp * HG + (wave % HG);
-    // This wave's first query row (sequence-local); packed: token 0 for waves 0, 1.
-    const int i0 = PACK ? (wave < 2 ? 0 : 1 << 30) : tok0 + (wave / HG) * BQ;
-    const int hoff = PACK ? (wave & 1) : 0;          // packed: the wave's key half
-    const int prows = PACK ? Lq * G : 0;             // packed rows (<= 32)
-
-    const int wg_rows_end = min(Lq, tok0 + TB * BQ);
-    const int keys = a.causal ? min(Lk, koff + wg_rows_end) : Lk;   // keys the workgroup reads
-    const int nkb = keys > 0 ? (keys + BN - 1) / BN : 0;
-    const bool active = i0 < Lq;
-    const int last_key = a.causal ? min(Lk, koff + min(i0 + BQ, Lq)) - 1 : Lk - 1;
-    const int last_kb = last_key >= 0 ? last_key / BN : -1;
-    // Local attention (window > 0, causal only): row i also drops keys below
-    // koff + i - window + 1.  The workgroup streams key blocks kb0 .. nkb-1, kb0
-    // set by its first row; every wave computes from kb0 (the blocks before its
-    // own rows' windows are fully masked) to its last block.  Ring slots and the
-    // block loop run on the index relative to kb0.
-    const int win = a.window;
-    const int kbw = (win > 0 && nkb > 0) ? max(0, koff + tok0 - win + 1) / BN : 0;
-    // This workgroup's key blocks: the window's range cut to its chunk.
-    const int kb0 = max(kbw, chunk * a.kchunk);
-    const int kb1 = min(nkb, chunk * a.kchunk + a.kchunk);
-    const int nrel = max(0, kb1 - kb0);
-    const float cs = a.scale_log2;
-
-    const int64_t qstride = (int64_t)a.num_q_heads * D * 2;   // bytes per packed Q row
-    const int64_t kvstride = (int64_t)a.num_kv_heads * P::ROWB;
-
-    // Prologue: K(0), V(0) and K(1) in flight while Q is read.
-    DmaLane<D> dl;
-    PagedSrc<D> ps;
-    const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
-    // FP8 row scales: K scales of relative tile t in slot t % 3, V scales in slot 3 + t % 2.
-    const uint32_t scale_addr = ring_addr + 4 * P::TILEB;
-    const PGQA_LDS float* scale_lds = (const PGQA_LDS float*)(ring + 4 * P::TILEB);
-    // DMA of relative tile t (key block kb0 + t) of this wave's pool.
-    auto issue_paged = [&](int t, int ln) {
-        if constexpr (Q8)
-            issue_tile_paged_q8<D>(ps, ps.isv ? a.v_scale : a.k_scale, ring_addr, scale_addr, kb0 + t, t & 1,
-                                   ps.isv ? 3 + (t & 1) : t % 3, wave, ln, kvh, a.num_kv_heads);
-        else
-            issue_tile_paged<D>(ps, dl, ring_addr, kb0 + t, t & 1, ln);
-    };
-    if constexpr (PAGED) {
-        dma_lane_init_paged<D>(dl, lane);
-        ps.bt = (ConstI32Ptr)(a.block_table + (int64_t)s * a.max_blocks_per_seq);
-        ps.isv = wave >= 2;
-        ps.j0 = (wave & 1) * NPW;
-        ps.pool = ps.isv ? a.v : a.k;
-        ps.lbs = a.bs_log2;
-        ps.head_off = ((int64_t)kvh << a.bs_log2) * P::ROWB;
-        ps.blk_bytes = ((int64_t)a.num_kv_heads << a.bs_log2) * P::ROWB;
-        ps.last = Lk - 1;
-        ps.lo = win > 0 ? min(max(0, koff + tok0 - win + 1), Lk - 1) : 0;
-        ps.nb = a.num_blocks;
-        ps.nt = a.kv_nt != 0;
-        if (nrel > 0) {
-            paged_load_ids<D, Q8>(ps, kb0);
-            issue_paged(0, lane);
-            if (!ps.isv && nrel > 1) {
-                paged_load_ids<D, Q8>(ps, kb0 + 1);
-                issue_paged(1, lane);
-            }
-        }
-    } else {
-        dma_lane_init<D>(dl, wave, lane, kvstride);
-        issue_tile<D>(a, dl, ring_addr, kb0, 0, seq0, Lk, kvh, wave, lane, kvstride);
-        if (wave < 2 && nrel > 1) issue_tile<D>(a, dl, ring_addr, kb0 + 1, 1, seq0, Lk, kvh, wave, lane, kvstride);
-    }
-
-    // Q^T operand: lane holds row (i0 + l32), d = 16*kk + 8*half .. +8.
-    u32x4 qreg[KSTEPS];
-    {
-        const int row = min(i0 + l32, Lq - 1);
-        const char* qp = a.q + (int64_t)(seq0 + row) * qstride + (int64_t)head * D * 2 + half * 16;
-        if constexpr (PACK) {
-            const int r = min(l32, prows - 1);
-            qp = a.q + (int64_t)(seq0 + r / G) * qstride + (int64_t)(kvh * G + r % G) * D * 2 + half * 16;
-        }
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) qreg[kk] = (*(const u32x4*)(qp + kk * 32) & a.q_and) ^ a.q_xor;
-    }
-
-    float m = kMaxInit, lsum = 0.0f;
-    f32x16 o[DBLK];
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
-
-    // V^T operand addressing (ds_read_b64_tr_b16): in each 16-lane group, lane j
-    // supplies row (key0 + j/4), dims d0 + 4*(j%4) .. +3 of the V tile; lane i
-    // of the group then receives dims d0 + i of keys key0 .. key0+3.
-    const int gl = lane & 15;
-    const int vrow = gl >> 2;                          // + key0
-    const int vdim = 16 * ((lane >> 4) & 1) + 4 * (gl & 3);   // + 32*db
-    // Per-lane LDS offsets, fixed for the whole key loop.  K operand, step kk:
-    // row l32 (+32 per key half, which keeps the swizzle key), chunk 2*kk + half,
-    // i.e. kx ^ (kk << 5).  V operand, dim block db, keys +8h: rows
-    // 4*half + vrow + 8h (+16 per key step, same key), chunk 4*db + vdim/8; the
-    // key of row r + 8 is key(r) ^ 2, so this is (vx ^ (db << 6) ^ (h << 5)) +
-    // 8h rows.  The XORs only touch the chunk field of the offset.
-    const int kx = swz<D>(l32, half);
-    const int vx = swz<D>(4 * half + vrow, vdim >> 3) + ((vdim & 7) << 1);
-    const u32 ones_bf16x2 = 0x3F803F80u;   // (1.0, 1.0) in bf16
-
-    // S^T = K Q^T for key block kb (K slot kb % 2): per 32-key half kb2, lane
-    // (l32, half) gets row l32, keys 32*kb2 + 8*(i/4) + 4*half + i%4.
-    auto scores = [&](f32x16 (&st)[2], auto slot) {
-        // (FP8 pages: the one bf16 K tile.)
-        const PGQA_LDS char* kt = ring + (Q8 ? 0 : decltype(slot)::value * P::TILEB);
-#pragma unroll
-        for (int kb2 = 0; kb2 < NH; ++kb2) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) st[kb2][i] = 0.0f;
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk)
-                st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, lds_read_16(kt + 32 * (kb2 + hoff) * P::ROWB + (kx ^ (kk << 5)))),
-                    __builtin_bit_cast(bf16x8, qreg[kk]), st[kb2], 0, 0, 0);
-        }
-    };
-
-    // One key block: softmax of the block's scores `cur`, overlapped with the
-    // next block's scores into `nxt` (when HAS_NEXT), then O^T += V^T P^T.
-    auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], int kr, auto par, auto has_next) {
-        constexpr int PAR = decltype(par)::value;   // kr % 2
-        const int j0 = (kb0 + kr) * BN;
-        // FP8 pages: scores times the keys' row scales (key offsets as in the masking below).
-        if constexpr (Q8) {
-            const PGQA_LDS float* ks = scale_lds + (kr % 3) * BN + 32 * hoff + 4 * (lane_now() >> 5);
-#pragma unroll
-            for (int g = 0; g < 4 * NH; ++g) {
-                const f32x4 k4 = *(const PGQA_LDS f32x4*)(ks + 8 * g);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) cur[g >> 2][4 * (g & 3) + t] *= k4[t];
-            }
-        }
-        // Masking (last block of the sequence, a block crossing the diagonal,
-        // or one crossing the window's lower edge): key j0 + off is kept iff
-        // llim <= off <= lim, with off = 32*kb2 + 8*(i/4) + i%4 and the lane's
-        // 4*half folded into both bounds.
-        if ((j0 + BN > Lk) || (a.causal && j0 + BN - 1 > koff + i0) || (win > 0 && j0 < koff + i0 + BQ - win)) {
-            const int ln = lane_now();
-            // The lane's row position (packed: its row's token).
-            const int lrow = koff + (PACK ? (ln & 31) / G : i0 + (ln & 31));
-            const int lim = (a.causal ? min(lrow, Lk - 1) : Lk - 1) - j0 - 4 * (ln >> 5) - 32 * hoff;
-            if (win > 0) {
-                const int llim = lrow - win + 1 - j0 - 4 * (ln >> 5) - 32 * hoff;
-#pragma unroll
-                for (int kb2 = 0; kb2 < NH; ++kb2)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int off = 32 * kb2 + 8 * (i >> 2) + (i & 3);
-                        cur[kb2][i] = (off <= lim && off >= llim) ? cur[kb2][i] : -INFINITY;
-                    }
-            } else {
-                // (No window: one comparison per score.)
-#pragma unroll
-                for (int kb2 = 0; kb2 < NH; ++kb2)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int off = 32 * kb2 + 8 * (i >> 2) + (i & 3);
-                        cur[kb2][i] = off <= lim ? cur[kb2][i] : -INFINITY;
-                    }
-            }
-        }
-        float mt = cur[0][0];
-#pragma unroll
-        for (int kb2 = 0; kb2 < NH; ++kb2)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, cur[kb2][i]);
-        mt = max_xor32(mt) * cs;
-        const bool need = mt > m + 8.0f;
-        if (__builtin_expect(__any(need), 0)) {
-            if (need) {
-                const float alpha = __builtin_amdgcn_exp2f(m - mt);
-                m = mt;
-                lsum *= alpha;
-#pragma unroll
-                for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-            }
-        }
-        // The MFMA + softmax interleave runs at raised wave priority, so of the
-        // two workgroups sharing a SIMD the one in this phase issues first and
-        // the other's P.V products fill the matrix pipe around it.
-        __builtin_amdgcn_s_setprio(3);
-        if constexpr (decltype(has_next)::value) scores(nxt, std::integral_constant<int, 1 - PAR>{});
-        // P^T operand for 16-key step kk: keys 16kk + 8*(jj/4) + 4*half + jj%4,
-        // i.e. accumulator entries 8*(kk%2) .. +7 of half kk/2.  The row sum
-        // adds the bf16-rounded weights, the same ones the PV product uses.
-        u32x4 pb[2 * NH];
-#pragma unroll
-        for (int kk = 0; kk < 2 * NH; ++kk) {
-            float p[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(cur[kk >> 1][8 * (kk & 1) + j], cs, -m));
-            if constexpr (Q8) {
-                // Weights times the values' row scales (accumulator entry 8*(kk%2) + j
-                // of half kk/2 is key 16*kk + 8*(j/4) + 4*half + j%4); the row sum
-                // takes the plain weights.
-                const PGQA_LDS float* vs = scale_lds + (3 + PAR) * BN + 16 * (kk + 2 * hoff) + 4 * (lane_now() >> 5);
-                const f32x4 v0 = *(const PGQA_LDS f32x4*)vs;
-                const f32x4 v1 = *(const PGQA_LDS f32x4*)(vs + 8);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    lsum += p[2 * j] + p[2 * j + 1];
-                    const f32x4& vv = j < 2 ? v0 : v1;
-                    pb[kk][j] = pack_bf16x2_rne_hw(p[2 * j] * vv[(2 * j) & 3], p[2 * j + 1] * vv[(2 * j + 1) & 3]);
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pb[kk][j] = pack_bf16x2_rne_hw(p[2 * j], p[2 * j + 1]);
-                    lsum = dot2_bf16(pb[kk][j], ones_bf16x2, lsum);
-                }
-            }
-        }
-        if constexpr (decltype(has_next)::value) {
-            // Interleave: per next-block MFMA one K read and a slice of the
-            // softmax arithmetic, so the VALU work hides under the matrix pipe
-            // and only a few K fragments are live at a time.
-            __builtin_amdgcn_sched_group_barrier(0x100, PGQA_KREADS_AHEAD, 0);   // K reads ahead
-#pragma unroll
-            for (int i = 0; i < NH * KSTEPS; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                if (i + PGQA_KREADS_AHEAD < NH * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // K read
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_setprio(0);
-        // O^T += V^T P^T: A = V^T for dims 32*db + l32, keys {16kk + 4*half + 0..3, +8 ..}.
-        const PGQA_LDS char* vt = ring + (Q8 ? 1 : 2 + PAR) * P::TILEB;
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-            u32x4 va[2 * NH];
-#pragma unroll
-            for (int kk = 0; kk < 2 * NH; ++kk) {
-                const PGQA_LDS char* vk = vt + 16 * (kk + 2 * hoff) * P::ROWB;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PGQA_LDS i16x4*)(vk + (vx ^ (db << 6))));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PGQA_LDS i16x4*)(vk + 8 * P::ROWB + (vx ^ (db << 6) ^ 32)));
-                va[kk] = u32x4{__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
-                               __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y};
-            }
-#pragma unroll
-            for (int kk = 0; kk < 2 * NH; ++kk)
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[kk]),
-                                                                __builtin_bit_cast(bf16x8, pb[kk]), o[db], 0, 0, 0);
-        }
-    };
-
-    // Top of block kb: every wave's DMA has landed (K(kb+1), V(kb)) and every
-    // wave is done with K(kb) and V(kb-1), so their slots are refilled with
-    // K(kb+2) and V(kb+1).
-    auto top = [&](int kr) {
-        const int tb = (PAGED ? !ps.isv : wave < 2) ? kr + 2 : kr + 1;
-        // The block ids of the tile issued below are loaded before the DMA wait
-        // and the barrier, which cover their latency; no scalar load is then in
-        // flight during the block's LDS reads (whose waits would otherwise also
-        // wait for it, scalar loads returning out of order).
-        if constexpr (PAGED)
-            if (tb < nrel) paged_load_ids<D, Q8>(ps, kb0 + tb);
-        wait_vmcnt<0>();
-        __syncthreads();
-        if (tb < nrel) {
-            if constexpr (PAGED) {
-                issue_paged(tb, lane_now());
-            } else {
-                issue_tile<D>(a, dl, ring_addr, kb0 + tb, tb & 1, seq0, Lk, kvh, wave, lane_now(), kvstride);
-            }
-        }
-        // FP8 pages: the codes of K(kr+1) and V(kr) have landed; into the bf16
-        // tiles, which every wave is done with (the codes just issued go to the
-        // other stages).
-        if constexpr (Q8) convert_q8<D>(ring, kr + 1 < nrel ? (kr + 1) & 1 : -1, kr & 1);
-    };
-    // Blocks kb0 .. kb0 + kend are computed (kend = last_kb - kb0, or -1 for a
-    // wave with no rows or no keys); each but the last overlaps the next block's
-    // scores.  The two score
-    // buffers alternate, so the loop runs two blocks per trip and every block
-    // fully rewrites the buffer it fills; the ring parity is a compile-time
-    // constant in each copy.  Waves past their last block keep the workgroup's
-    // barriers and DMA going to the end.
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    f32x16 sa[2], sb[2];
-    wait_vmcnt<0>();
-    __syncthreads();
-    if constexpr (Q8)
-        if (nrel > 0) convert_q8<D>(ring, 0, -1);
-    const int kend = active && last_kb >= 0 ? min(last_kb, kb1 - 1) - kb0 : -1;
-    if (kend >= 0) scores(sa, I0{});
-    int kb = 0;
-    for (; kb + 2 <= kend; kb += 2) {
-        top(kb);
-        step(sa, sb, kb, I0{}, std::true_type{});
-        top(kb + 1);
-        step(sb, sa, kb + 1, I1{}, std::true_type{});
-    }
-    if (kb + 1 == kend) {
-        top(kb);
-        step(sa, sb, kb, I0{}, std::true_type{});
-        top(kb + 1);
-        step(sb, sa, kb + 1, I1{}, std::false_type{});
-        kb += 2;
-    } else if (kb == kend) {
-        top(kb);
-        step(sa, sb, kb, I0{}, std::false_type{});
-        kb += 1;
-    }
-    for (; kb < nrel; ++kb) top(kb);
-
-    // Epilogue: O / l rounded to bf16, staged through the idle ring so that
-    // each output row is written whole.  The wave's 32 x D tile goes to LDS
-    // (swizzled like the K/V tiles), then each lane writes one 16-byte chunk of
-    // one row, CPR consecutive lanes per row.
-    __syncthreads();   // every wave is done with the ring
-    if constexpr (PACK) {
-        // The two key halves of the same rows: wave 1's running max, sum and
-        // output go through LDS (value-major, lane-minor: conflict-free) to wave 0,
-        // which rescales both to the larger max and adds them.
-        PGQA_LDS float* xs = (PGQA_LDS float*)(ring + 2 * BQ * P::ROWB);
-        const int ln = lane_now();
-        if (wave == 1 && active) {
-#pragma unroll
-            for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) xs[(16 * db + i) * 64 + ln] = o[db][i];
-            xs[16 * DBLK * 64 + ln] = m;
-            xs[(16 * DBLK + 1) * 64 + ln] = lsum;
-        }
-        __syncthreads();
-        if (wave != 0) return;
-        const float m1 = xs[16 * DBLK * 64 + ln];
-        const float l1 = xs[(16 * DBLK + 1) * 64 + ln];
-        const float mx = fmaxf(m, m1);
-        const float a0 = __builtin_amdgcn_exp2f(m - mx);
-        const float a1 = __builtin_amdgcn_exp2f(m1 - mx);
-        m = mx;
-        lsum = lsum * a0 + l1 * a1;
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[db][i] = o[db][i] * a0 + xs[(16 * db + i) * 64 + ln] * a1;
-    }
-    if (!active) return;
-    const int lane_e = lane_now();
-    const int half_e = lane_e >> 5;
-    const int l32_e = lane_e & 31;
-    lsum += shfl_xor_f32(lsum, 32);
-    // Output row of the lane's row l32_e: token and query head (packed: the
-    // row's token and head; else row i0 + l32_e of the wave's head).
-    auto out_row = [&](int r, int& tok, int& hq) {
-        if constexpr (PACK) {
-            tok = r / G;
-            hq = kvh * G + r % G;
-        } else {
-            tok = i0 + r;
-            hq = head;
-        }
-    };
-    const int rows_here = PACK ? prows : Lq - i0;   // valid rows of the wave's tile
-    if (split) {
-        // Partial of this key chunk: unnormalised O, running max m and sum l
-        // (both halves of the wave hold the row's m); a row with no key in the
-        // chunk leaves O = 0, l = 0.
-        if (l32_e < rows_here) {
-            int tok, hq;
-            out_row(l32_e, tok, hq);
-            const int64_t prow = ((int64_t)(seq0 + tok) * a.num_q_heads + hq) * a.nchunk + chunk;
-            float* po = a.part_o + prow * D + 4 * half_e;
-#pragma unroll
-            for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-                for (int qd = 0; qd < 4; ++qd)
-                    *(f32x4*)(po + 32 * db + 8 * qd) = f32x4{o[db][4 * qd], o[db][4 * qd + 1], o[db][4 * qd + 2],
-                                                            o[db][4 * qd + 3]};
-            if (half_e == 0) *(float2*)(a.part_ml + prow * 2) = make_float2(m, lsum);
-        }
-        return;
-    }
-    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-    PGQA_LDS char* ot = ring + wave * (BQ * P::ROWB);
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-            // dims 32*db + 8*qd + 4*half_e .. +3 of row l32_e: chunk 4*db + qd, byte 8*half_e
-            u32x2 w;
-            w.x = pack_bf16x2_rne_hw(o[db][4 * qd + 0] * inv, o[db][4 * qd + 1] * inv);
-            w.y = pack_bf16x2_rne_hw(o[db][4 * qd + 2] * inv, o[db][4 * qd + 3] * inv);
-            *(PGQA_LDS u32x2*)(ot + swz<D>(l32_e, 4 * db + qd) + 8 * half_e) = w;
-        }
-    const int c = lane_e % P::CPR;
-#pragma unroll
-    for (int t = 0; t < BQ / P::RPL; ++t) {
-        const int r = t * P::RPL + lane_e / P::CPR;
-        const u32x4 val = lds_read_16(ot + swz<D>(r, c));
-        if (r < rows_here) {
-            int tok, hq;
-            out_row(r, tok, hq);
-            *(u32x4*)(a.out + (int64_t)(seq0 + tok) * qstride + (int64_t)hq * D * 2 + c * 16) = val;
-        }
-    }
+    tile(s, kvh, grp, qtile, seq0, Lq, Lk, chunk * a.kchunk, chunk * a.kchunk + a.kchunk, split, chunk, -1);
 }
 
 // Merge of the key-chunk partials of split sequences: a query row's Hq x D
@@ -1035,6 +1164,86 @@ __global__ __launch_bounds__(256) void extend_merge_kernel(PrefillArgs a) {
     }
 }
 
+// Merge of the stream-K partials (packed rows): workgroup w merges the pair that
+// begins in share w and is cut at its end, if any (each cut pair has exactly one
+// such share).  Its pieces lie in shares w .. wl: slot 2w + 1 (or 2w when the
+// pair begins at the share's start) and slot 2v for each later share v (the
+// piece that opens share v).  Log-sum-exp over the pieces in key order with a
+// running maximum, as extend_merge_kernel does over key chunks.  Workgroup
+// (w, g) takes rows g * RPP .. of share w's pair, each thread 4 dims of one row.
+template <int D>
+constexpr int sk_merge_groups() { return BQ / (256 / (D / 4)); }
+
+template <int D>
+__global__ __launch_bounds__(256) void sk_merge_kernel(PrefillArgs a) {
+    const int w = blockIdx.x / sk_merge_groups<D>();
+    const int g = blockIdx.x % sk_merge_groups<D>();
+    const int4 cut = *(const int4*)(a.sk_cut + 4 * w);
+    const int p = __builtin_amdgcn_readfirstlane(cut.x);
+    if (p < 0) return;
+    const int u0 = __builtin_amdgcn_readfirstlane(cut.y);
+    const int u1 = __builtin_amdgcn_readfirstlane(cut.z);
+    const int total = __builtin_amdgcn_readfirstlane(cut.w);
+    const int nw = a.sk_nw;
+    const int lo = (int)((int64_t)w * total / nw);
+    const int wl = (int)(((int64_t)u1 * nw - 1) / total);   // share holding unit u1 - 1
+    const int sq = p / a.num_kv_heads;
+    const int kvh = p - sq * a.num_kv_heads;
+    const int G = a.num_q_heads / a.num_kv_heads;
+    int b0, lq;
+    if (a.fixed_qlen > 0) {
+        b0 = min(sq * a.fixed_qlen, a.total_tokens);
+        lq = min(b0 + a.fixed_qlen, a.total_tokens) - b0;
+    } else {
+        b0 = __builtin_amdgcn_readfirstlane(clampi(a.cu_seqlens[sq], 0, a.total_tokens));
+        lq = __builtin_amdgcn_readfirstlane(clampi(a.cu_seqlens[sq + 1], b0, a.total_tokens)) - b0;
+    }
+    const int rows = min(lq * G, BQ);
+    constexpr int TPR = D / 4;          // threads per row
+    constexpr int RPP = 256 / TPR;      // rows per pass
+    const int c4 = (int)threadIdx.x % TPR;
+    const int r = g * RPP + (int)threadIdx.x / TPR;
+    if (r < rows) {
+        float M = -INFINITY, L = 0.0f;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        // Four pieces per trip, their loads issued together (share w's piece
+        // comes first, so M is finite after it; a share past wl or an empty one
+        // adds nothing).
+        for (int v0 = w; v0 <= wl; v0 += 4) {
+            float2 ml[4];
+            f32x4 oc[4];
+            bool ok[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int v = v0 + j;
+                ok[j] = v <= wl && (int)((int64_t)v * total / nw) < (int)((int64_t)(v + 1) * total / nw);
+                const int slot = ok[j] ? 2 * v + ((v == w && u0 > lo) ? 1 : 0) : 2 * w;
+                const int64_t row = (int64_t)slot * BQ + r;
+                ml[j] = *(const float2*)(a.part_ml + row * 2);
+                oc[j] = *(const f32x4*)(a.part_o + row * D + 4 * c4);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (!ok[j]) continue;
+                const float mn = fmaxf(M, ml[j].x);
+                const float sa = __builtin_amdgcn_exp2f(M - mn);
+                const float sb = __builtin_amdgcn_exp2f(ml[j].x - mn);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = acc[i] * sa + oc[j][i] * sb;
+                L = L * sa + ml[j].y * sb;
+                M = mn;
+            }
+        }
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        const int tok = r / G;
+        const int hq = kvh * G + r % G;
+        u32x2 o;
+        o.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+        o.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+        *(u32x2*)(a.out + (((int64_t)(b0 + tok) * a.num_q_heads + hq) * D + 4 * c4) * 2) = o;
+    }
+}
+
 typedef void (*PrefillFn)(PrefillArgs);
 
 template <int D, bool PAGED, bool Q8>
@@ -1058,6 +1267,36 @@ PrefillFn pick_hg(int h, bool pack) {
 // one 32-row tile.
 bool use_pack(int group, int max_q_len) {
     return PGQA_EXT_PACK && max_q_len > 0 && group <= BQ && (int64_t)max_q_len * group <= BQ;
+}
+
+#ifndef PGQA_EXT_SK
+#define PGQA_EXT_SK 1
+#endif
+
+#ifndef PGQA_SK_PAIR_UNITS
+#define PGQA_SK_PAIR_UNITS 3
+#endif
+
+constexpr int kSkMaxPairs = 4096;   // every share's workgroup scans all pairs: 16 per thread at most
+
+int cu_count();
+
+// Stream-K shares of a packed-rows call: one per workgroup slot (two per CU, the
+// kernel's occupancy), but no more than the call has work units (an upper bound
+// from the host-side sizes), or 0 when the pairs are too many for the
+// per-workgroup scan.
+int sk_shares(int64_t npairs, int max_context_len, int window, int max_q_len) {
+    if (!PGQA_EXT_SK || npairs <= 0 || npairs > kSkMaxPairs) return 0;
+    int64_t blocks = ((int64_t)max_context_len + BN - 1) / BN;
+    if (window > 0) blocks = std::min<int64_t>(blocks, ((int64_t)window + max_q_len + 2 * BN - 2) / BN);
+    const int64_t units = npairs * (std::max<int64_t>(blocks, 1) + PGQA_SK_PAIR_UNITS);
+    return (int)std::min<int64_t>((int64_t)2 * cu_count(), units);
+}
+
+// Workspace of nw shares: the per-share cut records, then two partial slots of
+// 32 rows per share (output rows, then (m, l)).
+size_t sk_workspace_bytes(int nw, int head_dim) {
+    return (size_t)nw * 16 + (size_t)2 * nw * BQ * (head_dim + 2) * 4;
 }
 
 // Kernel for a head_dim and group size; hg = heads per workgroup (packed: the
@@ -1149,9 +1388,13 @@ int64_t launch_grid(PrefillArgs& a, int hg, int group, int64_t total_rows) {
 }
 
 hipError_t launch(PrefillFn fn, PrefillArgs& a, int hg, int group, int head_dim, hipStream_t stream) {
-    const int64_t wgs = launch_grid(a, hg, group, a.total_tokens);
+    const int64_t wgs = a.sk_nw > 0 ? a.sk_nw : launch_grid(a, hg, group, a.total_tokens);
     if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
-    if (log_enabled())
+    if (log_enabled() && a.sk_nw > 0)
+        log_line("extend B=%d rows=%d Hq=%d Hkv=%d d=%d%s window=%d: packed rows, %d stream-K shares, %s K/V loads",
+                 a.batch, a.total_tokens, a.num_q_heads, a.num_kv_heads, head_dim, a.k_scale ? " fp8" : "",
+                 a.window, a.sk_nw, a.kv_nt ? "non-temporal" : "cached");
+    else if (log_enabled())
         log_line("%s B=%d rows=%d Hq=%d Hkv=%d d=%d%s window=%d: %lld workgroups (%s tile lists, %d query-tile "
                  "levels, %d pairs per XCD, %d head(s) per wave group), key chunks %d x %d blocks%s, %s K/V loads",
                  a.block_table ? "extend" : "prefill", a.batch, a.total_tokens, a.num_q_heads, a.num_kv_heads,
@@ -1249,6 +1492,28 @@ hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream) {
     a.window = L.window;
     grid_dims(a, hg, group, L.max_q_len);
     a.nchunk = 1;
+    if (pack) {
+        // Packed rows: stream-K shares when the workspace holds their partials.
+        const int nw = sk_shares((int64_t)L.batch * L.num_kv_heads, L.max_context_len, L.window, L.max_q_len);
+        if (nw > 0 && L.workspace && L.workspace_bytes >= sk_workspace_bytes(nw, L.head_dim)) {
+            a.sk_nw = nw;
+            a.sk_pair_units = PGQA_SK_PAIR_UNITS;
+            a.kchunk = kNoSplit;
+            a.kv_nt = 1;   // each K/V byte goes to one workgroup
+            a.sk_cut = (int32_t*)L.workspace;
+            a.part_o = (float*)((char*)L.workspace + (size_t)nw * 16);
+            a.part_ml = a.part_o + (int64_t)2 * nw * BQ * L.head_dim;
+            hipError_t err = launch(fn, a, hg, group, L.head_dim, stream);
+            if (err != hipSuccess) return err;
+            if (L.head_dim == 128)
+                hipLaunchKernelGGL(sk_merge_kernel<128>, dim3((unsigned)nw * sk_merge_groups<128>()), dim3(256), 0,
+                                   stream, a);
+            else
+                hipLaunchKernelGGL(sk_merge_kernel<64>, dim3((unsigned)nw * sk_merge_groups<64>()), dim3(256), 0,
+                                   stream, a);
+            return hipGetLastError();
+        }
+    }
     const int64_t per_chunk = (int64_t)L.total_q * L.num_q_heads * (L.head_dim + 2) * 4;
     const int64_t max_chunks = (L.workspace && per_chunk > 0) ? (int64_t)(L.workspace_bytes / per_chunk) : 0;
     a.kchunk = kNoSplit;
@@ -1305,7 +1570,10 @@ size_t extend_workspace_bytes(int32_t batch, int32_t total_q, int32_t max_q_len,
     grid_dims(a, hg, group, max_q_len);
     int nc = 1, kc = kNoSplit;
     extend_split(grid_size(a, hg, group), max_context_len, 1 << 20, &nc, &kc);
-    return nc > 1 ? (size_t)total_q * num_q_heads * nc * (head_dim + 2) * 4 : 0;
+    const size_t chunks = nc > 1 ? (size_t)total_q * num_q_heads * nc * (head_dim + 2) * 4 : 0;
+    // (The window is not an argument here: the bound without one covers it.)
+    const int nw = pack ? sk_shares((int64_t)batch * num_kv_heads, max_context_len, 0, max_q_len) : 0;
+    return std::max(chunks, nw > 0 ? sk_workspace_bytes(nw, head_dim) : (size_t)0);
 }
 
 }  // namespace pgqa

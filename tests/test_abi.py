@@ -271,15 +271,21 @@ def test_fp8_extend_validation(lib):
 
 
 def test_extend_workspace_size(lib):
-    # 8 sequences x 8 KV heads of 4 query tokens: far fewer pieces than the GPU has slots,
-    # so the long contexts are split
-    n = lib.gqa_paged_extend_workspace_size(8, 32, 4, 64, 8, 128, 32768)
-    assert n > 0 and n % (32 * 64 * 130 * 4) == 0
-    # 64 x 8 pieces fill the slots once: no split
-    assert lib.gqa_paged_extend_workspace_size(64, 256, 4, 32, 8, 128, 4096) == 0
+    def shares(nw, d):   # per share: its cut record, two partial slots of 32 rows (output, then m and l)
+        return nw * 16 + 2 * nw * 32 * (d + 2) * 4
+    # Packed rows (q_len x group <= 32): room for the stream-K partials of one share per
+    # workgroup slot (two per CU; without a GPU the library assumes 256 CUs), whatever
+    # the context lengths ...
+    assert lib.gqa_paged_extend_workspace_size(8, 32, 4, 64, 8, 128, 32768) == shares(512, 128)
+    assert lib.gqa_paged_extend_workspace_size(64, 256, 4, 32, 8, 128, 200) == shares(512, 128)
+    # ... but no more shares than the call has work units: 2 pairs x (1 block + 3)
+    assert lib.gqa_paged_extend_workspace_size(2, 2, 1, 8, 1, 64, 10) == shares(8, 64)
+    # 8 sequences x 8 KV heads of 40 query tokens (not packed): far fewer pieces than the
+    # GPU has slots, so the long contexts are split into key chunks
+    n = lib.gqa_paged_extend_workspace_size(8, 320, 40, 64, 8, 128, 32768)
+    assert n > 0 and n % (320 * 64 * 130 * 4) == 0
     # 16 sequences x 512 query tokens fill the GPU without a split
     assert lib.gqa_paged_extend_workspace_size(16, 8192, 512, 32, 8, 128, 3584) == 0
-    assert lib.gqa_paged_extend_workspace_size(64, 256, 4, 32, 8, 128, 200) == 0   # short contexts
     assert lib.gqa_paged_extend_workspace_size(2, 8, 4, 30, 8, 128, 4096) == 0     # Hq % Hkv != 0
 
 
