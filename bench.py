@@ -64,12 +64,13 @@ TRAFFIC_PARTS = {
                  _DECODE_SRC),
     "window": ("long_ctx_decode, window 4096",
                ["decode_split_kernel<2,128,8,1,2>", "decode_merge_kernel<2,128,8>"], _DECODE_SRC),
-    "mqa": ("mqa_decode", ["prefill_kernel<128,1,true,false,true>", "extend_merge_kernel<128>"],
+    "mqa": ("mqa_decode", ["prefill_kernel<128,1,true,false,true>", "sk_merge_kernel<128>"],
             _DECODE_SRC + _PREFILL_SRC[:1]),
     "prefill": ("varlen_prefill", ["prefill_kernel<128,4,false,false,false>"], _PREFILL_SRC),
     "chunked_prefill": ("chunked_prefill", ["prefill_kernel<128,4,true,false,false>"], _PREFILL_SRC),
-    "spec_verify": ("spec_verify", ["prefill_kernel<128,1,true,false,true>"], _PREFILL_SRC),
-    "fp8_spec": ("spec_verify over FP8 pages", ["prefill_kernel<128,1,true,true,true>"], _PREFILL_SRC),
+    "spec_verify": ("spec_verify", ["prefill_kernel<128,1,true,false,true>", "sk_merge_kernel<128>"], _PREFILL_SRC),
+    "fp8_spec": ("spec_verify over FP8 pages", ["prefill_kernel<128,1,true,true,true>", "sk_merge_kernel<128>"],
+                 _PREFILL_SRC),
     "fp8": ("llama3_8b_decode over FP8 pages", ["decode_split_kernel<2,128,4,1,1>", "decode_merge_kernel<2,128,4>"],
             _DECODE_SRC),
     "shared": ("shared_prefix_decode", ["decode_split_kernel<2,128,4,1,2>", "decode_merge_kernel<2,128,4>"],
@@ -387,8 +388,9 @@ def mqa_leg(args, torch, pg, W, T, traffic=None):
     """MQA decode (B = 256, lognormal contexts, 32 query heads on one KV head,
     bs 32).  With one KV head and a group of 32 the library routes the call to
     the matrix-core multi-token kernel (the query heads form the packed rows of
-    one 32-row MFMA tile, two waves sharing every key block, contexts cut into
-    key chunks merged afterwards); the VALU
+    one 32-row MFMA tile, two waves sharing every key block, the batch's key
+    blocks cut into one equal stream-K share per workgroup slot, cut sequences
+    merged afterwards); the VALU
     split kernel on the same pools (forced by an explicit 1,024-share split) is
     timed beside it.  Calls rotate over four pool copies.  Bytes = the K/V read."""
     case = W.make_workload("mqa_decode")
