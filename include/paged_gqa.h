@@ -285,13 +285,20 @@ int gqa_paged_extend(const void* q, const int32_t* cu_q, const void* k_cache, co
 
 /*
  * Bytes of device workspace gqa_paged_extend can use for these sizes (0 when it
- * would not split): when the call has too few (query tile, sequence, KV head)
- * pieces to balance the GPU (short queries, e.g. a few draft tokens per
- * sequence), the library cuts long key ranges into chunks handled by separate
- * workgroups, which write fp32 partials (running max, sum and unnormalised
- * output per row and query head) that a second kernel merges exactly (log-sum-
- * exp, in chunk order; deterministic).  A smaller (or NULL) workspace only
- * means fewer (or no) chunks.  Returns 0 for invalid sizes.
+ * would not split).  Two ways of splitting write fp32 partials (running max, sum
+ * and unnormalised output per row and query head) that a second kernel merges
+ * exactly (log-sum-exp in key order; deterministic):
+ *   - key chunks: when the call has too few (query tile, sequence, KV head)
+ *     pieces to balance the GPU, long key ranges are cut into chunks handled by
+ *     separate workgroups;
+ *   - stream-K shares: when every sequence's query tokens times the group fit
+ *     one 32-row tile (q_len * Hq / Hkv <= 32, e.g. a few draft tokens) and the
+ *     call has at most 4,096 (sequence, KV head) pairs, all pairs' key blocks
+ *     are cut into one equal share per workgroup slot of the GPU (about 17 MB
+ *     at head_dim 128 on 256 CUs, whatever the lengths).
+ * A smaller (or NULL) workspace only means fewer chunks, key chunks instead of
+ * shares, or no split.  The size depends on the GPU's CU count (the current
+ * device's).  Returns 0 for invalid sizes.
  */
 size_t gqa_paged_extend_workspace_size(int32_t batch, int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
                                        int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len);
