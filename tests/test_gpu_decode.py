@@ -146,10 +146,10 @@ def test_workspace_reuse(orc):
 @pytest.mark.parametrize("hq,d,bs", [(32, 128, 16), (32, 64, 8), (64, 128, 4), (32, 128, 256)])
 def test_one_kv_head_matrix_core_route(orc, hq, d, bs):
     """One KV head and Hq a multiple of 32 run on the matrix cores (query heads as
-    tile rows, keys in chunks of 1280 = 20 blocks of 64): empty, one-token, page- and
-    chunk-edge and long contexts against the oracle, sharpened queries too,
-    deterministic, and within tolerance of the split-KV kernel (an explicit split
-    count keeps that path)."""
+    tile rows; G = 32: the batch's key blocks in equal stream-K shares, G = 64: key
+    chunks of 20 blocks of 64): empty, one-token, page- and chunk-edge and long
+    contexts against the oracle, sharpened queries too, deterministic, and within
+    tolerance of the split-KV kernel (an explicit split count keeps that path)."""
     lens = [0, 1, bs - 1, bs, bs + 1, 1023, 1024, 1025, 1279, 1280, 1281, 2561, 3000, 5000]
     case = W.make_decode_case(lens, hq, 1, d, bs, W.BF16, seed=hq * 7 + d + bs)
     say(f"decode one KV head hq={hq} d{d} bs{bs}")
@@ -168,3 +168,21 @@ def test_one_kv_head_matrix_core_route(orc, hq, d, bs):
     case.q = q4
     sharp = to_f64(DevDecode(case).decode())
     assert_close(sharp, oracle_decode(orc, case), W.BF16, "sharpened")
+
+
+def test_one_kv_head_many_sequences(orc, monkeypatch, capfd):
+    """More sequences than the stream-K scan takes (4,096 pairs): the one-KV-head
+    route falls back to key chunks, still against the oracle."""
+    rng = np.random.default_rng(1480)
+    lens = rng.integers(0, 120, 4100)
+    case = W.make_decode_case(lens, 32, 1, 128, 16, W.BF16, seed=1481)
+    say("decode one KV head, 4100 sequences")
+    dev = DevDecode(case)
+    capfd.readouterr()
+    monkeypatch.setenv("PGQA_LOG", "1")
+    out = dev.decode()
+    torch.cuda.synchronize()
+    monkeypatch.setenv("PGQA_LOG", "0")
+    err = capfd.readouterr().err
+    assert "stream-K" not in err and "extend B=4100" in err, err
+    assert_close(to_f64(out), oracle_decode(orc, case), W.BF16, "4100 sequences")
