@@ -33,9 +33,11 @@
 //  * Scores: v_dot2_f32_bf16 partial dot products, then a reduce-scatter
 //    butterfly of DPP exchanges over the LPT lanes of the row: each exchange
 //    both adds and halves the heads a lane keeps, so a lane ends with the full
-//    score of one head (11 DPP steps instead of 16 for 4 heads, and one exp per
-//    lane instead of 4).  The weights are then broadcast back across the row
-//    (DPP row_newbcast) for the P.V accumulation in fp32.
+//    score of one head (5 DPP adds instead of 16 for 4 heads, and one exp per
+//    lane instead of 4).  Each lane holds its query heads in a lane-dependent
+//    register order, so every exchange is a plain add (no per-lane select).
+//    The weights are then broadcast back across the row (DPP row_newbcast)
+//    for the P.V accumulation in fp32.
 //  * Online softmax in log2 units with the scale folded into the exponent,
 //    p = exp2(s * scale*log2e - m) (a negative or zero scale is applied as the
 //    sign of the query bits, so the folded factor is always positive), each
@@ -48,11 +50,14 @@
 //    outside [lo, ctx) become -inf and those V rows are zeroed, so NaN in
 //    unused slots (or in pages dropped before the window) cannot leak.
 //  * Low-precision pages (FP8 E4M3 codes, one fp32 scale per token and KV head
-//    row): the same kernel with KES = 1.  A tile moves the same 16 KB of codes
-//    (twice the tokens), plus the tile's row scales by 4-byte-per-lane DMA;
-//    each lane converts its 8 codes of a row to bf16 right after the LDS read
-//    (one instruction per pair, exact), so the scores and P.V are the bf16
-//    path's; the K scale multiplies a token's score and the V scale its weight.
+//    row): the same kernel with KES = 1.  A tile moves the 8 KB of a bf16
+//    tile's K and V as codes (twice the tokens), plus the tile's row scales by
+//    4-byte-per-lane DMA.  A lane converts its 8 K codes of a row to bf16 right
+//    before the dot products (one instruction per pair, exact); for P.V it
+//    interleaves the bytes of two token rows first, so each conversion yields
+//    the two rows' values of one dim, the pair v_dot2 takes.  Scores and P.V are
+//    the bf16 path's; the K scale multiplies a token's score and the V scale
+//    its weight.
 //  * Large groups (G >= 16) use G/8 waves per workgroup sharing one ring; each
 //    wave owns 8 query heads.
 #include "device_common.hpp"
@@ -153,41 +158,45 @@ constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
 
 // Reduce-scatter of GW per-lane partial dot products over the LPT lanes of a
 // token row.  Split step s (partner distance LPT >> (s+1)) halves the values a
-// lane keeps: the lane with that distance bit set keeps the upper half of its
-// heads.  After NSPLIT steps each lane holds VPL full sums, for heads
-// head_off(lane) .. +VPL; the remaining steps only add.
+// lane keeps; after NSPLIT steps each lane holds VPL full sums, for heads
+// head_off(lane) .. +VPL, and the remaining steps only add.  So that every step
+// is one add with no per-lane select, register slot j of a lane holds head
+// j ^ head_off(lane) (the query slices are loaded in that order): each step then
+// keeps the lower half of the live slots and sends the upper half, and the
+// partner's upper half holds the same heads as this lane's lower half.  Bit s
+// of head_off (value GW >> (s+1)) is the lane's distance bit of step s; the
+// distance-4 exchange (row_half_mirror) pairs lane l with l ^ 7, so when it
+// splits, the bits of the later split steps are taken relative to bit 2, which
+// that partner flips with them.
 template <int LPT, int GW>
 struct Scatter {
     static constexpr int NSPLIT = ilog2c(GW) < ilog2c(LPT) ? ilog2c(GW) : ilog2c(LPT);
     static constexpr int VPL = GW >> NSPLIT;
+    static constexpr bool MIRROR = LPT >= 8 && ilog2c(LPT) - 3 < NSPLIT;   // the distance-4 step splits
 
     __device__ static int head_off(int lane) {
         int off = 0;
 #pragma unroll
-        for (int s = 0; s < NSPLIT; ++s)
-            if (lane & (LPT >> (s + 1))) off += GW >> (s + 1);
+        for (int s = 0; s < NSPLIT; ++s) {
+            const int d = LPT >> (s + 1);
+            int bit = (lane & d) != 0;
+            if (MIRROR && d < 4) bit ^= (lane >> 2) & 1;
+            if (bit) off += GW >> (s + 1);
+        }
         return off;
     }
     // Lane (within the token group) that holds head g, and which of its values.
     static constexpr int owner(int g) {
-        int lane = 0, rem = g;
+        int lane = 0;
         for (int s = 0; s < NSPLIT; ++s) {
-            const int half = GW >> (s + 1);
-            if (rem >= half) {
-                lane |= LPT >> (s + 1);
-                rem -= half;
-            }
+            const int d = LPT >> (s + 1);
+            int bit = (g & (GW >> (s + 1))) != 0;
+            if (MIRROR && d < 4) bit ^= (lane >> 2) & 1;
+            if (bit) lane |= d;
         }
         return lane;
     }
-    static constexpr int slot(int g) {
-        int rem = g;
-        for (int s = 0; s < NSPLIT; ++s) {
-            const int half = GW >> (s + 1);
-            if (rem >= half) rem -= half;
-        }
-        return rem;
-    }
+    static constexpr int slot(int g) { return g & (VPL - 1); }
 };
 
 // Exchange with a partner at distance DLT inside an aligned group of 2*DLT lanes
@@ -202,21 +211,17 @@ __device__ __forceinline__ float xchg(float x) {
     else return dpp_f32<0xB1>(x);                              // quad_perm [1,0,3,2]
 }
 
+// v holds the GW values in the lane's head order (slot j = head j ^ head_off).
 template <int DLT, int N>
-__device__ __forceinline__ void scatter_steps(float* v, int lane) {
+__device__ __forceinline__ void scatter_steps(float* v) {
     if constexpr (DLT >= 1) {
         if constexpr (N > 1) {
-            const bool hi = (lane & DLT) != 0;
 #pragma unroll
-            for (int k = 0; k < N / 2; ++k) {
-                const float keep = hi ? v[N / 2 + k] : v[k];
-                const float send = hi ? v[k] : v[N / 2 + k];
-                v[k] = keep + xchg<DLT>(send);
-            }
-            scatter_steps<DLT / 2, N / 2>(v, lane);
+            for (int k = 0; k < N / 2; ++k) v[k] += xchg<DLT>(v[N / 2 + k]);
+            scatter_steps<DLT / 2, N / 2>(v);
         } else {
             v[0] += xchg<DLT>(v[0]);
-            scatter_steps<DLT / 2, 1>(v, lane);
+            scatter_steps<DLT / 2, 1>(v);
         }
     }
 }
@@ -224,14 +229,16 @@ __device__ __forceinline__ void scatter_steps(float* v, int lane) {
 // Value of lane OWNER of this lane's token group, broadcast to the whole group.
 template <int LPT, int OWNER>
 __device__ __forceinline__ float group_bcast(float x, int lane) {
+    // Every lane reads a valid source lane, so the DPP move needs no old value
+    // (update_dpp with a zero old value costs a v_mov of zero per broadcast).
     if constexpr (LPT == 16) {
-        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + OWNER, 0xF, 0xF, false));
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + OWNER, 0xF, 0xF, false));
     } else if constexpr (LPT == 4) {
         constexpr int ctrl = OWNER | (OWNER << 2) | (OWNER << 4) | (OWNER << 6);
-        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, false));
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, false));
     } else if constexpr (LPT == 2) {
         constexpr int ctrl = OWNER | (OWNER << 2) | ((2 + OWNER) << 4) | ((2 + OWNER) << 6);
-        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, false));
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, false));
     } else {
         const int src = (lane & ~(LPT - 1)) | OWNER;
         return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
@@ -250,11 +257,21 @@ __device__ __forceinline__ int tiles_of(int ctx, int cap, int tt, int window) {
     return ctx > 0 ? (ctx + tt - 1) / tt - window_lo(ctx, window) / tt : 0;
 }
 
+// a.b over one bf16 pair with no accumulator.  Written as the three-operand
+// v_dot2_f32_bf16 with an inline zero: the builtin with a 0.0f accumulator is
+// emitted as a v_mov of zero plus the tied-accumulator v_dot2c form, one extra
+// VALU instruction per dot product.  Plain register arithmetic, no memory access.
+__device__ __forceinline__ float dot2_bf16_first(u32 a, u32 b) {
+    float r;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // q . k for one lane's 16-byte slices (fp32 accumulation).
 template <int ES>
 __device__ __forceinline__ float slice_dot(const u32x4& q, const u32x4& k) {
     if constexpr (ES == 2) {
-        float acc = dot2_bf16(q.x, k.x, 0.0f);
+        float acc = dot2_bf16_first(q.x, k.x);
         acc = dot2_bf16(q.y, k.y, acc);
         acc = dot2_bf16(q.z, k.z, acc);
         return dot2_bf16(q.w, k.w, acc);
@@ -464,22 +481,33 @@ __device__ __forceinline__ void tile_compute(const PGQA_LDS char* tb, const u32x
     const PGQA_LDS float* ksc = (const PGQA_LDS float*)(tb + 2 * Gm::KVB) + (lane / Gm::LPT) * RPT;
     const PGQA_LDS float* vsc = ksc + Gm::TT;
 
-    u32x4 kxs[PF ? RPT : 1], vxs[PF ? RPT : 1];
+    // FP8 pages prefetch the raw codes (8 bytes a row): K rows are converted
+    // right before their dot products, V rows pairwise inside P.V.
+    u32x4 kxs[PF && !Q8 ? RPT : 1], vxs[PF && !Q8 ? RPT : 1];
+    u32x2 kcs[PF && Q8 ? RPT : 1], vcs[PF && Q8 ? RPT : 1];
     if constexpr (PF) {
 #pragma unroll
-        for (int r = 0; r < RPT; ++r) kxs[r] = kv_slice<ES, D, KES>(kb, r);
+        for (int r = 0; r < RPT; ++r) {
+            if constexpr (Q8) kcs[r] = lds_read_8(kb + r * Gm::CROWB);
+            else kxs[r] = kv_slice<ES, D, KES>(kb, r);
+        }
 #pragma unroll
-        for (int r = 0; r < RPT; ++r) vxs[r] = kv_slice<ES, D, KES>(vb, r);
+        for (int r = 0; r < RPT; ++r) {
+            if constexpr (Q8) vcs[r] = lds_read_8(vb + r * Gm::CROWB);
+            else vxs[r] = kv_slice<ES, D, KES>(vb, r);
+        }
         __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the arithmetic
     }
     float s[RPT][VPL];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-        const u32x4 kx = PF ? kxs[PF ? r : 0] : kv_slice<ES, D, KES>(kb, r);
+        u32x4 kx;
+        if constexpr (PF && Q8) kx = fp8x8_to_bf16(kcs[r]);
+        else kx = PF ? kxs[PF ? r : 0] : kv_slice<ES, D, KES>(kb, r);
         float v[GW];
 #pragma unroll
         for (int g = 0; g < GW; ++g) v[g] = slice_dot<ES>(qv[g], kx);
-        scatter_steps<Gm::LPT / 2, GW>(v, lane);
+        scatter_steps<Gm::LPT / 2, GW>(v);
         const bool valid = FULL || (tok0 + r * TPR < ctx && tok0 + r * TPR >= lo);
         if constexpr (Q8) {
             const float ks = ksc[r];
@@ -548,19 +576,42 @@ __device__ __forceinline__ void tile_compute(const PGQA_LDS char* tb, const u32x
             }
             u32 pg[GW];
             bcast_heads_u32<Gm::LPT, GW>(pk, pg, lane);
-            u32x4 v0 = PF ? vxs[PF ? r : 0] : kv_slice<ES, D, KES>(vb, r);
-            u32x4 v1 = PF ? vxs[PF ? r + 1 : 0] : kv_slice<ES, D, KES>(vb, r + 1);
-            if (!FULL) {
-                if (!ok0) v0 = u32x4{0, 0, 0, 0};
-                if (!ok1) v1 = u32x4{0, 0, 0, 0};
-            }
-            const u32 w0[4] = {v0.x, v0.y, v0.z, v0.w};
-            const u32 w1[4] = {v1.x, v1.y, v1.z, v1.w};
             u32 vp[EPL];
+            if constexpr (Q8) {
+                // Codes of rows r and r+1 (8 dims each): interleave the bytes of
+                // the two rows, then each conversion of a byte pair yields the
+                // (row r, row r+1) bf16 pair of one dim.  A zero code is +0.
+                u32x2 c0 = PF ? vcs[PF ? r : 0] : lds_read_8(vb + r * Gm::CROWB);
+                u32x2 c1 = PF ? vcs[PF ? r + 1 : 0] : lds_read_8(vb + (r + 1) * Gm::CROWB);
+                if (!FULL) {
+                    if (!ok0) c0 = u32x2{0, 0};
+                    if (!ok1) c1 = u32x2{0, 0};
+                }
+                const u32 a[2] = {c0.x, c0.y};
+                const u32 b[2] = {c1.x, c1.y};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                vp[2 * i] = __builtin_amdgcn_perm(w1[i], w0[i], 0x05040100u);      // (row r, row r+1) of dim 2i
-                vp[2 * i + 1] = __builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u);  // ... of dim 2i+1
+                for (int i = 0; i < 2; ++i) {
+                    const u32 lo = __builtin_amdgcn_perm(b[i], a[i], 0x05010400u);   // dims 4i, 4i+1
+                    const u32 hi = __builtin_amdgcn_perm(b[i], a[i], 0x07030602u);   // dims 4i+2, 4i+3
+                    vp[4 * i] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+                    vp[4 * i + 1] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+                    vp[4 * i + 2] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+                    vp[4 * i + 3] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+                }
+            } else {
+                u32x4 v0 = PF ? vxs[PF ? r : 0] : kv_slice<ES, D, KES>(vb, r);
+                u32x4 v1 = PF ? vxs[PF ? r + 1 : 0] : kv_slice<ES, D, KES>(vb, r + 1);
+                if (!FULL) {
+                    if (!ok0) v0 = u32x4{0, 0, 0, 0};
+                    if (!ok1) v1 = u32x4{0, 0, 0, 0};
+                }
+                const u32 w0[4] = {v0.x, v0.y, v0.z, v0.w};
+                const u32 w1[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    vp[2 * i] = __builtin_amdgcn_perm(w1[i], w0[i], 0x05040100u);      // (row r, row r+1) of dim 2i
+                    vp[2 * i + 1] = __builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u);  // ... of dim 2i+1
+                }
             }
 #pragma unroll
             for (int g = 0; g < GW; ++g)
@@ -691,12 +742,14 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
         win.num_blocks = a.num_blocks;
         if (Gm::TPRD <= (1 << a.bs_log2)) win.load((tf * TT) >> a.bs_log2, lane);
 
-        // This wave's query slices: GW heads x 16 bytes.
+        // This wave's query slices: GW heads x 16 bytes, slot g holding head
+        // g ^ head_off (the reduce-scatter's order).
         u32x4 qv[GW];
+        const int hoff = S::head_off(lane);
 #pragma unroll
         for (int g = 0; g < GW; ++g)
-            qv[g] = (*(const u32x4*)(a.q + ((int64_t)(b * a.num_q_heads + qh0 + g) * D + c * EPL) * ES) & a.q_and) ^
-                    a.q_xor;
+            qv[g] = (*(const u32x4*)(a.q + ((int64_t)(b * a.num_q_heads + qh0 + (g ^ hoff)) * D + c * EPL) * ES) &
+                     a.q_and) ^ a.q_xor;
 
         // Running max / sum of the heads this lane owns; o for all GW heads.
         float m[VPL], l[VPL], o[GW][EPL];
