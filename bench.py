@@ -11,6 +11,11 @@ kernels launched one by one (``--graph`` replays each step as a captured HIP
 graph instead).  ``roofline`` times the decode call alone (split + merge) with
 HIP events on its stream, in a second pass.
 
+Before any timing (the headline's W warm-up steps included) each item first runs
+untimed calls for at least ``--settle-ms`` milliseconds (default 100): after the
+CPU-side set-up of an item the GPU has idled and needs tens of milliseconds of
+sustained work to reach its working clocks.  The timed regions are unchanged.
+
 Inputs stay resident in HBM.  Every decode-type item rotates over several copies
 of its page pools (4 for the decode batches, 4 for the long-context pools), so
 the 256 MB Infinity Cache cannot serve a call from the previous one.
@@ -83,6 +88,8 @@ def _args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed calls of each item before its warm-up and timing, so the GPU is at its working clocks")
     ap.add_argument("--only", default="", help=f"comma list of items to run ({', '.join(LEGS)}); default: all")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     for leg in LEGS[1:]:
@@ -204,11 +211,31 @@ def _events(torch, n):
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
 
+SETTLE_MS = 100.0   # untimed work before each item's timing (see _settle)
+
+
+def _settle(torch, f, ms=None, min_calls=0):
+    """Untimed calls f(0), f(1), ... until at least `ms` milliseconds of wall time have
+    passed and at least min_calls were made.  After the CPU-side set-up of an item the
+    GPU has idled and runs below its working clocks for tens of milliseconds of
+    sustained work (varlen prefill measured 175 -> 148 us per call over the first
+    ~40 ms), so every timing starts after this phase; nothing inside a timed region
+    changes.  Returns the number of calls made."""
+    ms = SETTLE_MS if ms is None else ms
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while i < min_calls or (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            f(i)
+            i += 1
+        torch.cuda.synchronize()
+    return i
+
+
 def _timed_calls(torch, f, n, warm=5):
     """Mean / median / p10 / p90 microseconds of f(i) over n calls, HIP events on the current stream."""
-    for i in range(warm):
-        f(i)
-    torch.cuda.synchronize()
+    _settle(torch, f, min_calls=warm)
     evs = _events(torch, n)
     for i in range(n):
         evs[i][0].record()
@@ -275,6 +302,8 @@ def decode_leg(args, torch, pg, W, T):
         if ev is not None:
             ev[1].record()
 
+    # Clock settle (untimed, not counted as warm-up steps), then the W warm-up steps.
+    _settle(torch, step)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -437,9 +466,7 @@ def prefill_leg(args, torch, pg, W, T, traffic=None):
         if ev is not None:
             ev[1].record()
 
-    for _ in range(max(3, args.warmup // 4)):
-        step()
-    torch.cuda.synchronize()
+    _settle(torch, lambda i: step(), min_calls=max(3, args.warmup // 4))
     n = max(10, args.steps // 4)
     evs = _events(torch, n)
     t0 = time.perf_counter()
@@ -506,9 +533,7 @@ def extend_leg(key, args, torch, pg, W, T, traffic=None, fp8=False):
         if ev is not None:
             ev[1].record()
 
-    for i in range(max(4, args.warmup // 4)):
-        step(i)
-    torch.cuda.synchronize()
+    _settle(torch, step, min_calls=max(4, args.warmup // 4))
     n = max(10, args.steps // 4)
     evs = _events(torch, n)
     t0 = time.perf_counter()
@@ -565,9 +590,7 @@ def fp8_leg(args, torch, pg, W, T, traffic=None):
         if ev is not None:
             ev[1].record()
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    _settle(torch, step, min_calls=args.warmup)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
@@ -637,9 +660,7 @@ def shared_prefix_leg(args, torch, pg, W, T, traffic=None):
             pg.gqa_paged_decode(q, kc_, vc_, table_, ctx, maxctx, scale=scale, out=out, workspace=ws)
             if ev is not None:
                 ev[1].record()
-        for i in range(max(5, args.warmup // 2)):
-            step(i)
-        torch.cuda.synchronize()
+        _settle(torch, step, min_calls=max(5, args.warmup // 2))
         evs = _events(torch, n)
         t0 = time.perf_counter()
         for i in range(n):
@@ -739,7 +760,9 @@ def cpu_baseline(args, W, gpu):
 
 
 def main(argv=None):
+    global SETTLE_MS
     args = _args(argv)
+    SETTLE_MS = max(0.0, args.settle_ms)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -774,7 +797,8 @@ def main(argv=None):
     traffic = recorded_traffic(os.path.join(here, "profiles", "traffic_counters.json"))
     line = {"metric": "decode KV-read GB/s (Llama-3-8B-shaped GQA decode, B=64)", "value": None, "unit": "GB/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), bf16-rounded)"}
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), bf16-rounded)",
+            "settle_ms": args.settle_ms}
     outs, gpu_us = {}, {}
     if "decode" in legs:
         dec = decode_leg(args, torch, pg, W, T)
