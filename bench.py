@@ -69,12 +69,13 @@ TRAFFIC_PARTS = {
                  _DECODE_SRC),
     "window": ("long_ctx_decode, window 4096",
                ["decode_split_kernel<2,128,8,1,2>", "decode_merge_kernel<2,128,8>"], _DECODE_SRC),
-    "mqa": ("mqa_decode", ["prefill_kernel<128,1,true,false,true>", "sk_merge_kernel<128>"],
+    "mqa": ("mqa_decode", ["prefill_kernel<128,1,true,false,true,true>", "sk_merge_kernel<128>"],
             _DECODE_SRC + _PREFILL_SRC[:1]),
-    "prefill": ("varlen_prefill", ["prefill_kernel<128,4,false,false,false>"], _PREFILL_SRC),
-    "chunked_prefill": ("chunked_prefill", ["prefill_kernel<128,4,true,false,false>"], _PREFILL_SRC),
-    "spec_verify": ("spec_verify", ["prefill_kernel<128,1,true,false,true>", "sk_merge_kernel<128>"], _PREFILL_SRC),
-    "fp8_spec": ("spec_verify over FP8 pages", ["prefill_kernel<128,1,true,true,true>", "sk_merge_kernel<128>"],
+    "prefill": ("varlen_prefill", ["prefill_kernel<128,4,false,false,false,false>"], _PREFILL_SRC),
+    "chunked_prefill": ("chunked_prefill", ["prefill_kernel<128,4,true,false,false,false>"], _PREFILL_SRC),
+    "spec_verify": ("spec_verify", ["prefill_kernel<128,1,true,false,true,false>", "sk_merge_kernel<128>"],
+                    _PREFILL_SRC),
+    "fp8_spec": ("spec_verify over FP8 pages", ["prefill_kernel<128,1,true,true,true,false>", "sk_merge_kernel<128>"],
                  _PREFILL_SRC),
     "fp8": ("llama3_8b_decode over FP8 pages", ["decode_split_kernel<2,128,4,1,1>", "decode_merge_kernel<2,128,4>"],
             _DECODE_SRC),

@@ -430,10 +430,11 @@ __device__ __forceinline__ void convert_q8(PGQA_LDS char* ring, int kpar, int vp
 // fill one 32-row MFMA tile instead of G mostly empty ones.  Waves 0 and 1 then
 // share every key block, each taking one 32-key half with its own running max,
 // sum and output, merged through LDS at the end; waves 2 and 3 only fetch V.
-template <int D, int HG, bool PAGED, bool Q8 = false, bool PACK = false>
+template <int D, int HG, bool PAGED, bool Q8 = false, bool PACK = false, bool P16 = false>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     static_assert(PAGED || !Q8, "FP8 K/V only from pages");
     static_assert(!PACK || (PAGED && HG == 1), "packed rows: paged, one workgroup per KV head");
+    static_assert(!P16 || (PACK && !Q8), "16-row waves: packed rows over bf16 pages");
     using P = PGeo<D>;
     constexpr int NH = PACK ? 1 : 2;          // 32-key halves of a block each wave computes
     constexpr int TB = 4 / HG;               // 32-row token blocks per workgroup
@@ -464,7 +465,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         const int tok0 = qtile * TB * BQ;
         const int head = kvh * G + grp * HG + (wave % HG);
         // This wave's first query row (sequence-local); packed: token 0 for waves 0, 1.
-        const int i0 = PACK ? (wave < 2 ? 0 : 1 << 30) : tok0 + (wave / HG) * BQ;
+        const int i0 = PACK ? (P16 || wave < 2 ? 0 : 1 << 30) : tok0 + (wave / HG) * BQ;
         const int hoff = PACK ? (wave & 1) : 0;          // packed: the wave's key half
         const int prows = PACK ? Lq * G : 0;             // packed rows (<= 32)
 
@@ -534,7 +535,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
         // Q^T operand: lane holds row (i0 + l32), d = 16*kk + 8*half .. +8.
         u32x4 qreg[KSTEPS];
-        {
+        if constexpr (!P16) {
             const int row = min(i0 + l32, Lq - 1);
             const char* qp = a.q + (int64_t)(seq0 + row) * qstride + (int64_t)head * D * 2 + half * 16;
             if constexpr (PACK) {
@@ -741,6 +742,200 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
             // other stages).
             if constexpr (Q8) convert_q8<D>(ring, kr + 1 < nrel ? (kr + 1) & 1 : -1, kr & 1);
         };
+        if constexpr (P16) {
+            // 16-row waves (packed rows, more than 16 of them): wave (rh, hoff)
+            // takes rows 16 rh .. +15 of the packed tile and keys 32 hoff .. +31 of
+            // every block, so all four waves compute (two per SIMD with two
+            // workgroups per CU) on v_mfma_f32_16x16x32_bf16, whose lane l holds
+            // A[l % 16][8 (l / 16) + j], B[8 (l / 16) + j][l % 16] and
+            // D[4 (l / 16) + i][l % 16].  S^T = K Q^T per 16-key group g: lane
+            // (n = l % 16, q = l / 16) gets row 16 rh + n, keys 16 g + 4 q + i of the
+            // half.  O^T += V^T P^T over the half's 32 keys in the order
+            // k = 8 q + 4 g + i <-> key 16 g + 4 q + i, so the lane's B operand is its
+            // own 8 weights and its A operand two transposed reads of 4 keys.  The two
+            // key halves of a row half merge through LDS at the end.
+            constexpr int KS = D / 32;    // k-steps of S^T
+            constexpr int DB = D / 16;    // 16-dim blocks of O^T
+            const int rh = wave >> 1;
+            const int ln0 = lane_now();
+            const int n16 = ln0 & 15;
+            const int q4 = ln0 >> 4;
+            u32x4 qv[KS];
+            {
+                const int r = min(16 * rh + n16, prows - 1);
+                const char* qp = a.q + (int64_t)(seq0 + r / G) * qstride + (int64_t)(kvh * G + r % G) * D * 2 + q4 * 16;
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) qv[kk] = (*(const u32x4*)(qp + kk * 64) & a.q_and) ^ a.q_xor;
+            }
+            // K operand: row n16 (+16 g + 32 hoff: the swizzle key depends on row % 16),
+            // chunk q4 + 4 kk, i.e. kx16 ^ (kk << 6).  V operand (transposed read,
+            // dims 16 db + 4 (n16 % 4) .. +3 of key row 4 q4 + n16 / 4, +16 for the
+            // second read): chunk 2 db + (n16 % 4) / 2, i.e. vx16 ^ (db << 5).
+            const int kx16 = swz<D>(n16, q4);
+            const int vx16 = swz<D>(4 * q4 + (n16 >> 2), (n16 & 3) >> 1) + ((n16 & 1) << 3);
+            auto scores16 = [&](f32x4 (&st)[2], auto slot) {
+                const PGQA_LDS char* kt = ring + decltype(slot)::value * P::TILEB + 32 * hoff * P::ROWB;
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    st[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int kk = 0; kk < KS; ++kk)
+                        st[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, lds_read_16(kt + 16 * g * P::ROWB + (kx16 ^ (kk << 6)))),
+                            __builtin_bit_cast(bf16x8, qv[kk]), st[g], 0, 0, 0);
+                }
+            };
+            float m16 = kMaxInit, l16 = 0.0f;   // l16: this lane's share of the row sum
+            f32x4 o16[DB];
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o16[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            // The row's token (packed: row / G) for the causal and window limits.
+            const int lrow16 = koff + min(16 * rh + n16, prows - 1) / G;
+            auto step16 = [&](f32x4 (&cur)[2], f32x4 (&nxt)[2], int kr, auto par, auto has_next) {
+                constexpr int PAR = decltype(par)::value;
+                const int j0 = (kb0 + kr) * BN;
+                if ((j0 + BN > Lk) || (a.causal && j0 + BN - 1 > koff) || win > 0) {
+                    // Key 16 g + i of the lane's 4-key run (offset 32 hoff + 4 q4 in the block).
+                    const int base = j0 + 32 * hoff + 4 * q4;
+                    const int lim = (a.causal ? min(lrow16, Lk - 1) : Lk - 1) - base;
+                    const int llim = win > 0 ? lrow16 - win + 1 - base : -(1 << 30);
+#pragma unroll
+                    for (int g = 0; g < 2; ++g)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int off = 16 * g + i;
+                            cur[g][i] = (off <= lim && off >= llim) ? cur[g][i] : -INFINITY;
+                        }
+                }
+                float mt = fmaxf(fmaxf(fmaxf(cur[0][0], cur[0][1]), fmaxf(cur[0][2], cur[0][3])),
+                                 fmaxf(fmaxf(cur[1][0], cur[1][1]), fmaxf(cur[1][2], cur[1][3])));
+                mt = fmaxf(mt, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(mt), 0x401F)));   // lane ^ 16
+                mt = max_xor32(mt) * cs;
+                const bool need = mt > m16 + 8.0f;
+                if (__builtin_expect(__any(need), 0)) {
+                    if (need) {
+                        const float alpha = __builtin_amdgcn_exp2f(m16 - mt);
+                        m16 = mt;
+                        l16 *= alpha;
+#pragma unroll
+                        for (int db = 0; db < DB; ++db)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) o16[db][i] *= alpha;
+                    }
+                }
+                if constexpr (decltype(has_next)::value) scores16(nxt, std::integral_constant<int, 1 - PAR>{});
+                u32x4 pb;
+                {
+                    float p[8];
+#pragma unroll
+                    for (int g = 0; g < 2; ++g)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) p[4 * g + i] = __builtin_amdgcn_exp2f(fmaf(cur[g][i], cs, -m16));
+                    pb = u32x4{pack_bf16x2_rne_hw(p[0], p[1]), pack_bf16x2_rne_hw(p[2], p[3]),
+                               pack_bf16x2_rne_hw(p[4], p[5]), pack_bf16x2_rne_hw(p[6], p[7])};
+                    // The row sum adds the bf16-rounded weights the product uses.
+                    l16 = dot2_bf16(pb.x, ones_bf16x2, l16);
+                    l16 = dot2_bf16(pb.y, ones_bf16x2, l16);
+                    l16 = dot2_bf16(pb.z, ones_bf16x2, l16);
+                    l16 = dot2_bf16(pb.w, ones_bf16x2, l16);
+                }
+                const PGQA_LDS char* vt = ring + (2 + PAR) * P::TILEB + 32 * hoff * P::ROWB;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PGQA_LDS i16x4*)(vt + (vx16 ^ (db << 5))));
+                    const i16x4 hi =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((PGQA_LDS i16x4*)(vt + 16 * P::ROWB + (vx16 ^ (db << 5))));
+                    const u32x4 va = u32x4{__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
+                                           __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y};
+                    o16[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
+                                                                      __builtin_bit_cast(bf16x8, pb), o16[db], 0, 0, 0);
+                }
+            };
+            using J0 = std::integral_constant<int, 0>;
+            using J1 = std::integral_constant<int, 1>;
+            f32x4 sa16[2], sb16[2];
+            wait_vmcnt<0>();
+            __syncthreads();
+            const int kend16 = Lq > 0 && last_kb >= 0 ? min(last_kb, kb1 - 1) - kb0 : -1;
+            if (kend16 >= 0) scores16(sa16, J0{});
+            int kb = 0;
+            for (; kb + 2 <= kend16; kb += 2) {
+                top(kb);
+                step16(sa16, sb16, kb, J0{}, std::true_type{});
+                top(kb + 1);
+                step16(sb16, sa16, kb + 1, J1{}, std::true_type{});
+            }
+            if (kb + 1 == kend16) {
+                top(kb);
+                step16(sa16, sb16, kb, J0{}, std::true_type{});
+                top(kb + 1);
+                step16(sb16, sa16, kb + 1, J1{}, std::false_type{});
+                kb += 2;
+            } else if (kb == kend16) {
+                top(kb);
+                step16(sa16, sb16, kb, J0{}, std::false_type{});
+                kb += 1;
+            }
+            for (; kb < nrel; ++kb) top(kb);
+
+            // Key halves: wave (rh, 1) hands its running max, sum and output to
+            // wave (rh, 0) through the idle ring (value-major, lane-minor).
+            __syncthreads();
+            PGQA_LDS float* xs = (PGQA_LDS float*)ring + rh * (4 * DB + 2) * 64;
+            const int ln = lane_now();
+            if (hoff == 1) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) xs[(4 * db + i) * 64 + ln] = o16[db][i];
+                xs[4 * DB * 64 + ln] = m16;
+                xs[(4 * DB + 1) * 64 + ln] = l16;
+            }
+            __syncthreads();
+            if (hoff == 1 || Lq <= 0) return;
+            {
+                const float m1 = xs[4 * DB * 64 + ln];
+                const float l1 = xs[(4 * DB + 1) * 64 + ln];
+                const float mx = fmaxf(m16, m1);
+                const float a0 = __builtin_amdgcn_exp2f(m16 - mx);
+                const float a1 = __builtin_amdgcn_exp2f(m1 - mx);
+                m16 = mx;
+                l16 = l16 * a0 + l1 * a1;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o16[db][i] = o16[db][i] * a0 + xs[(4 * db + i) * 64 + ln] * a1;
+            }
+            // The row sum over the four lanes of the row (lanes n, n+16, n+32, n+48).
+            l16 += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(l16), 0x401F));
+            l16 += shfl_xor_f32(l16, 32);
+            const int r = 16 * rh + (ln & 15);
+            const int qe = ln >> 4;
+            if (r >= prows) return;
+            const int tok = r / G;
+            const int hq = kvh * G + r % G;
+            if (split) {
+                // Partial rows as the 32-row path writes them: O (dims 16 db + 4 qe ..
+                // +3 from this lane), then (m, l) from the row's first lane.
+                const int64_t prow = slot >= 0 ? (int64_t)slot * BQ + r
+                                               : ((int64_t)(seq0 + tok) * a.num_q_heads + hq) * a.nchunk + chunk;
+                float* po = a.part_o + prow * D + 4 * qe;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) *(f32x4*)(po + 16 * db) = o16[db];
+                if (qe == 0) *(float2*)(a.part_ml + prow * 2) = make_float2(m16, l16);
+                return;
+            }
+            const float inv = l16 > 0.0f ? 1.0f / l16 : 0.0f;
+            char* op = a.out + (int64_t)(seq0 + tok) * qstride + (int64_t)hq * D * 2 + 8 * qe;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                u32x2 w;
+                w.x = pack_bf16x2_rne_hw(o16[db][0] * inv, o16[db][1] * inv);
+                w.y = pack_bf16x2_rne_hw(o16[db][2] * inv, o16[db][3] * inv);
+                *(u32x2*)(op + 32 * db) = w;
+            }
+            return;
+        } else {
         // Blocks kb0 .. kb0 + kend are computed (kend = last_kb - kb0, or -1 for a
         // wave with no rows or no keys); each but the last overlaps the next block's
         // scores.  The two score
@@ -871,6 +1066,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                 *(u32x4*)(a.out + (int64_t)(seq0 + tok) * qstride + (int64_t)hq * D * 2 + c * 16) = val;
             }
         }
+        }   // !P16
     };
 
     if constexpr (PACK) {
@@ -1247,12 +1443,14 @@ __global__ __launch_bounds__(256) void sk_merge_kernel(PrefillArgs a) {
 typedef void (*PrefillFn)(PrefillArgs);
 
 template <int D, bool PAGED, bool Q8>
-PrefillFn pick_hg(int h, bool pack) {
+PrefillFn pick_hg(int h, bool pack, bool p16 = false) {
     if constexpr (!PAGED) {
         return Q8 || pack ? nullptr
                           : (h == 4 ? prefill_kernel<D, 4, false> : (h == 2 ? prefill_kernel<D, 2, false>
                                                                                : prefill_kernel<D, 1, false>));
     } else {
+        if constexpr (!Q8)
+            if (pack && p16) return prefill_kernel<D, 1, true, false, true, true>;
         if (pack) return prefill_kernel<D, 1, true, Q8, true>;
         return h == 4 ? prefill_kernel<D, 4, PAGED, Q8>
                       : (h == 2 ? prefill_kernel<D, 2, PAGED, Q8> : prefill_kernel<D, 1, PAGED, Q8>);
@@ -1267,6 +1465,16 @@ PrefillFn pick_hg(int h, bool pack) {
 // one 32-row tile.
 bool use_pack(int group, int max_q_len) {
     return PGQA_EXT_PACK && max_q_len > 0 && group <= BQ && (int64_t)max_q_len * group <= BQ;
+}
+
+#ifndef PGQA_PACK16
+#define PGQA_PACK16 1
+#endif
+
+// Packed rows in 16-row waves (bf16 pages, more than 16 rows: both row halves of
+// the tile are used, so all four waves compute).
+bool use_pack16(int group, int max_q_len, bool q8) {
+    return PGQA_PACK16 && !q8 && use_pack(group, max_q_len) && (int64_t)max_q_len * group > 16;
 }
 
 #ifndef PGQA_EXT_SK
@@ -1302,18 +1510,18 @@ size_t sk_workspace_bytes(int nw, int head_dim) {
 // Kernel for a head_dim and group size; hg = heads per workgroup (packed: the
 // whole group, one workgroup per KV head).
 template <bool PAGED>
-bool pick(int head_dim, int group, PrefillFn* fn, int* hg, bool q8 = false, bool pack = false) {
+bool pick(int head_dim, int group, PrefillFn* fn, int* hg, bool q8 = false, bool pack = false, bool p16 = false) {
     const int h = group >= 4 ? 4 : group;
     if (group != 1 && group != 2 && group % 4 != 0) return false;
     if (group > 64) return false;
     if ((q8 || pack) && !PAGED) return false;
     *hg = pack ? group : h;
     if (head_dim == 128) {
-        *fn = q8 ? pick_hg<128, PAGED, true>(h, pack) : pick_hg<128, PAGED, false>(h, pack);
+        *fn = q8 ? pick_hg<128, PAGED, true>(h, pack) : pick_hg<128, PAGED, false>(h, pack, p16);
         return true;
     }
     if (head_dim == 64) {
-        *fn = q8 ? pick_hg<64, PAGED, true>(h, pack) : pick_hg<64, PAGED, false>(h, pack);
+        *fn = q8 ? pick_hg<64, PAGED, true>(h, pack) : pick_hg<64, PAGED, false>(h, pack, p16);
         return true;
     }
     return false;
@@ -1391,16 +1599,16 @@ hipError_t launch(PrefillFn fn, PrefillArgs& a, int hg, int group, int head_dim,
     const int64_t wgs = a.sk_nw > 0 ? a.sk_nw : launch_grid(a, hg, group, a.total_tokens);
     if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (log_enabled() && a.sk_nw > 0)
-        log_line("extend B=%d rows=%d Hq=%d Hkv=%d d=%d%s window=%d: packed rows, %d stream-K shares, %s K/V loads",
+        log_line("extend B=%d rows=%d Hq=%d Hkv=%d d=%d%s window=%d: packed rows%s, %d stream-K shares, %s K/V loads",
                  a.batch, a.total_tokens, a.num_q_heads, a.num_kv_heads, head_dim, a.k_scale ? " fp8" : "",
-                 a.window, a.sk_nw, a.kv_nt ? "non-temporal" : "cached");
+                 a.window, a.pack == 2 ? " in 16-row waves" : "", a.sk_nw, a.kv_nt ? "non-temporal" : "cached");
     else if (log_enabled())
         log_line("%s B=%d rows=%d Hq=%d Hkv=%d d=%d%s window=%d: %lld workgroups (%s tile lists, %d query-tile "
-                 "levels, %d pairs per XCD, %d head(s) per wave group), key chunks %d x %d blocks%s, %s K/V loads",
+                 "levels, %d pairs per XCD, %d head(s) per wave group%s), key chunks %d x %d blocks%s, %s K/V loads",
                  a.block_table ? "extend" : "prefill", a.batch, a.total_tokens, a.num_q_heads, a.num_kv_heads,
                  head_dim, a.k_scale ? " fp8" : "", a.window, (long long)wgs, a.dense ? "dense" : "full", a.nqt,
-                 a.pairs_per_xcd, hg, a.nchunk, a.nchunk > 1 ? a.kchunk : 0, a.chunk_lpt ? " (longest first)" : "",
-                 a.kv_nt ? "non-temporal" : "cached");
+                 a.pairs_per_xcd, hg, a.pack == 2 ? ", 16-row waves" : "", a.nchunk, a.nchunk > 1 ? a.kchunk : 0,
+                 a.chunk_lpt ? " (longest first)" : "", a.kv_nt ? "non-temporal" : "cached");
     hipLaunchKernelGGL(fn, dim3((unsigned)wgs), dim3(256), lds_bytes(head_dim, a.k_scale != nullptr), stream, a);
     return hipGetLastError();
 }
@@ -1463,9 +1671,10 @@ hipError_t launch_extend(const ExtendLaunch& L, hipStream_t stream) {
            : !extend_supported(L.head_dim, group, 1 << L.block_size_log2))
         return hipErrorInvalidValue;
     const bool pack = use_pack(group, L.max_q_len);
-    pick<true>(L.head_dim, group, &fn, &hg, q8, pack);
+    const bool p16 = use_pack16(group, L.max_q_len, q8);
+    pick<true>(L.head_dim, group, &fn, &hg, q8, pack, p16);
     PrefillArgs a = {};
-    a.pack = pack ? 1 : 0;
+    a.pack = pack ? (p16 ? 2 : 1) : 0;   // 2: 16-row waves
     a.k_scale = L.k_scale;
     a.v_scale = L.v_scale;
     a.q = (const char*)L.q;

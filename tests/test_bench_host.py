@@ -25,7 +25,7 @@ def _pmc(dirpath: Path, counter: str, rows):
 def test_record_then_read_traffic(tmp_path):
     split = "void pgqa::(anonymous namespace)::decode_split_kernel<2, 128, 4, 1, 2>(pgqa::(anonymous namespace)::DecodeArgs)"
     merge = "void pgqa::(anonymous namespace)::decode_merge_kernel<2, 128, 4>(pgqa::(anonymous namespace)::DecodeArgs)"
-    pre = "void pgqa::(anonymous namespace)::prefill_kernel<128, 4, false, false, false>(pgqa::(anonymous namespace)::PrefillArgs)"
+    pre = "void pgqa::(anonymous namespace)::prefill_kernel<128, 4, false, false, false, false>(pgqa::(anonymous namespace)::PrefillArgs)"
     # two counter instances per dispatch are summed; dispatches are averaged
     _pmc(tmp_path / "fetch_decode", "FETCH_SIZE", [(1, split, 100), (1, split, 50), (2, split, 170), (3, merge, 10)])
     _pmc(tmp_path / "write_decode", "WRITE_SIZE", [(1, split, 3), (2, split, 5), (3, merge, 1)])

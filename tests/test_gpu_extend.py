@@ -206,9 +206,10 @@ def test_key_split_is_deterministic():
 ])
 def test_packed_rows(orc, hq, hkv, qlens, window):
     """Calls whose query tokens times the group fit one 32-row tile run on the
-    packed-rows kernel (rows = (token, head) pairs, two waves splitting each key
-    block): ragged token counts, causal masks between the packed tokens,
-    windows, and long contexts that split into key chunks."""
+    packed-rows kernel (rows = (token, head) pairs; up to 16 rows two waves split
+    each key block, past 16 all four waves compute, 16 rows by a key half each):
+    ragged token counts, causal masks between the packed tokens, windows, and
+    long contexts that split into key chunks."""
     prefix = [3000, 0, 61, 64, 1500, 127 - qlens[5]]
     c = W.make_extend_case(prefix, qlens, hq, hkv, 128, 16, W.BF16, seed=990 + hq + hkv + sum(qlens) + window)
     say(f"extend packed rows {hq}/{hkv} q_lens {qlens} window {window}")

@@ -45,6 +45,12 @@ def _route(monkeypatch, capfd, fn):
     # a window: each pair's units start at its first row's window edge
     ("window", [20000, 500, 7000, 64], [2, 2, 1, 2], 32, 4, 128, 1000),
     ("window inside a block", [20000, 500, 7000, 64], [2, 2, 1, 2], 32, 4, 128, 37),
+    # more than 16 packed rows: 16-row waves (24 rows of G = 12; 8 heads x 4 tokens
+    # under a window; one token of 32 heads at d 64)
+    ("ragged, 16-row waves", [3000, 0, 61, 64, 1500, 120, 9000, 5, 0, 777], [2, 1, 2, 0, 2, 1, 2, 1, 0, 2], 24, 2,
+     128, 0),
+    ("window, 16-row waves", [20000, 500, 7000, 64], [4, 3, 1, 4], 64, 8, 128, 1000),
+    ("d64, 16-row waves", [9000, 33, 2000, 0], [1, 1, 1, 1], 32, 1, 64, 0),
 ])
 def test_streamk_against_oracle(orc, monkeypatch, capfd, name, prefix, qlens, hq, hkv, d, window):
     c = W.make_extend_case(prefix, qlens, hq, hkv, d, 16, W.BF16, seed=4100 + sum(prefix) % 997 + hq + d + window)
@@ -52,6 +58,8 @@ def test_streamk_against_oracle(orc, monkeypatch, capfd, name, prefix, qlens, hq
     dev = DevExtend(c)
     out, err = _route(monkeypatch, capfd, lambda: _extend(dev, c, window))
     assert "stream-K shares" in err, err
+    # More than 16 packed rows (32 heads of one token here) run in 16-row waves.
+    assert ("in 16-row waves" in err) == (max(qlens) * (hq // hkv) > 16), err
     ref = oracle_extend(orc, c, window=window)
     assert_close(to_f64(out), ref, W.BF16, f"stream-K {name}")
     plain = _extend(dev, c, window, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
@@ -117,7 +125,7 @@ def test_streamk_fp8_pages(orc, monkeypatch, capfd):
     say("stream-K fp8")
     out, err = _route(monkeypatch, capfd, lambda: pg.gqa_paged_extend_fp8(
         q, cu_q, dk, dv, ds, dvs, table, ctx, c.max_q_len, c.max_context_len, scale=float(c.scale)))
-    assert "fp8" in err and "stream-K shares" in err, err
+    assert "fp8" in err and "stream-K shares" in err and "16-row" not in err, err
     assert_close(to_f64(out), ref, W.BF16, "fp8 stream-K")
     plain = pg.gqa_paged_extend_fp8(q, cu_q, dk, dv, ds, dvs, table, ctx, c.max_q_len, c.max_context_len,
                                     scale=float(c.scale), workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
@@ -131,7 +139,7 @@ def test_mqa_decode_streamk(orc, monkeypatch, capfd):
     say("MQA decode stream-K")
     out, err = _route(monkeypatch, capfd, lambda: pg.gqa_paged_decode(
         dev.q, dev.kc, dev.vc, dev.table, dev.ctx, c.max_context_len, scale=float(c.scale)))
-    assert "stream-K shares" in err, err
+    assert "stream-K shares" in err and "in 16-row waves" in err, err
     kc = W.nan_pool(c.num_blocks, 1, 32, 128, c.dtype)
     vc = W.nan_pool(c.num_blocks, 1, 32, 128, c.dtype)
     orc.paged_kv_write(c.k, c.v, c.cu_ctx, c.start_pos, c.block_table, kc, vc)
