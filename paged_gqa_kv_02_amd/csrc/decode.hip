@@ -118,9 +118,11 @@ struct DecodeArgs {
     int32_t window;      // > 0: only the newest `window` positions are attended to
     const float* k_scale;   // FP8 pages: row scales [num_blocks, Hkv, block_size]
     const float* v_scale;
+    int32_t seg_mode;       // 1: one workgroup per (sequence, KV head) segment, whole (no partials, no merge)
 };
 
 constexpr int kStages = PGQA_DECODE_STAGES;   // ring depth (tiles) of the split kernel
+constexpr int kSegModeTiles = 2;              // segments this short take one workgroup each, no merge
 constexpr int kRows = PGQA_DECODE_RPT;        // 1 KB wave rows per tile, for K and for V
 constexpr int kRows8 = PGQA_DECODE_RPT8;      // compute rows per tile over FP8 pages
 static_assert(kStages >= 2 && kStages <= 6, "ring depth");
@@ -704,25 +706,38 @@ __global__ __launch_bounds__(64 * W) void decode_split_kernel(DecodeArgs a) {
             else *(float*)dst = 0.0f;
         }
     }
-    if (w >= NW) return;
-    int64_t X = w * total / NW;
-    const int64_t X1 = (w + 1) * total / NW;
-
-    // Segment (b, h) and tile t of the first tile of this share.
-    int b;
-    {
-        int lo = 0, hi = B - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if ((int64_t)Hkv * pref[mid] <= X) lo = mid;
-            else hi = mid - 1;
+    int64_t X, X1;
+    int b, h, t0, tiles_b;
+    if (a.seg_mode) {
+        // One workgroup per segment: workgroup w runs all tiles of segment
+        // (w / Hkv, w % Hkv) as one whole piece (empty ones are zero-filled above).
+        b = blockIdx.x / Hkv;
+        h = blockIdx.x % Hkv;
+        if (b >= B) return;
+        tiles_b = pref[b + 1] - pref[b];
+        if (tiles_b == 0) return;
+        t0 = 0;
+        X = (int64_t)Hkv * pref[b] + (int64_t)h * tiles_b;
+        X1 = X + tiles_b;
+    } else {
+        if (w >= NW) return;
+        X = w * total / NW;
+        X1 = (w + 1) * total / NW;
+        // Segment (b, h) and tile t of the first tile of this share.
+        {
+            int lo = 0, hi = B - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if ((int64_t)Hkv * pref[mid] <= X) lo = mid;
+                else hi = mid - 1;
+            }
+            b = lo;
         }
-        b = lo;
+        tiles_b = pref[b + 1] - pref[b];
+        const int64_t rem = X - (int64_t)Hkv * pref[b];
+        h = (int)(rem / tiles_b);
+        t0 = (int)(rem % tiles_b);
     }
-    int tiles_b = pref[b + 1] - pref[b];
-    int64_t rem = X - (int64_t)Hkv * pref[b];
-    int h = (int)(rem / tiles_b);
-    int t0 = (int)(rem % tiles_b);
 
     const int c = lane % LPT;
     const int tg = lane / LPT;
@@ -1146,7 +1161,17 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     // CU (8-row tiles) against 87-93 us at 4 (16-row tiles).
     if (e.waves == 1) lds = std::max(lds, lds_per_cu() / (L.k_scale ? PGQA_DECODE_LDS_DIV8 : PGQA_DECODE_LDS_DIV));
     int nw = L.num_splits;
-    if (nw <= 0) {
+    // Latency-bound calls (every segment at most kSegModeTiles tiles, no split
+    // count asked for): one workgroup per segment writes its outputs directly,
+    // so the merge kernel is not launched.  (At most kDecodeMaxSplits segments:
+    // the workspace of a call without a split count is laid out for that many
+    // shares.)
+    const int64_t segs = (int64_t)L.batch * L.num_kv_heads;
+    a.seg_mode = (nw <= 0 && segs <= kDecodeMaxSplits &&
+                  ((int64_t)L.max_context_len + e.tt - 1) / e.tt <= kSegModeTiles) ? 1 : 0;
+    if (a.seg_mode) {
+        nw = (int)segs;
+    } else if (nw <= 0) {
         nw = occupancy(e.split, threads, lds) * cu_count();
         if (nw > kDecodeMaxSplits) nw = kDecodeMaxSplits;
     }
@@ -1156,7 +1181,12 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     a.part_ml = a.part_o + slots * (L.num_q_heads / L.num_kv_heads) * L.head_dim;
     a.tile_pref = (int32_t*)(a.part_ml + slots * (L.num_q_heads / L.num_kv_heads) * 2);
 
-    if (log_enabled())
+    if (log_enabled() && a.seg_mode)
+        log_line("decode B=%d Hq=%d Hkv=%d d=%d bs=%d%s window=%d: split-KV kernel, one workgroup per segment "
+                 "(%d x %d waves), LDS %zu B; no merge",
+                 L.batch, L.num_q_heads, L.num_kv_heads, L.head_dim, 1 << L.block_size_log2,
+                 L.k_scale ? " fp8" : (L.is_bf16 ? " bf16" : " f32"), L.window, nw, e.waves, lds);
+    else if (log_enabled())
         log_line("decode B=%d Hq=%d Hkv=%d d=%d bs=%d%s window=%d: split-KV kernel, %d workgroups x %d waves "
                  "(%s splits), LDS %zu B; merge %d workgroups",
                  L.batch, L.num_q_heads, L.num_kv_heads, L.head_dim, 1 << L.block_size_log2,
@@ -1164,7 +1194,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
                  L.num_splits > 0 ? "caller's" : "occupancy", lds, L.batch * L.num_kv_heads * e.merge_slices);
     hipLaunchKernelGGL(e.split, dim3(nw), dim3(threads), lds, stream, a);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    if (err != hipSuccess || a.seg_mode) return err;
     hipLaunchKernelGGL(e.merge, dim3(L.batch * L.num_kv_heads * e.merge_slices), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
