@@ -163,12 +163,19 @@ size_t gqa_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads,
  * Work is split into num_splits equal shares of all (sequence, KV head) tiles
  * (0 = library choice, which fills the GPU); the partials of a sequence cut
  * across shares are merged exactly (log-sum-exp, in share order) by a second
- * kernel.  The result is deterministic for a given num_splits.
+ * kernel.  The result is deterministic for a given num_splits.  With
+ * num_splits = 0 and max_context_len within two of the kernel's tiles (tiles of
+ * 16 tokens for bf16 at head_dim 128, 32 at head_dim 64, 8 for fp32 at head_dim
+ * 128, 64 at head_dim 16; FP8 pages twice the bf16 length), each (sequence, KV
+ * head) gets one workgroup that writes its outputs directly and no merge kernel
+ * runs.
  * With one KV head and Hq a multiple of 32 (bf16, head_dim 64 or 128, block_size
  * >= 8 for d 64 / >= 4 for d 128, window 0, num_splits 0), the call runs on the
  * matrix cores instead: the Hq query heads of a token are the rows of the MFMA
- * tile, the keys are cut into chunks of 1024 merged by log-sum-exp (partials in
- * the same workspace); the result is deterministic as well.
+ * tile (Hq = 32: one tile of 16-row waves), the batch's key blocks are cut into
+ * equal stream-K shares whose partials are merged by log-sum-exp (or, past 4,096
+ * sequences or with a smaller workspace, into chunks of 20 blocks of 64 keys);
+ * partials use the same workspace and the result is deterministic as well.
  *   q            [batch, Hq, d]
  *   k_cache, v_cache [num_blocks, Hkv, block_size, d]
  *   block_table  [batch, max_blocks_per_seq]; entries past ceil(ctx/bs) never read
