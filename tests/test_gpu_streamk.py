@@ -33,6 +33,14 @@ def _route(monkeypatch, capfd, fn):
     return out, capfd.readouterr().err
 
 
+# 1,200 sequences x 2 KV heads: more pairs per scanning thread than it keeps in
+# registers, and shares whose pair range (mostly pairs without query rows) runs
+# past the pairs handed over in LDS.
+_rng = np.random.default_rng(4242)
+_MANY_Q = np.where(_rng.random(1200) < 0.75, 0, _rng.choice([1, 2, 4], 1200)).tolist()
+_MANY_P = _rng.integers(0, 300, 1200).tolist()
+
+
 @pytest.mark.parametrize("name,prefix,qlens,hq,hkv,d,window", [
     # one long sequence: every pair is cut into many pieces (hundreds of shares)
     ("one long pair", [100000 - 1], [1], 32, 1, 128, 0),
@@ -51,6 +59,7 @@ def _route(monkeypatch, capfd, fn):
      128, 0),
     ("window, 16-row waves", [20000, 500, 7000, 64], [4, 3, 1, 4], 64, 8, 128, 1000),
     ("d64, 16-row waves", [9000, 33, 2000, 0], [1, 1, 1, 1], 32, 1, 64, 0),
+    ("many pairs, mostly empty", _MANY_P, _MANY_Q, 16, 2, 128, 0),
 ])
 def test_streamk_against_oracle(orc, monkeypatch, capfd, name, prefix, qlens, hq, hkv, d, window):
     c = W.make_extend_case(prefix, qlens, hq, hkv, d, 16, W.BF16, seed=4100 + sum(prefix) % 997 + hq + d + window)
