@@ -5,13 +5,15 @@ partials that a merge kernel combines.  Checked against the fp64 oracle, against
 the same call without a workspace (one workgroup per pair), and for the route
 taken (PGQA_LOG)."""
 
+import re
+
 import numpy as np
 import pytest
 import torch
 
 import workload as W
 import paged_gqa_kv_02_amd as pg
-from gpu_helpers import DevDecode, DevExtend, assert_close, oracle_extend, say, to_dev, to_f64
+from gpu_helpers import DevDecode, DevExtend, assert_close, oracle_decode, oracle_extend, say, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -154,3 +156,49 @@ def test_mqa_decode_streamk(orc, monkeypatch, capfd):
     orc.paged_kv_write(c.k, c.v, c.cu_ctx, c.start_pos, c.block_table, kc, vc)
     ref = orc.gqa_paged_decode(c.q, kc, vc, c.block_table, c.context_lens, c.scale)
     assert_close(to_f64(out), ref, W.BF16, "MQA decode")
+
+
+def test_one_workspace_across_routes(orc, monkeypatch, capfd):
+    """One workspace buffer shared, in turn, by the one-KV-head stream-K decode, the
+    split-KV decode, the packed stream-K extend and the key-chunk extend, with
+    different inputs each time: whatever a route leaves in the buffer, the next
+    call's outputs still match the oracle (no route depends on what another wrote)."""
+    mqa_a = W.make_decode_case([900, 1, 2500, 64, 0, 5000], 32, 1, 128, 32, W.BF16, seed=811)
+    mqa_b = W.make_decode_case([3000, 17, 640, 129], 32, 1, 128, 32, W.BF16, seed=812)
+    gqa = W.make_decode_case([700, 33, 2100, 4096, 515], 32, 8, 128, 16, W.BF16, seed=813)
+    sk = W.make_extend_case([3000, 0, 61, 1500, 9000], [2, 1, 2, 2, 1], 32, 2, 128, 16, W.BF16, seed=814)
+    chunks = W.make_extend_case([20000, 3000], [96, 40], 32, 8, 128, 16, W.BF16, seed=815)
+    need = max(pg.gqa_paged_decode_workspace_size(6, 32, 1, 128, 0),
+               pg.gqa_paged_decode_workspace_size(5, 32, 8, 128, 5),
+               pg.gqa_paged_extend_workspace_size(sk.batch, int(sk.q_lens.sum()), int(sk.q_lens.max()), 32, 2, 128,
+                                                  int(sk.context_lens.max())),
+               pg.gqa_paged_extend_workspace_size(chunks.batch, int(chunks.q_lens.sum()), int(chunks.q_lens.max()),
+                                                  32, 8, 128, int(chunks.context_lens.max())))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    dm_a, dm_b, dg = DevDecode(mqa_a), DevDecode(mqa_b), DevDecode(gqa)
+    de_sk, de_ch = DevExtend(sk), DevExtend(chunks)
+
+    def dec(dev, c, splits=0):
+        return pg.gqa_paged_decode(dev.q, dev.kc, dev.vc, dev.table, dev.ctx, c.max_context_len,
+                                   scale=float(c.scale), num_splits=splits, workspace=ws)
+
+    steps = [
+        ("MQA stream-K decode A", lambda: dec(dm_a, mqa_a), lambda: oracle_decode(orc, mqa_a), "stream-K shares"),
+        ("split-KV decode", lambda: dec(dg, gqa, 5), lambda: oracle_decode(orc, gqa), None),
+        ("packed stream-K extend", lambda: _extend(de_sk, sk, workspace=ws), lambda: oracle_extend(orc, sk),
+         "stream-K shares"),
+        ("MQA stream-K decode B", lambda: dec(dm_b, mqa_b), lambda: oracle_decode(orc, mqa_b), "stream-K shares"),
+        ("key-chunk extend", lambda: _extend(de_ch, chunks, workspace=ws), lambda: oracle_extend(orc, chunks),
+         "key chunks"),
+        ("MQA stream-K decode A again", lambda: dec(dm_a, mqa_a), lambda: oracle_decode(orc, mqa_a),
+         "stream-K shares"),
+    ]
+    for name, run, ref, route in steps:
+        say(f"shared workspace: {name}")
+        out, err = _route(monkeypatch, capfd, run)
+        if route == "key chunks":
+            m = re.search(r"key chunks (\d+) x", err)
+            assert m and int(m.group(1)) > 1, (name, err)
+        elif route is not None:
+            assert route in err, (name, err)
+        assert_close(to_f64(out), ref(), W.BF16, f"shared workspace: {name}")
