@@ -162,7 +162,9 @@ def test_one_workspace_across_routes(orc, monkeypatch, capfd):
     """One workspace buffer shared, in turn, by the one-KV-head stream-K decode, the
     split-KV decode, the packed stream-K extend and the key-chunk extend, with
     different inputs each time: whatever a route leaves in the buffer, the next
-    call's outputs still match the oracle (no route depends on what another wrote)."""
+    call's outputs still match the oracle (no route depends on what another wrote).
+    The buffer starts as all-ones bytes (NaN floats, -1 ints): no call needs it
+    initialised."""
     mqa_a = W.make_decode_case([900, 1, 2500, 64, 0, 5000], 32, 1, 128, 32, W.BF16, seed=811)
     mqa_b = W.make_decode_case([3000, 17, 640, 129], 32, 1, 128, 32, W.BF16, seed=812)
     gqa = W.make_decode_case([700, 33, 2100, 4096, 515], 32, 8, 128, 16, W.BF16, seed=813)
@@ -174,7 +176,7 @@ def test_one_workspace_across_routes(orc, monkeypatch, capfd):
                                                   int(sk.context_lens.max())),
                pg.gqa_paged_extend_workspace_size(chunks.batch, int(chunks.q_lens.sum()), int(chunks.q_lens.max()),
                                                   32, 8, 128, int(chunks.context_lens.max())))
-    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
     dm_a, dm_b, dg = DevDecode(mqa_a), DevDecode(mqa_b), DevDecode(gqa)
     de_sk, de_ch = DevExtend(sk), DevExtend(chunks)
 
